@@ -1,0 +1,207 @@
+"""Seeded synthetic inputs for MLA / GQLA decode, shared by the tests, the bench and the oracle.
+
+This module only draws numbers and lays them out; it holds none of the method's arithmetic
+(no projection, norm, rotation, softmax or attention). Everything it returns is an *input*:
+weights, token activations, query vectors, sequence lengths, block tables and, for the
+large workloads, the latent-cache rows themselves.
+
+Shapes and value distributions follow the workloads described for this method:
+
+* multi-head latent attention with d_c-wide latents and one shared d_r-wide rotary key per
+  position (Smallem article 13, "L'attention latente : compresser le cache", sections
+  "L'idée : garder un résumé" and "L'obstacle : RoPE"), DeepSeek-sized latents of 512
+  under a 7,168-wide model (same article, "Pourquoi DeepSeek n'observe pas cette perte");
+* the GQLA variant whose up-projections are indexed by g groups (gist.science summary of
+  arXiv 2605.15250, section 2 "Architecture").
+
+Drawing rules: numpy ``default_rng([seed, stream])`` with one stream per tensor, weights
+``N(0, 1/fan_in)``, activations and queries ``N(0, 1)``, RMS gain 1. Floating tensors are
+rounded once, here, to the workload's storage dtype with round-to-nearest-even (torch's
+float32 -> bfloat16 cast), so the GPU and the oracle receive the very same bits.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+# stream ids of default_rng([seed, stream]); one per tensor kind
+S_W_DKV, S_GAMMA, S_W_KR, S_W_UK, S_W_UV, S_X, S_Q_NOPE, S_Q_PE, S_LENS, S_TABLE = range(10)
+S_CACHE_C, S_CACHE_KR, S_Q_ABS, S_X_NEW, S_POS_SHIFT = 10, 11, 12, 13, 14
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One decode workload: shapes, storage dtype and the sequence-length recipe."""
+
+    name: str
+    dtype: str            # "f32" or "bf16": storage type of every float tensor
+    batch: int            # B sequences
+    s_q: int              # query tokens per sequence in one decode step
+    d_model: int          # C
+    n_heads: int          # H (= h_q)
+    d_nope: int           # D, per-head non-rotary query/key width
+    d_v: int              # D_v, per-head value width
+    d_c: int              # latent width (r_kv)
+    d_r: int              # shared rotary key width (d^R_h)
+    n_groups: int         # G; G == H is plain MLA
+    block_size: int       # tokens per paged cache block
+    ctx: int              # context length (upper bound when ctx_min is set)
+    ctx_min: Optional[int] = None   # lengths ~ U[ctx_min, ctx] when set, else all == ctx
+    random_table: bool = False      # random physical block ids, else identity layout
+    n_split: int = 0                # split-K chunks hint (0: let the library choose)
+    spare_blocks: int = 64
+    seed: int = 21000
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def elt(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def row(self) -> int:
+        """Elements in one latent-cache row [c || k_r]."""
+        return self.d_c + self.d_r
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads of this method, seed 21000 + k for workload k.
+CONFIGS = {
+    1: Workload("smallem-fp32", "f32", batch=1, s_q=1, d_model=512, n_heads=8, d_nope=64,
+                d_v=64, d_c=128, d_r=32, n_groups=8, block_size=64, ctx=512, seed=21001),
+    2: Workload("mid-bf16", "bf16", batch=16, s_q=1, d_model=4096, n_heads=32, d_nope=128,
+                d_v=128, d_c=512, d_r=64, n_groups=32, block_size=64, ctx=4096, seed=21002),
+    3: Workload("dsv3-paged", "bf16", batch=64, s_q=1, d_model=7168, n_heads=128, d_nope=128,
+                d_v=128, d_c=512, d_r=64, n_groups=128, block_size=64, ctx=8192,
+                ctx_min=1024, random_table=True, seed=21003),
+    4: Workload("long-128k", "bf16", batch=4, s_q=1, d_model=7168, n_heads=128, d_nope=128,
+                d_v=128, d_c=512, d_r=64, n_groups=128, block_size=64, ctx=131072,
+                n_split=64, seed=21004),
+    5: Workload("gqla-g8", "bf16", batch=32, s_q=1, d_model=7168, n_heads=128, d_nope=128,
+                d_v=128, d_c=512, d_r=64, n_groups=8, block_size=64, ctx=32768,
+                random_table=True, seed=21005),
+}
+
+
+def rng(w: Workload, stream: int, extra: int = 0) -> np.random.Generator:
+    return np.random.default_rng([w.seed, stream, extra])
+
+
+def to_storage(a: np.ndarray, w: Workload) -> torch.Tensor:
+    """float32 numpy array -> CPU tensor in the workload's storage dtype (RNE for bf16)."""
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(w.torch_dtype)
+
+
+def normal(w: Workload, stream: int, shape, std: float = 1.0, extra: int = 0) -> torch.Tensor:
+    a = rng(w, stream, extra).standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return to_storage(a, w)
+
+
+# ----------------------------------------------------------------------------- weights
+def weights(w: Workload, random_gamma: bool = False) -> dict:
+    """W_DKV [C, d_c], gamma [d_c], W_KR [C, d_r], W_UK [d_c, G*D], W_UV [d_c, G*D_v].
+
+    Row-major ``[in, out]``: a row vector times the matrix, as the pages write ``x · W``.
+    """
+    C, G = w.d_model, w.n_groups
+    out = {
+        "w_dkv": normal(w, S_W_DKV, (C, w.d_c), std=C ** -0.5),
+        "w_kr": normal(w, S_W_KR, (C, w.d_r), std=C ** -0.5),
+        "w_uk": normal(w, S_W_UK, (w.d_c, G * w.d_nope), std=w.d_c ** -0.5),
+        "w_uv": normal(w, S_W_UV, (w.d_c, G * w.d_v), std=w.d_c ** -0.5),
+    }
+    if random_gamma:
+        g = 1.0 + 0.25 * rng(w, S_GAMMA).standard_normal(size=(w.d_c,), dtype=np.float32)
+        out["gamma"] = to_storage(g, w)
+    else:
+        out["gamma"] = to_storage(np.ones((w.d_c,), np.float32), w)
+    return out
+
+
+# ----------------------------------------------------------------------------- lengths / paging
+def seq_lens(w: Workload) -> np.ndarray:
+    """int32 [B]: cache length of each sequence after the step's s_q new tokens."""
+    if w.ctx_min is None:
+        return np.full((w.batch,), w.ctx, dtype=np.int32)
+    r = rng(w, S_LENS)
+    return r.integers(w.ctx_min, w.ctx, size=(w.batch,), endpoint=True).astype(np.int32)
+
+
+def block_table(w: Workload, lens: np.ndarray, max_blocks: Optional[int] = None,
+                random: Optional[bool] = None):
+    """Paged layout. Returns (table int32 [B, max_blocks], num_blocks).
+
+    Sequence b owns ceil(L_b / bs) blocks; unused table entries hold -1. With a random table
+    the physical ids are a seeded permutation of all blocks (plus spare blocks nobody owns),
+    otherwise sequence b's blocks are laid out one after the other.
+    """
+    bs = w.block_size
+    need = [(int(L) + bs - 1) // bs for L in lens]
+    mb = max(need) if max_blocks is None else max_blocks
+    assert mb >= max(need)
+    total = sum(need)
+    random = w.random_table if random is None else random
+    num_blocks = total + (w.spare_blocks if random else 0)
+    ids = rng(w, S_TABLE).permutation(num_blocks) if random else np.arange(num_blocks)
+    table = np.full((len(lens), mb), -1, dtype=np.int32)
+    k = 0
+    for b, n in enumerate(need):
+        table[b, :n] = ids[k:k + n]
+        k += n
+    return table, num_blocks
+
+
+# ----------------------------------------------------------------------------- activations
+def tokens(w: Workload, n_tok: int, extra: int = 0) -> torch.Tensor:
+    """x [n_tok, C] ~ N(0, 1): hidden states of positions entering the cache."""
+    return normal(w, S_X, (n_tok, w.d_model), extra=extra)
+
+
+def queries(w: Workload) -> dict:
+    """q_nope [B, s_q, H, D], q_pe [B, s_q, H, d_r] ~ N(0, 1) (not yet rotated)."""
+    shp = (w.batch, w.s_q, w.n_heads)
+    return {"q_nope": normal(w, S_Q_NOPE, shp + (w.d_nope,)),
+            "q_pe": normal(w, S_Q_PE, shp + (w.d_r,))}
+
+
+def query_positions(w: Workload, lens: np.ndarray) -> np.ndarray:
+    """int32 [B, s_q]: position of query i of sequence b is L_b - s_q + i."""
+    i = np.arange(w.s_q, dtype=np.int64)
+    return (lens.astype(np.int64)[:, None] - w.s_q + i[None, :]).astype(np.int32)
+
+
+def absorbed_queries(w: Workload) -> torch.Tensor:
+    """Directly drawn absorbed query rows [B, s_q, H, d_c + d_r] for decode-only tests.
+
+    Latent part ~ N(0, D/d_c) -- the spread of q_nope (N(0,1), width D) times a W_UK drawn
+    N(0, 1/d_c) -- and rotary part ~ N(0, 1), so scores have the spread of real ones.
+    """
+    shp = (w.batch, w.s_q, w.n_heads)
+    lat = rng(w, S_Q_ABS).standard_normal(size=shp + (w.d_c,), dtype=np.float32)
+    lat *= np.float32((w.d_nope / w.d_c) ** 0.5)
+    rot = rng(w, S_Q_ABS, 1).standard_normal(size=shp + (w.d_r,), dtype=np.float32)
+    return to_storage(np.concatenate([lat, rot], axis=-1), w)
+
+
+def cache_pool(w: Workload, num_blocks: int, extra: int = 0) -> torch.Tensor:
+    """A whole paged cache [num_blocks, bs, d_c + d_r] of directly drawn rows ~ N(0, 1).
+
+    Stand-in history for workloads whose full history is too large to push through the
+    append step on the host: an RMS-normalised latent with unit gain has unit mean square,
+    and x · W_KR with x ~ N(0,1), W_KR ~ N(0, 1/C) is N(0, 1) before rotation (a rotation
+    keeps it so), so N(0, 1) rows have the magnitudes of appended rows. Every slot is
+    drawn; which rows belong to which sequence is decided by the block table alone.
+    """
+    a = rng(w, S_CACHE_C, extra).standard_normal(
+        size=(num_blocks, w.block_size, w.row), dtype=np.float32)
+    return to_storage(a, w)
