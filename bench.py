@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark of one absorbed MLA decode step on one MI355X.
+
+A step is one pass of the whole decode path over one batch: append the step's new positions to
+the paged latent cache (W_DKV projection, RMSNorm, RoPE on k_r), carry the queries into latent
+space (W_UK absorption + RoPE), the split-K attention core over [c || k_r], and the log-sum-exp
+merge with the W_UV projection. Inputs are seeded synthetic tensors already resident in HBM.
+
+Prints one JSON line: tokens/s (query tokens per second, one layer), the dominant kernel's
+roofline (the split-K core, timed with HIP events on the stream it runs on) and the CPU
+oracle's throughput on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+SPLITK_SRC = os.path.join(ROOT, "mla_latent_kv_21_amd", "csrc", "decode_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_traffic.json")
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(SPLITK_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(config: int):
+    """HBM bytes per launch of the split-K kernel from committed rocprofv3 counter runs, or
+    None when they were taken on different kernel source or another workload."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha256_16") != kernel_hash() or t.get("config") != config:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, lens, budget_s: float):
+    """The oracle's reconstructed-K/V decode timed on host cores, head by head on one sequence
+    at its full context, until the time budget is spent; scaled to the whole step."""
+    import oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count()))
+    b = int(np.argmax(lens))
+    L = int(lens[b])
+    ws = w.replace(batch=1)
+    nb = (L + w.block_size - 1) // w.block_size
+    rows = O.f64(W.cache_pool(ws, nb, extra=99).reshape(nb * w.block_size, w.row)[:L])
+    q = W.queries(ws.replace(s_q=w.s_q))
+    qpos = W.query_positions(ws.replace(s_q=w.s_q), np.array([L], np.int32))
+    wts = W.weights(ws)
+    heads = list(range(0, w.n_heads, max(1, w.n_heads // 64)))
+    done, t0 = 0, time.perf_counter()
+    for h in heads:
+        O.decode_reconstructed(q["q_nope"][0], q["q_pe"][0], qpos[0], rows, wts["w_uk"],
+                               wts["w_uv"], w.n_groups, w.d_c, w.d_v, 10000.0, heads=[h])
+        done += 1
+        if time.perf_counter() - t0 > budget_s and done >= 2:
+            break
+    t = time.perf_counter() - t0
+    # per query token of one sequence at length L, all heads; the step holds B such tokens
+    per_seq_step = t * w.n_heads / done
+    scale = float(np.sum(lens)) / L          # other sequences, by their length
+    step_s = per_seq_step * scale
+    return {"value": w.batch * w.s_q / step_s, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"reconstructed-K/V oracle (f64) on sequence {b} (L={L}), {done} of "
+                      f"{w.n_heads} heads, {t:.1f} s; scaled by heads and by total length"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=4,
+                    help="workload index (default 4: H=128, d_c=512, 4 x 131,072 context)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is a design note, not part of this build)", flush=True)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    from mla_latent_kv_21_amd import accounting as A
+    from mla_latent_kv_21_amd import binding as M
+
+    if not os.path.exists(M.LIB_PATH):
+        from mla_latent_kv_21_amd.build import build
+        build()
+    dev = torch.device("cuda:0")
+    w = W.CONFIGS[args.config]
+    lens = W.seq_lens(w)
+    table, nb = W.block_table(w, lens)
+    B, s_q, H = w.batch, w.s_q, w.n_heads
+    d = M.dims_of(w)
+    g = lambda a: (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
+
+    cache = W.cache_pool_device(w, nb, dev)
+    wts = {k: g(v) for k, v in W.weights(w).items()}
+    x_new = g(W.tokens(w, B * s_q, extra=1))
+    seq_idx = g(np.repeat(np.arange(B, dtype=np.int32), s_q))
+    qpos_np = W.query_positions(w, lens)
+    pos_new = g(qpos_np.reshape(-1))
+    q = {k: g(v) for k, v in W.queries(w).items()}
+    q_pos = g(qpos_np)
+    tab, lens_d = g(table), g(lens)
+    q_abs = torch.empty(B, s_q, H, w.row, dtype=w.torch_dtype, device=dev)
+    out = torch.empty(B, s_q, H, w.d_v, dtype=w.torch_dtype, device=dev)
+    lse = torch.empty(B, s_q, H, dtype=torch.float32, device=dev)
+    ns = w.n_split or M.mla_auto_split(d, B, s_q, table.shape[1])
+    ws = torch.empty(M.mla_decode_workspace_bytes(d, B, s_q, ns, table.shape[1]),
+                     dtype=torch.uint8, device=dev)
+    ws_app = torch.empty(max(M.mla_cache_append_workspace_bytes(d, B * s_q), 256),
+                         dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    n_steps = args.steps
+    ev_core = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_steps)]
+
+    def step(i=None):
+        M.mla_cache_append(d, x_new, seq_idx, pos_new, wts["w_dkv"], wts["gamma"], wts["w_kr"],
+                           tab, nb, cache, workspace=ws_app)
+        M.mla_absorb_q(d, q["q_nope"], q["q_pe"], q_pos, wts["w_uk"], q_abs)
+        if i is not None:
+            ev_core[i][0].record(stream)
+        M.mla_decode_splitk(d, q_abs, cache, tab, lens_d, ns, ws)
+        if i is not None:
+            ev_core[i][1].record(stream)
+        M.mla_decode_merge(d, q_abs, cache, tab, lens_d, wts["w_uv"], out, lse, ns, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(n_steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / n_steps
+    core_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_core]))
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError("non-finite decode output")
+
+    tr = A.decode_traffic(lens, s_q, H, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt)
+    core_bytes = tr["core_bytes"]
+    achieved = core_bytes / (core_ms * 1e-3) / 1e9
+    traffic = measured_traffic(args.config)
+    tokens_per_s = B * s_q / (ms_step * 1e-3)
+    rec = {
+        "metric": "MLA decode tokens/s, latent-cache GB/s & % roofline (H=128, d_c=512)",
+        "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": n_steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded latent cache and weights, shapes of the workload)",
+        "config": {"workload": w.name, "batch": B, "s_q": s_q, "heads": H, "groups": w.n_groups,
+                   "d_c": w.d_c, "d_r": w.d_r, "context": int(lens.max()),
+                   "context_total": int(lens.sum()), "block_size": w.block_size,
+                   "n_split": ns, "d_model": w.d_model},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "decode_mfma_kernel (split-K core)", "launch_ms": core_ms,
+                     "algorithmic_bytes_per_launch": core_bytes},
+        "latent_cache_GBps": tr["cache_bytes"] / (core_ms * 1e-3) / 1e9,
+        "step_latent_cache_GBps": tr["cache_bytes"] / (ms_step * 1e-3) / 1e9,
+        "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, lens, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

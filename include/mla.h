@@ -1,0 +1,216 @@
+/*
+ * mla.h -- C ABI of libmla.so: multi-head latent attention (MLA) decode over a compressed,
+ * paged latent KV cache, and the grouped GQLA variant, on AMD MI355X (gfx950).
+ *
+ * The operations follow these pages:
+ *  [Smallem]  smallbard.com, Smallem article 13, "L'attention latente : compresser le cache"
+ *  [KV-cache] mkdocs.reaper.mx, DeepSeek-V4.1-Flash, "Le cache clé-valeur"
+ *  [Slides]   cours.spawnkit.ai, session 18 slides, "Cache KV, mémoire récurrente, MLA et bas rang"
+ *  [GQLA]     gist.science summary of arXiv 2605.15250, "GQLA – Attention Latente par Groupes
+ *             de Requêtes pour le Décodage Adaptatif au Matériel"
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Notation: C = d_model, H = n_heads (h_q), D = d_nope (d_h), D_v = d_v, d_c = latent width
+ *    (r_kv), d_r = shared rotary key width (d^R_h), G = n_groups, bs = block_size.
+ *  - Weights are row-major [in, out]: a row vector multiplies them from the left, as the pages
+ *    write x · W. Group g of W_UK / W_UV is columns [g*D, (g+1)*D) / [g*D_v, (g+1)*D_v);
+ *    head h belongs to group h / (H / G) ([GQLA] section 2, "Architecture"). G == H is MLA.
+ *  - Latent cache: [num_blocks, bs, d_c + d_r]; row = [c || k_r] with k_r already rotated.
+ *    Position p of sequence b lives in slot block_table[b*max_blocks + p/bs]*bs + p%bs.
+ *  - Expanded GQA cache: [num_blocks, bs, G*D + G*D_v + d_r]; row =
+ *    [K_0 .. K_{G-1} || V_0 .. V_{G-1} || k_r], same block table as the latent cache.
+ *  - RoPE: pair (2j, 2j+1) of a d_r-wide vector turns by pos * rope_base^(-2j/d_r), the
+ *    angle formed in double precision; positions are 0-based.
+ *  - A step appends s_q positions per sequence first; seq_lens[b] = L_b counts them, and query
+ *    i (0-based) of sequence b sits at position L_b - s_q + i and sees positions 0 .. itself.
+ *  - Every float tensor (activations, weights, caches, q_abs, out) has type dims->dtype; all
+ *    arithmetic accumulates in fp32; bf16 results round to nearest, ties to even. lse is fp32.
+ *  - Ownership: the caller owns every buffer (device memory unless noted) and the stream.
+ *    The library allocates nothing, frees nothing, never synchronises and keeps no state, so
+ *    calls are reentrant. Work is enqueued on `stream` (NULL = the default stream) and the
+ *    call returns at once. Device pointers must be 16-byte aligned.
+ *  - Errors: the status is decided on the host before anything is enqueued, except
+ *    MLA_ERR_HIP, which reports a failed launch. Nothing is printed and nothing aborts.
+ *    Integer arrays that live on the device (block tables, positions, lengths) are not read on
+ *    the host: kernels clamp what they use to the buffers they were given (a block id outside
+ *    [0, num_blocks), or a position past max_blocks*bs, leaves that position out), so a bad
+ *    table cannot make them touch memory out of bounds. mla_validate_block_table() checks a
+ *    host copy for callers who want the error instead.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1 } mla_dtype;
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,        /* a required pointer is NULL */
+  MLA_ERR_SHAPE = -2,       /* a dimension is out of range or inconsistent */
+  MLA_ERR_DTYPE = -3,       /* dims->dtype is not an mla_dtype */
+  MLA_ERR_RANGE = -4,       /* a count (batch, s_q, n_tok, n_split, ...) is out of range */
+  MLA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the *_workspace_bytes() size */
+  MLA_ERR_ALIGN = -6,       /* a device pointer is not 16-byte aligned */
+  MLA_ERR_HIP = -7,         /* a kernel launch failed */
+  MLA_ERR_BLOCK_TABLE = -8  /* mla_validate_block_table(): bad or shared block id */
+} mla_status;
+
+/* dims->flags bits */
+#define MLA_FLAG_GENERIC_KERNELS 1 /* use the portable kernels even where an MFMA kernel fits */
+
+/* Largest split count mla_decode / gqla_decode accept. */
+#define MLA_MAX_SPLIT 256
+
+typedef struct mla_dims {
+  int32_t d_model;     /* C: width of the hidden states appended to the cache */
+  int32_t n_heads;     /* H: query heads */
+  int32_t d_nope;      /* D: per-head content (non-rotary) query/key width */
+  int32_t d_v;         /* D_v: per-head value width */
+  int32_t d_c;         /* d_c: latent width */
+  int32_t d_r;         /* d_r: shared rotary key width (even, may be 0) */
+  int32_t n_groups;    /* G: groups indexing W_UK / W_UV; divides H; G == H is plain MLA */
+  int32_t block_size;  /* bs: positions per cache block */
+  int32_t dtype;       /* mla_dtype of every float tensor */
+  int32_t flags;       /* MLA_FLAG_* */
+  float rope_base;     /* RoPE base, e.g. 10000 */
+  float rms_eps;       /* epsilon of the latent RMSNorm */
+  float softmax_scale; /* 0 selects 1/sqrt(D + d_r) */
+} mla_dims;
+
+/*
+ * mla_cache_append -- write the cache row of n_tok new positions ([Smallem] "L'idée : garder
+ * un résumé", "L'obstacle : RoPE" and the cache extension in "Le code"; [Slides] "Carte du
+ * mécanisme"):
+ *     c   = RMSNorm(x · W_DKV) * gamma,  RMSNorm(y) = y / sqrt(mean_j y_j^2 + rms_eps)
+ *     k_r = RoPE(x · W_KR, pos)
+ *     latent_cache[slot(seq_idx[n], pos[n])] = [c || k_r]
+ *  x [n_tok, C]; seq_idx, pos int32 [n_tok] (device); w_dkv [C, d_c]; rms_gamma [d_c];
+ *  w_kr [C, d_r]; block_table int32 [batch, max_blocks] (device); latent_cache as above.
+ *  Every new position must have its own slot (two tokens writing one slot race).
+ *  workspace: at least mla_cache_append_workspace_bytes(dims, n_tok) bytes of device memory.
+ *  n_tok == 0 enqueues nothing and returns MLA_OK. Tokens whose slot falls outside the cache
+ *  (negative id, id >= num_blocks, position >= max_blocks*bs, seq_idx outside [0, batch)) are
+ *  not written.
+ */
+size_t mla_cache_append_workspace_bytes(const mla_dims* dims, int32_t n_tok);
+mla_status mla_cache_append(const mla_dims* dims, int32_t n_tok, const void* x,
+                            const int32_t* seq_idx, const int32_t* pos, const void* w_dkv,
+                            const void* rms_gamma, const void* w_kr, const int32_t* block_table,
+                            int32_t batch, int32_t max_blocks, int32_t num_blocks,
+                            void* latent_cache, void* workspace, size_t ws_bytes,
+                            hipStream_t stream);
+
+/*
+ * mla_absorb_q -- carry the queries into latent space once ([Smallem] "Ce que DeepSeek fait de
+ * plus": q · (c · W) = (q · W^T) · c; [GQLA] "Chemin MQA-Absorbé" with group-indexed W_UK):
+ *     q_abs[b,i,h] = [ q_nope[b,i,h] · W_UK[:, g(h)]^T  ||  RoPE(q_pe[b,i,h], q_pos[b,i]) ]
+ *  q_nope [batch, s_q, H, D]; q_pe [batch, s_q, H, d_r]; q_pos int32 [batch, s_q] (device);
+ *  w_uk [d_c, G*D]; q_abs [batch, s_q, H, d_c + d_r] (output).
+ */
+mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_nope,
+                        const void* q_pe, const int32_t* q_pos, const void* w_uk, void* q_abs,
+                        hipStream_t stream);
+
+/*
+ * mla_decode -- absorbed decode over the latent cache ([Smallem] "Ce que DeepSeek fait de plus";
+ * [GQLA] "Chemin MQA-Absorbé"): for every sequence b, query i and head h,
+ *     z_t = scale * (q_abs[b,i,h] . row_t)          for visible positions t
+ *     o   = sum_t softmax(z)_t * c_t                (the latent part of the rows)
+ *     out[b,i,h] = o · W_UV[:, g(h)],   lse[b,i,h] = log sum_t exp(z_t)
+ *  The history is split into n_split chunks per (sequence, query) that are reduced
+ *  independently and merged by their log-sum-exp; the result does not depend on n_split
+ *  beyond rounding.
+ *  q_abs [batch, s_q, H, d_c + d_r]; block_table int32 [batch, max_blocks], seq_lens int32
+ *  [batch] (device; s_q <= L_b <= max_blocks*bs expected: a query with no visible position
+ *  gets out = 0 and lse = -inf); w_uv [d_c, G*D_v]; out [batch, s_q, H, D_v];
+ *  lse fp32 [batch, s_q, H] or NULL.
+ *  n_split: 1 .. MLA_MAX_SPLIT, or 0 to let the library pick from batch, s_q and max_blocks.
+ *  workspace: mla_decode_workspace_bytes(dims, batch, s_q, n_split, max_blocks) bytes.
+ */
+size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                  int32_t n_split, int32_t max_blocks);
+mla_status mla_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_abs,
+                      const void* latent_cache, int32_t num_blocks, const int32_t* block_table,
+                      int32_t max_blocks, const int32_t* seq_lens, const void* w_uv,
+                      int32_t n_split, void* workspace, size_t ws_bytes, void* out, float* lse,
+                      hipStream_t stream);
+
+/*
+ * The two halves of mla_decode, for callers that time or schedule them separately; calling
+ * mla_decode_splitk then mla_decode_merge on one stream with the same arguments and workspace
+ * is exactly mla_decode.
+ *  mla_decode_splitk -- every (split, query, sequence) reduces its positions and writes its
+ *    partial (o / l, log2-domain lse) into the workspace.
+ *  mla_decode_merge -- merges the partials of each (sequence, query, head) by their
+ *    log-sum-exp and applies the head's group of W_UV; q_abs, cache, table and lengths are
+ *    read again only for splits the matrix-core kernel flagged for exact recomputation
+ *    (scores that outgrew its fixed per-head reference by 2^64).
+ */
+mla_status mla_decode_splitk(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_abs,
+                             const void* latent_cache, int32_t num_blocks,
+                             const int32_t* block_table, int32_t max_blocks,
+                             const int32_t* seq_lens, int32_t n_split, void* workspace,
+                             size_t ws_bytes, hipStream_t stream);
+mla_status mla_decode_merge(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_abs,
+                            const void* latent_cache, int32_t num_blocks,
+                            const int32_t* block_table, int32_t max_blocks,
+                            const int32_t* seq_lens, const void* w_uv, int32_t n_split,
+                            void* workspace, size_t ws_bytes, void* out, float* lse,
+                            hipStream_t stream);
+
+/*
+ * gqla_expand -- expand latent rows into the GQA cache once ([GQLA] "Chemin GQA"):
+ *     gqa_row = [c · W_UK[:, 0] .. c · W_UK[:, G-1] || c · W_UV[:, 0] .. c · W_UV[:, G-1] || k_r]
+ *  for positions start_pos[b] .. seq_lens[b]-1 of every sequence (start_pos NULL: from 0).
+ *  The GQA cache shares the latent cache's block table and block size.
+ */
+mla_status gqla_expand(const mla_dims* dims, int32_t batch, const void* latent_cache,
+                       int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                       const int32_t* seq_lens, const int32_t* start_pos, const void* w_uk,
+                       const void* w_uv, void* gqa_cache, hipStream_t stream);
+
+/*
+ * gqla_decode -- standard grouped-query decode over the expanded cache ([GQLA] "Chemin GQA"):
+ * head h of group g compares [q_nope ; RoPE(q_pe, q_pos)] with [K_g ; k_r] and averages V_g.
+ *  q_nope [batch, s_q, H, D]; q_pe [batch, s_q, H, d_r]; q_pos int32 [batch, s_q] (device);
+ *  out [batch, s_q, H, D_v]; lse as in mla_decode; seq_lens and n_split as in mla_decode.
+ *  workspace: gqla_decode_workspace_bytes(dims, batch, s_q, n_split, max_blocks) bytes.
+ */
+size_t gqla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                   int32_t n_split, int32_t max_blocks);
+mla_status gqla_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_nope,
+                       const void* q_pe, const int32_t* q_pos, const void* gqa_cache,
+                       int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                       const int32_t* seq_lens, int32_t n_split, void* workspace,
+                       size_t ws_bytes, void* out, float* lse, hipStream_t stream);
+
+/* Split count n_split = 0 resolves to, for these sizes. */
+int32_t mla_auto_split(const mla_dims* dims, int32_t batch, int32_t s_q, int32_t max_blocks);
+
+/* Static, NUL-terminated description of a status. */
+const char* mla_status_string(mla_status status);
+
+/*
+ * mla_validate_block_table -- host-side check of a block table (host memory): every position
+ * 0 .. host_seq_lens[b]-1 of every sequence maps to a block id in [0, num_blocks), no block is
+ * used by two (sequence, block index) pairs, and host_seq_lens[b] <= max_blocks*bs.
+ * Returns MLA_OK, MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_RANGE or MLA_ERR_BLOCK_TABLE.
+ */
+mla_status mla_validate_block_table(const mla_dims* dims, const int32_t* host_table,
+                                    int32_t batch, int32_t max_blocks,
+                                    const int32_t* host_seq_lens, int32_t num_blocks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

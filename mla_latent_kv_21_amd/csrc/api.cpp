@@ -1,0 +1,303 @@
+// C ABI of libmla (declared and documented in include/mla.h): host-side validation, workspace
+// sizing and dispatch to the kernel launchers. Nothing here allocates, synchronises or prints.
+#include <math.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+#include "mla.h"
+
+namespace {
+
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+mla_status check_dims(const mla_dims* d) {
+  if (d == nullptr) return MLA_ERR_NULL;
+  if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return MLA_ERR_DTYPE;
+  if (d->d_model < 1 || d->n_heads < 1 || d->d_nope < 1 || d->d_v < 1 || d->d_c < 1 ||
+      d->d_r < 0 || (d->d_r & 1) || d->n_groups < 1 || d->block_size < 1)
+    return MLA_ERR_SHAPE;
+  if (d->n_heads % d->n_groups != 0) return MLA_ERR_SHAPE;
+  // LDS budgets of the portable kernels: query row + value row + 2 KiB of per-pass state,
+  // and 16 merged latent rows in the combine.
+  if (d->d_c + d->d_r > 4096 || d->d_nope + d->d_r > 4096 || d->d_v > 1024 || d->d_c > 1024 ||
+      d->d_nope > 1024)
+    return MLA_ERR_SHAPE;
+  if (!(d->rope_base > 0.f) || !(d->rms_eps >= 0.f) || !(d->softmax_scale >= 0.f) ||
+      !isfinite(d->rope_base) || !isfinite(d->softmax_scale))
+    return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+int resolve_split(const mla_dims& d, int batch, int s_q, int max_blocks) {
+  // Aim at one workgroup per CU (256 CUs), with at least kSplitAlign positions per split.
+  const int rows = batch * s_q;
+  int n = cdiv(256, rows > 0 ? rows : 1);
+  const int max_by_len = cdiv(max_blocks * d.block_size, mla::kSplitAlign);
+  if (n > max_by_len) n = max_by_len;
+  if (n > 64) n = 64;
+  return n < 1 ? 1 : n;
+}
+
+mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "a dimension is out of range or inconsistent";
+    case MLA_ERR_DTYPE: return "unknown dtype";
+    case MLA_ERR_RANGE: return "a count is out of range";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case MLA_ERR_HIP: return "a kernel launch failed";
+    case MLA_ERR_BLOCK_TABLE: return "block table holds a bad or shared block id";
+  }
+  return "unknown status";
+}
+
+int32_t mla_auto_split(const mla_dims* dims, int32_t batch, int32_t s_q, int32_t max_blocks) {
+  if (check_dims(dims) != MLA_OK || batch < 1 || s_q < 1 || max_blocks < 1) return 0;
+  return resolve_split(*dims, batch, s_q, max_blocks);
+}
+
+size_t mla_cache_append_workspace_bytes(const mla_dims* dims, int32_t n_tok) {
+  if (check_dims(dims) != MLA_OK || n_tok < 0) return 0;
+  const mla::AppendPlan p = mla::append_plan(*dims, n_tok);
+  const size_t n = n_tok < 2048 ? n_tok : 2048;  // tokens per pass
+  return static_cast<size_t>(p.n_ksplit) * n * (dims->d_c + dims->d_r) * sizeof(float);
+}
+
+mla_status mla_cache_append(const mla_dims* dims, int32_t n_tok, const void* x,
+                            const int32_t* seq_idx, const int32_t* pos, const void* w_dkv,
+                            const void* rms_gamma, const void* w_kr, const int32_t* block_table,
+                            int32_t batch, int32_t max_blocks, int32_t num_blocks,
+                            void* latent_cache, void* workspace, size_t ws_bytes,
+                            hipStream_t stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_tok < 0 || batch < 0 || max_blocks < 1 || num_blocks < 1) return MLA_ERR_RANGE;
+  if (n_tok == 0) return MLA_OK;
+  if (!x || !seq_idx || !pos || !w_dkv || !rms_gamma || !block_table || !latent_cache ||
+      (dims->d_r > 0 && !w_kr))
+    return MLA_ERR_NULL;
+  if (batch < 1) return MLA_ERR_RANGE;
+  if (static_cast<int64_t>(max_blocks) * dims->block_size > INT32_MAX) return MLA_ERR_RANGE;
+  if (!aligned16(x) || !aligned16(w_dkv) || !aligned16(rms_gamma) ||
+      (w_kr && !aligned16(w_kr)) || !aligned16(latent_cache) || !aligned16(block_table))
+    return MLA_ERR_ALIGN;
+  const size_t need = mla_cache_append_workspace_bytes(dims, n_tok);
+  if (workspace == nullptr || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_append(*dims, n_tok, x, seq_idx, pos, w_dkv, rms_gamma, w_kr,
+                                       block_table, batch, max_blocks, num_blocks, latent_cache,
+                                       workspace, stream));
+}
+
+mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_nope,
+                        const void* q_pe, const int32_t* q_pos, const void* w_uk, void* q_abs,
+                        hipStream_t stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || s_q < 1) return MLA_ERR_RANGE;
+  if (batch == 0) return MLA_OK;
+  if (!q_nope || !q_pos || !w_uk || !q_abs || (dims->d_r > 0 && !q_pe)) return MLA_ERR_NULL;
+  if (static_cast<int64_t>(batch) * s_q > 65535 * 16) return MLA_ERR_RANGE;
+  if (!aligned16(q_nope) || (q_pe && !aligned16(q_pe)) || !aligned16(w_uk) || !aligned16(q_abs))
+    return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_absorb(*dims, batch, s_q, q_nope, q_pe, q_pos, w_uk, q_abs, stream));
+}
+
+size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                  int32_t n_split, int32_t max_blocks) {
+  if (check_dims(dims) != MLA_OK || batch < 1 || s_q < 1 || max_blocks < 1 || n_split < 0 ||
+      n_split > MLA_MAX_SPLIT)
+    return 0;
+  const int ns = n_split == 0 ? resolve_split(*dims, batch, s_q, max_blocks) : n_split;
+  return mla::partials_bytes(batch, s_q, dims->n_heads, ns, dims->d_c);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared validation of the decode calls; on success *ns holds the resolved split count.
+mla_status check_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_abs,
+                        const void* latent_cache, int32_t num_blocks, const int32_t* block_table,
+                        int32_t max_blocks, const int32_t* seq_lens, int32_t n_split,
+                        const void* workspace, size_t ws_bytes, int* ns) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || s_q < 1 || max_blocks < 1 || num_blocks < 1 || n_split < 0 ||
+      n_split > MLA_MAX_SPLIT)
+    return MLA_ERR_RANGE;
+  if (batch > 65535 || s_q > 65535 || static_cast<int64_t>(batch) * s_q > 65535 * 16)
+    return MLA_ERR_RANGE;
+  if (static_cast<int64_t>(max_blocks) * dims->block_size > INT32_MAX) return MLA_ERR_RANGE;
+  if (batch == 0) return MLA_OK;
+  if (!q_abs || !latent_cache || !block_table || !seq_lens) return MLA_ERR_NULL;
+  if (!aligned16(q_abs) || !aligned16(latent_cache)) return MLA_ERR_ALIGN;
+  *ns = n_split == 0 ? resolve_split(*dims, batch, s_q, max_blocks) : n_split;
+  const size_t need = mla::partials_bytes(batch, s_q, dims->n_heads, *ns, dims->d_c);
+  if (workspace == nullptr || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_splitk(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_abs,
+                             const void* latent_cache, int32_t num_blocks,
+                             const int32_t* block_table, int32_t max_blocks,
+                             const int32_t* seq_lens, int32_t n_split, void* workspace,
+                             size_t ws_bytes, hipStream_t stream) {
+  int ns = 0;
+  const mla_status st = check_decode(dims, batch, s_q, q_abs, latent_cache, num_blocks,
+                                     block_table, max_blocks, seq_lens, n_split, workspace,
+                                     ws_bytes, &ns);
+  if (st != MLA_OK || batch == 0) return st;
+  return hip_status(mla::launch_decode_splitk(*dims, batch, s_q, q_abs, latent_cache, num_blocks,
+                                              block_table, max_blocks, seq_lens, ns, workspace,
+                                              stream));
+}
+
+mla_status mla_decode_merge(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_abs,
+                            const void* latent_cache, int32_t num_blocks,
+                            const int32_t* block_table, int32_t max_blocks,
+                            const int32_t* seq_lens, const void* w_uv, int32_t n_split,
+                            void* workspace, size_t ws_bytes, void* out, float* lse,
+                            hipStream_t stream) {
+  int ns = 0;
+  const mla_status st = check_decode(dims, batch, s_q, q_abs, latent_cache, num_blocks,
+                                     block_table, max_blocks, seq_lens, n_split, workspace,
+                                     ws_bytes, &ns);
+  if (st != MLA_OK || batch == 0) return st;
+  if (!w_uv || !out) return MLA_ERR_NULL;
+  if (!aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_decode_merge(*dims, batch, s_q, q_abs, latent_cache, num_blocks,
+                                             block_table, max_blocks, seq_lens, w_uv, ns,
+                                             workspace, out, lse, stream));
+}
+
+mla_status mla_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_abs,
+                      const void* latent_cache, int32_t num_blocks, const int32_t* block_table,
+                      int32_t max_blocks, const int32_t* seq_lens, const void* w_uv,
+                      int32_t n_split, void* workspace, size_t ws_bytes, void* out, float* lse,
+                      hipStream_t stream) {
+  int ns = 0;
+  mla_status st = check_decode(dims, batch, s_q, q_abs, latent_cache, num_blocks, block_table,
+                               max_blocks, seq_lens, n_split, workspace, ws_bytes, &ns);
+  if (st != MLA_OK || batch == 0) return st;
+  if (!w_uv || !out) return MLA_ERR_NULL;
+  if (!aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  st = hip_status(mla::launch_decode_splitk(*dims, batch, s_q, q_abs, latent_cache, num_blocks,
+                                            block_table, max_blocks, seq_lens, ns, workspace,
+                                            stream));
+  if (st != MLA_OK) return st;
+  return hip_status(mla::launch_decode_merge(*dims, batch, s_q, q_abs, latent_cache, num_blocks,
+                                             block_table, max_blocks, seq_lens, w_uv, ns,
+                                             workspace, out, lse, stream));
+}
+
+mla_status gqla_expand(const mla_dims* dims, int32_t batch, const void* latent_cache,
+                       int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                       const int32_t* seq_lens, const int32_t* start_pos, const void* w_uk,
+                       const void* w_uv, void* gqa_cache, hipStream_t stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || max_blocks < 1 || num_blocks < 1) return MLA_ERR_RANGE;
+  if (batch == 0) return MLA_OK;
+  if (batch > 65535) return MLA_ERR_RANGE;
+  if (static_cast<int64_t>(max_blocks) * dims->block_size > INT32_MAX) return MLA_ERR_RANGE;
+  if (!latent_cache || !block_table || !seq_lens || !w_uk || !w_uv || !gqa_cache)
+    return MLA_ERR_NULL;
+  if (!aligned16(latent_cache) || !aligned16(w_uk) || !aligned16(w_uv) || !aligned16(gqa_cache))
+    return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_expand(*dims, batch, latent_cache, num_blocks, block_table,
+                                       max_blocks, seq_lens, start_pos, w_uk, w_uv, gqa_cache,
+                                       stream));
+}
+
+size_t gqla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                   int32_t n_split, int32_t max_blocks) {
+  if (check_dims(dims) != MLA_OK || batch < 1 || s_q < 1 || max_blocks < 1 || n_split < 0 ||
+      n_split > MLA_MAX_SPLIT)
+    return 0;
+  const int ns = n_split == 0 ? resolve_split(*dims, batch, s_q, max_blocks) : n_split;
+  return mla::partials_bytes(batch, s_q, dims->n_heads, ns, dims->d_v);
+}
+
+mla_status gqla_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_nope,
+                       const void* q_pe, const int32_t* q_pos, const void* gqa_cache,
+                       int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                       const int32_t* seq_lens, int32_t n_split, void* workspace,
+                       size_t ws_bytes, void* out, float* lse, hipStream_t stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || s_q < 1 || max_blocks < 1 || num_blocks < 1 || n_split < 0 ||
+      n_split > MLA_MAX_SPLIT)
+    return MLA_ERR_RANGE;
+  if (batch == 0) return MLA_OK;
+  if (batch > 65535 || s_q > 65535 || static_cast<int64_t>(batch) * s_q > 65535 * 16)
+    return MLA_ERR_RANGE;
+  if (static_cast<int64_t>(max_blocks) * dims->block_size > INT32_MAX) return MLA_ERR_RANGE;
+  if (!q_nope || !q_pos || !gqa_cache || !block_table || !seq_lens || !out ||
+      (dims->d_r > 0 && !q_pe))
+    return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || (q_pe && !aligned16(q_pe)) || !aligned16(gqa_cache) || !aligned16(out))
+    return MLA_ERR_ALIGN;
+  const int ns = n_split == 0 ? resolve_split(*dims, batch, s_q, max_blocks) : n_split;
+  const size_t need = mla::partials_bytes(batch, s_q, dims->n_heads, ns, dims->d_v);
+  if (workspace == nullptr || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_gqa_decode(*dims, batch, s_q, q_nope, q_pe, q_pos, gqa_cache,
+                                           num_blocks, block_table, max_blocks, seq_lens, ns,
+                                           workspace, out, lse, stream));
+}
+
+mla_status mla_validate_block_table(const mla_dims* dims, const int32_t* host_table,
+                                    int32_t batch, int32_t max_blocks,
+                                    const int32_t* host_seq_lens, int32_t num_blocks) {
+  if (dims == nullptr || host_table == nullptr || host_seq_lens == nullptr) return MLA_ERR_NULL;
+  if (dims->block_size < 1) return MLA_ERR_SHAPE;
+  if (batch < 0 || max_blocks < 1 || num_blocks < 1) return MLA_ERR_RANGE;
+  const int64_t cap = static_cast<int64_t>(max_blocks) * dims->block_size;
+  for (int b = 0; b < batch; ++b) {
+    if (host_seq_lens[b] < 0 || host_seq_lens[b] > cap) return MLA_ERR_RANGE;
+  }
+  for (int b = 0; b < batch; ++b) {
+    const int nb = cdiv(host_seq_lens[b], dims->block_size);
+    for (int j = 0; j < nb; ++j) {
+      const int id = host_table[static_cast<int64_t>(b) * max_blocks + j];
+      if (id < 0 || id >= num_blocks) return MLA_ERR_BLOCK_TABLE;
+    }
+  }
+  // A block used twice: sweep the id space in 64Ki-id windows with a bitmap on the stack
+  // (the library allocates nothing).
+  constexpr int kWin = 1 << 16;
+  uint64_t seen[kWin / 64];
+  for (int64_t lo = 0; lo < num_blocks; lo += kWin) {
+    for (int i = 0; i < kWin / 64; ++i) seen[i] = 0;
+    for (int b = 0; b < batch; ++b) {
+      const int nb = cdiv(host_seq_lens[b], dims->block_size);
+      for (int j = 0; j < nb; ++j) {
+        const int64_t id = host_table[static_cast<int64_t>(b) * max_blocks + j];
+        if (id < lo || id >= lo + kWin) continue;
+        const int64_t r = id - lo;
+        const uint64_t bit = 1ull << (r & 63);
+        if (seen[r >> 6] & bit) return MLA_ERR_BLOCK_TABLE;
+        seen[r >> 6] |= bit;
+      }
+    }
+  }
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Internal launchers of libmla: the C ABI in api.cpp validates arguments, then calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mla.h"
+
+namespace mla {
+
+// Split-K plan of the append projection (shared by the workspace query and the launch).
+struct AppendPlan {
+  int n_ksplit, k_chunk, col_blocks, tok_tiles;
+};
+AppendPlan append_plan(const mla_dims& d, int n_tok);
+
+hipError_t launch_append(const mla_dims& d, int n_tok, const void* x, const int32_t* seq_idx,
+                         const int32_t* pos, const void* w_dkv, const void* gamma,
+                         const void* w_kr, const int32_t* table, int batch, int max_blocks,
+                         int num_blocks, void* cache, void* ws, hipStream_t s);
+
+hipError_t launch_absorb(const mla_dims& d, int batch, int s_q, const void* q_nope,
+                         const void* q_pe, const int32_t* q_pos, const void* w_uk, void* q_abs,
+                         hipStream_t s);
+
+// Workspace of one split-K decode, each part 256-byte aligned: partial o [B, s_q, H, n_split,
+// width] fp32, partial lse2 [B, s_q, H, n_split] fp32 (log2 domain of scale*score), and
+// recompute flags [B, s_q, n_split] int32.
+size_t partials_bytes(int batch, int s_q, int heads, int n_split, int width);
+
+// Split-K core: every (split, query, sequence) writes its partials (and recompute flag).
+hipError_t launch_decode_splitk(const mla_dims& d, int batch, int s_q, const void* q_abs,
+                                const void* cache, int num_blocks, const int32_t* table,
+                                int max_blocks, const int32_t* seq_lens, int n_split, void* ws,
+                                hipStream_t s);
+// Merge: flagged splits recomputed, log-sum-exp merge over splits, W_UV per group.
+hipError_t launch_decode_merge(const mla_dims& d, int batch, int s_q, const void* q_abs,
+                               const void* cache, int num_blocks, const int32_t* table,
+                               int max_blocks, const int32_t* seq_lens, const void* w_uv,
+                               int n_split, void* ws, void* out, float* lse, hipStream_t s);
+
+hipError_t launch_expand(const mla_dims& d, int batch, const void* cache, int num_blocks,
+                         const int32_t* table, int max_blocks, const int32_t* seq_lens,
+                         const int32_t* start_pos, const void* w_uk, const void* w_uv,
+                         void* gqa, hipStream_t s);
+
+hipError_t launch_gqa_decode(const mla_dims& d, int batch, int s_q, const void* q_nope,
+                             const void* q_pe, const int32_t* q_pos, const void* gqa,
+                             int num_blocks, const int32_t* table, int max_blocks,
+                             const int32_t* seq_lens, int n_split, void* ws, void* out,
+                             float* lse, hipStream_t s);
+
+// Whether the MFMA decode kernel handles these dims (bf16, d_c 512, d_r 64, H % 32 == 0).
+bool mfma_decode_fits(const mla_dims& d);
+hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void* q_abs,
+                              const void* cache, int num_blocks, const int32_t* table,
+                              int max_blocks, const int32_t* seq_lens, int n_split,
+                              float* part_o, float* part_lse, int* redo, hipStream_t s);
+
+inline float softmax_scale_of(const mla_dims& d) {
+  return d.softmax_scale > 0.f ? d.softmax_scale
+                               : 1.0f / sqrtf(static_cast<float>(d.d_nope + d.d_r));
+}
+
+constexpr int kSplitAlign = 64;  // split boundaries fall on multiples of this many positions
+
+}  // namespace mla

@@ -199,7 +199,7 @@ def visible_lengths(L: int, s_q: int) -> list:
 
 
 def decode_reconstructed(q_nope, q_pe, q_pos, hist, w_uk, w_uv, n_groups: int, d_c: int,
-                         d_v: int, base: float, scale: float | None = None):
+                         d_v: int, base: float, scale: float | None = None, heads=None):
     """Reconstructed (non-absorbed) decode of one sequence -- the gold answer.
 
     q_nope [s_q, H, D], q_pe [s_q, H, d_r] (not rotated), q_pos [s_q], hist [L, d_c + d_r]
@@ -210,24 +210,25 @@ def decode_reconstructed(q_nope, q_pe, q_pos, hist, w_uk, w_uv, n_groups: int, d
     rebuilt for all L positions ([Smallem] "L'idée : garder un résumé"); the query is
     [q_nope_h ; rotation(q_pe_h, pos)] ([Smallem] "L'obstacle : RoPE"); then softmax
     attention over the positions the query may see.
-    Returns (out [s_q, H, D_v], lse [s_q, H]).
+    Returns (out [s_q, H, D_v], lse [s_q, H]); with `heads`, only those heads, in that order.
     """
     q_nope, q_pe, hist, w_uk, w_uv = f64(q_nope), f64(q_pe), f64(hist), f64(w_uk), f64(w_uv)
     s_q, H, D = q_nope.shape
     L = hist.shape[0]
     scale = softmax_scale(D, q_pe.shape[-1]) if scale is None else scale
     c, k_r = hist[:, :d_c], hist[:, d_c:]
-    out = np.zeros((s_q, H, d_v))
-    lse = np.zeros((s_q, H))
+    heads = list(range(H)) if heads is None else list(heads)
+    out = np.zeros((s_q, len(heads), d_v))
+    lse = np.zeros((s_q, len(heads)))
     lim = visible_lengths(L, s_q)
-    for h in range(H):
+    for j, h in enumerate(heads):
         g = group_of(h, H, n_groups)
         K = np.concatenate([c @ w_uk[:, g * D:(g + 1) * D], k_r], axis=1)
         V = c @ w_uv[:, g * d_v:(g + 1) * d_v]
         for i in range(s_q):
             q = np.concatenate([q_nope[i, h], rope(q_pe[i, h], q_pos[i], base)])
             n = lim[i]
-            out[i, h], lse[i, h] = attend(q, K[:n], V[:n], scale)
+            out[i, j], lse[i, j] = attend(q, K[:n], V[:n], scale)
     return out, lse
 
 
@@ -250,37 +251,43 @@ def absorb_query(q_nope, q_pe, q_pos, w_uk, n_groups: int, base: float) -> np.nd
     return np.stack(out, axis=-2)
 
 
-def decode_absorbed_latent(q_abs, hist, d_c: int, scale: float):
+def decode_absorbed_latent(q_abs, hist, d_c: int, scale: float, heads=None):
     """Latent-space decode of one sequence: the attention of [Smallem] "Ce que DeepSeek fait
     de plus" run on the cached rows themselves.
 
     q_abs [s_q, H, d_c + d_r], hist [L, d_c + d_r]. Scores are scale * (q_abs . row), i.e.
     the latent part against c plus the rotary part against k_r in one product over the
     concatenation ([Smallem] "Deux produits ou une concaténation ?"); the probabilities
-    weight the latents c. Returns (o_lat [s_q, H, d_c], lse [s_q, H]).
+    weight the latents c. Returns (o_lat [s_q, H, d_c], lse [s_q, H]); with `heads`, only
+    those heads, in that order.
     """
     q_abs, hist = f64(q_abs), f64(hist)
     s_q, H, _ = q_abs.shape
     L = hist.shape[0]
-    o = np.zeros((s_q, H, d_c))
-    lse = np.zeros((s_q, H))
+    heads = list(range(H)) if heads is None else list(heads)
+    o = np.zeros((s_q, len(heads), d_c))
+    lse = np.zeros((s_q, len(heads)))
     lim = visible_lengths(L, s_q)
     for i in range(s_q):
         n = lim[i]
-        for h in range(H):
-            o[i, h], lse[i, h] = attend(q_abs[i, h], hist[:n], hist[:n, :d_c], scale)
+        for j, h in enumerate(heads):
+            o[i, j], lse[i, j] = attend(q_abs[i, h], hist[:n], hist[:n, :d_c], scale)
     return o, lse
 
 
-def project_values(o_lat, w_uv, n_groups: int, d_v: int) -> np.ndarray:
+def project_values(o_lat, w_uv, n_groups: int, d_v: int, n_heads: int | None = None,
+                   heads=None) -> np.ndarray:
     """out_h = o_lat_h · W_UV[:, g(h)]: the weighted latent mapped to the head's values once
-    ([Smallem] "Ce que DeepSeek fait de plus")."""
+    ([Smallem] "Ce que DeepSeek fait de plus"). With `heads`, o_lat holds those heads only
+    (in that order) out of n_heads."""
     o_lat, w_uv = f64(o_lat), f64(w_uv)
-    *lead, H, _ = o_lat.shape
+    *lead, Hs, _ = o_lat.shape
+    H = Hs if n_heads is None else n_heads
+    heads = list(range(Hs)) if heads is None else list(heads)
     outs = []
-    for h in range(H):
+    for j, h in enumerate(heads):
         g = group_of(h, H, n_groups)
-        outs.append(o_lat[..., h, :] @ w_uv[:, g * d_v:(g + 1) * d_v])
+        outs.append(o_lat[..., j, :] @ w_uv[:, g * d_v:(g + 1) * d_v])
     return np.stack(outs, axis=-2)
 
 
@@ -309,7 +316,7 @@ def gqa_expand_rows(hist, w_uk, w_uv, n_groups: int, d_c: int, d_nope: int, d_v:
 
 
 def decode_gqa(q_nope, q_pe, q_pos, gqa_rows, n_groups: int, d_v: int, base: float,
-               scale: float | None = None):
+               scale: float | None = None, heads=None):
     """Standard grouped-query decode over an expanded cache ([GQLA] "Chemin GQA").
 
     Head h of group g compares [q_nope_h ; rotation(q_pe_h)] with [K_g ; k_r] and averages
@@ -321,15 +328,16 @@ def decode_gqa(q_nope, q_pe, q_pos, gqa_rows, n_groups: int, d_v: int, base: flo
     scale = softmax_scale(D, q_pe.shape[-1]) if scale is None else scale
     L = rows.shape[0]
     k_r = rows[:, G * D + G * d_v:]
-    out = np.zeros((s_q, H, d_v))
-    lse = np.zeros((s_q, H))
+    heads = list(range(H)) if heads is None else list(heads)
+    out = np.zeros((s_q, len(heads), d_v))
+    lse = np.zeros((s_q, len(heads)))
     lim = visible_lengths(L, s_q)
-    for h in range(H):
+    for j, h in enumerate(heads):
         g = group_of(h, H, G)
         K = np.concatenate([rows[:, g * D:(g + 1) * D], k_r], axis=1)
         V = rows[:, G * D + g * d_v:G * D + (g + 1) * d_v]
         for i in range(s_q):
             q = np.concatenate([q_nope[i, h], rope(q_pe[i, h], q_pos[i], base)])
             n = lim[i]
-            out[i, h], lse[i, h] = attend(q, K[:n], V[:n], scale)
+            out[i, j], lse[i, j] = attend(q, K[:n], V[:n], scale)
     return out, lse

@@ -1,0 +1,91 @@
+"""Shared builders for the GPU parity tests: seeded inputs (workloads), library calls through
+the C ABI (binding) and expected values from the oracle, on the same input bits."""
+import numpy as np
+import torch
+
+import oracle as O
+import workloads as W
+from mla_latent_kv_21_amd import binding as M
+
+DEV = "cuda:0"
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def note(msg: str):
+    print(f"[case] {msg}", flush=True)
+
+
+def rel_err(y, ref) -> float:
+    """Normwise error max|y - ref| / max|ref| over a whole tensor."""
+    y, ref = O.f64(y), O.f64(ref)
+    assert y.shape == ref.shape, (y.shape, ref.shape)
+    assert np.all(np.isfinite(y)), "non-finite values in the GPU result"
+    return float(np.max(np.abs(y - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def dev(t):
+    return t.to(DEV) if isinstance(t, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(t)).to(DEV)
+
+
+# ----------------------------------------------------------------------------- decode cases
+def decode_case(w, lens, s_q=1, random_table=True, poison=True, extra=0, max_blocks=None):
+    lens = np.asarray(lens, np.int32)
+    wq = w.replace(batch=len(lens), s_q=s_q)
+    table, nb = W.block_table(wq, lens, random=random_table, max_blocks=max_blocks)
+    pool = W.cache_pool(wq, nb, extra=extra)
+    if poison:
+        mask = O.owned_slot_mask(table, lens, nb, w.block_size)
+        pool.view(-1, w.row)[torch.from_numpy(~mask)] = float("nan")
+    return dict(w=wq, lens=lens, table=table, nb=nb, pool=pool, q_abs=W.absorbed_queries(wq),
+                w_uv=W.weights(wq)["w_uv"])
+
+
+def decode_ws_layout(c, n_split):
+    w = c["w"]
+    rows = w.batch * w.s_q * w.n_heads * n_split
+    al = lambda x: (x + 255) // 256 * 256
+    off_flags = al(rows * w.d_c * 4) + al(rows * 4)
+    return off_flags, w.batch * w.s_q * n_split
+
+
+def run_decode(c, n_split=0, generic=False, gpu=None):
+    """mla_decode on the GPU; returns (out, lse, recompute flags) on the host."""
+    w = c["w"]
+    d = M.dims_of(w, generic=generic)
+    g = gpu or {}
+    q = g.get("q") if "q" in g else dev(c["q_abs"])
+    pool = g.get("pool") if "pool" in g else dev(c["pool"])
+    tab = dev(c["table"])
+    lens = dev(c["lens"])
+    wuv = dev(c["w_uv"])
+    out = torch.empty(w.batch, w.s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=DEV)
+    lse = torch.empty(w.batch, w.s_q, w.n_heads, dtype=torch.float32, device=DEV)
+    ns = n_split or M.mla_auto_split(d, w.batch, w.s_q, c["table"].shape[1])
+    ws = torch.empty(M.mla_decode_workspace_bytes(d, w.batch, w.s_q, ns, c["table"].shape[1]),
+                     dtype=torch.uint8, device=DEV)
+    M.mla_decode(d, q, pool, tab, lens, wuv, out, lse, n_split=ns, workspace=ws)
+    torch.cuda.synchronize()
+    off, n = decode_ws_layout(c, ns)
+    flags = ws[off:off + 4 * n].view(torch.int32).cpu().numpy().copy()
+    return out.cpu(), lse.cpu(), flags
+
+
+def oracle_decode(c, seqs=None, heads=None):
+    """Expected (out [b, s_q, h, D_v], lse) of the absorbed definition, from the same bits."""
+    w = c["w"]
+    seqs = range(w.batch) if seqs is None else seqs
+    scale = O.softmax_scale(w.d_nope, w.d_r)
+    outs, lses = [], []
+    for b in seqs:
+        rows = O.gather_rows(c["pool"], c["table"], b, int(c["lens"][b]))
+        o_lat, lse = O.decode_absorbed_latent(c["q_abs"][b], rows, w.d_c, scale, heads=heads)
+        outs.append(O.project_values(o_lat, c["w_uv"], w.n_groups, w.d_v, n_heads=w.n_heads,
+                                     heads=heads))
+        lses.append(lse)
+    return np.stack(outs), np.stack(lses)
+
+
+def pick(t, seqs, heads):
+    t = O.f64(t)
+    t = t[list(seqs)]
+    return t[:, :, list(heads)] if heads is not None else t

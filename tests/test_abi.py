@@ -1,0 +1,146 @@
+"""The C ABI without a GPU: every declared symbol is exported, host-side validation returns the
+documented status before anything is launched, workspace sizes follow their formula, and the
+host block-table checker catches bad and shared block ids."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+from mla_latent_kv_21_amd import binding as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(M.LIB_PATH):
+        from mla_latent_kv_21_amd.build import build
+        build()
+    return M.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w]+\s*\*?\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("mla_cache_append", "mla_absorb_q", "mla_decode", "gqla_expand", "gqla_decode"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    for name in M.EXPORTS:
+        assert name in declared_functions()
+
+
+def dims(**kw):
+    base = dict(d_model=7168, n_heads=128, d_nope=128, d_v=128, d_c=512, d_r=64, n_groups=128,
+                block_size=64, dtype="bf16")
+    base.update(kw)
+    return M.make_dims(**base)
+
+
+P = ctypes.c_void_p
+FAKE = 0x10000  # an aligned address that is never dereferenced: validation fails first
+
+
+def decode_call(L, d, batch=2, s_q=1, q=FAKE, cache=FAKE, nb=8, table=FAKE, mb=4, lens=FAKE,
+                wuv=FAKE, n_split=0, ws=None, ws_bytes=0, out=FAKE):
+    dp = ctypes.byref(d) if d is not None else None
+    return L.mla_decode(dp, batch, s_q, P(q), P(cache), nb, P(table), mb, P(lens), P(wuv),
+                        n_split, P(ws), ws_bytes, P(out), None, None)
+
+
+def test_decode_validation(L):
+    d = dims()
+    assert decode_call(L, None) == -1
+    assert decode_call(L, dims(dtype=7)) == -3
+    assert decode_call(L, dims(n_groups=3)) == -2          # 3 does not divide 128
+    assert decode_call(L, dims(d_r=63)) == -2              # odd rotary width
+    assert decode_call(L, d, batch=0) == 0                 # empty batch: nothing to do
+    assert decode_call(L, d, s_q=0) == -4
+    assert decode_call(L, d, n_split=M.MLA_MAX_SPLIT + 1) == -4
+    assert decode_call(L, d, q=0) == -1
+    assert decode_call(L, d, q=FAKE + 4) == -6             # misaligned
+    assert decode_call(L, d, ws=None) == -5                # missing workspace
+    need = L.mla_decode_workspace_bytes(ctypes.byref(d), 2, 1, 0, 4)
+    assert decode_call(L, d, ws=FAKE, ws_bytes=need - 1) == -5
+
+
+def test_workspace_sizes(L):
+    d = dims()
+    ns = L.mla_auto_split(ctypes.byref(d), 4, 1, 2048)
+    assert ns == 64                                      # 4 sequences x 64 chunks = 256 CUs
+    n = L.mla_decode_workspace_bytes(ctypes.byref(d), 4, 1, 64, 2048)
+    rows = 4 * 128 * 64
+    al = lambda x: (x + 255) // 256 * 256
+    assert n == al(rows * 512 * 4) + al(rows * 4) + al(4 * 64 * 4)
+    g = L.gqla_decode_workspace_bytes(ctypes.byref(d), 4, 2, 8, 2048)
+    rows = 4 * 2 * 128 * 8
+    assert g == al(rows * 128 * 4) + al(rows * 4) + al(4 * 2 * 8 * 4)
+    assert L.mla_decode_workspace_bytes(ctypes.byref(d), 4, 1, M.MLA_MAX_SPLIT + 1, 2048) == 0
+    # auto split: never more splits than 64-position chunks of the longest sequence
+    assert L.mla_auto_split(ctypes.byref(d), 1, 1, 1) == 1
+    assert L.mla_auto_split(ctypes.byref(d), 64, 1, 128) == 4
+
+
+def test_append_absorb_expand_validation(L):
+    d = dims()
+    bd = ctypes.byref(d)
+    # n_tok == 0 is a no-op
+    assert L.mla_cache_append(bd, 0, None, None, None, None, None, None, None, 1, 1, 1, None,
+                              None, 0, None) == 0
+    assert L.mla_cache_append(bd, 4, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None,
+                              P(FAKE), 1, 4, 8, P(FAKE), P(FAKE), 1 << 30, None) == -1  # no W_KR
+    assert L.mla_cache_append(bd, 4, P(FAKE), P(FAKE), P(FAKE), P(FAKE + 2), P(FAKE), P(FAKE),
+                              P(FAKE), 1, 4, 8, P(FAKE), P(FAKE), 1 << 30, None) == -6
+    need = L.mla_cache_append_workspace_bytes(bd, 4)
+    assert need > 0
+    assert L.mla_cache_append(bd, 4, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                              P(FAKE), 1, 4, 8, P(FAKE), P(FAKE), need - 1, None) == -5
+    assert L.mla_absorb_q(bd, 2, 0, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == -4
+    assert L.mla_absorb_q(bd, 0, 1, None, None, None, None, None, None) == 0
+    assert L.mla_absorb_q(bd, 2, 1, None, P(FAKE), P(FAKE), P(FAKE), P(FAKE), None) == -1
+    assert L.gqla_expand(bd, 2, P(FAKE), 0, P(FAKE), 4, P(FAKE), None, P(FAKE), P(FAKE),
+                         P(FAKE), None) == -4       # no blocks
+    assert L.gqla_expand(bd, 2, P(FAKE), 8, P(FAKE), 4, P(FAKE), None, P(FAKE), None,
+                         P(FAKE), None) == -1
+    assert L.gqla_decode(bd, 2, 1, P(FAKE), P(FAKE), P(FAKE), P(FAKE), 8, P(FAKE), 4, P(FAKE),
+                         0, None, 0, P(FAKE), None, None) == -5
+
+
+def test_status_strings(L):
+    for st in M.STATUS:
+        assert len(M.status_string(st)) >= 2
+    assert M.status_string(12345) == "unknown status"
+
+
+def test_validate_block_table(L):
+    d = dims(block_size=4)
+    table = torch.tensor([[3, 0, -1], [1, 2, 5]], dtype=torch.int32)
+    lens = torch.tensor([6, 12], dtype=torch.int32)
+    assert M.mla_validate_block_table(d, table, lens, 6) == 0
+    assert M.mla_validate_block_table(d, table, lens, 5) == -8     # id 5 out of range
+    bad = table.clone(); bad[1, 0] = 3
+    assert M.mla_validate_block_table(d, bad, lens, 6) == -8       # block 3 used twice
+    assert M.mla_validate_block_table(d, table, torch.tensor([6, 13], dtype=torch.int32), 6) == -4
+    # unused entries (past ceil(L/bs)) are never looked at
+    ok = table.clone(); ok[0, 2] = 99
+    assert M.mla_validate_block_table(d, ok, lens, 6) == 0
+    # a large random permutation table is accepted, a single collision is caught
+    r = np.random.default_rng(0)
+    ids = r.permutation(200_000).astype(np.int32)
+    big = torch.from_numpy(ids[:131072].reshape(64, 2048).copy())
+    blens = torch.full((64,), 2048 * 4, dtype=torch.int32)
+    assert M.mla_validate_block_table(d, big, blens, 200_000) == 0
+    big[63, 2047] = big[0, 0]
+    assert M.mla_validate_block_table(d, big, blens, 200_000) == -8

@@ -1,0 +1,196 @@
+"""GPU parity of mla_cache_append, mla_absorb_q, gqla_expand and gqla_decode, and of the whole
+decode step end to end, against the oracle's reconstructed-K/V answer.
+
+Integer work is checked bit-exactly: the set of cache slots the append writes equals the
+oracle's slot set (every other slot keeps its NaN sentinel), and appending in chunks writes
+the same bytes as appending at once.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_cases import DEV, TOL, decode_case, dev, note, oracle_decode, rel_err, run_decode
+from mla_latent_kv_21_amd import binding as M
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+BASE, EPS = 10000.0, 1e-6
+
+
+def ulp_close(gpu, ref, dtype):
+    """Each stored value within one storage ulp of the oracle's f64 value plus the fp32
+    accumulation error of its row (1e-5 of the row's largest magnitude): values that cancel
+    to near zero have tiny ulps but carry the absolute error of their fp32 sums."""
+    g, ref = O.f64(gpu), O.f64(ref)
+    slack = 1e-5 * np.max(np.abs(ref), axis=-1, keepdims=True)
+    if dtype == "bf16":
+        _, e = np.frexp(np.abs(ref))
+        ulp = np.ldexp(1.0, np.maximum(e, -125) - 8)
+        return bool(np.all(np.abs(g - ref) <= ulp + slack))
+    return bool(np.all(np.abs(g - ref) <= 1e-6 * np.abs(ref) + slack))
+
+
+def append_case(w, lens, n_tok_extra=0):
+    """History of every sequence appended token by token from seeded x; returns GPU cache."""
+    lens = np.asarray(lens, np.int32)
+    table, nb = W.block_table(w.replace(batch=len(lens)), lens)
+    seq = np.concatenate([np.full(L, b, np.int32) for b, L in enumerate(lens)])
+    pos = np.concatenate([np.arange(L, dtype=np.int32) for L in lens])
+    x = W.tokens(w, len(seq), extra=n_tok_extra)
+    wts = W.weights(w, random_gamma=True)
+    return dict(lens=lens, table=table, nb=nb, seq=seq, pos=pos, x=x, wts=wts)
+
+
+def gpu_append(w, a, chunks=1):
+    d = M.dims_of(w)
+    cache = torch.full((a["nb"], w.block_size, w.row), float("nan"), dtype=w.torch_dtype,
+                       device=DEV)
+    tab = dev(a["table"])
+    n = len(a["seq"])
+    edges = np.linspace(0, n, chunks + 1).astype(int)
+    for lo, hi in zip(edges[:-1], edges[1:]):
+        M.mla_cache_append(d, dev(a["x"][lo:hi]), dev(a["seq"][lo:hi]), dev(a["pos"][lo:hi]),
+                           dev(a["wts"]["w_dkv"]), dev(a["wts"]["gamma"]), dev(a["wts"]["w_kr"]),
+                           tab, a["nb"], cache)
+    torch.cuda.synchronize()
+    return cache.cpu()
+
+
+@pytest.mark.parametrize("cfg,lens", [(1, [512]), (2, [40, 130]), (3, [3, 70]), (5, [65])])
+def test_append_matches_oracle(cfg, lens):
+    w = W.CONFIGS[cfg]
+    a = append_case(w, lens)
+    note(f"append cfg={cfg} lens={lens}")
+    cache = gpu_append(w, a)
+    ref = O.latent_rows(a["x"], a["wts"]["w_dkv"], a["wts"]["gamma"], a["wts"]["w_kr"], a["pos"],
+                        BASE, EPS)
+    flat = cache.view(-1, w.row)
+    k = 0
+    for b, L in enumerate(a["lens"]):
+        got = O.gather_rows(cache, a["table"], b, int(L))
+        assert ulp_close(got, ref[k:k + L], w.dtype)
+        k += L
+    # integer addressing, bit-exact: exactly the oracle's slots were written
+    owned = O.owned_slot_mask(a["table"], a["lens"], a["nb"], w.block_size)
+    written = ~torch.isnan(flat.float()).all(dim=1).numpy()
+    assert np.array_equal(written, owned)
+
+
+def test_chunked_append_is_bit_exact():
+    w = W.CONFIGS[3]
+    a = append_case(w, [100, 37])
+    note("append bulk vs 3 chunks")
+    one = gpu_append(w, a, chunks=1)
+    three = gpu_append(w, a, chunks=3)
+    assert torch.equal(one.view(torch.int16), three.view(torch.int16))
+
+
+@pytest.mark.parametrize("cfg,s_q", [(1, 1), (2, 1), (3, 1), (5, 4)])
+def test_absorb_matches_oracle(cfg, s_q):
+    w = W.CONFIGS[cfg].replace(batch=3, s_q=s_q)
+    q = W.queries(w)
+    lens = np.array([5000, 17, 131000], np.int32)[:w.batch]
+    qpos = W.query_positions(w, lens)
+    wts = W.weights(w)
+    d = M.dims_of(w)
+    out = torch.empty(w.batch, s_q, w.n_heads, w.row, dtype=w.torch_dtype, device=DEV)
+    note(f"absorb cfg={cfg} s_q={s_q}")
+    M.mla_absorb_q(d, dev(q["q_nope"]), dev(q["q_pe"]), dev(qpos), dev(wts["w_uk"]), out)
+    torch.cuda.synchronize()
+    ref = O.absorb_query(q["q_nope"], q["q_pe"], qpos, wts["w_uk"], w.n_groups, BASE)
+    assert rel_err(out.cpu(), ref) <= (1e-5 if w.dtype == "f32" else 4e-3)
+
+
+@pytest.mark.parametrize("cfg,lens,s_q", [(1, [512], 1), (2, [300, 45], 1), (5, [200], 2),
+                                          (3, [129, 1], 1)])
+def test_end_to_end_matches_reconstructed_oracle(cfg, lens, s_q):
+    """x -> append -> absorb -> decode on the GPU versus keys and values rebuilt explicitly."""
+    w = W.CONFIGS[cfg].replace(batch=len(lens), s_q=s_q)
+    a = append_case(w, lens)
+    note(f"end to end cfg={cfg} lens={lens} s_q={s_q}")
+    cache = gpu_append(w, a)
+    q = W.queries(w)
+    qpos = W.query_positions(w, a["lens"])
+    d = M.dims_of(w)
+    q_abs = torch.empty(w.batch, s_q, w.n_heads, w.row, dtype=w.torch_dtype, device=DEV)
+    M.mla_absorb_q(d, dev(q["q_nope"]), dev(q["q_pe"]), dev(qpos), dev(a["wts"]["w_uk"]), q_abs)
+    out = torch.empty(w.batch, s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=DEV)
+    lse = torch.empty(w.batch, s_q, w.n_heads, dtype=torch.float32, device=DEV)
+    M.mla_decode(d, q_abs, dev(cache), dev(a["table"]), dev(a["lens"]), dev(a["wts"]["w_uv"]),
+                 out, lse)
+    torch.cuda.synchronize()
+    rows_all = O.round_storage(O.latent_rows(a["x"], a["wts"]["w_dkv"], a["wts"]["gamma"],
+                                             a["wts"]["w_kr"], a["pos"], BASE, EPS), w.dtype)
+    k = 0
+    tol = TOL[w.dtype]
+    for b, L in enumerate(a["lens"]):
+        ref, ref_lse = O.decode_reconstructed(q["q_nope"][b], q["q_pe"][b], qpos[b],
+                                              rows_all[k:k + L], a["wts"]["w_uk"],
+                                              a["wts"]["w_uv"], w.n_groups, w.d_c, w.d_v, BASE)
+        k += L
+        assert rel_err(out[b].cpu(), ref) <= tol
+        assert np.max(np.abs(lse[b].cpu().double().numpy() - ref_lse)) <= tol
+
+
+def gqa_cache_empty(w, nb):
+    return torch.full((nb, w.block_size, w.n_groups * (w.d_nope + w.d_v) + w.d_r), float("nan"),
+                      dtype=w.torch_dtype, device=DEV)
+
+
+def test_gqla_expand_matches_oracle():
+    w = W.CONFIGS[5]
+    c = decode_case(w, [70, 129], extra=21)
+    wts = W.weights(c["w"])
+    start = np.array([0, 64], np.int32)   # second sequence: only positions 64.. are expanded
+    d = M.dims_of(c["w"])
+    g = gqa_cache_empty(w, c["nb"])
+    note("gqla_expand with a start offset")
+    M.gqla_expand(d, dev(c["pool"]), dev(c["table"]), dev(c["lens"]), dev(wts["w_uk"]),
+                  dev(wts["w_uv"]), g, start_pos=dev(start))
+    torch.cuda.synchronize()
+    g = g.cpu()
+    for b, L in enumerate(c["lens"]):
+        rows = O.gather_rows(c["pool"], c["table"], b, int(L))
+        ref = O.gqa_expand_rows(rows, wts["w_uk"], wts["w_uv"], w.n_groups, w.d_c, w.d_nope, w.d_v)
+        got = O.gather_rows(g, c["table"], b, int(L))
+        s = int(start[b])
+        assert ulp_close(got[s:], ref[s:], w.dtype) or rel_err(got[s:], ref[s:]) <= 4e-3
+        assert np.isnan(got[:s]).all()                   # prefix left untouched
+
+
+@pytest.mark.parametrize("s_q", [1, 2, 4])
+def test_gqla_paths_agree_with_oracle(s_q):
+    """GQA path (expand once, then grouped decode) and absorbed path on the same weights and
+    latents: both match the reconstructed oracle and each other."""
+    w = W.CONFIGS[5].replace(s_q=s_q)
+    c = decode_case(w, [s_q, 333, 1100], s_q=s_q, extra=22)
+    wts = W.weights(c["w"])
+    q = W.queries(c["w"])
+    qpos = W.query_positions(c["w"], c["lens"])
+    d = M.dims_of(c["w"])
+    note(f"gqla both paths s_q={s_q}")
+    g = gqa_cache_empty(w, c["nb"])
+    M.gqla_expand(d, dev(c["pool"]), dev(c["table"]), dev(c["lens"]), dev(wts["w_uk"]),
+                  dev(wts["w_uv"]), g)
+    out_g = torch.empty(c["w"].batch, s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=DEV)
+    lse_g = torch.empty(c["w"].batch, s_q, w.n_heads, dtype=torch.float32, device=DEV)
+    M.gqla_decode(d, dev(q["q_nope"]), dev(q["q_pe"]), dev(qpos), g, dev(c["table"]),
+                  dev(c["lens"]), out_g, lse_g)
+    q_abs = torch.empty(c["w"].batch, s_q, w.n_heads, w.row, dtype=w.torch_dtype, device=DEV)
+    M.mla_absorb_q(d, dev(q["q_nope"]), dev(q["q_pe"]), dev(qpos), dev(wts["w_uk"]), q_abs)
+    out_a = torch.empty_like(out_g)
+    M.mla_decode(d, q_abs, dev(c["pool"]), dev(c["table"]), dev(c["lens"]), dev(wts["w_uv"]), out_a)
+    torch.cuda.synchronize()
+    out_g, out_a = out_g.cpu(), out_a.cpu()
+    for b, L in enumerate(c["lens"]):
+        rows = O.gather_rows(c["pool"], c["table"], b, int(L))
+        ref, ref_lse = O.decode_reconstructed(q["q_nope"][b], q["q_pe"][b], qpos[b], rows,
+                                              wts["w_uk"], wts["w_uv"], w.n_groups, w.d_c,
+                                              w.d_v, BASE)
+        assert rel_err(out_g[b], ref) <= TOL["bf16"]
+        assert rel_err(out_a[b], ref) <= TOL["bf16"]
+        assert np.max(np.abs(lse_g[b].cpu().double().numpy() - ref_lse)) <= TOL["bf16"]
+    assert rel_err(out_g, out_a.double()) <= TOL["bf16"]

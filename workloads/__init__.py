@@ -205,3 +205,13 @@ def cache_pool(w: Workload, num_blocks: int, extra: int = 0) -> torch.Tensor:
     a = rng(w, S_CACHE_C, extra).standard_normal(
         size=(num_blocks, w.block_size, w.row), dtype=np.float32)
     return to_storage(a, w)
+
+
+def cache_pool_device(w: Workload, num_blocks: int, device, extra: int = 0) -> torch.Tensor:
+    """Like cache_pool, drawn by torch's seeded generator on the device (for large benchmark
+    caches that would take seconds to draw on the host). Seed: seed * 1000 + extra."""
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed * 1000 + extra)
+    a = torch.randn((num_blocks, w.block_size, w.row), generator=g, device=device,
+                    dtype=torch.float32)
+    return a.to(w.torch_dtype)
