@@ -19,6 +19,7 @@ mla_status check_dims(const mla_dims* d) {
       d->d_r < 0 || (d->d_r & 1) || d->n_groups < 1 || d->block_size < 1)
     return MLA_ERR_SHAPE;
   if (d->n_heads % d->n_groups != 0) return MLA_ERR_SHAPE;
+  if (d->d_c % 8 != 0) return MLA_ERR_SHAPE;  // 16-byte weight loads never straddle c and k_r
   // LDS budgets of the portable kernels: query row + value row + 2 KiB of per-pass state,
   // and 16 merged latent rows in the combine.
   if (d->d_c + d->d_r > 4096 || d->d_nope + d->d_r > 4096 || d->d_v > 1024 || d->d_c > 1024 ||
@@ -136,7 +137,7 @@ mla_status check_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const 
   if (batch < 0 || s_q < 1 || max_blocks < 1 || num_blocks < 1 || n_split < 0 ||
       n_split > MLA_MAX_SPLIT)
     return MLA_ERR_RANGE;
-  if (batch > 65535 || s_q > 65535 || static_cast<int64_t>(batch) * s_q > 65535 * 16)
+  if (batch > 65535 || s_q > 65535 || static_cast<int64_t>(batch) * s_q > 65535)
     return MLA_ERR_RANGE;
   if (static_cast<int64_t>(max_blocks) * dims->block_size > INT32_MAX) return MLA_ERR_RANGE;
   if (batch == 0) return MLA_OK;
@@ -245,7 +246,7 @@ mla_status gqla_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const v
       n_split > MLA_MAX_SPLIT)
     return MLA_ERR_RANGE;
   if (batch == 0) return MLA_OK;
-  if (batch > 65535 || s_q > 65535 || static_cast<int64_t>(batch) * s_q > 65535 * 16)
+  if (batch > 65535 || s_q > 65535 || static_cast<int64_t>(batch) * s_q > 65535)
     return MLA_ERR_RANGE;
   if (static_cast<int64_t>(max_blocks) * dims->block_size > INT32_MAX) return MLA_ERR_RANGE;
   if (!q_nope || !q_pos || !gqa_cache || !block_table || !seq_lens || !out ||

@@ -14,9 +14,20 @@ namespace {
 
 constexpr int kTokTile = 16;   // tokens per projection workgroup
 constexpr int kColTile = 64;   // output columns per projection workgroup
-constexpr int kKStage = 64;    // k values staged in LDS per step
-constexpr int kKChunk = 512;   // C values reduced by one partial sum
+constexpr int kKStage = 256;   // k values staged in LDS per step (one k_chunk)
+constexpr int kKChunk = 256;   // C values reduced by one partial sum
 constexpr int kMaxTok = 2048;  // tokens per pass of the two kernels
+
+template <typename T>
+__device__ __forceinline__ void load16(const T* src, int n_avail, T* dst) {
+  // 16 bytes of T from global into LDS; the ragged / unaligned case element by element
+  constexpr int kVec = 16 / sizeof(T);
+  if (n_avail >= kVec && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  } else {
+    for (int u = 0; u < kVec; ++u) dst[u] = u < n_avail ? src[u] : T{};
+  }
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void append_project(const T* __restrict__ x,
@@ -24,44 +35,58 @@ __global__ __launch_bounds__(256) void append_project(const T* __restrict__ x,
                                                       const T* __restrict__ w_kr, int n_tok,
                                                       int C, int d_c, int d_r, int k_chunk,
                                                       float* __restrict__ y_part) {
-  __shared__ float xs[kTokTile][kKStage + 1];
+  // One workgroup: 64 output columns x one k_chunk-wide range of C x up to 16 tokens. Weights
+  // and activations are staged through LDS with 16-byte loads issued together; thread (column
+  // c, quarter kq) sums a quarter of the range for every token, and the quarters are added in
+  // a fixed order through LDS.
+  constexpr int kVec = 16 / sizeof(T);
+  __shared__ __attribute__((aligned(16))) T xs[kTokTile][kKStage];
+  __shared__ __attribute__((aligned(16))) T wsm[kKStage][kColTile];
+  __shared__ float part[4][kTokTile][kColTile];
   const int ncols = d_c + d_r;
-  const int col = blockIdx.x * kColTile + (threadIdx.x & 63);
-  const int tr = threadIdx.x >> 6;  // 0..3: token lane
+  const int c0 = blockIdx.x * kColTile;
   const int ks = blockIdx.y;
   const int n0 = blockIdx.z * kTokTile;
+  const int ntok = min(kTokTile, n_tok - n0);
   const int k0 = ks * k_chunk, k1 = min(C, k0 + k_chunk);
-  const T* wcol = nullptr;
-  int wstride = 0, wc = 0;
-  if (col < d_c) {
-    wcol = w_dkv; wstride = d_c; wc = col;
-  } else if (col < ncols) {
-    wcol = w_kr; wstride = d_r; wc = col - d_c;
+  const int kn = k1 - k0;
+  for (int e = threadIdx.x; e < ntok * (kKStage / kVec); e += 256) {
+    const int r = e / (kKStage / kVec), kv = (e % (kKStage / kVec)) * kVec;
+    load16(x + static_cast<int64_t>(n0 + r) * C + k0 + kv, kn - kv, &xs[r][kv]);
   }
-  float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int kk = k0; kk < k1; kk += kKStage) {
-    for (int e = threadIdx.x; e < kTokTile * kKStage; e += 256) {
-      const int r = e / kKStage, k = e % kKStage;
-      const int n = n0 + r, kg = kk + k;
-      xs[r][k] = (n < n_tok && kg < k1) ? ld(x, static_cast<int64_t>(n) * C + kg) : 0.f;
+  for (int e = threadIdx.x; e < kKStage * (kColTile / kVec); e += 256) {
+    const int k = e / (kColTile / kVec), cv = (e % (kColTile / kVec)) * kVec;
+    const int kg = k0 + k, cg = c0 + cv;
+    if (k >= kn || cg >= ncols) {
+      for (int u = 0; u < kVec; ++u) wsm[k][cv + u] = T{};
+    } else if (cg < d_c) {
+      load16(w_dkv + static_cast<int64_t>(kg) * d_c + cg, d_c - cg, &wsm[k][cv]);
+    } else {
+      load16(w_kr + static_cast<int64_t>(kg) * d_r + (cg - d_c), ncols - cg, &wsm[k][cv]);
     }
-    __syncthreads();
-    if (wcol != nullptr) {
-      const int kn = min(kKStage, k1 - kk);
-      for (int k = 0; k < kn; ++k) {
-        const float w = ld(wcol, static_cast<int64_t>(kk + k) * wstride + wc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] += xs[tr + 4 * r][k] * w;
-      }
-    }
-    __syncthreads();
   }
-  if (col < ncols) {
+  __syncthreads();
+  const int c = threadIdx.x & 63, kq = threadIdx.x >> 6;
+  const int kb = kq * (kKStage / 4), ke = min(kn, kb + kKStage / 4);
+  float acc[kTokTile];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = n0 + tr + 4 * r;
-      if (n < n_tok) y_part[(static_cast<int64_t>(ks) * n_tok + n) * ncols + col] = acc[r];
-    }
+  for (int r = 0; r < kTokTile; ++r) acc[r] = 0.f;
+  for (int k = kb; k < ke; ++k) {
+    const float wv = ld(&wsm[k][0], c);
+#pragma unroll
+    for (int r = 0; r < kTokTile; ++r)
+      if (r < ntok) acc[r] += ld(&xs[r][0], k) * wv;
+  }
+#pragma unroll
+  for (int r = 0; r < kTokTile; ++r)
+    if (r < ntok) part[kq][r][c] = acc[r];
+  __syncthreads();
+  for (int e = threadIdx.x; e < ntok * kColTile; e += 256) {
+    const int r = e / kColTile, cc = e % kColTile;
+    const int col = c0 + cc;
+    if (col >= ncols) continue;
+    const float y = ((part[0][r][cc] + part[1][r][cc]) + part[2][r][cc]) + part[3][r][cc];
+    y_part[(static_cast<int64_t>(ks) * n_tok + n0 + r) * ncols + col] = y;
   }
 }
 
@@ -77,8 +102,17 @@ __global__ __launch_bounds__(256) void append_finalize(
   const int ncols = d_c + d_r;
   float ss = 0.f;
   for (int c = threadIdx.x; c < ncols; c += blockDim.x) {
+    // partial sums added in the fixed order k = 0, 1, ...; loads issued eight at a time
     float y = 0.f;
-    for (int k = 0; k < n_ksplit; ++k) y += y_part[(static_cast<int64_t>(k) * n_tok + n) * ncols + c];
+    int k = 0;
+    for (; k + 8 <= n_ksplit; k += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = y_part[(static_cast<int64_t>(k + u) * n_tok + n) * ncols + c];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) y += v[u];
+    }
+    for (; k < n_ksplit; ++k) y += y_part[(static_cast<int64_t>(k) * n_tok + n) * ncols + c];
     ys[c] = y;
     if (c < d_c) ss += y * y;
   }
@@ -102,7 +136,7 @@ __global__ __launch_bounds__(256) void append_finalize(
 }  // namespace
 
 AppendPlan append_plan(const mla_dims& d, int n_tok) {
-  // Fixed 512-wide ranges of C per partial sum, added in a fixed order: a row's result does
+  // Fixed 256-wide ranges of C per partial sum, added in a fixed order: a row's result does
   // not depend on how many tokens are appended with it. Tokens go through in chunks of at
   // most kMaxTok, which bounds the workspace.
   AppendPlan p;

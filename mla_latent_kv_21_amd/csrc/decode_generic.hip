@@ -130,83 +130,137 @@ __global__ __launch_bounds__(256) void decode_generic(GenericArgs a) {
   for (int h = 0; h < a.H; ++h) split_head<T, kGqa>(a, b, i, k, h, qs, os, ps, sl, red);
 }
 
-constexpr int kCombRows = 16;
-
-// Merge the n_split partials of 16 (sequence, query) rows of one head, then project through
-// the head's group of W_UV (w_uv NULL: no projection). With `redo` set, splits the MFMA kernel
-// flagged are first recomputed here for this head by the portable split routine.
-template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(GenericArgs a, const int* __restrict__ redo,
-                                                      int M, int dv, const T* __restrict__ w_uv,
-                                                      T* __restrict__ out, float* lse_out) {
+// Merge of one (sequence, query) row of one head: weights exp2(lse_k - max) / sum over the
+// splits, then the weighted sum of the n_split partial vectors, each thread owning two
+// columns and keeping eight split loads in flight. With `redo` set, splits the MFMA kernel
+// flagged are first recomputed for this head by the portable split routine. Writes the merged
+// vector (fp32) to o_lat and the natural-log lse.
+__global__ __launch_bounds__(256) void merge_kernel(GenericArgs a, const int* __restrict__ redo,
+                                                    int is_bf16, float* __restrict__ o_lat,
+                                                    float* lse_out) {
   extern __shared__ float smem[];
-  const int pw = a.part_w, n_split = a.n_split, H = a.H;
-  float* os = smem;                      // [kCombRows][pw]
-  float* wts = os + kCombRows * pw;      // [kCombRows][n_split]
+  const int n_split = a.n_split, pw = a.part_w, H = a.H;
+  float* wts = smem;                     // [n_split]
   __shared__ float red[16];
-  const int h = blockIdx.x;
-  const int m0 = blockIdx.y * kCombRows;
-  const int g = h / (H / a.G);
+  const int h = blockIdx.x, m = blockIdx.y;
+  const int64_t rh = static_cast<int64_t>(m) * H + h;
   if (redo != nullptr) {
-    float* qs = wts + kCombRows * n_split;
+    float* qs = wts + ((n_split + 3) & ~3);
     float* ro = qs + a.q_w;
     float* ps = ro + pw;
     int64_t* sl = reinterpret_cast<int64_t*>(ps + kTok);
-    for (int r = 0; r < kCombRows; ++r) {
-      const int m = m0 + r;
-      if (m >= M) break;
-      for (int k = 0; k < n_split; ++k) {
-        if (redo[static_cast<int64_t>(m) * n_split + k] != 0)
-          split_head<T, false>(a, m / a.s_q, m % a.s_q, k, h, qs, ro, ps, sl, red);
+    for (int k = 0; k < n_split; ++k) {
+      if (redo[static_cast<int64_t>(m) * n_split + k] == 0) continue;
+      if (is_bf16)
+        split_head<bf16, false>(a, m / a.s_q, m % a.s_q, k, h, qs, ro, ps, sl, red);
+      else
+        split_head<float, false>(a, m / a.s_q, m % a.s_q, k, h, qs, ro, ps, sl, red);
+    }
+  }
+  const float* L = a.part_lse + rh * n_split;
+  float mx = -INFINITY;
+  for (int k = threadIdx.x; k < n_split; k += blockDim.x) mx = fmaxf(mx, L[k]);
+  mx = block_max(mx, red);
+  float sum = 0.f;
+  for (int k = threadIdx.x; k < n_split; k += blockDim.x)
+    sum += (mx == -INFINITY) ? 0.f : exp2f(L[k] - mx);
+  sum = block_sum(sum, red);
+  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+  for (int k = threadIdx.x; k < n_split; k += blockDim.x)
+    wts[k] = (mx == -INFINITY) ? 0.f : exp2f(L[k] - mx) * inv;
+  if (threadIdx.x == 0 && lse_out != nullptr)
+    lse_out[rh] = (mx == -INFINITY) ? -INFINITY : (mx + log2f(sum)) * kLn2;
+  __syncthreads();
+  const float* P = a.part_o + rh * n_split * pw;
+  for (int e = 2 * threadIdx.x; e < pw; e += 2 * blockDim.x) {
+    float ax = 0.f, ay = 0.f;
+    int k = 0;
+    for (; k + 8 <= n_split; k += 8) {
+      float2 v[8];
+      float wk[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        wk[u] = wts[k + u];
+        // empty splits (weight 0) were never written: do not read them
+        v[u] = wk[u] != 0.f ? *reinterpret_cast<const float2*>(P + static_cast<int64_t>(k + u) * pw + e)
+                            : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) { ax += wk[u] * v[u].x; ay += wk[u] * v[u].y; }
+    }
+    for (; k < n_split; ++k) {
+      const float wk = wts[k];
+      if (wk == 0.f) continue;
+      const float2 v = *reinterpret_cast<const float2*>(P + static_cast<int64_t>(k) * pw + e);
+      ax += wk * v.x;
+      ay += wk * v.y;
+    }
+    *reinterpret_cast<float2*>(o_lat + rh * pw + e) = make_float2(ax, ay);
+  }
+}
+
+constexpr int kProjRows = 16;
+constexpr int kProjCols = 32;
+
+// out[m, h] = o_lat[m, h] · W_UV[:, g(h)] for up to 16 rows m of one head and 32 output
+// columns: thread (column c, j-group jg) reduces W_UV rows j = jg*64 .. jg*64+63 for every row
+// (each W_UV element is loaded once per workgroup, the loads of a thread all in flight), then
+// the 8 j-groups are summed through LDS. w_uv NULL: out = o_lat (GQA path).
+template <typename T>
+__global__ __launch_bounds__(256) void project_kernel(const float* __restrict__ o_lat, int M,
+                                                      int H, int G, int pw, int dv,
+                                                      const T* __restrict__ w_uv,
+                                                      T* __restrict__ out) {
+  extern __shared__ float psm[];
+  float* os = psm;                          // [kProjRows][pw]
+  float* red = psm + kProjRows * pw;        // [8][kProjRows][kProjCols]
+  const int h = blockIdx.x, c0 = blockIdx.y * kProjCols, m0 = blockIdx.z * kProjRows;
+  const int g = h / (H / G);
+  const int rows = min(kProjRows, M - m0);
+  for (int e = threadIdx.x; e < rows * pw; e += blockDim.x) {
+    const int r = e / pw, j = e % pw;
+    os[e] = o_lat[(static_cast<int64_t>(m0 + r) * H + h) * pw + j];
+  }
+  __syncthreads();
+  const int c = threadIdx.x & (kProjCols - 1), jg = threadIdx.x / kProjCols;  // jg 0..7
+  const int v = c0 + c;
+  if (w_uv == nullptr) {
+    if (jg < rows && v < dv) st(out, (static_cast<int64_t>(m0 + jg) * H + h) * dv + v, os[jg * pw + v]);
+    if (jg + 8 < rows && v < dv)
+      st(out, (static_cast<int64_t>(m0 + jg + 8) * H + h) * dv + v, os[(jg + 8) * pw + v]);
+    return;
+  }
+  const int64_t ldw = static_cast<int64_t>(G) * dv;
+  const T* wc = w_uv + static_cast<int64_t>(g) * dv + (v < dv ? v : 0);
+  const int jper = (pw + 7) / 8;
+  const int j0 = jg * jper, j1 = min(pw, j0 + jper);
+  float acc[kProjRows];
+#pragma unroll
+  for (int r = 0; r < kProjRows; ++r) acc[r] = 0.f;
+  for (int j = j0; j < j1; j += 16) {
+    float wv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) wv[u] = (j + u < j1) ? ld(wc, (j + u) * ldw) : 0.f;
+#pragma unroll
+    for (int r = 0; r < kProjRows; ++r) {
+      if (r < rows) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (j + u < j1) acc[r] += os[r * pw + j + u] * wv[u];
       }
     }
-    __syncthreads();
   }
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  for (int r = wv; r < kCombRows; r += 4) {
-    const int m = m0 + r;
-    if (m >= M) continue;
-    const float* L = a.part_lse + (static_cast<int64_t>(m) * H + h) * n_split;
-    float mx = -INFINITY;
-    for (int k = lane; k < n_split; k += 64) mx = fmaxf(mx, L[k]);
-    mx = wave_max(mx);
+#pragma unroll
+  for (int r = 0; r < kProjRows; ++r)
+    if (r < rows) red[(jg * kProjRows + r) * kProjCols + c] = acc[r];
+  __syncthreads();
+  for (int e = threadIdx.x; e < rows * kProjCols; e += blockDim.x) {
+    const int r = e / kProjCols, cc = e % kProjCols;
+    if (c0 + cc >= dv) continue;
     float sum = 0.f;
-    for (int k = lane; k < n_split; k += 64) sum += (mx == -INFINITY) ? 0.f : exp2f(L[k] - mx);
-    sum = wave_sum(sum);
-    for (int k = lane; k < n_split; k += 64)
-      wts[r * n_split + k] = (mx == -INFINITY) ? 0.f : exp2f(L[k] - mx) / sum;
-    if (lane == 0 && lse_out != nullptr)
-      lse_out[static_cast<int64_t>(m) * H + h] = (mx == -INFINITY) ? -INFINITY : (mx + log2f(sum)) * kLn2;
-  }
-  __syncthreads();
-  for (int r = 0; r < kCombRows; ++r) {
-    const int m = m0 + r;
-    if (m >= M) break;
-    const float* P = a.part_o + (static_cast<int64_t>(m) * H + h) * n_split * pw;
-    for (int e = threadIdx.x; e < pw; e += blockDim.x) {
-      float acc = 0.f;
-      for (int k = 0; k < n_split; ++k) {
-        const float w = wts[r * n_split + k];
-        if (w != 0.f) acc += w * P[static_cast<int64_t>(k) * pw + e];  // empty splits: w == 0
-      }
-      os[r * pw + e] = acc;
-    }
-  }
-  __syncthreads();
-  const int64_t ldw = static_cast<int64_t>(a.G) * dv;
-  for (int idx = threadIdx.x; idx < kCombRows * dv; idx += blockDim.x) {
-    const int r = idx / dv, v = idx % dv;
-    const int m = m0 + r;
-    if (m >= M) continue;
-    float acc;
-    if (w_uv != nullptr) {
-      acc = 0.f;
-      const float* o = os + r * pw;
-      for (int j = 0; j < pw; ++j) acc += o[j] * ld(w_uv, j * ldw + static_cast<int64_t>(g) * dv + v);
-    } else {
-      acc = os[r * pw + v];
-    }
-    st(out, (static_cast<int64_t>(m) * H + h) * dv + v, acc);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) sum += red[(q * kProjRows + r) * kProjCols + cc];
+    st(out, (static_cast<int64_t>(m0 + r) * H + h) * dv + c0 + cc, sum);
   }
 }
 
@@ -219,13 +273,19 @@ hipError_t run_generic(const GenericArgs& a, int batch, hipStream_t s) {
 
 template <typename T>
 hipError_t run_combine(const GenericArgs& a, const int* redo, int batch, int dv, const void* w_uv,
-                       void* out, float* lse, hipStream_t s) {
+                       float* o_lat, void* out, float* lse, hipStream_t s) {
   const int M = batch * a.s_q;
-  const dim3 grid(a.H, cdiv(M, kCombRows));
-  size_t lds = static_cast<size_t>(kCombRows) * (a.part_w + a.n_split) * sizeof(float);
+  size_t lds = ((a.n_split + 3) & ~3) * sizeof(float);
   if (redo != nullptr) lds += split_head_lds(a);
-  hipLaunchKernelGGL(combine_kernel<T>, grid, dim3(256), lds, s, a, redo, M, dv,
-                     static_cast<const T*>(w_uv), static_cast<T*>(out), lse);
+  hipLaunchKernelGGL(merge_kernel, dim3(a.H, M), dim3(256), lds, s, a, redo,
+                     static_cast<int>(sizeof(T) == 2), o_lat, lse);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t plds = (static_cast<size_t>(kProjRows) * a.part_w +
+                       8 * kProjRows * kProjCols) * sizeof(float);
+  hipLaunchKernelGGL(project_kernel<T>, dim3(a.H, cdiv(dv, kProjCols), cdiv(M, kProjRows)),
+                     dim3(256), plds, s, o_lat, M, a.H, a.G, a.part_w, dv,
+                     static_cast<const T*>(w_uv), static_cast<T*>(out));
   return hipGetLastError();
 }
 
@@ -234,6 +294,7 @@ struct Partials {
   float* o;
   float* lse;
   int* redo;
+  float* o_lat;  // merged rows [B, s_q, H, width]
 };
 
 Partials partials_of(void* ws, int batch, int s_q, int heads, int n_split, int width) {
@@ -245,6 +306,8 @@ Partials partials_of(void* ws, int batch, int s_q, int heads, int n_split, int w
   p.lse = reinterpret_cast<float*>(base);
   base += (rows * sizeof(float) + 255) / 256 * 256;
   p.redo = reinterpret_cast<int*>(base);
+  base += (static_cast<size_t>(batch) * s_q * n_split * sizeof(int) + 255) / 256 * 256;
+  p.o_lat = reinterpret_cast<float*>(base);
   return p;
 }
 
@@ -273,7 +336,8 @@ size_t partials_bytes(int batch, int s_q, int heads, int n_split, int width) {
   const size_t o = (rows * width * sizeof(float) + 255) / 256 * 256;
   const size_t l = (rows * sizeof(float) + 255) / 256 * 256;
   const size_t f = (static_cast<size_t>(batch) * s_q * n_split * sizeof(int) + 255) / 256 * 256;
-  return o + l + f;
+  const size_t m = (static_cast<size_t>(batch) * s_q * heads * width * sizeof(float) + 255) / 256 * 256;
+  return o + l + f + m;
 }
 
 hipError_t launch_decode_splitk(const mla_dims& d, int batch, int s_q, const void* q_abs,
@@ -299,8 +363,8 @@ hipError_t launch_decode_merge(const mla_dims& d, int batch, int s_q, const void
                                     seq_lens, n_split, p);
   // Only the MFMA kernel writes recompute flags; the portable kernel computes every split.
   const int* redo = uses_mfma(d) ? p.redo : nullptr;
-  return d.dtype == MLA_BF16 ? run_combine<bf16>(a, redo, batch, d.d_v, w_uv, out, lse, s)
-                             : run_combine<float>(a, redo, batch, d.d_v, w_uv, out, lse, s);
+  return d.dtype == MLA_BF16 ? run_combine<bf16>(a, redo, batch, d.d_v, w_uv, p.o_lat, out, lse, s)
+                             : run_combine<float>(a, redo, batch, d.d_v, w_uv, p.o_lat, out, lse, s);
 }
 
 hipError_t launch_gqa_decode(const mla_dims& d, int batch, int s_q, const void* q_nope,
@@ -320,8 +384,9 @@ hipError_t launch_gqa_decode(const mla_dims& d, int batch, int s_q, const void* 
   hipError_t e = d.dtype == MLA_BF16 ? run_generic<bf16, true>(a, batch, s)
                                      : run_generic<float, true>(a, batch, s);
   if (e != hipSuccess) return e;
-  return d.dtype == MLA_BF16 ? run_combine<bf16>(a, nullptr, batch, d.d_v, nullptr, out, lse, s)
-                             : run_combine<float>(a, nullptr, batch, d.d_v, nullptr, out, lse, s);
+  return d.dtype == MLA_BF16
+             ? run_combine<bf16>(a, nullptr, batch, d.d_v, nullptr, p.o_lat, out, lse, s)
+             : run_combine<float>(a, nullptr, batch, d.d_v, nullptr, p.o_lat, out, lse, s);
 }
 
 }  // namespace mla

@@ -40,8 +40,8 @@ constexpr int kTileTok = 32;
 constexpr int kTileBytes = kTileTok * kRowBytes;  // 36,864
 constexpr int kTileChunks = kTileTok * kChunks;   // 2,304
 constexpr int kKSteps = kRowElems / 16;           // 36 MFMA K-steps for the scores
-constexpr int kLatSteps = kLat / 16;              // 32 of them over the latent part
-constexpr int kRopeSteps = kKSteps - kLatSteps;   // 4 over the rotary part
+constexpr int kRegSteps = 28;                     // query K-steps kept in registers
+constexpr int kLdsSteps = kKSteps - kRegSteps;    // the rest (incl. the rotary part) in LDS
 constexpr float kHead = 64.0f;                    // P <= 2^kHead, else recompute (log2)
 constexpr int kGrp = 4;                           // score K-steps per LDS read group
 
@@ -119,10 +119,19 @@ __device__ __forceinline__ int tile_valid(const MfmaArgs& a, int b, int pos0, in
 template <int NW>
 struct Shared {
   bf16x8 p[2][NW][2][64];  // P fragments: [parity][head block][K-step][lane]
-  bf16x8 qr[NW][kRopeSteps][64];  // rotary part of the queries (B operands of the last steps)
+  bf16x8 qr[NW][kLdsSteps][64];   // query B operands of the last K-steps
   float inv_l[NW * 32];
   int over[NW];            // a head of the wave outgrew its reference
 };
+
+typedef short __attribute__((ext_vector_type(4))) i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i receives
+// element (i % 4) of the 8 bytes addressed by lanes 4k + i/4, for k = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)((lds_char_t*)p));
+}
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -158,34 +167,38 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   const int l32 = lane & 31, hi = lane >> 5;
 
   // Absorbed queries of this wave's 32 heads as MFMA B operands: lane -> head 32w + l32,
-  // K-step ks covers row elements [16 ks + 8 hi, +8). The latent steps stay in registers for
-  // the whole split; the rotary steps are parked in LDS to leave registers for the pipeline.
-  bf16x8 qf[kLatSteps];
+  // K-step ks covers row elements [16 ks + 8 hi, +8). The first kRegSteps stay in registers
+  // for the whole split; the last ones (the rotary part among them) are parked in LDS to
+  // leave registers for the pipeline.
+  bf16x8 qf[kRegSteps];
   {
     const char* qp = reinterpret_cast<const char*>(a.q_abs) +
                      (row0 + 32 * w + l32) * kRowBytes + hi * 16;
 #pragma unroll
-    for (int ks = 0; ks < kLatSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+    for (int ks = 0; ks < kRegSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
 #pragma unroll
-    for (int r = 0; r < kRopeSteps; ++r)
-      sh.qr[w][r][lane] = *reinterpret_cast<const bf16x8*>(qp + (kLatSteps + r) * 32);
+    for (int r = 0; r < kLdsSteps; ++r)
+      sh.qr[w][r][lane] = *reinterpret_cast<const bf16x8*>(qp + (kRegSteps + r) * 32);
   }
 
   // Per-lane LDS byte offsets inside a ring slot; the rest of every swizzled address is a
   // compile-time constant carried in the instruction's offset field.
-  //  scores: position l32, chunk 8g + 2u + hi -> qb[u] + 128 g
+  //  scores (A operand): position l32, chunk 8g + 2u + hi -> qb[u] + 128 g
   int qb[kGrp];
 #pragma unroll
   for (int u = 0; u < kGrp; ++u) qb[u] = l32 * kRowBytes + (((2 * u + hi) ^ (l32 & 7)) << 4);
-  //  values: position 16 k2 + 8 (e>>2) + 4 hi + (e&3), latent column (512/NW) w + 32 db + l32
-  //  -> vb[db&1][e&3] + (16 k2 + 8 (e>>2)) * 1152 + (db>>1) * 128
-  int vb[2][4];
+  //  values (B operand, transposing reads): in 16-lane group G = lane/16, source lane
+  //  s = 4 kk + q addresses position 16 k2 + 8 rb + 4 (G/2) + kk and latent columns
+  //  (512/NW) w + 32 db + 16 (G%2) + 4 q .. +3 -> vt[db&1] + (16 k2 + 8 rb) * 1152 + (db>>1) * 128
+  int vt[2];
+  {
+    const int G = lane >> 4, s16 = lane & 15, kk = s16 >> 2, q = s16 & 3;
+    const int tokA = 4 * (G >> 1) + kk;  // position within the 16-position step, < 8
 #pragma unroll
-  for (int dp = 0; dp < 2; ++dp)
-#pragma unroll
-    for (int e3 = 0; e3 < 4; ++e3)
-      vb[dp][e3] = (4 * hi + e3) * kRowBytes + (((4 * dp + (l32 >> 3)) ^ (4 * hi + e3)) << 4) +
-                   2 * (l32 & 7) + (8 / NW) * w * 128;
+    for (int dp = 0; dp < 2; ++dp)
+      vt[dp] = tokA * kRowBytes + (((4 * dp + 2 * (G & 1) + (q >> 1)) ^ tokA) << 4) +
+               8 * (q & 1) + (8 / NW) * w * 128;
+  }
 
   f32x16 o[NW * kDB];
 #pragma unroll
@@ -197,76 +210,76 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   bool over = false;
   const int ntiles = cdiv(t1 - t0, kTileTok);
 
-  issue_tile<NW>(a, ring[0], b, t0, w, lane);
-  if (ntiles > 1) issue_tile<NW>(a, ring[1], b, t0 + kTileTok, w, lane);
-  wait_dma();
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int slot = t % 3;
-    const char* cur = ring[slot];
-    const int pos0 = t0 + t * kTileTok;
-    const int nvalid = tile_valid(a, b, pos0, t1);
-    // ---- scores S^T[position][head] over the 576-wide rows; fragments are read one group
-    // ahead of their MFMAs (same-opcode accumulation into one register set is forwarded).
+  // ---- scores S^T[position][head] of one tile over the 576-wide rows; fragments are read
+  // one group ahead of their MFMAs.
+  auto scores = [&](const char* cur) __attribute__((always_inline)) -> f32x16 {
     f32x16 sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-    {
-      bf16x8 cf[kGrp], nf[kGrp];
+    bf16x8 cf[kGrp], nf[kGrp];
 #pragma unroll
-      for (int u = 0; u < kGrp; ++u) cf[u] = *reinterpret_cast<const bf16x8*>(cur + qb[u]);
+    for (int u = 0; u < kGrp; ++u) cf[u] = *reinterpret_cast<const bf16x8*>(cur + qb[u]);
 #pragma unroll
-      for (int g = 0; g < kKSteps / kGrp; ++g) {
-        if (g + 1 < kKSteps / kGrp) {
+    for (int g = 0; g < kKSteps / kGrp; ++g) {
+      if (g + 1 < kKSteps / kGrp) {
 #pragma unroll
-          for (int u = 0; u < kGrp; ++u)
-            nf[u] = *reinterpret_cast<const bf16x8*>(cur + qb[u] + 128 * (g + 1));
-        }
-#pragma unroll
-        for (int u = 0; u < kGrp; ++u) {
-          const int ks = g * kGrp + u;
-          const bf16x8 qv = ks < kLatSteps ? qf[ks < kLatSteps ? ks : 0] : sh.qr[w][ks - kLatSteps][lane];
-          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf[u], qv, sc, 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < kGrp; ++u) cf[u] = nf[u];
+        for (int u = 0; u < kGrp; ++u)
+          nf[u] = *reinterpret_cast<const bf16x8*>(cur + qb[u] + 128 * (g + 1));
       }
-    }
-    // ---- softmax numerators against the head's fixed reference m_ref (log2 units): the
-    // first finite tile max. A tile exceeding it by more than kHead marks the split for
-    // recomputation by the portable kernel instead of rescaling O, so O is only ever
-    // touched by MFMAs here.
-    float mt = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int tp = 8 * (r >> 2) + 4 * hi + (r & 3);
-      sc[r] = tp < nvalid ? sc[r] * a.scale_log2 : -INFINITY;
-      mt = fmaxf(mt, sc[r]);
+      for (int u = 0; u < kGrp; ++u) {
+        const int ks = g * kGrp + u;
+        const bf16x8 qv = ks < kRegSteps ? qf[ks < kRegSteps ? ks : 0] : sh.qr[w][ks - kRegSteps][lane];
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf[u], qv, sc, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kGrp; ++u) cf[u] = nf[u];
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    return sc;
+  };
+
+  // ---- softmax numerators of one tile against the head's fixed reference m_ref (log2
+  // units): the first finite tile max. A tile exceeding it by more than kHead marks the split
+  // for exact recomputation instead of rescaling O, so O is only ever touched by MFMAs. The
+  // numerators are left in P's LDS slot `par` as the next MFMA's A operand.
+  auto softmax = [&](f32x16 sc, int nvalid, int par) __attribute__((always_inline)) {
+    if (nvalid < kTileTok) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * hi + (r & 3) >= nvalid) sc[r] = -INFINITY;
+    }
+    float mr = sc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mr = fmaxf(mr, sc[r]);
+    mr = fmaxf(mr, __shfl_xor(mr, 32, 64));
+    const float mt = mr * a.scale_log2;
     if (m_ref == -INFINITY) m_ref = mt;  // nothing accumulated yet for this head
     over = over || (mt > m_ref + kHead);
+    const float neg = m_ref == -INFINITY ? 0.f : -m_ref;  // all-masked so far: p = 0 anyway
     float psum = 0.f;
     bf16x8 pf[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = sc[r] == -INFINITY ? 0.f : exp2f(sc[r] - m_ref);
+      const float p = exp2f(fmaf(sc[r], a.scale_log2, neg));
       psum += p;
       pf[r >> 3][r & 7] = static_cast<__bf16>(p);
     }
     l_part += psum;
-    const int par = t & 1;
     sh.p[par][w][0][lane] = pf[0];
     sh.p[par][w][1][lane] = pf[1];
-    __builtin_amdgcn_sched_barrier(0);
-    // The next tile's loads land here, and P becomes visible to every wave.
-    wait_dma();
-    __syncthreads();
-    if (t + 2 < ntiles) issue_tile<NW>(a, ring[slot == 0 ? 2 : slot - 1], b, pos0 + 2 * kTileTok, w, lane);
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- O[heads x wave's latent columns] += P · V, one K-step (16 positions) at a time
+  };
+
+  // ---- O[heads x wave's latent columns] += P · V for one tile, 16 positions per K-step
+  // Rows of a partial tile past the history are zeroed in LDS before its P · V (their scores
+  // are masked, but 0 x NaN would still poison O).
+  auto zero_tail = [&](char* cur, int nvalid) __attribute__((always_inline)) {
+    const int from = nvalid * kChunks, to = kTileChunks;
+    for (int c = from + static_cast<int>(threadIdx.x); c < to; c += NW * 64)
+      *reinterpret_cast<uint4*>(cur + 16 * c) = make_uint4(0u, 0u, 0u, 0u);
+  };
+
+  auto pv = [&](const char* cur, int par) __attribute__((always_inline)) {
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       bf16x8 pa[NW];
@@ -274,21 +287,47 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       for (int hb = 0; hb < NW; ++hb) pa[hb] = sh.p[par][hb][k2][lane];
 #pragma unroll
       for (int db = 0; db < kDB; ++db) {
-        bf16x8 vf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int tp = 16 * k2 + 8 * (e >> 2) + 4 * hi + (e & 3);
-          const __bf16 x = *reinterpret_cast<const __bf16*>(
-              cur + vb[db & 1][e & 3] + (16 * k2 + 8 * (e >> 2)) * kRowBytes + (db >> 1) * 128);
-          vf[e] = tp < nvalid ? x : static_cast<__bf16>(0.f);
-        }
+        const char* vp = cur + vt[db & 1] + 16 * k2 * kRowBytes + (db >> 1) * 128;
+        const i16x4 v0 = lds_read_tr(vp);
+        const i16x4 v1 = lds_read_tr(vp + 8 * kRowBytes);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int hb = 0; hb < NW; ++hb)
           o[hb * kDB + db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[hb], vf, o[hb * kDB + db],
                                                                      0, 0, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // ---- pipeline: tiles t and t+1 sit in the ring while tile t+2 streams in; the scores and
+  // softmax of tile t+1 are formed before P · V of tile t so their VALU work can overlap it.
+  issue_tile<NW>(a, ring[0], b, t0, w, lane);
+  if (ntiles > 1) issue_tile<NW>(a, ring[1], b, t0 + kTileTok, w, lane);
+  wait_dma();
+  __syncthreads();
+  {
+    const int nv0 = tile_valid(a, b, t0, t1);
+    softmax(scores(ring[0]), nv0, 0);
+    if (nv0 < kTileTok) zero_tail(ring[0], nv0);
+  }
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int slot = t % 3;
+    const int nslot = slot == 2 ? 0 : slot + 1;
+    const int pos0 = t0 + t * kTileTok;
+    // P(t) and the zeroed tail of tile t become visible to every wave, tile t+1 has landed,
+    // the slot of tile t-1 is free.
+    wait_dma();
+    __syncthreads();
+    if (t + 2 < ntiles) issue_tile<NW>(a, ring[slot == 0 ? 2 : slot - 1], b, pos0 + 2 * kTileTok, w, lane);
+    // On the last tile the next slot holds stale data; with no valid position the softmax
+    // below masks every score and leaves m_ref, l and the flag unchanged.
+    const int nv_next = t + 1 < ntiles ? tile_valid(a, b, pos0 + kTileTok, t1) : 0;
+    const f32x16 sc = scores(ring[nslot]);
+    pv(ring[slot], t & 1);
+    softmax(sc, nv_next, (t + 1) & 1);
+    // zeroed before the next barrier, which also orders it after every wave's scores
+    if (t + 1 < ntiles && nv_next < kTileTok) zero_tail(ring[nslot], nv_next);
   }
 
   // ---- partials: o / l and m_ref + log2(l) per head, plus the recompute flag

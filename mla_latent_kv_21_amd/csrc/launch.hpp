@@ -25,8 +25,8 @@ hipError_t launch_absorb(const mla_dims& d, int batch, int s_q, const void* q_no
                          hipStream_t s);
 
 // Workspace of one split-K decode, each part 256-byte aligned: partial o [B, s_q, H, n_split,
-// width] fp32, partial lse2 [B, s_q, H, n_split] fp32 (log2 domain of scale*score), and
-// recompute flags [B, s_q, n_split] int32.
+// width] fp32, partial lse2 [B, s_q, H, n_split] fp32 (log2 domain of scale*score), recompute
+// flags [B, s_q, n_split] int32, and the merged rows [B, s_q, H, width] fp32.
 size_t partials_bytes(int batch, int s_q, int heads, int n_split, int width);
 
 // Split-K core: every (split, query, sequence) writes its partials (and recompute flag).
