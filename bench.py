@@ -89,6 +89,9 @@ def main():
                     help="workload index (default 4: H=128, d_c=512, 4 x 131,072 context)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the timed steps, copy a bf16 buffer of this many MiB three "
+                         "times (a plain copy of known size for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -184,6 +187,16 @@ def main():
         "step_latent_cache_GBps": tr["cache_bytes"] / (ms_step * 1e-3) / 1e9,
         "wall_s": wall,
     }
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 2
+        src = torch.randn(n, device=dev).to(torch.bfloat16)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)  # one elementwise kernel: reads and writes 2n bytes
+        torch.cuda.synchronize()
+        rec["copy_calibration"] = {"bytes_read": 2 * n, "bytes_written": 2 * n, "launches": 3,
+                                   "kernel": "torch elementwise neg (bf16)"}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, lens, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
