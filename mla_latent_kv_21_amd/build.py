@@ -25,6 +25,11 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags. decode_mfma.hip keeps its compiler-generated MFMA results in VGPRs
+# (its O accumulator lives in AGPRs through explicit instructions).
+EXTRA = {"decode_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith(".hip") or f.endswith(".cpp"))
@@ -33,7 +38,7 @@ def sources():
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), *lang, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -19,14 +19,19 @@ constexpr int kKChunk = 256;   // C values reduced by one partial sum
 constexpr int kMaxTok = 2048;  // tokens per pass of the two kernels
 
 template <typename T>
-__device__ __forceinline__ void load16(const T* src, int n_avail, T* dst) {
-  // 16 bytes of T from global into LDS; the ragged / unaligned case element by element
+__device__ __forceinline__ uint4 load16(const T* src, int n_avail) {
+  // 16 bytes of T; the ragged or unaligned case element by element (missing ones are zero)
   constexpr int kVec = 16 / sizeof(T);
-  if (n_avail >= kVec && (reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
-    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
-  } else {
-    for (int u = 0; u < kVec; ++u) dst[u] = u < n_avail ? src[u] : T{};
-  }
+  if (n_avail >= kVec && (reinterpret_cast<uintptr_t>(src) & 15u) == 0)
+    return *reinterpret_cast<const uint4*>(src);
+  union {
+    uint4 v;
+    T e[kVec];
+  } u;
+  u.v = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = 0; i < kVec; ++i)
+    if (i < n_avail) u.e[i] = src[i];
+  return u.v;
 }
 
 template <typename T>
@@ -50,20 +55,40 @@ __global__ __launch_bounds__(256) void append_project(const T* __restrict__ x,
   const int ntok = min(kTokTile, n_tok - n0);
   const int k0 = ks * k_chunk, k1 = min(C, k0 + k_chunk);
   const int kn = k1 - k0;
-  for (int e = threadIdx.x; e < ntok * (kKStage / kVec); e += 256) {
+  // every 16-byte load of the stage is issued before the first LDS store
+  constexpr int kXIt = kTokTile * (kKStage / kVec) / 256;   // 2 (bf16) or 4 (fp32)
+  constexpr int kWIt = kKStage * (kColTile / kVec) / 256;   // 8 (bf16) or 16 (fp32)
+  uint4 xr[kXIt], wr[kWIt];
+#pragma unroll
+  for (int i = 0; i < kXIt; ++i) {
+    const int e = threadIdx.x + 256 * i;
     const int r = e / (kKStage / kVec), kv = (e % (kKStage / kVec)) * kVec;
-    load16(x + static_cast<int64_t>(n0 + r) * C + k0 + kv, kn - kv, &xs[r][kv]);
+    xr[i] = r < ntok ? load16(x + static_cast<int64_t>(n0 + r) * C + k0 + kv, kn - kv)
+                     : make_uint4(0u, 0u, 0u, 0u);
   }
-  for (int e = threadIdx.x; e < kKStage * (kColTile / kVec); e += 256) {
+#pragma unroll
+  for (int i = 0; i < kWIt; ++i) {
+    const int e = threadIdx.x + 256 * i;
     const int k = e / (kColTile / kVec), cv = (e % (kColTile / kVec)) * kVec;
     const int kg = k0 + k, cg = c0 + cv;
-    if (k >= kn || cg >= ncols) {
-      for (int u = 0; u < kVec; ++u) wsm[k][cv + u] = T{};
-    } else if (cg < d_c) {
-      load16(w_dkv + static_cast<int64_t>(kg) * d_c + cg, d_c - cg, &wsm[k][cv]);
-    } else {
-      load16(w_kr + static_cast<int64_t>(kg) * d_r + (cg - d_c), ncols - cg, &wsm[k][cv]);
-    }
+    if (k >= kn || cg >= ncols)
+      wr[i] = make_uint4(0u, 0u, 0u, 0u);
+    else if (cg < d_c)
+      wr[i] = load16(w_dkv + static_cast<int64_t>(kg) * d_c + cg, d_c - cg);
+    else
+      wr[i] = load16(w_kr + static_cast<int64_t>(kg) * d_r + (cg - d_c), ncols - cg);
+  }
+#pragma unroll
+  for (int i = 0; i < kXIt; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    const int r = e / (kKStage / kVec), kv = (e % (kKStage / kVec)) * kVec;
+    *reinterpret_cast<uint4*>(&xs[r][kv]) = xr[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kWIt; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    const int k = e / (kColTile / kVec), cv = (e % (kColTile / kVec)) * kVec;
+    *reinterpret_cast<uint4*>(&wsm[k][cv]) = wr[i];
   }
   __syncthreads();
   const int c = threadIdx.x & 63, kq = threadIdx.x >> 6;
@@ -90,8 +115,97 @@ __global__ __launch_bounds__(256) void append_project(const T* __restrict__ x,
   }
 }
 
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int kWtStride = kKStage * 2 + 16;  // bytes per transposed weight column in LDS
+
+// bf16 projection on matrix cores, same partial sums as append_project (fixed 256-wide
+// ranges of C, so a row's bits do not depend on the other tokens appended with it). One
+// workgroup per (64 output columns, 256-wide range of C, 32 tokens); wave w computes the
+// 32 columns 32 (w & 1) .. for the half (w >> 1) of the range, and the two halves are added
+// in that order through LDS.
+//  * A operand (tokens x k): rows of x, 16 bytes per lane straight from memory;
+//  * B operand (k x columns): the weight tile is staged in LDS transposed (column-major, rows
+//    padded to 528 bytes), so each lane's 8 consecutive k of one column are one 16-byte read.
+__global__ __launch_bounds__(256) void append_project_mfma(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ w_dkv,
+                                                           const uint16_t* __restrict__ w_kr,
+                                                           int n_tok, int C, int d_c, int d_r,
+                                                           float* __restrict__ y_part) {
+  __shared__ __attribute__((aligned(16))) char wt[kColTile * kWtStride];
+  __shared__ float half1[2][16][64];
+  const int ncols = d_c + d_r;
+  const int c0 = blockIdx.x * kColTile;
+  const int ks = blockIdx.y;
+  const int n0 = blockIdx.z * 32;
+  const int k0 = ks * kKStage;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int cb = w & 1, kh = w >> 1;
+  // x fragments first (they do not depend on the staging)
+  const int n = n0 + l32;
+  bf16x8 af[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    const int k = k0 + 128 * kh + 16 * st + 8 * hi;
+    af[st] = bf16x8{};
+    if (n < n_tok && k + 8 <= C)
+      af[st] = *reinterpret_cast<const bf16x8*>(x + static_cast<int64_t>(n) * C + k);
+  }
+  // weight tile [256 k x 64 columns]: 16-byte loads (8 columns of one k), all in flight,
+  // then scattered into the transposed LDS layout
+  uint4 wr[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    const int k = e >> 3, cv = (e & 7) * 8;
+    const int kg = k0 + k, cg = c0 + cv;
+    wr[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (kg < C && cg < ncols) {
+      const uint16_t* src = cg < d_c ? w_dkv + static_cast<int64_t>(kg) * d_c + cg
+                                     : w_kr + static_cast<int64_t>(kg) * d_r + (cg - d_c);
+      wr[i] = *reinterpret_cast<const uint4*>(src);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int e = threadIdx.x + 256 * i;
+    const int k = e >> 3, cv = (e & 7) * 8;
+    const uint32_t v[4] = {wr[i].x, wr[i].y, wr[i].z, wr[i].w};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint16_t b = static_cast<uint16_t>(u & 1 ? v[u >> 1] >> 16 : v[u >> 1] & 0xffffu);
+      *reinterpret_cast<uint16_t*>(wt + (cv + u) * kWtStride + 2 * k) = b;
+    }
+  }
+  __syncthreads();
+  f32x16 acc = {};
+  const char* bcol = wt + (32 * cb + l32) * kWtStride + 2 * (128 * kh + 8 * hi);
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    const bf16x8 bf = *reinterpret_cast<const bf16x8*>(bcol + 32 * st);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[st], bf, acc, 0, 0, 0);
+  }
+  // D register r holds token 8 (r / 4) + 4 hi + r % 4, column l32
+  if (kh == 1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) half1[cb][r][lane] = acc[r];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const int col = c0 + 32 * cb + l32;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int tok = n0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (tok < n_tok && col < ncols)
+        y_part[(static_cast<int64_t>(ks) * n_tok + tok) * ncols + col] = acc[r] + half1[cb][r][lane];
+    }
+  }
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void append_finalize(
+__global__ __launch_bounds__(1024) void append_finalize(
     const float* __restrict__ y_part, int n_ksplit, int n_tok, const T* __restrict__ gamma,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ table, int batch, int max_blocks, int num_blocks, int bs,
@@ -102,17 +216,17 @@ __global__ __launch_bounds__(256) void append_finalize(
   const int ncols = d_c + d_r;
   float ss = 0.f;
   for (int c = threadIdx.x; c < ncols; c += blockDim.x) {
-    // partial sums added in the fixed order k = 0, 1, ...; loads issued eight at a time
+    // partial sums added in the fixed order k = 0, 1, ...; sixteen loads in flight
     float y = 0.f;
-    int k = 0;
-    for (; k + 8 <= n_ksplit; k += 8) {
-      float v[8];
+    for (int k = 0; k < n_ksplit; k += 16) {
+      float v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = y_part[(static_cast<int64_t>(k + u) * n_tok + n) * ncols + c];
+      for (int u = 0; u < 16; ++u)
+        v[u] = k + u < n_ksplit ? y_part[(static_cast<int64_t>(k + u) * n_tok + n) * ncols + c] : 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) y += v[u];
+      for (int u = 0; u < 16; ++u)
+        if (k + u < n_ksplit) y += v[u];
     }
-    for (; k < n_ksplit; ++k) y += y_part[(static_cast<int64_t>(k) * n_tok + n) * ncols + c];
     ys[c] = y;
     if (c < d_c) ss += y * y;
   }
@@ -156,16 +270,28 @@ hipError_t launch_append(const mla_dims& d, int n_tok, const void* x, const int3
   float* y_part = static_cast<float*>(ws);
   const size_t lds = static_cast<size_t>(d.d_c + d.d_r) * sizeof(float);
   const size_t elt = d.dtype == MLA_BF16 ? 2 : 4;
+  const int ncols = d.d_c + d.d_r;
+  const dim3 fin_block(ncols >= 1024 ? 1024 : (ncols + 63) / 64 * 64);
+  // matrix-core projection: every 16-byte weight and activation load stays inside one row
+  // and one of the two weight matrices (16-byte-aligned base pointers are a library rule)
+  const bool mfma_ok = !(d.flags & MLA_FLAG_GENERIC_KERNELS) && d.d_model % 8 == 0 &&
+                       d.d_c % 8 == 0 && d.d_r % 8 == 0;
   for (int t0 = 0; t0 < n_tok; t0 += kMaxTok) {
     const int n = n_tok - t0 < kMaxTok ? n_tok - t0 : kMaxTok;
     const AppendPlan p = append_plan(d, n);
     const dim3 g1(p.col_blocks, p.n_ksplit, p.tok_tiles);
     const void* xc = static_cast<const char*>(x) + static_cast<size_t>(t0) * d.d_model * elt;
     if (d.dtype == MLA_BF16) {
-      hipLaunchKernelGGL(append_project<bf16>, g1, dim3(256), 0, s, static_cast<const bf16*>(xc),
-                         static_cast<const bf16*>(w_dkv), static_cast<const bf16*>(w_kr), n,
-                         d.d_model, d.d_c, d.d_r, p.k_chunk, y_part);
-      hipLaunchKernelGGL(append_finalize<bf16>, dim3(n), dim3(256), lds, s, y_part, p.n_ksplit,
+      if (mfma_ok)
+        hipLaunchKernelGGL(append_project_mfma, dim3(p.col_blocks, p.n_ksplit, cdiv(n, 32)),
+                           dim3(256), 0, s, static_cast<const uint16_t*>(xc),
+                           static_cast<const uint16_t*>(w_dkv), static_cast<const uint16_t*>(w_kr),
+                           n, d.d_model, d.d_c, d.d_r, y_part);
+      else
+        hipLaunchKernelGGL(append_project<bf16>, g1, dim3(256), 0, s, static_cast<const bf16*>(xc),
+                           static_cast<const bf16*>(w_dkv), static_cast<const bf16*>(w_kr), n,
+                           d.d_model, d.d_c, d.d_r, p.k_chunk, y_part);
+      hipLaunchKernelGGL(append_finalize<bf16>, dim3(n), fin_block, lds, s, y_part, p.n_ksplit,
                          n, static_cast<const bf16*>(gamma), seq_idx + t0, pos + t0, table,
                          batch, max_blocks, num_blocks, d.block_size, d.d_c, d.d_r, d.rms_eps,
                          d.rope_base, static_cast<bf16*>(cache));
@@ -174,7 +300,7 @@ hipError_t launch_append(const mla_dims& d, int n_tok, const void* x, const int3
                          static_cast<const float*>(xc), static_cast<const float*>(w_dkv),
                          static_cast<const float*>(w_kr), n, d.d_model, d.d_c, d.d_r, p.k_chunk,
                          y_part);
-      hipLaunchKernelGGL(append_finalize<float>, dim3(n), dim3(256), lds, s, y_part, p.n_ksplit,
+      hipLaunchKernelGGL(append_finalize<float>, dim3(n), fin_block, lds, s, y_part, p.n_ksplit,
                          n, static_cast<const float*>(gamma), seq_idx + t0, pos + t0, table,
                          batch, max_blocks, num_blocks, d.block_size, d.d_c, d.d_r, d.rms_eps,
                          d.rope_base, static_cast<float*>(cache));

@@ -130,137 +130,187 @@ __global__ __launch_bounds__(256) void decode_generic(GenericArgs a) {
   for (int h = 0; h < a.H; ++h) split_head<T, kGqa>(a, b, i, k, h, qs, os, ps, sl, red);
 }
 
-// Merge of one (sequence, query) row of one head: weights exp2(lse_k - max) / sum over the
-// splits, then the weighted sum of the n_split partial vectors, each thread owning two
-// columns and keeping eight split loads in flight. With `redo` set, splits the MFMA kernel
-// flagged are first recomputed for this head by the portable split routine. Writes the merged
-// vector (fp32) to o_lat and the natural-log lse.
-__global__ __launch_bounds__(256) void merge_kernel(GenericArgs a, const int* __restrict__ redo,
-                                                    int is_bf16, float* __restrict__ o_lat,
-                                                    float* lse_out) {
-  extern __shared__ float smem[];
-  const int n_split = a.n_split, pw = a.part_w, H = a.H;
-  float* wts = smem;                     // [n_split]
-  __shared__ float red[16];
-  const int h = blockIdx.x, m = blockIdx.y;
-  const int64_t rh = static_cast<int64_t>(m) * H + h;
-  if (redo != nullptr) {
-    float* qs = wts + ((n_split + 3) & ~3);
-    float* ro = qs + a.q_w;
-    float* ps = ro + pw;
-    int64_t* sl = reinterpret_cast<int64_t*>(ps + kTok);
-    for (int k = 0; k < n_split; ++k) {
-      if (redo[static_cast<int64_t>(m) * n_split + k] == 0) continue;
-      if (is_bf16)
-        split_head<bf16, false>(a, m / a.s_q, m % a.s_q, k, h, qs, ro, ps, sl, red);
-      else
-        split_head<float, false>(a, m / a.s_q, m % a.s_q, k, h, qs, ro, ps, sl, red);
-    }
-  }
-  const float* L = a.part_lse + rh * n_split;
-  float mx = -INFINITY;
-  for (int k = threadIdx.x; k < n_split; k += blockDim.x) mx = fmaxf(mx, L[k]);
-  mx = block_max(mx, red);
-  float sum = 0.f;
-  for (int k = threadIdx.x; k < n_split; k += blockDim.x)
-    sum += (mx == -INFINITY) ? 0.f : exp2f(L[k] - mx);
-  sum = block_sum(sum, red);
-  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
-  for (int k = threadIdx.x; k < n_split; k += blockDim.x)
-    wts[k] = (mx == -INFINITY) ? 0.f : exp2f(L[k] - mx) * inv;
-  if (threadIdx.x == 0 && lse_out != nullptr)
-    lse_out[rh] = (mx == -INFINITY) ? -INFINITY : (mx + log2f(sum)) * kLn2;
-  __syncthreads();
-  const float* P = a.part_o + rh * n_split * pw;
-  for (int e = 2 * threadIdx.x; e < pw; e += 2 * blockDim.x) {
-    float ax = 0.f, ay = 0.f;
-    int k = 0;
-    for (; k + 8 <= n_split; k += 8) {
-      float2 v[8];
-      float wk[8];
+// Up to kVec consecutive elements of T (16 bytes) as floats; the vector load needs the
+// address 16-byte aligned, the ragged or unaligned case goes element by element.
+template <typename T>
+__device__ __forceinline__ void load_vec(const T* p, int n_avail, bool vec_ok,
+                                         float (&v)[16 / sizeof(T)]) {
+  constexpr int kVec = 16 / sizeof(T);
+  if (vec_ok && n_avail >= kVec) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(p);
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        wk[u] = wts[k + u];
-        // empty splits (weight 0) were never written: do not read them
-        v[u] = wk[u] != 0.f ? *reinterpret_cast<const float2*>(P + static_cast<int64_t>(k + u) * pw + e)
-                            : make_float2(0.f, 0.f);
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = __uint_as_float(w[e] << 16);
+        v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
       }
+    } else {
+      v[0] = __uint_as_float(raw.x); v[1] = __uint_as_float(raw.y);
+      v[2] = __uint_as_float(raw.z); v[3] = __uint_as_float(raw.w);
+    }
+  } else {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) { ax += wk[u] * v[u].x; ay += wk[u] * v[u].y; }
-    }
-    for (; k < n_split; ++k) {
-      const float wk = wts[k];
-      if (wk == 0.f) continue;
-      const float2 v = *reinterpret_cast<const float2*>(P + static_cast<int64_t>(k) * pw + e);
-      ax += wk * v.x;
-      ay += wk * v.y;
-    }
-    *reinterpret_cast<float2*>(o_lat + rh * pw + e) = make_float2(ax, ay);
+    for (int e = 0; e < kVec; ++e) v[e] = e < n_avail ? ld(p, e) : 0.f;
   }
 }
 
-constexpr int kProjRows = 16;
-constexpr int kProjCols = 32;
+constexpr int kMaxMergeW = 1024;  // partial row width (d_c or D_v) the merge keeps in LDS
 
-// out[m, h] = o_lat[m, h] · W_UV[:, g(h)] for up to 16 rows m of one head and 32 output
-// columns: thread (column c, j-group jg) reduces W_UV rows j = jg*64 .. jg*64+63 for every row
-// (each W_UV element is loaded once per workgroup, the loads of a thread all in flight), then
-// the 8 j-groups are summed through LDS. w_uv NULL: out = o_lat (GQA path).
+// One workgroup per (head h, query row m): merges the n_split partials of the row by their
+// log-sum-exp (weights 2^(lse_k - max) / sum), then applies the head's group of W_UV
+// (out = o_lat · W_UV[:, g(h)]) or, with w_uv NULL (GQA path), stores o_lat itself.
+//  * splits the matrix-core kernel flagged are first recomputed exactly (split_head);
+//  * the partial rows are read with 16-byte loads, 16 splits in flight per thread;
+//  * W_UV is read with 16-byte loads: thread (column group cg, row subgroup rs) owns kVec
+//    output columns and the W_UV rows j = rs, rs + nrs, ...; the row subgroups' sums are
+//    added through LDS in subgroup order.
 template <typename T>
-__global__ __launch_bounds__(256) void project_kernel(const float* __restrict__ o_lat, int M,
-                                                      int H, int G, int pw, int dv,
-                                                      const T* __restrict__ w_uv,
-                                                      T* __restrict__ out) {
-  extern __shared__ float psm[];
-  float* os = psm;                          // [kProjRows][pw]
-  float* red = psm + kProjRows * pw;        // [8][kProjRows][kProjCols]
-  const int h = blockIdx.x, c0 = blockIdx.y * kProjCols, m0 = blockIdx.z * kProjRows;
-  const int g = h / (H / G);
-  const int rows = min(kProjRows, M - m0);
-  for (int e = threadIdx.x; e < rows * pw; e += blockDim.x) {
-    const int r = e / pw, j = e % pw;
-    os[e] = o_lat[(static_cast<int64_t>(m0 + r) * H + h) * pw + j];
+__global__ __launch_bounds__(256) void merge_kernel(GenericArgs a, const int* __restrict__ redo,
+                                                    const T* __restrict__ w_uv, int dv,
+                                                    T* __restrict__ out, float* lse_out) {
+  constexpr int kVec = 16 / static_cast<int>(sizeof(T));
+  extern __shared__ float smem[];
+  __shared__ float red[16];
+  __shared__ float wts[MLA_MAX_SPLIT];
+  __shared__ __attribute__((aligned(16))) float o_s[kMaxMergeW];
+  __shared__ float4 mpart[256];
+  __shared__ float psum[256 * kVec];
+  const int n_split = a.n_split, pw = a.part_w, H = a.H;
+  const int h = blockIdx.x, m = blockIdx.y;
+  const int64_t rh = static_cast<int64_t>(m) * H + h;
+  const int tk = threadIdx.x;  // one split per thread: n_split <= MLA_MAX_SPLIT = blockDim.x
+  if (redo != nullptr) {
+    // the row's flags are read at once and gathered into a bit set (one word per wave)
+    __shared__ unsigned long long flagged[MLA_MAX_SPLIT / 64];
+    const bool f = tk < n_split && redo[static_cast<int64_t>(m) * n_split + tk] != 0;
+    const unsigned long long bits = __ballot(f);
+    if ((threadIdx.x & 63) == 0) flagged[threadIdx.x >> 6] = bits;
+    __syncthreads();
+    float* qs = smem;
+    float* ro = qs + a.q_w;
+    float* ps = ro + pw;
+    int64_t* sl = reinterpret_cast<int64_t*>(ps + kTok);
+    for (int word = 0; word < static_cast<int>(blockDim.x) / 64; ++word) {
+      unsigned long long left = flagged[word];
+      while (left != 0) {
+        const int k = word * 64 + __builtin_ctzll(left);
+        left &= left - 1;
+        split_head<T, false>(a, m / a.s_q, m % a.s_q, k, h, qs, ro, ps, sl, red);
+      }
+    }
   }
+  // ---- weights
+  const float lk = tk < n_split ? a.part_lse[rh * n_split + tk] : -INFINITY;
+  const float mx = block_max(lk, red);
+  const float ek = (tk < n_split && mx != -INFINITY) ? exp2f(lk - mx) : 0.f;
+  const float sum = block_sum(ek, red);
+  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+  if (tk < n_split) wts[tk] = ek * inv;
+  if (threadIdx.x == 0 && lse_out != nullptr)
+    lse_out[rh] = (mx == -INFINITY) ? -INFINITY : (mx + log2f(sum)) * kLn2;
   __syncthreads();
-  const int c = threadIdx.x & (kProjCols - 1), jg = threadIdx.x / kProjCols;  // jg 0..7
-  const int v = c0 + c;
-  if (w_uv == nullptr) {
-    if (jg < rows && v < dv) st(out, (static_cast<int64_t>(m0 + jg) * H + h) * dv + v, os[jg * pw + v]);
-    if (jg + 8 < rows && v < dv)
-      st(out, (static_cast<int64_t>(m0 + jg + 8) * H + h) * dv + v, os[(jg + 8) * pw + v]);
+  // ---- o_lat = sum_k w_k o_k into LDS
+  const float* P = a.part_o + rh * n_split * pw;
+  const int nq = pw >> 2;
+  if ((pw & 3) == 0) {
+    // thread (column quad cq, split group grp), split groups added in group order
+    const int ngrp = min(4, static_cast<int>(blockDim.x) / nq);
+    const int per = cdiv(n_split, ngrp);
+    const int cq = threadIdx.x % nq, grp = threadIdx.x / nq;
+    for (int q0 = 0; q0 < nq; q0 += blockDim.x) {   // pw > 1024 never happens (kMaxMergeW)
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      const int qq = q0 + cq;
+      if (grp < ngrp && qq < nq) {
+        const int k0 = grp * per, k1 = min(n_split, k0 + per);
+        for (int k = k0; k < k1; k += 16) {
+          float4 v[16];
+          float wk[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            wk[u] = k + u < k1 ? wts[k + u] : 0.f;
+            // empty splits (weight 0) were never written: do not read them
+            v[u] = wk[u] != 0.f
+                       ? *reinterpret_cast<const float4*>(P + static_cast<int64_t>(k + u) * pw + 4 * qq)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            acc.x = fmaf(wk[u], v[u].x, acc.x);
+            acc.y = fmaf(wk[u], v[u].y, acc.y);
+            acc.z = fmaf(wk[u], v[u].z, acc.z);
+            acc.w = fmaf(wk[u], v[u].w, acc.w);
+          }
+        }
+        mpart[grp * nq + cq] = acc;
+      }
+      __syncthreads();
+      if (threadIdx.x < nq && q0 + static_cast<int>(threadIdx.x) < nq) {
+        float4 r = mpart[threadIdx.x];
+        for (int q = 1; q < ngrp; ++q) {
+          const float4 t = mpart[q * nq + threadIdx.x];
+          r.x += t.x; r.y += t.y; r.z += t.z; r.w += t.w;
+        }
+        *reinterpret_cast<float4*>(o_s + 4 * (q0 + threadIdx.x)) = r;
+      }
+      __syncthreads();
+    }
+  } else {
+    for (int e = threadIdx.x; e < pw; e += blockDim.x) {
+      float acc = 0.f;
+      for (int k = 0; k < n_split; ++k) {
+        const float wk = wts[k];
+        if (wk != 0.f) acc = fmaf(wk, P[static_cast<int64_t>(k) * pw + e], acc);
+      }
+      o_s[e] = acc;
+    }
+    __syncthreads();
+  }
+  T* orow = out + rh * dv;
+  if (w_uv == nullptr) {  // GQA path: the merged rows are the output (pw == dv)
+    for (int v = threadIdx.x; v < dv; v += blockDim.x) st(orow, v, o_s[v]);
     return;
   }
-  const int64_t ldw = static_cast<int64_t>(G) * dv;
-  const T* wc = w_uv + static_cast<int64_t>(g) * dv + (v < dv ? v : 0);
-  const int jper = (pw + 7) / 8;
-  const int j0 = jg * jper, j1 = min(pw, j0 + jper);
-  float acc[kProjRows];
+  // ---- out = o_lat · W_UV[:, g(h)]
+  const int g = h / (H / a.G);
+  const int ncg = cdiv(dv, kVec);             // <= 256 (D_v <= 1024)
+  const int nrs = static_cast<int>(blockDim.x) / ncg;
+  const int cg = threadIdx.x % ncg, rs = threadIdx.x / ncg;
+  const int64_t ldw = static_cast<int64_t>(a.G) * dv;
+  const bool vec_ok = (ldw * static_cast<int64_t>(sizeof(T))) % 16 == 0 &&
+                      (reinterpret_cast<uintptr_t>(w_uv) & 15u) == 0;
+  float acc[kVec];
 #pragma unroll
-  for (int r = 0; r < kProjRows; ++r) acc[r] = 0.f;
-  for (int j = j0; j < j1; j += 16) {
-    float wv[16];
+  for (int e = 0; e < kVec; ++e) acc[e] = 0.f;
+  if (rs < nrs) {
+    const T* wc = w_uv + static_cast<int64_t>(g) * dv + cg * kVec;
+    const int navail = dv - cg * kVec;
+    for (int jb = rs; jb < pw; jb += 16 * nrs) {
+      float wv[16][kVec];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) wv[u] = (j + u < j1) ? ld(wc, (j + u) * ldw) : 0.f;
+      for (int u = 0; u < 16; ++u) {
+        const int j = jb + nrs * u;
+        load_vec(wc + static_cast<int64_t>(j < pw ? j : 0) * ldw, j < pw ? navail : 0, vec_ok,
+                 wv[u]);
+      }
 #pragma unroll
-    for (int r = 0; r < kProjRows; ++r) {
-      if (r < rows) {
+      for (int u = 0; u < 16; ++u) {
+        const int j = jb + nrs * u;
+        if (j >= pw) break;
+        const float o = o_s[j];
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
-          if (j + u < j1) acc[r] += os[r * pw + j + u] * wv[u];
+        for (int e = 0; e < kVec; ++e) acc[e] = fmaf(o, wv[u][e], acc[e]);
       }
     }
   }
 #pragma unroll
-  for (int r = 0; r < kProjRows; ++r)
-    if (r < rows) red[(jg * kProjRows + r) * kProjCols + c] = acc[r];
+  for (int e = 0; e < kVec; ++e) psum[threadIdx.x * kVec + e] = acc[e];
   __syncthreads();
-  for (int e = threadIdx.x; e < rows * kProjCols; e += blockDim.x) {
-    const int r = e / kProjCols, cc = e % kProjCols;
-    if (c0 + cc >= dv) continue;
-    float sum = 0.f;
-#pragma unroll
-    for (int q = 0; q < 8; ++q) sum += red[(q * kProjRows + r) * kProjCols + cc];
-    st(out, (static_cast<int64_t>(m0 + r) * H + h) * dv + c0 + cc, sum);
+  for (int v = threadIdx.x; v < dv; v += blockDim.x) {
+    const int c = v / kVec, e = v - c * kVec;
+    float r = 0.f;
+    for (int q = 0; q < nrs; ++q) r += psum[(q * ncg + c) * kVec + e];
+    st(orow, v, r);
   }
 }
 
@@ -273,19 +323,11 @@ hipError_t run_generic(const GenericArgs& a, int batch, hipStream_t s) {
 
 template <typename T>
 hipError_t run_combine(const GenericArgs& a, const int* redo, int batch, int dv, const void* w_uv,
-                       float* o_lat, void* out, float* lse, hipStream_t s) {
+                       void* out, float* lse, hipStream_t s) {
   const int M = batch * a.s_q;
-  size_t lds = ((a.n_split + 3) & ~3) * sizeof(float);
-  if (redo != nullptr) lds += split_head_lds(a);
-  hipLaunchKernelGGL(merge_kernel, dim3(a.H, M), dim3(256), lds, s, a, redo,
-                     static_cast<int>(sizeof(T) == 2), o_lat, lse);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t plds = (static_cast<size_t>(kProjRows) * a.part_w +
-                       8 * kProjRows * kProjCols) * sizeof(float);
-  hipLaunchKernelGGL(project_kernel<T>, dim3(a.H, cdiv(dv, kProjCols), cdiv(M, kProjRows)),
-                     dim3(256), plds, s, o_lat, M, a.H, a.G, a.part_w, dv,
-                     static_cast<const T*>(w_uv), static_cast<T*>(out));
+  const size_t lds = redo != nullptr ? split_head_lds(a) : 0;
+  hipLaunchKernelGGL(merge_kernel<T>, dim3(a.H, M), dim3(256), lds, s, a, redo,
+                     static_cast<const T*>(w_uv), dv, static_cast<T*>(out), lse);
   return hipGetLastError();
 }
 
@@ -294,7 +336,6 @@ struct Partials {
   float* o;
   float* lse;
   int* redo;
-  float* o_lat;  // merged rows [B, s_q, H, width]
 };
 
 Partials partials_of(void* ws, int batch, int s_q, int heads, int n_split, int width) {
@@ -306,8 +347,6 @@ Partials partials_of(void* ws, int batch, int s_q, int heads, int n_split, int w
   p.lse = reinterpret_cast<float*>(base);
   base += (rows * sizeof(float) + 255) / 256 * 256;
   p.redo = reinterpret_cast<int*>(base);
-  base += (static_cast<size_t>(batch) * s_q * n_split * sizeof(int) + 255) / 256 * 256;
-  p.o_lat = reinterpret_cast<float*>(base);
   return p;
 }
 
@@ -336,8 +375,7 @@ size_t partials_bytes(int batch, int s_q, int heads, int n_split, int width) {
   const size_t o = (rows * width * sizeof(float) + 255) / 256 * 256;
   const size_t l = (rows * sizeof(float) + 255) / 256 * 256;
   const size_t f = (static_cast<size_t>(batch) * s_q * n_split * sizeof(int) + 255) / 256 * 256;
-  const size_t m = (static_cast<size_t>(batch) * s_q * heads * width * sizeof(float) + 255) / 256 * 256;
-  return o + l + f + m;
+  return o + l + f;
 }
 
 hipError_t launch_decode_splitk(const mla_dims& d, int batch, int s_q, const void* q_abs,
@@ -363,8 +401,8 @@ hipError_t launch_decode_merge(const mla_dims& d, int batch, int s_q, const void
                                     seq_lens, n_split, p);
   // Only the MFMA kernel writes recompute flags; the portable kernel computes every split.
   const int* redo = uses_mfma(d) ? p.redo : nullptr;
-  return d.dtype == MLA_BF16 ? run_combine<bf16>(a, redo, batch, d.d_v, w_uv, p.o_lat, out, lse, s)
-                             : run_combine<float>(a, redo, batch, d.d_v, w_uv, p.o_lat, out, lse, s);
+  return d.dtype == MLA_BF16 ? run_combine<bf16>(a, redo, batch, d.d_v, w_uv, out, lse, s)
+                             : run_combine<float>(a, redo, batch, d.d_v, w_uv, out, lse, s);
 }
 
 hipError_t launch_gqa_decode(const mla_dims& d, int batch, int s_q, const void* q_nope,
@@ -385,8 +423,8 @@ hipError_t launch_gqa_decode(const mla_dims& d, int batch, int s_q, const void* 
                                      : run_generic<float, true>(a, batch, s);
   if (e != hipSuccess) return e;
   return d.dtype == MLA_BF16
-             ? run_combine<bf16>(a, nullptr, batch, d.d_v, nullptr, p.o_lat, out, lse, s)
-             : run_combine<float>(a, nullptr, batch, d.d_v, nullptr, p.o_lat, out, lse, s);
+             ? run_combine<bf16>(a, nullptr, batch, d.d_v, nullptr, out, lse, s)
+             : run_combine<float>(a, nullptr, batch, d.d_v, nullptr, out, lse, s);
 }
 
 }  // namespace mla

@@ -1,5 +1,5 @@
 // Split-K absorbed MLA decode on gfx950 matrix cores: bf16 latent cache with d_c = 512,
-// d_r = 64 (1,152-byte rows), H a multiple of 32, fp32 accumulation.
+// d_r = 64 (1,152-byte rows), H in {32, 64, 128}, fp32 accumulation.
 //
 // What is computed is the latent-space attention of Smallem article 13, "Ce que DeepSeek fait
 // de plus": scores of each absorbed query row against the whole [c || k_r] row (one product
@@ -9,20 +9,25 @@
 // HBM exactly once and sharing it across all H heads:
 //
 //  * one workgroup per (split, query, sequence); NW = H/32 waves; wave w owns heads
-//    [32w, 32w+32) for the scores and latent columns [512w/NW, 512(w+1)/NW) for the output;
+//    [32w, 32w+32) for the scores and latent columns [512w/NW, 512(w+1)/NW) of all heads for
+//    the output;
 //  * 32-position tiles (36,864 B, always inside one cache block) stream HBM -> LDS with
-//    global_load_lds_dwordx4 into a 3-deep ring, so two tiles are in flight while one is
-//    used; 16-byte chunks are XOR-swizzled by position so both LDS read patterns below are
-//    bank-conflict free;
+//    global_load_lds_dwordx4 into a 4-slot ring, two tiles in flight; 16-byte
+//    chunks are XOR-swizzled by position so every LDS read pattern below is free of bank
+//    conflicts;
 //  * scores S^T[32 positions x 32 heads] = tile · Q^T with v_mfma_f32_32x32x16_bf16 over the
 //    576-wide rows, the wave's absorbed queries held in registers for the whole split;
-//  * online softmax in the log2 domain with a lazy rescale (the running max is only raised
-//    when a tile exceeds it by more than 2^8, so P <= 256 and the O rescale is rare);
-//  * P (bf16) leaves each wave in the exact register layout the next MFMA consumes as its A
-//    operand (the position order inside a K-step is permuted consistently on both operands)
-//    and is exchanged through LDS; O[H x 512/NW] += P · V with V gathered position-major
-//    from the same LDS tile;
-//  * each split writes (O / l, m + log2 l) partials; the combine kernel merges splits.
+//  * softmax against a fixed per-head reference (the first finite tile max, log2 domain):
+//    O is never rescaled; a tile exceeding the reference by more than 2^64 flags the split,
+//    which the merge kernel then recomputes exactly;
+//  * P (bf16) leaves each wave in the register layout the P · V product consumes as its A
+//    operand (the position order inside a K-step is permuted identically on both operands)
+//    and is exchanged through LDS; O[H x 512/NW] += P · V with V read by transposing LDS
+//    reads from the same tile;
+//  * the loop body is scheduled by hand: the scores of tile t+1 run with their LDS reads
+//    several steps ahead, then P · V of tile t runs with the softmax of tile t+1 spread
+//    between its products, so the matrix cores are fed while the VALU and LDS work;
+//  * each split writes (O / l, m + log2 l) partials; the merge kernel combines the splits.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -31,6 +36,7 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef short __attribute__((ext_vector_type(4))) i16x4;
 
 constexpr int kRowElems = 576;            // d_c + d_r
 constexpr int kRowBytes = kRowElems * 2;  // 1,152
@@ -40,24 +46,21 @@ constexpr int kTileTok = 32;
 constexpr int kTileBytes = kTileTok * kRowBytes;  // 36,864
 constexpr int kTileChunks = kTileTok * kChunks;   // 2,304
 constexpr int kKSteps = kRowElems / 16;           // 36 MFMA K-steps for the scores
-constexpr int kRegSteps = 28;                     // query K-steps kept in registers
-constexpr int kLdsSteps = kKSteps - kRegSteps;    // the rest (incl. the rotary part) in LDS
 constexpr float kHead = 64.0f;                    // P <= 2^kHead, else recompute (log2)
-constexpr int kGrp = 4;                           // score K-steps per LDS read group
-
-struct MfmaArgs {
-  const uint16_t* q_abs;
-  const uint16_t* cache;
-  const int32_t* table;
-  const int32_t* lens;
-  int num_blocks, max_blocks, bs, s_q, n_split;
-  float scale_log2;
-  float* part_o;
-  float* part_lse;
-  int* redo;  // [B, s_q, n_split]: 1 where the split must be recomputed
-};
+constexpr int kPre = 6;                           // score fragments read ahead of their MFMA
+constexpr int kSlots = 4;                         // ring slots: two tiles in flight
 
 typedef __attribute__((address_space(3))) char lds_char_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+
+// Physical 16-byte chunk of logical chunk c in tile row t is c ^ swz(t). swz is a linear map
+// of the row's low four bits into three bits (a row's 72 chunks stay in their groups of 8).
+// It is chosen so that the score reads (16 bytes per lane, 32 rows x one chunk pair) and the
+// transposing value reads (8 bytes per lane, 4 rows x 2 chunks per 16 lanes) hit distinct
+// banks within every 128- and 256-byte LDS beat.
+__host__ __device__ constexpr int swz(int t) {
+  return ((t & 1) ? 3 : 0) ^ ((t & 2) ? 4 : 0) ^ ((t & 4) ? 2 : 0) ^ ((t & 8) ? 1 : 0);
+}
 
 // One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane i's 16 bytes from
 // gbase + off land at LDS byte address lds + 16 i. Issued from asm so that the compiler does
@@ -81,57 +84,56 @@ __device__ __forceinline__ unsigned lds_addr(const char* p) {
   return static_cast<unsigned>(reinterpret_cast<size_t>((lds_char_t*)p));
 }
 
-// Wait until every global -> LDS copy this wave issued has landed.
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// s_waitcnt immediate that waits for vmcnt <= n only (expcnt and lgkmcnt at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <int NW>
-__device__ __forceinline__ void issue_tile(const MfmaArgs& a, char* buf, int b, int pos0,
-                                           int w, int lane_in) {
-  // pos0 is a multiple of 32 and bs a multiple of 32, so the tile sits inside one block.
-  const int jb = pos0 / a.bs;
-  const int id = a.table[static_cast<int64_t>(b) * a.max_blocks + jb];
-  const bool ok = id >= 0 && id < a.num_blocks;
-  const char* base = reinterpret_cast<const char*>(a.cache) +
-                     (static_cast<int64_t>(ok ? id : 0) * a.bs + (pos0 - jb * a.bs)) * kRowBytes;
-  // The lane id goes through an empty asm so the per-lane offsets below are recomputed at
-  // each issue (a few VALU ops) instead of being hoisted out of the loop into registers.
-  int lane = lane_in;
-  asm volatile("" : "+v"(lane));
-  const unsigned lbase = lds_addr(buf);
-  constexpr int kIters = kTileChunks / (NW * 64);
-#pragma unroll
-  for (int j = 0; j < kIters; ++j) {
-    const int p = (j * NW + w) * 64 + lane;  // LDS chunk index this lane fills
-    const int t = p / kChunks;
-    const int c = (p - t * kChunks) ^ (t & 7);
-    dma16(base, static_cast<unsigned>(t * kRowBytes + c * 16), lbase + (j * NW + w) * 64 * 16);
-  }
+// Wait until at most `later` global -> LDS copies issued by this wave are still in flight:
+// copies complete in issue order, so everything issued before them has landed.
+template <int kLater>
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLater)); }
+
+// O += A · B with O held in accumulation registers (AGPRs). The score products use the
+// compiler's MFMA in its VGPR form (this file is built with MFMA results in VGPRs), so that
+// O (256 AGPRs) and the score accumulator never compete for one register file. The compiler
+// does not track this instruction's hazards: the leading s_nop covers a VALU write of A or B
+// just before it (two wait states); O is only ever written by this instruction, and is read
+// only after the explicit wait that follows the main loop.
+__device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& a, const bf16x8& b) {
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
 }
-
-// Positions of the tile (relative) that hold valid history: 0 for a bad block id.
-__device__ __forceinline__ int tile_valid(const MfmaArgs& a, int b, int pos0, int t1) {
-  const int jb = pos0 / a.bs;
-  const int id = a.table[static_cast<int64_t>(b) * a.max_blocks + jb];
-  const int n = t1 - pos0 < kTileTok ? t1 - pos0 : kTileTok;
-  return (id >= 0 && id < a.num_blocks) ? n : 0;
-}
-
-template <int NW>
-struct Shared {
-  bf16x8 p[2][NW][2][64];  // P fragments: [parity][head block][K-step][lane]
-  bf16x8 qr[NW][kLdsSteps][64];   // query B operands of the last K-steps
-  float inv_l[NW * 32];
-  int over[NW];            // a head of the wave outgrew its reference
-};
-
-typedef short __attribute__((ext_vector_type(4))) i16x4;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 // Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i receives
 // element (i % 4) of the 8 bytes addressed by lanes 4k + i/4, for k = 0..3.
 __device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)((lds_char_t*)p));
 }
+
+__device__ __forceinline__ bf16x8 lds16(const char* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// max over the lane pair (lane, lane ^ 32), without going through LDS
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+template <int NW>
+struct Shared {
+  bf16x8 p[2][NW][2][64];         // P fragments: [parity][head block][K-step][lane]
+};
+// After the loop the ring is free and holds the per-head 1/l and the waves' flags.
+template <int NW>
+struct Tail {
+  float inv_l[NW * 32];
+  int over[NW];                   // a head of the wave outgrew its reference
+};
+
+struct SoftState {
+  float m1, m2, m3, m4, m5, m6, mr, neg, psum;
+  bf16x8 pf[2];
+};
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -140,64 +142,74 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
                         int num_blocks, int max_blocks, int bs, int s_q, int n_split,
                         float scale_log2, float* __restrict__ part_o,
                         float* __restrict__ part_lse, int* __restrict__ redo) {
-  const MfmaArgs a{q_abs, cache, table, lens, num_blocks, max_blocks, bs, s_q, n_split,
-                   scale_log2, part_o, part_lse, redo};
   constexpr int H = NW * 32;
-  constexpr int kDB = 16 / NW;  // 32-column latent blocks per wave for P · V
-  __shared__ __attribute__((aligned(16))) char ring[3][kTileBytes];
+  constexpr int kDB = 16 / NW;                      // 32-column latent blocks per wave
+  constexpr int kPV = 2 * kDB * NW;                 // P · V products per tile (32)
+  constexpr int kDma = kTileChunks / (NW * 64);     // copies per wave per tile
+  __shared__ __attribute__((aligned(16))) char ring[kSlots][kTileBytes];
   __shared__ Shared<NW> sh;
+  static_assert(sizeof(ring) + sizeof(Shared<NW>) <= 160 * 1024, "LDS");
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int k = blockIdx.x, qi = blockIdx.y, b = blockIdx.z;
-  const int capacity = a.max_blocks * a.bs;
-  const int lim = visible_count(a.lens[b], a.s_q, qi, capacity);
+  const int capacity = max_blocks * bs;
+  const int lim = visible_count(lens[b], s_q, qi, capacity);
   int t0, t1;
-  split_range(lim, a.n_split, k, kSplitAlign, &t0, &t1);
-  const int64_t row0 = (static_cast<int64_t>(b) * a.s_q + qi) * H;  // first (b, qi, h) row
-  const int64_t split_id = (static_cast<int64_t>(b) * a.s_q + qi) * a.n_split + k;
+  split_range(lim, n_split, k, kSplitAlign, &t0, &t1);
+  const int64_t row0 = (static_cast<int64_t>(b) * s_q + qi) * H;  // first (b, qi, h) row
+  const int64_t split_id = (static_cast<int64_t>(b) * s_q + qi) * n_split + k;
 
   if (t0 >= t1) {  // empty split: weight zero in the merge; its o partial is never read
     for (int h = threadIdx.x; h < H; h += blockDim.x)
-      a.part_lse[(row0 + h) * a.n_split + k] = -INFINITY;
-    if (threadIdx.x == 0) a.redo[split_id] = 0;
+      part_lse[(row0 + h) * n_split + k] = -INFINITY;
+    if (threadIdx.x == 0) redo[split_id] = 0;
     return;
   }
 
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // Absorbed queries of this wave's 32 heads as MFMA B operands: lane -> head 32w + l32,
-  // K-step ks covers row elements [16 ks + 8 hi, +8). The first kRegSteps stay in registers
-  // for the whole split; the last ones (the rotary part among them) are parked in LDS to
-  // leave registers for the pipeline.
-  bf16x8 qf[kRegSteps];
+  // Absorbed queries of this wave's 32 heads as MFMA B operands, in registers for the whole
+  // split: lane -> head 32w + l32, K-step ks covers row elements [16 ks + 8 hi, +8).
+  bf16x8 qf[kKSteps];
   {
-    const char* qp = reinterpret_cast<const char*>(a.q_abs) +
-                     (row0 + 32 * w + l32) * kRowBytes + hi * 16;
+    const char* qp = reinterpret_cast<const char*>(q_abs) + (row0 + 32 * w + l32) * kRowBytes +
+                     hi * 16;
 #pragma unroll
-    for (int ks = 0; ks < kRegSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
-#pragma unroll
-    for (int r = 0; r < kLdsSteps; ++r)
-      sh.qr[w][r][lane] = *reinterpret_cast<const bf16x8*>(qp + (kRegSteps + r) * 32);
+    for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
   }
 
-  // Per-lane LDS byte offsets inside a ring slot; the rest of every swizzled address is a
-  // compile-time constant carried in the instruction's offset field.
-  //  scores (A operand): position l32, chunk 8g + 2u + hi -> qb[u] + 128 g
-  int qb[kGrp];
+  // Per-lane byte offsets; the rest of every swizzled address is a compile-time constant.
+  //  copies: LDS chunk p = (j NW + w) 64 + lane of a slot holds row p / 72, physical chunk
+  //  p % 72, i.e. logical chunk (p % 72) ^ swz(row) of the cache rows.
+  unsigned doff[kDma];
 #pragma unroll
-  for (int u = 0; u < kGrp; ++u) qb[u] = l32 * kRowBytes + (((2 * u + hi) ^ (l32 & 7)) << 4);
+  for (int j = 0; j < kDma; ++j) {
+    const int p = (j * NW + w) * 64 + lane;
+    const int t = p / kChunks;
+    const int c = p - t * kChunks;
+    doff[j] = static_cast<unsigned>(t * kRowBytes + ((c ^ swz(t)) << 4));
+  }
+  //  scores (A operand): position l32, K-step ks = 4 g + u reads logical chunk 2 ks + hi
+  //  = 8 g + 2 u + hi -> qb[u] + 128 g
+  int qb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) qb[u] = l32 * kRowBytes + (((2 * u + hi) ^ swz(l32)) << 4);
   //  values (B operand, transposing reads): in 16-lane group G = lane/16, source lane
   //  s = 4 kk + q addresses position 16 k2 + 8 rb + 4 (G/2) + kk and latent columns
-  //  (512/NW) w + 32 db + 16 (G%2) + 4 q .. +3 -> vt[db&1] + (16 k2 + 8 rb) * 1152 + (db>>1) * 128
-  int vt[2];
+  //  (512/NW) w + 32 db + 16 (G%2) + 4 q .. +3 -> vt[db&1][rb] + 16 k2 * 1152 + (db>>1) * 128
+  int vt[2][2];
   {
     const int G = lane >> 4, s16 = lane & 15, kk = s16 >> 2, q = s16 & 3;
-    const int tokA = 4 * (G >> 1) + kk;  // position within the 16-position step, < 8
+    const int tokA = 4 * (G >> 1) + kk;
 #pragma unroll
     for (int dp = 0; dp < 2; ++dp)
-      vt[dp] = tokA * kRowBytes + (((4 * dp + 2 * (G & 1) + (q >> 1)) ^ tokA) << 4) +
-               8 * (q & 1) + (8 / NW) * w * 128;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        const int t = 8 * rb + tokA;
+        vt[dp][rb] = t * kRowBytes + (((4 * dp + 2 * (G & 1) + (q >> 1)) ^ swz(t)) << 4) +
+                     8 * (q & 1) + (8 / NW) * w * 128;
+      }
   }
 
   f32x16 o[NW * kDB];
@@ -210,31 +222,40 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   bool over = false;
   const int ntiles = cdiv(t1 - t0, kTileTok);
 
-  // ---- scores S^T[position][head] of one tile over the 576-wide rows; fragments are read
-  // one group ahead of their MFMAs.
+  // Cache address of the tile at pos0 (a multiple of 32 inside one block) and its number of
+  // valid positions (0 for a bad block id, whose rows are then never used).
+  auto tile_src = [&](int pos0, int* nvalid) -> const char* {
+    const int jb = pos0 / bs;
+    const int id = table[static_cast<int64_t>(b) * max_blocks + jb];
+    const bool ok = id >= 0 && id < num_blocks;
+    const int n = t1 - pos0 < kTileTok ? t1 - pos0 : kTileTok;
+    *nvalid = ok ? n : 0;
+    return reinterpret_cast<const char*>(cache) +
+           (static_cast<int64_t>(ok ? id : 0) * bs + (pos0 - jb * bs)) * kRowBytes;
+  };
+  auto issue_tile = [&](const char* src, char* slot) __attribute__((always_inline)) {
+    const unsigned lbase = lds_addr(slot) + w * 64 * 16;
+#pragma unroll
+    for (int j = 0; j < kDma; ++j) dma16(src, doff[j], lbase + j * NW * 64 * 16);
+  };
+
+  // ---- scores S^T[position][head] of one tile over the 576-wide rows, each fragment read
+  // kPre products ahead of its MFMA.
   auto scores = [&](const char* cur) __attribute__((always_inline)) -> f32x16 {
     f32x16 sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-    bf16x8 cf[kGrp], nf[kGrp];
+    bf16x8 af[kPre];
 #pragma unroll
-    for (int u = 0; u < kGrp; ++u) cf[u] = *reinterpret_cast<const bf16x8*>(cur + qb[u]);
+    for (int i = 0; i < kPre; ++i) af[i] = lds16(cur + qb[i & 3] + 128 * (i >> 2));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int g = 0; g < kKSteps / kGrp; ++g) {
-      if (g + 1 < kKSteps / kGrp) {
-#pragma unroll
-        for (int u = 0; u < kGrp; ++u)
-          nf[u] = *reinterpret_cast<const bf16x8*>(cur + qb[u] + 128 * (g + 1));
-      }
-#pragma unroll
-      for (int u = 0; u < kGrp; ++u) {
-        const int ks = g * kGrp + u;
-        const bf16x8 qv = ks < kRegSteps ? qf[ks < kRegSteps ? ks : 0] : sh.qr[w][ks - kRegSteps][lane];
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf[u], qv, sc, 0, 0, 0);
-      }
+    for (int ks = 0; ks < kKSteps; ++ks) {
+      const bf16x8 acur = af[ks % kPre];
+      const int nx = ks + kPre;
+      if (nx < kKSteps) af[ks % kPre] = lds16(cur + qb[nx & 3] + 128 * (nx >> 2));
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur, qf[ks], sc, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < kGrp; ++u) cf[u] = nf[u];
     }
     return sc;
   };
@@ -242,35 +263,60 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   // ---- softmax numerators of one tile against the head's fixed reference m_ref (log2
   // units): the first finite tile max. A tile exceeding it by more than kHead marks the split
   // for exact recomputation instead of rescaling O, so O is only ever touched by MFMAs. The
-  // numerators are left in P's LDS slot `par` as the next MFMA's A operand.
-  auto softmax = [&](f32x16 sc, int nvalid, int par) __attribute__((always_inline)) {
-    if (nvalid < kTileTok) {
+  // numerators are left in P's LDS slot `par` as the A operand of the next P · V.
+  // Split in pieces (compile-time numbers) so the unmasked case can be spread between the
+  // P · V products.
+  constexpr int kSoftPieces = 18;
+  auto soft_piece = [&](int piece, f32x16& sc, SoftState& s, int par)
+                        __attribute__((always_inline)) {
+    if (piece == 0) {
+      s.m1 = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+      s.m2 = fmaxf(fmaxf(sc[3], sc[4]), sc[5]);
+      s.m3 = fmaxf(fmaxf(sc[6], sc[7]), sc[8]);
+    } else if (piece == 1) {
+      s.m4 = fmaxf(fmaxf(sc[9], sc[10]), sc[11]);
+      s.m5 = fmaxf(fmaxf(sc[12], sc[13]), sc[14]);
+      s.m6 = fmaxf(fmaxf(sc[15], s.m1), s.m2);
+    } else if (piece == 2) {
+      s.mr = fmaxf(fmaxf(fmaxf(s.m3, s.m4), s.m5), s.m6);
+    } else if (piece == 3) {
+      s.mr = max_xor32(s.mr);
+    } else if (piece == 4) {
+      const float mt = s.mr * scale_log2;
+      if (m_ref == -INFINITY) m_ref = mt;  // nothing accumulated yet for this head
+      over = over || (mt > m_ref + kHead);
+      s.neg = m_ref == -INFINITY ? 0.f : -m_ref;  // all masked so far: p = 0 anyway
+      s.psum = 0.f;
+    } else if (piece <= 12) {
+      const int r = 2 * (piece - 5);
+      // v_exp_f32: results below 2^-126 may flush to zero, negligible against l >= 1
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, s.neg));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], scale_log2, s.neg));
+      s.psum += p0 + p1;
+      sc[r] = p0;
+      sc[r + 1] = p1;
+    } else if (piece <= 16) {
+      const int r = 4 * (piece - 13);
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + 4 * hi + (r & 3) >= nvalid) sc[r] = -INFINITY;
+      for (int e = 0; e < 4; ++e) s.pf[r >> 3][(r & 7) + e] = static_cast<__bf16>(sc[r + e]);
+    } else {
+      l_part += s.psum;
+      sh.p[par][w][0][lane] = s.pf[0];
+      sh.p[par][w][1][lane] = s.pf[1];
     }
-    float mr = sc[0];
+  };
+  auto mask_tail = [&](f32x16& sc, int nvalid) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mr = fmaxf(mr, sc[r]);
-    mr = fmaxf(mr, __shfl_xor(mr, 32, 64));
-    const float mt = mr * a.scale_log2;
-    if (m_ref == -INFINITY) m_ref = mt;  // nothing accumulated yet for this head
-    over = over || (mt > m_ref + kHead);
-    const float neg = m_ref == -INFINITY ? 0.f : -m_ref;  // all-masked so far: p = 0 anyway
-    float psum = 0.f;
-    bf16x8 pf[2];
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + 4 * hi + (r & 3) >= nvalid) sc[r] = -INFINITY;
+  };
+  auto softmax_all = [&](f32x16 sc, int nvalid, int par) __attribute__((always_inline)) {
+    if (nvalid < kTileTok) mask_tail(sc, nvalid);
+    SoftState s;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = exp2f(fmaf(sc[r], a.scale_log2, neg));
-      psum += p;
-      pf[r >> 3][r & 7] = static_cast<__bf16>(p);
-    }
-    l_part += psum;
-    sh.p[par][w][0][lane] = pf[0];
-    sh.p[par][w][1][lane] = pf[1];
+    for (int i = 0; i < kSoftPieces; ++i) soft_piece(i, sc, s, par);
   };
 
-  // ---- O[heads x wave's latent columns] += P · V for one tile, 16 positions per K-step
   // Rows of a partial tile past the history are zeroed in LDS before its P · V (their scores
   // are masked, but 0 x NaN would still poison O).
   auto zero_tail = [&](char* cur, int nvalid) __attribute__((always_inline)) {
@@ -279,80 +325,120 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       *reinterpret_cast<uint4*>(cur + 16 * c) = make_uint4(0u, 0u, 0u, 0u);
   };
 
-  auto pv = [&](const char* cur, int par) __attribute__((always_inline)) {
+  // ---- O[heads x wave's latent columns] += P · V for one tile, 16 positions per K-step,
+  // with the softmax pieces of the next tile's scores `sc` between the products.
+  auto pv = [&](const char* cur, int par, f32x16& sc, int npar) __attribute__((always_inline)) {
+    SoftState s;
+    bf16x8 pa[2][NW];
+    i16x4 va[2][2];  // [buffer][rb]
 #pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      bf16x8 pa[NW];
+    for (int hb = 0; hb < NW; ++hb) pa[0][hb] = sh.p[par][hb][0][lane];
+    va[0][0] = lds_read_tr(cur + vt[0][0]);
+    va[0][1] = lds_read_tr(cur + vt[0][1]);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int hb = 0; hb < NW; ++hb) pa[hb] = sh.p[par][hb][k2][lane];
-#pragma unroll
-      for (int db = 0; db < kDB; ++db) {
-        const char* vp = cur + vt[db & 1] + 16 * k2 * kRowBytes + (db >> 1) * 128;
-        const i16x4 v0 = lds_read_tr(vp);
-        const i16x4 v1 = lds_read_tr(vp + 8 * kRowBytes);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int hb = 0; hb < NW; ++hb)
-          o[hb * kDB + db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[hb], vf, o[hb * kDB + db],
-                                                                     0, 0, 0);
+    for (int i = 0; i < kPV; ++i) {
+      const int k2 = i / (kDB * NW), db = (i / NW) % kDB, hb = i % NW;
+      const int buf = (i / NW) & 1;
+      if (hb == 0 && i + NW < kPV) {  // fragment of the next (k2, db)
+        const int n2 = (i + NW) / (kDB * NW), ndb = ((i + NW) / NW) % kDB;
+        const char* vp = cur + 16 * n2 * kRowBytes + (ndb >> 1) * 128;
+        va[buf ^ 1][0] = lds_read_tr(vp + vt[ndb & 1][0]);
+        va[buf ^ 1][1] = lds_read_tr(vp + vt[ndb & 1][1]);
       }
+      if (i == kPV / 4) {
+#pragma unroll
+        for (int h2 = 0; h2 < NW; ++h2) pa[1][h2] = sh.p[par][h2][1][lane];
+      }
+      const bf16x8 vf = __builtin_bit_cast(
+          bf16x8, __builtin_shufflevector(va[buf][0], va[buf][1], 0, 1, 2, 3, 4, 5, 6, 7));
+      mfma_o(o[hb * kDB + db], pa[k2][hb], vf);
+      // pieces start two products in, once the last score product has landed
+      if (i >= 2 && i - 2 < kSoftPieces) soft_piece(i - 2, sc, s, npar);
+      __builtin_amdgcn_sched_barrier(0);
     }
+#pragma unroll
+    for (int i = kPV - 2; i < kSoftPieces; ++i) soft_piece(i, sc, s, npar);
   };
 
-  // ---- pipeline: tiles t and t+1 sit in the ring while tile t+2 streams in; the scores and
-  // softmax of tile t+1 are formed before P · V of tile t so their VALU work can overlap it.
-  issue_tile<NW>(a, ring[0], b, t0, w, lane);
-  if (ntiles > 1) issue_tile<NW>(a, ring[1], b, t0 + kTileTok, w, lane);
-  wait_dma();
-  __syncthreads();
+  // ---- pipeline. Iteration t: tile t+1 has landed, tiles t+2 and t+3 are in flight (t+3
+  // issued into the slot tile t-1 used), the scores of tile t+1 are formed, then P · V of
+  // tile t runs with the softmax of tile t+1 spread between its products.
   {
-    const int nv0 = tile_valid(a, b, t0, t1);
-    softmax(scores(ring[0]), nv0, 0);
+    int nv0, nvx;
+    issue_tile(tile_src(t0, &nv0), ring[0]);
+    if (ntiles > 1) issue_tile(tile_src(t0 + kTileTok, &nvx), ring[1]);
+    if (ntiles > 2) issue_tile(tile_src(t0 + 2 * kTileTok, &nvx), ring[2]);
+    if (ntiles > 2)
+      wait_dma<2 * kDma>();
+    else if (ntiles > 1)
+      wait_dma<kDma>();
+    else
+      wait_dma<0>();
+    __syncthreads();
+    softmax_all(scores(ring[0]), nv0, 0);
     if (nv0 < kTileTok) zero_tail(ring[0], nv0);
   }
 
   for (int t = 0; t < ntiles; ++t) {
-    const int slot = t % 3;
-    const int nslot = slot == 2 ? 0 : slot + 1;
+    const int slot = t & (kSlots - 1);
+    const int nslot = (t + 1) & (kSlots - 1);
     const int pos0 = t0 + t * kTileTok;
-    // P(t) and the zeroed tail of tile t become visible to every wave, tile t+1 has landed,
-    // the slot of tile t-1 is free.
-    wait_dma();
+    // tile t+1 has landed (tile t+2 may still be in flight); after the barrier P(t) and the
+    // zeroed tail of tile t are visible to every wave and the slot of tile t-1 is free
+    if (t + 2 < ntiles)
+      wait_dma<kDma>();
+    else
+      wait_dma<0>();
     __syncthreads();
-    if (t + 2 < ntiles) issue_tile<NW>(a, ring[slot == 0 ? 2 : slot - 1], b, pos0 + 2 * kTileTok, w, lane);
-    // On the last tile the next slot holds stale data; with no valid position the softmax
-    // below masks every score and leaves m_ref, l and the flag unchanged.
-    const int nv_next = t + 1 < ntiles ? tile_valid(a, b, pos0 + kTileTok, t1) : 0;
-    const f32x16 sc = scores(ring[nslot]);
-    pv(ring[slot], t & 1);
-    softmax(sc, nv_next, (t + 1) & 1);
-    // zeroed before the next barrier, which also orders it after every wave's scores
+    if (t + 3 < ntiles) {
+      int nv3;
+      issue_tile(tile_src(pos0 + 3 * kTileTok, &nv3), ring[(t + 3) & (kSlots - 1)]);
+    }
+    // One body for every iteration (separate paths would split the query registers' live
+    // ranges): on the last tile the next slot holds stale data, and with no valid position
+    // the mask turns every score into -inf, which leaves m_ref, l and the flag unchanged.
+    int nv_next = 0;
+    if (t + 1 < ntiles) tile_src(pos0 + kTileTok, &nv_next);
+    f32x16 sc = scores(ring[nslot]);
+    if (nv_next < kTileTok) mask_tail(sc, nv_next);
+    pv(ring[slot], t & 1, sc, (t + 1) & 1);
+    // zeroed before the next barrier; other waves may still be reading these rows for their
+    // scores, which are masked anyway
     if (t + 1 < ntiles && nv_next < kTileTok) zero_tail(ring[nslot], nv_next);
   }
 
-  // ---- partials: o / l and m_ref + log2(l) per head, plus the recompute flag
+  // ---- partials: o / l and m_ref + log2(l) per head, plus the recompute flag.
+  // The last O products must have landed before VALU reads of O: 32 wait states, more than
+  // any matrix-core result latency.
+  asm volatile("s_nop 15\n\ts_nop 15"
+               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                 "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
+                 "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
   const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
   const bool wover = __builtin_amdgcn_ballot_w64(over) != 0;
-  if (lane == 0) sh.over[w] = wover ? 1 : 0;
+  Tail<NW>& tl = *reinterpret_cast<Tail<NW>*>(ring[0]);
+  __syncthreads();  // every wave is done with the ring
+  if (lane == 0) tl.over[w] = wover ? 1 : 0;
   if (lane < 32) {
     const int h = 32 * w + lane;
-    sh.inv_l[h] = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    a.part_lse[(row0 + h) * a.n_split + k] = l_tot > 0.f ? m_ref + log2f(l_tot) : -INFINITY;
+    tl.inv_l[h] = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    part_lse[(row0 + h) * n_split + k] = l_tot > 0.f ? m_ref + log2f(l_tot) : -INFINITY;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     int any = 0;
 #pragma unroll
-    for (int j = 0; j < NW; ++j) any |= sh.over[j];
-    a.redo[split_id] = any;
+    for (int j = 0; j < NW; ++j) any |= tl.over[j];
+    redo[split_id] = any;
   }
 #pragma unroll
   for (int hb = 0; hb < NW; ++hb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int h = 32 * hb + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const float il = sh.inv_l[h];
-      float* dst = a.part_o + ((row0 + h) * a.n_split + k) * kLat + (kLat / NW) * w + l32;
+      const float il = tl.inv_l[h];
+      float* dst = part_o + ((row0 + h) * n_split + k) * kLat + (kLat / NW) * w + l32;
 #pragma unroll
       for (int db = 0; db < kDB; ++db) dst[32 * db] = o[hb * kDB + db][r] * il;
     }
@@ -370,25 +456,13 @@ hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void*
                               const void* cache, int num_blocks, const int32_t* table,
                               int max_blocks, const int32_t* seq_lens, int n_split,
                               float* part_o, float* part_lse, int* redo, hipStream_t s) {
-  MfmaArgs a;
-  a.q_abs = static_cast<const uint16_t*>(q_abs);
-  a.cache = static_cast<const uint16_t*>(cache);
-  a.table = table;
-  a.lens = seq_lens;
-  a.num_blocks = num_blocks;
-  a.max_blocks = max_blocks;
-  a.bs = d.block_size;
-  a.s_q = s_q;
-  a.n_split = n_split;
-  a.scale_log2 = softmax_scale_of(d) * 1.4426950408889634f;
-  a.part_o = part_o;
-  a.part_lse = part_lse;
-  a.redo = redo;
+  const float scale_log2 = softmax_scale_of(d) * 1.4426950408889634f;
   const dim3 grid(n_split, s_q, batch);
-#define MLA_LAUNCH(NW_)                                                                        \
-  hipLaunchKernelGGL(decode_mfma_kernel<NW_>, grid, dim3(64 * NW_), 0, s, a.q_abs, a.cache,     \
-                     a.table, a.lens, a.num_blocks, a.max_blocks, a.bs, a.s_q, a.n_split,       \
-                     a.scale_log2, a.part_o, a.part_lse, a.redo)
+#define MLA_LAUNCH(NW_)                                                                      \
+  hipLaunchKernelGGL(decode_mfma_kernel<NW_>, grid, dim3(64 * NW_), 0, s,                     \
+                     static_cast<const uint16_t*>(q_abs), static_cast<const uint16_t*>(cache), \
+                     table, seq_lens, num_blocks, max_blocks, d.block_size, s_q, n_split,      \
+                     scale_log2, part_o, part_lse, redo)
   switch (d.n_heads) {
     case 128: MLA_LAUNCH(4); break;
     case 64: MLA_LAUNCH(2); break;
