@@ -20,6 +20,7 @@ mla_status check_dims(const mla_dims* d) {
     return MLA_ERR_SHAPE;
   if (d->n_heads % d->n_groups != 0) return MLA_ERR_SHAPE;
   if (d->d_c % 8 != 0) return MLA_ERR_SHAPE;  // 16-byte weight loads never straddle c and k_r
+  if (d->d_v % 4 != 0) return MLA_ERR_SHAPE;  // the merge reads partial rows as float4
   // LDS budgets of the portable kernels: query row + value row + 2 KiB of per-pass state,
   // and 16 merged latent rows in the combine.
   if (d->d_c + d->d_r > 4096 || d->d_nope + d->d_r > 4096 || d->d_v > 1024 || d->d_c > 1024 ||

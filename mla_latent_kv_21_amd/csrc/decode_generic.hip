@@ -15,7 +15,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kTok = 256;  // positions scored per pass (one per thread)
+constexpr int kTok = 512;  // most positions scored per pass (one per thread, <= blockDim.x)
 
 struct GenericArgs {
   const void* q;          // latent path: q_abs; GQA path: q_nope
@@ -36,9 +36,9 @@ struct GenericArgs {
 };
 
 // One (sequence b, query i, split k, head h) partial: online softmax over the split's positions
-// 256 at a time, one position per thread for the scores, one value column per thread for the
-// weighted sum. All threads of the (256-wide) block take part. Scratch: qs[q_w], os[part_w],
-// ps[kTok], sl[kTok], red[16] in LDS.
+// blockDim.x at a time, one position per thread for the scores, one value column per thread
+// for the weighted sum. All threads of the block (at most kTok) take part. Scratch: qs[q_w],
+// os[part_w], ps[kTok], sl[kTok], red[16] in LDS.
 template <typename T, bool kGqa>
 __device__ void split_head(const GenericArgs& a, int b, int i, int k, int h, float* qs, float* os,
                            float* ps, int64_t* sl, float* red) {
@@ -73,7 +73,8 @@ __device__ void split_head(const GenericArgs& a, int b, int i, int k, int h, flo
   __syncthreads();
 
   float m = -INFINITY, l = 0.f;
-  for (int tt = t0; tt < t1; tt += kTok) {
+  const int pass = static_cast<int>(blockDim.x);
+  for (int tt = t0; tt < t1; tt += pass) {
     const int t = tt + threadIdx.x;
     float s = -INFINITY;
     int64_t slot = -1;
@@ -95,7 +96,7 @@ __device__ void split_head(const GenericArgs& a, int b, int i, int k, int h, flo
     const float alpha = (m == -INFINITY) ? 0.f : exp2f(m - mn);
     l = l * alpha + tsum;
     m = mn;
-    const int nt = min(kTok, t1 - tt);
+    const int nt = min(pass, t1 - tt);
     for (int e = threadIdx.x; e < a.part_w; e += blockDim.x) {
       float acc = os[e] * alpha;
       for (int u = 0; u < nt; ++u) {
@@ -130,187 +131,203 @@ __global__ __launch_bounds__(256) void decode_generic(GenericArgs a) {
   for (int h = 0; h < a.H; ++h) split_head<T, kGqa>(a, b, i, k, h, qs, os, ps, sl, red);
 }
 
-// Up to kVec consecutive elements of T (16 bytes) as floats; the vector load needs the
-// address 16-byte aligned, the ragged or unaligned case goes element by element.
+// 16 bytes of T (kVec elements) from p as raw bits; the vector load needs p 16-byte aligned,
+// the ragged or unaligned case goes element by element (missing elements are zero).
 template <typename T>
-__device__ __forceinline__ void load_vec(const T* p, int n_avail, bool vec_ok,
-                                         float (&v)[16 / sizeof(T)]) {
+__device__ __forceinline__ uint4 load_raw16(const T* p, int n_avail, bool vec_ok) {
   constexpr int kVec = 16 / sizeof(T);
-  if (vec_ok && n_avail >= kVec) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(p);
-    if constexpr (sizeof(T) == 2) {
-      const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  if (vec_ok && n_avail >= kVec) return *reinterpret_cast<const uint4*>(p);
+  union {
+    uint4 v;
+    T e[kVec];
+  } u;
+  u.v = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        v[2 * e] = __uint_as_float(w[e] << 16);
-        v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
-      }
-    } else {
-      v[0] = __uint_as_float(raw.x); v[1] = __uint_as_float(raw.y);
-      v[2] = __uint_as_float(raw.z); v[3] = __uint_as_float(raw.w);
+  for (int e = 0; e < kVec; ++e)
+    if (e < n_avail) u.e[e] = p[e];
+  return u.v;
+}
+
+// The kVec elements of T held in 16 raw bytes, as floats.
+template <typename T>
+__device__ __forceinline__ void widen16(const uint4 raw, float (&v)[16 / sizeof(T)]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = __uint_as_float(w[e] << 16);
+      v[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
     }
   } else {
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) v[e] = e < n_avail ? ld(p, e) : 0.f;
+    v[0] = __uint_as_float(raw.x); v[1] = __uint_as_float(raw.y);
+    v[2] = __uint_as_float(raw.z); v[3] = __uint_as_float(raw.w);
   }
 }
 
 constexpr int kMaxMergeW = 1024;  // partial row width (d_c or D_v) the merge keeps in LDS
+constexpr int kMergeThreads = 512;
+constexpr int kMergeU = 16;       // loads in flight per thread per batch
 
 // One workgroup per (head h, query row m): merges the n_split partials of the row by their
 // log-sum-exp (weights 2^(lse_k - max) / sum), then applies the head's group of W_UV
 // (out = o_lat · W_UV[:, g(h)]) or, with w_uv NULL (GQA path), stores o_lat itself.
-//  * splits the matrix-core kernel flagged are first recomputed exactly (split_head);
-//  * the partial rows are read with 16-byte loads, 16 splits in flight per thread;
-//  * W_UV is read with 16-byte loads: thread (column group cg, row subgroup rs) owns kVec
-//    output columns and the W_UV rows j = rs, rs + nrs, ...; the row subgroups' sums are
-//    added through LDS in subgroup order.
+// Every split's partial row is written (an empty split writes zeros), so the partial rows,
+// the first W_UV rows and the lse values are all requested at once, before any arithmetic:
+//  * thread (column quad cq, split group grp) sums float4 columns of its splits; the groups
+//    are added through LDS in group order;
+//  * thread (column group cg, row subgroup rs) owns kVec output columns and the W_UV rows
+//    j = rs, rs + nrs, ...; the subgroups are added through LDS in subgroup order;
+//  * splits the matrix-core kernel flagged are first recomputed exactly (split_head), after
+//    which their lse and partial row are read again.
 template <typename T>
-__global__ __launch_bounds__(256) void merge_kernel(GenericArgs a, const int* __restrict__ redo,
-                                                    const T* __restrict__ w_uv, int dv,
-                                                    T* __restrict__ out, float* lse_out) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(GenericArgs a,
+                                                              const int* __restrict__ redo,
+                                                              const T* __restrict__ w_uv, int dv,
+                                                              T* __restrict__ out,
+                                                              float* lse_out) {
   constexpr int kVec = 16 / static_cast<int>(sizeof(T));
   extern __shared__ float smem[];
   __shared__ float red[16];
   __shared__ float wts[MLA_MAX_SPLIT];
   __shared__ __attribute__((aligned(16))) float o_s[kMaxMergeW];
-  __shared__ float4 mpart[256];
-  __shared__ float psum[256 * kVec];
+  __shared__ float4 mpart[kMergeThreads];
+  __shared__ float psum[kMergeThreads * kVec];
+  __shared__ unsigned long long flagged[kMergeThreads / 64];
   const int n_split = a.n_split, pw = a.part_w, H = a.H;
   const int h = blockIdx.x, m = blockIdx.y;
   const int64_t rh = static_cast<int64_t>(m) * H + h;
-  const int tk = threadIdx.x;  // one split per thread: n_split <= MLA_MAX_SPLIT = blockDim.x
-  if (redo != nullptr) {
-    // the row's flags are read at once and gathered into a bit set (one word per wave)
-    __shared__ unsigned long long flagged[MLA_MAX_SPLIT / 64];
-    const bool f = tk < n_split && redo[static_cast<int64_t>(m) * n_split + tk] != 0;
-    const unsigned long long bits = __ballot(f);
-    if ((threadIdx.x & 63) == 0) flagged[threadIdx.x >> 6] = bits;
+  const int tid = threadIdx.x;
+  const float* P = a.part_o + rh * n_split * pw;
+
+  // ---- everything this thread needs first is requested here
+  float lk = tid < n_split ? a.part_lse[rh * n_split + tid] : -INFINITY;
+  const bool flag = redo != nullptr && tid < n_split &&
+                    redo[static_cast<int64_t>(m) * n_split + tid] != 0;
+  const int nq = pw >> 2;  // pw % 4 == 0, nq <= kMergeThreads (checked on the host)
+  const int ngrp = min(16, kMergeThreads / nq);
+  const int per = cdiv(n_split, ngrp);
+  const int cq = tid % nq, grp = tid / nq;
+  const bool pthread = grp < ngrp;
+  const int k0 = pthread ? grp * per : 0, k1 = pthread ? min(n_split, k0 + per) : 0;
+  float4 v[kMergeU];
+  auto load_parts = [&](int kb) {
+#pragma unroll
+    for (int u = 0; u < kMergeU; ++u)
+      v[u] = kb + u < k1 ? *reinterpret_cast<const float4*>(P + static_cast<int64_t>(kb + u) * pw + 4 * cq)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+  };
+  load_parts(k0);
+  const int g = h / (H / a.G);
+  const int ncg = cdiv(dv, kVec);  // <= 128 (D_v <= 1024)
+  const int nrs = kMergeThreads / ncg;
+  const int cg = tid % ncg, rs = tid / ncg;
+  const bool wthread = w_uv != nullptr && rs < nrs;
+  const int64_t ldw = static_cast<int64_t>(a.G) * dv;
+  const T* wc = w_uv + static_cast<int64_t>(g) * dv + cg * kVec;
+  const int navail = dv - cg * kVec;
+  const bool vec_ok = w_uv != nullptr && (ldw * static_cast<int64_t>(sizeof(T))) % 16 == 0 &&
+                      (reinterpret_cast<uintptr_t>(w_uv) & 15u) == 0;
+  uint4 wraw[kMergeU];  // 16 raw bytes (kVec elements) of W_UV per row, widened at use
+  auto load_w = [&](int jb) {
+#pragma unroll
+    for (int u = 0; u < kMergeU; ++u) {
+      const int j = jb + nrs * u;
+      const bool in = wthread && j < pw;
+      wraw[u] = load_raw16(wc + static_cast<int64_t>(in ? j : 0) * ldw, in ? navail : 0, vec_ok);
+    }
+  };
+  load_w(rs);
+
+  // ---- splits flagged for exact recomputation (rare): recompute, then read them again
+  {
+    const unsigned long long bits = __ballot(flag);
+    if ((tid & 63) == 0) flagged[tid >> 6] = bits;
     __syncthreads();
-    float* qs = smem;
-    float* ro = qs + a.q_w;
-    float* ps = ro + pw;
-    int64_t* sl = reinterpret_cast<int64_t*>(ps + kTok);
-    for (int word = 0; word < static_cast<int>(blockDim.x) / 64; ++word) {
-      unsigned long long left = flagged[word];
-      while (left != 0) {
-        const int k = word * 64 + __builtin_ctzll(left);
-        left &= left - 1;
-        split_head<T, false>(a, m / a.s_q, m % a.s_q, k, h, qs, ro, ps, sl, red);
+    unsigned long long any = 0;
+#pragma unroll
+    for (int q = 0; q < kMergeThreads / 64; ++q) any |= flagged[q];
+    if (any != 0) {
+      float* qs = smem;
+      float* ro = qs + a.q_w;
+      float* ps = ro + pw;
+      int64_t* sl = reinterpret_cast<int64_t*>(ps + kTok);
+      for (int word = 0; word < kMergeThreads / 64; ++word) {
+        unsigned long long left = flagged[word];
+        while (left != 0) {
+          const int k = word * 64 + __builtin_ctzll(left);
+          left &= left - 1;
+          split_head<T, false>(a, m / a.s_q, m % a.s_q, k, h, qs, ro, ps, sl, red);
+        }
       }
+      lk = tid < n_split ? a.part_lse[rh * n_split + tid] : -INFINITY;
+      load_parts(k0);
     }
   }
+
   // ---- weights
-  const float lk = tk < n_split ? a.part_lse[rh * n_split + tk] : -INFINITY;
   const float mx = block_max(lk, red);
-  const float ek = (tk < n_split && mx != -INFINITY) ? exp2f(lk - mx) : 0.f;
+  const float ek = (tid < n_split && mx != -INFINITY) ? exp2f(lk - mx) : 0.f;
   const float sum = block_sum(ek, red);
   const float inv = sum > 0.f ? 1.0f / sum : 0.f;
-  if (tk < n_split) wts[tk] = ek * inv;
-  if (threadIdx.x == 0 && lse_out != nullptr)
+  if (tid < n_split) wts[tid] = ek * inv;
+  if (tid == 0 && lse_out != nullptr)
     lse_out[rh] = (mx == -INFINITY) ? -INFINITY : (mx + log2f(sum)) * kLn2;
   __syncthreads();
-  // ---- o_lat = sum_k w_k o_k into LDS
-  const float* P = a.part_o + rh * n_split * pw;
-  const int nq = pw >> 2;
-  if ((pw & 3) == 0) {
-    // thread (column quad cq, split group grp), split groups added in group order
-    const int ngrp = min(4, static_cast<int>(blockDim.x) / nq);
-    const int per = cdiv(n_split, ngrp);
-    const int cq = threadIdx.x % nq, grp = threadIdx.x / nq;
-    for (int q0 = 0; q0 < nq; q0 += blockDim.x) {   // pw > 1024 never happens (kMaxMergeW)
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      const int qq = q0 + cq;
-      if (grp < ngrp && qq < nq) {
-        const int k0 = grp * per, k1 = min(n_split, k0 + per);
-        for (int k = k0; k < k1; k += 16) {
-          float4 v[16];
-          float wk[16];
+
+  // ---- o_lat = sum_k w_k o_k into LDS (a split's weight 0 times its finite row adds 0)
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int kb = k0; kb < k1; kb += kMergeU) {
+    if (kb != k0) load_parts(kb);
 #pragma unroll
-          for (int u = 0; u < 16; ++u) {
-            wk[u] = k + u < k1 ? wts[k + u] : 0.f;
-            // empty splits (weight 0) were never written: do not read them
-            v[u] = wk[u] != 0.f
-                       ? *reinterpret_cast<const float4*>(P + static_cast<int64_t>(k + u) * pw + 4 * qq)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-          }
-#pragma unroll
-          for (int u = 0; u < 16; ++u) {
-            acc.x = fmaf(wk[u], v[u].x, acc.x);
-            acc.y = fmaf(wk[u], v[u].y, acc.y);
-            acc.z = fmaf(wk[u], v[u].z, acc.z);
-            acc.w = fmaf(wk[u], v[u].w, acc.w);
-          }
-        }
-        mpart[grp * nq + cq] = acc;
-      }
-      __syncthreads();
-      if (threadIdx.x < nq && q0 + static_cast<int>(threadIdx.x) < nq) {
-        float4 r = mpart[threadIdx.x];
-        for (int q = 1; q < ngrp; ++q) {
-          const float4 t = mpart[q * nq + threadIdx.x];
-          r.x += t.x; r.y += t.y; r.z += t.z; r.w += t.w;
-        }
-        *reinterpret_cast<float4*>(o_s + 4 * (q0 + threadIdx.x)) = r;
-      }
-      __syncthreads();
+    for (int u = 0; u < kMergeU; ++u) {
+      const float wk = kb + u < k1 ? wts[kb + u] : 0.f;
+      acc.x = fmaf(wk, v[u].x, acc.x);
+      acc.y = fmaf(wk, v[u].y, acc.y);
+      acc.z = fmaf(wk, v[u].z, acc.z);
+      acc.w = fmaf(wk, v[u].w, acc.w);
     }
-  } else {
-    for (int e = threadIdx.x; e < pw; e += blockDim.x) {
-      float acc = 0.f;
-      for (int k = 0; k < n_split; ++k) {
-        const float wk = wts[k];
-        if (wk != 0.f) acc = fmaf(wk, P[static_cast<int64_t>(k) * pw + e], acc);
-      }
-      o_s[e] = acc;
-    }
-    __syncthreads();
   }
+  if (pthread) mpart[grp * nq + cq] = acc;
+  __syncthreads();
+  if (tid < nq) {
+    float4 r = mpart[tid];
+    for (int q = 1; q < ngrp; ++q) {
+      const float4 t = mpart[q * nq + tid];
+      r.x += t.x; r.y += t.y; r.z += t.z; r.w += t.w;
+    }
+    *reinterpret_cast<float4*>(o_s + 4 * tid) = r;
+  }
+  __syncthreads();
   T* orow = out + rh * dv;
   if (w_uv == nullptr) {  // GQA path: the merged rows are the output (pw == dv)
-    for (int v = threadIdx.x; v < dv; v += blockDim.x) st(orow, v, o_s[v]);
+    for (int c = tid; c < dv; c += kMergeThreads) st(orow, c, o_s[c]);
     return;
   }
+
   // ---- out = o_lat · W_UV[:, g(h)]
-  const int g = h / (H / a.G);
-  const int ncg = cdiv(dv, kVec);             // <= 256 (D_v <= 1024)
-  const int nrs = static_cast<int>(blockDim.x) / ncg;
-  const int cg = threadIdx.x % ncg, rs = threadIdx.x / ncg;
-  const int64_t ldw = static_cast<int64_t>(a.G) * dv;
-  const bool vec_ok = (ldw * static_cast<int64_t>(sizeof(T))) % 16 == 0 &&
-                      (reinterpret_cast<uintptr_t>(w_uv) & 15u) == 0;
-  float acc[kVec];
+  float pacc[kVec];
 #pragma unroll
-  for (int e = 0; e < kVec; ++e) acc[e] = 0.f;
-  if (rs < nrs) {
-    const T* wc = w_uv + static_cast<int64_t>(g) * dv + cg * kVec;
-    const int navail = dv - cg * kVec;
-    for (int jb = rs; jb < pw; jb += 16 * nrs) {
-      float wv[16][kVec];
+  for (int e = 0; e < kVec; ++e) pacc[e] = 0.f;
+  for (int jb = rs; jb < pw; jb += kMergeU * nrs) {
+    if (jb != rs) load_w(jb);
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int j = jb + nrs * u;
-        load_vec(wc + static_cast<int64_t>(j < pw ? j : 0) * ldw, j < pw ? navail : 0, vec_ok,
-                 wv[u]);
-      }
+    for (int u = 0; u < kMergeU; ++u) {
+      const int j = jb + nrs * u;
+      const float o = j < pw ? o_s[j] : 0.f;
+      float wv[kVec];
+      widen16<T>(wraw[u], wv);
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int j = jb + nrs * u;
-        if (j >= pw) break;
-        const float o = o_s[j];
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) acc[e] = fmaf(o, wv[u][e], acc[e]);
-      }
+      for (int e = 0; e < kVec; ++e) pacc[e] = fmaf(o, wv[e], pacc[e]);
     }
   }
 #pragma unroll
-  for (int e = 0; e < kVec; ++e) psum[threadIdx.x * kVec + e] = acc[e];
+  for (int e = 0; e < kVec; ++e) psum[tid * kVec + e] = pacc[e];
   __syncthreads();
-  for (int v = threadIdx.x; v < dv; v += blockDim.x) {
-    const int c = v / kVec, e = v - c * kVec;
+  for (int c = tid; c < dv; c += kMergeThreads) {
+    const int cgi = c / kVec, e = c - cgi * kVec;
     float r = 0.f;
-    for (int q = 0; q < nrs; ++q) r += psum[(q * ncg + c) * kVec + e];
-    st(orow, v, r);
+    for (int q = 0; q < nrs; ++q) r += psum[(q * ncg + cgi) * kVec + e];
+    st(orow, c, r);
   }
 }
 
@@ -326,7 +343,7 @@ hipError_t run_combine(const GenericArgs& a, const int* redo, int batch, int dv,
                        void* out, float* lse, hipStream_t s) {
   const int M = batch * a.s_q;
   const size_t lds = redo != nullptr ? split_head_lds(a) : 0;
-  hipLaunchKernelGGL(merge_kernel<T>, dim3(a.H, M), dim3(256), lds, s, a, redo,
+  hipLaunchKernelGGL(merge_kernel<T>, dim3(a.H, M), dim3(kMergeThreads), lds, s, a, redo,
                      static_cast<const T*>(w_uv), dv, static_cast<T*>(out), lse);
   return hipGetLastError();
 }

@@ -160,9 +160,14 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   const int64_t row0 = (static_cast<int64_t>(b) * s_q + qi) * H;  // first (b, qi, h) row
   const int64_t split_id = (static_cast<int64_t>(b) * s_q + qi) * n_split + k;
 
-  if (t0 >= t1) {  // empty split: weight zero in the merge; its o partial is never read
+  if (t0 >= t1) {  // empty split: lse -inf (weight zero in the merge) and a zero partial row
     for (int h = threadIdx.x; h < H; h += blockDim.x)
       part_lse[(row0 + h) * n_split + k] = -INFINITY;
+    for (int e = threadIdx.x; e < H * (kLat / 4); e += blockDim.x) {
+      const int h = e / (kLat / 4), c4 = e - h * (kLat / 4);
+      *reinterpret_cast<float4*>(part_o + ((row0 + h) * n_split + k) * kLat + 4 * c4) =
+          make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     if (threadIdx.x == 0) redo[split_id] = 0;
     return;
   }
@@ -222,11 +227,24 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   bool over = false;
   const int ntiles = cdiv(t1 - t0, kTileTok);
 
+  // Block ids of the split, one per lane (lane i: block jbase + i of the sequence), so a
+  // tile's id is a v_readlane instead of a scalar load waited on in the loop; reloaded when
+  // the split moves past 64 blocks (tiles are visited in increasing order).
+  int jbase = t0 / bs;
+  auto load_ids = [&]() {
+    const int jj = jbase + lane;
+    return jj < max_blocks ? table[static_cast<int64_t>(b) * max_blocks + jj] : -1;
+  };
+  int ids = load_ids();
   // Cache address of the tile at pos0 (a multiple of 32 inside one block) and its number of
   // valid positions (0 for a bad block id, whose rows are then never used).
   auto tile_src = [&](int pos0, int* nvalid) -> const char* {
     const int jb = pos0 / bs;
-    const int id = table[static_cast<int64_t>(b) * max_blocks + jb];
+    if (jb - jbase >= 64) {
+      jbase = jb;
+      ids = load_ids();
+    }
+    const int id = __builtin_amdgcn_readlane(ids, jb - jbase);
     const bool ok = id >= 0 && id < num_blocks;
     const int n = t1 - pos0 < kTileTok ? t1 - pos0 : kTileTok;
     *nvalid = ok ? n : 0;
@@ -364,11 +382,13 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   // ---- pipeline. Iteration t: tile t+1 has landed, tiles t+2 and t+3 are in flight (t+3
   // issued into the slot tile t-1 used), the scores of tile t+1 are formed, then P · V of
   // tile t runs with the softmax of tile t+1 spread between its products.
+  // valid positions of the tiles after the current one: nv1 (t+1), nv2 (t+2)
+  int nv1 = 0, nv2 = 0;
   {
-    int nv0, nvx;
+    int nv0;
     issue_tile(tile_src(t0, &nv0), ring[0]);
-    if (ntiles > 1) issue_tile(tile_src(t0 + kTileTok, &nvx), ring[1]);
-    if (ntiles > 2) issue_tile(tile_src(t0 + 2 * kTileTok, &nvx), ring[2]);
+    if (ntiles > 1) issue_tile(tile_src(t0 + kTileTok, &nv1), ring[1]);
+    if (ntiles > 2) issue_tile(tile_src(t0 + 2 * kTileTok, &nv2), ring[2]);
     if (ntiles > 2)
       wait_dma<2 * kDma>();
     else if (ntiles > 1)
@@ -391,15 +411,14 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     else
       wait_dma<0>();
     __syncthreads();
-    if (t + 3 < ntiles) {
-      int nv3;
-      issue_tile(tile_src(pos0 + 3 * kTileTok, &nv3), ring[(t + 3) & (kSlots - 1)]);
-    }
+    int nv3 = 0;
+    if (t + 3 < ntiles) issue_tile(tile_src(pos0 + 3 * kTileTok, &nv3), ring[(t + 3) & (kSlots - 1)]);
     // One body for every iteration (separate paths would split the query registers' live
     // ranges): on the last tile the next slot holds stale data, and with no valid position
     // the mask turns every score into -inf, which leaves m_ref, l and the flag unchanged.
-    int nv_next = 0;
-    if (t + 1 < ntiles) tile_src(pos0 + kTileTok, &nv_next);
+    const int nv_next = t + 1 < ntiles ? nv1 : 0;
+    nv1 = nv2;
+    nv2 = nv3;
     f32x16 sc = scores(ring[nslot]);
     if (nv_next < kTileTok) mask_tail(sc, nv_next);
     pv(ring[slot], t & 1, sc, (t + 1) & 1);

@@ -66,6 +66,8 @@ def test_decode_validation(L):
     assert decode_call(L, dims(dtype=7)) == -3
     assert decode_call(L, dims(n_groups=3)) == -2          # 3 does not divide 128
     assert decode_call(L, dims(d_r=63)) == -2              # odd rotary width
+    assert decode_call(L, dims(d_v=126)) == -2             # value rows are merged as float4
+    assert decode_call(L, dims(d_c=500)) == -2             # latent width not a multiple of 8
     assert decode_call(L, d, batch=0) == 0                 # empty batch: nothing to do
     assert decode_call(L, d, s_q=0) == -4
     assert decode_call(L, d, n_split=M.MLA_MAX_SPLIT + 1) == -4
