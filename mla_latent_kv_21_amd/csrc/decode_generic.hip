@@ -30,8 +30,11 @@ struct GenericArgs {
   int q_w;       // query width (latent: d_c + d_r; GQA: D + d_r)
   int d_c, d_r, D, Dv;
   float scale_log2, base;
+  // Partials of split k for row r = (b s_q + i) H + h sit at [k * n_rows + r]: one split's rows
+  // are contiguous (a workgroup writes one block), a row's splits are n_rows apart.
   float* part_o;
   float* part_lse;
+  int n_rows;    // batch * s_q * H
   int part_w;    // value width (latent: d_c; GQA: D_v)
 };
 
@@ -106,7 +109,7 @@ __device__ void split_head(const GenericArgs& a, int b, int i, int k, int h, flo
     }
     __syncthreads();
   }
-  const int64_t pidx = qrow * a.n_split + k;
+  const int64_t pidx = static_cast<int64_t>(k) * a.n_rows + qrow;
   const bool any = l > 0.f;
   const float inv = any ? 1.0f / l : 0.f;
   for (int e = threadIdx.x; e < a.part_w; e += blockDim.x)
@@ -197,10 +200,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(GenericArgs a,
   const int h = blockIdx.x, m = blockIdx.y;
   const int64_t rh = static_cast<int64_t>(m) * H + h;
   const int tid = threadIdx.x;
-  const float* P = a.part_o + rh * n_split * pw;
+  const float* P = a.part_o + rh * pw;             // split k at + k * n_rows * pw
+  const int64_t kstride = static_cast<int64_t>(a.n_rows) * pw;
 
   // ---- everything this thread needs first is requested here
-  float lk = tid < n_split ? a.part_lse[rh * n_split + tid] : -INFINITY;
+  float lk = tid < n_split ? a.part_lse[static_cast<int64_t>(tid) * a.n_rows + rh] : -INFINITY;
   const bool flag = redo != nullptr && tid < n_split &&
                     redo[static_cast<int64_t>(m) * n_split + tid] != 0;
   const int nq = pw >> 2;  // pw % 4 == 0, nq <= kMergeThreads (checked on the host)
@@ -213,7 +217,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(GenericArgs a,
   auto load_parts = [&](int kb) {
 #pragma unroll
     for (int u = 0; u < kMergeU; ++u)
-      v[u] = kb + u < k1 ? *reinterpret_cast<const float4*>(P + static_cast<int64_t>(kb + u) * pw + 4 * cq)
+      v[u] = kb + u < k1 ? *reinterpret_cast<const float4*>(P + (kb + u) * kstride + 4 * cq)
                          : make_float4(0.f, 0.f, 0.f, 0.f);
   };
   load_parts(k0);
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(GenericArgs a,
           split_head<T, false>(a, m / a.s_q, m % a.s_q, k, h, qs, ro, ps, sl, red);
         }
       }
-      lk = tid < n_split ? a.part_lse[rh * n_split + tid] : -INFINITY;
+      lk = tid < n_split ? a.part_lse[static_cast<int64_t>(tid) * a.n_rows + rh] : -INFINITY;
       load_parts(k0);
     }
   }
@@ -367,7 +371,7 @@ Partials partials_of(void* ws, int batch, int s_q, int heads, int n_split, int w
   return p;
 }
 
-GenericArgs latent_args(const mla_dims& d, int s_q, const void* q_abs, const void* cache,
+GenericArgs latent_args(const mla_dims& d, int batch, int s_q, const void* q_abs, const void* cache,
                         int num_blocks, const int32_t* table, int max_blocks,
                         const int32_t* seq_lens, int n_split, const Partials& p) {
   GenericArgs a{};
@@ -377,7 +381,7 @@ GenericArgs latent_args(const mla_dims& d, int s_q, const void* q_abs, const voi
   a.row_w = d.d_c + d.d_r; a.q_w = d.d_c + d.d_r;
   a.d_c = d.d_c; a.d_r = d.d_r; a.D = d.d_nope; a.Dv = d.d_v;
   a.scale_log2 = softmax_scale_of(d) * kLog2e; a.base = d.rope_base;
-  a.part_o = p.o; a.part_lse = p.lse; a.part_w = d.d_c;
+  a.part_o = p.o; a.part_lse = p.lse; a.part_w = d.d_c; a.n_rows = batch * s_q * d.n_heads;
   return a;
 }
 
@@ -403,7 +407,7 @@ hipError_t launch_decode_splitk(const mla_dims& d, int batch, int s_q, const voi
   if (uses_mfma(d))
     return launch_decode_mfma(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
                               seq_lens, n_split, p.o, p.lse, p.redo, s);
-  const GenericArgs a = latent_args(d, s_q, q_abs, cache, num_blocks, table, max_blocks,
+  const GenericArgs a = latent_args(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
                                     seq_lens, n_split, p);
   return d.dtype == MLA_BF16 ? run_generic<bf16, false>(a, batch, s)
                              : run_generic<float, false>(a, batch, s);
@@ -414,7 +418,7 @@ hipError_t launch_decode_merge(const mla_dims& d, int batch, int s_q, const void
                                int max_blocks, const int32_t* seq_lens, const void* w_uv,
                                int n_split, void* ws, void* out, float* lse, hipStream_t s) {
   const Partials p = partials_of(ws, batch, s_q, d.n_heads, n_split, d.d_c);
-  const GenericArgs a = latent_args(d, s_q, q_abs, cache, num_blocks, table, max_blocks,
+  const GenericArgs a = latent_args(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
                                     seq_lens, n_split, p);
   // Only the MFMA kernel writes recompute flags; the portable kernel computes every split.
   const int* redo = uses_mfma(d) ? p.redo : nullptr;
@@ -435,7 +439,7 @@ hipError_t launch_gqa_decode(const mla_dims& d, int batch, int s_q, const void* 
   a.row_w = d.n_groups * (d.d_nope + d.d_v) + d.d_r; a.q_w = d.d_nope + d.d_r;
   a.d_c = d.d_c; a.d_r = d.d_r; a.D = d.d_nope; a.Dv = d.d_v;
   a.scale_log2 = softmax_scale_of(d) * kLog2e; a.base = d.rope_base;
-  a.part_o = p.o; a.part_lse = p.lse; a.part_w = d.d_v;
+  a.part_o = p.o; a.part_lse = p.lse; a.part_w = d.d_v; a.n_rows = batch * s_q * d.n_heads;
   hipError_t e = d.dtype == MLA_BF16 ? run_generic<bf16, true>(a, batch, s)
                                      : run_generic<float, true>(a, batch, s);
   if (e != hipSuccess) return e;

@@ -47,7 +47,8 @@ constexpr int kTileBytes = kTileTok * kRowBytes;  // 36,864
 constexpr int kTileChunks = kTileTok * kChunks;   // 2,304
 constexpr int kKSteps = kRowElems / 16;           // 36 MFMA K-steps for the scores
 constexpr float kHead = 64.0f;                    // P <= 2^kHead, else recompute (log2)
-constexpr int kPre = 6;                           // score fragments read ahead of their MFMA
+constexpr int kPre = 10;                          // score fragments read ahead of their MFMA
+constexpr int kVPre = 2;                          // P · V steps whose V fragments are in flight
 constexpr int kSlots = 4;                         // ring slots: two tiles in flight
 
 typedef __attribute__((address_space(3))) char lds_char_t;
@@ -159,15 +160,14 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   split_range(lim, n_split, k, kSplitAlign, &t0, &t1);
   const int64_t row0 = (static_cast<int64_t>(b) * s_q + qi) * H;  // first (b, qi, h) row
   const int64_t split_id = (static_cast<int64_t>(b) * s_q + qi) * n_split + k;
+  // partial rows of split k: [k * n_rows + row]; this workgroup's H rows are one block
+  const int64_t n_rows = static_cast<int64_t>(gridDim.z) * s_q * H;
+  const int64_t prow0 = k * n_rows + row0;
 
   if (t0 >= t1) {  // empty split: lse -inf (weight zero in the merge) and a zero partial row
-    for (int h = threadIdx.x; h < H; h += blockDim.x)
-      part_lse[(row0 + h) * n_split + k] = -INFINITY;
-    for (int e = threadIdx.x; e < H * (kLat / 4); e += blockDim.x) {
-      const int h = e / (kLat / 4), c4 = e - h * (kLat / 4);
-      *reinterpret_cast<float4*>(part_o + ((row0 + h) * n_split + k) * kLat + 4 * c4) =
-          make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+    for (int h = threadIdx.x; h < H; h += blockDim.x) part_lse[prow0 + h] = -INFINITY;
+    for (int e = threadIdx.x; e < H * (kLat / 4); e += blockDim.x)
+      *reinterpret_cast<float4*>(part_o + prow0 * kLat + 4 * e) = make_float4(0.f, 0.f, 0.f, 0.f);
     if (threadIdx.x == 0) redo[split_id] = 0;
     return;
   }
@@ -348,22 +348,24 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   auto pv = [&](const char* cur, int par, f32x16& sc, int npar) __attribute__((always_inline)) {
     SoftState s;
     bf16x8 pa[2][NW];
-    i16x4 va[2][2];  // [buffer][rb]
+    i16x4 va[kVPre + 1][2];  // V fragments of kVPre + 1 (k2, db) steps: [buffer][rb]
+    auto read_v = [&](int step, i16x4 (&dst)[2]) __attribute__((always_inline)) {
+      const int n2 = step / kDB, ndb = step % kDB;
+      const char* vp = cur + 16 * n2 * kRowBytes + (ndb >> 1) * 128;
+      dst[0] = lds_read_tr(vp + vt[ndb & 1][0]);
+      dst[1] = lds_read_tr(vp + vt[ndb & 1][1]);
+    };
 #pragma unroll
     for (int hb = 0; hb < NW; ++hb) pa[0][hb] = sh.p[par][hb][0][lane];
-    va[0][0] = lds_read_tr(cur + vt[0][0]);
-    va[0][1] = lds_read_tr(cur + vt[0][1]);
+#pragma unroll
+    for (int st = 0; st < kVPre; ++st) read_v(st, va[st]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kPV; ++i) {
       const int k2 = i / (kDB * NW), db = (i / NW) % kDB, hb = i % NW;
-      const int buf = (i / NW) & 1;
-      if (hb == 0 && i + NW < kPV) {  // fragment of the next (k2, db)
-        const int n2 = (i + NW) / (kDB * NW), ndb = ((i + NW) / NW) % kDB;
-        const char* vp = cur + 16 * n2 * kRowBytes + (ndb >> 1) * 128;
-        va[buf ^ 1][0] = lds_read_tr(vp + vt[ndb & 1][0]);
-        va[buf ^ 1][1] = lds_read_tr(vp + vt[ndb & 1][1]);
-      }
+      const int step = i / NW;
+      const int buf = step % (kVPre + 1);
+      if (hb == 0 && step + kVPre < 2 * kDB) read_v(step + kVPre, va[(step + kVPre) % (kVPre + 1)]);
       if (i == kPV / 4) {
 #pragma unroll
         for (int h2 = 0; h2 < NW; ++h2) pa[1][h2] = sh.p[par][h2][1][lane];
@@ -442,7 +444,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   if (lane < 32) {
     const int h = 32 * w + lane;
     tl.inv_l[h] = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    part_lse[(row0 + h) * n_split + k] = l_tot > 0.f ? m_ref + log2f(l_tot) : -INFINITY;
+    part_lse[prow0 + h] = l_tot > 0.f ? m_ref + log2f(l_tot) : -INFINITY;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -451,16 +453,31 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     for (int j = 0; j < NW; ++j) any |= tl.over[j];
     redo[split_id] = any;
   }
+  // O / l leaves through the ring one 32-head block at a time (rows padded by 32 bytes so the
+  // two half-waves' rows fall on different banks) and is written with 16-byte stores.
+  constexpr int kStageRow = kLat * 4 + 32;
+  char* stage = ring[0] + 1024;  // after the Tail
+  static_assert(1024 + 32 * kStageRow <= kSlots * kTileBytes, "stage fits in the ring");
+  static_assert(sizeof(Tail<NW>) <= 1024, "tail fits before the stage");
+  float* dst = part_o + prow0 * kLat;
 #pragma unroll
   for (int hb = 0; hb < NW; ++hb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int h = 32 * hb + 8 * (r >> 2) + 4 * hi + (r & 3);
-      const float il = tl.inv_l[h];
-      float* dst = part_o + ((row0 + h) * n_split + k) * kLat + (kLat / NW) * w + l32;
+      const int hl = 8 * (r >> 2) + 4 * hi + (r & 3);
+      const float il = tl.inv_l[32 * hb + hl];
 #pragma unroll
-      for (int db = 0; db < kDB; ++db) dst[32 * db] = o[hb * kDB + db][r] * il;
+      for (int db = 0; db < kDB; ++db)
+        *reinterpret_cast<float*>(stage + hl * kStageRow + ((kLat / NW) * w + 32 * db + l32) * 4) =
+            o[hb * kDB + db][r] * il;
     }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 32 * (kLat / 4); e += NW * 64) {
+      const int row = e / (kLat / 4), c4 = e - row * (kLat / 4);
+      *reinterpret_cast<float4*>(dst + (32 * hb + row) * kLat + 4 * c4) =
+          *reinterpret_cast<const float4*>(stage + row * kStageRow + 16 * c4);
+    }
+    __syncthreads();
   }
 }
 
