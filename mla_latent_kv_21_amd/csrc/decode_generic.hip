@@ -169,7 +169,7 @@ __device__ __forceinline__ void widen16(const uint4 raw, float (&v)[16 / sizeof(
 
 constexpr int kMaxMergeW = 1024;  // partial row width (d_c or D_v) the merge keeps in LDS
 constexpr int kMergeThreads = 512;
-constexpr int kMergeU = 16;       // loads in flight per thread per batch
+constexpr int kMergeU = 8;        // loads in flight per thread per batch (two workgroups per CU)
 
 // One workgroup per (head h, query row m): merges the n_split partials of the row by their
 // log-sum-exp (weights 2^(lse_k - max) / sum), then applies the head's group of W_UV
@@ -183,7 +183,7 @@ constexpr int kMergeU = 16;       // loads in flight per thread per batch
 //  * splits the matrix-core kernel flagged are first recomputed exactly (split_head), after
 //    which their lse and partial row are read again.
 template <typename T>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(GenericArgs a,
+__global__ __launch_bounds__(kMergeThreads, 4) void merge_kernel(GenericArgs a,
                                                               const int* __restrict__ redo,
                                                               const T* __restrict__ w_uv, int dv,
                                                               T* __restrict__ out,

@@ -147,6 +147,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   constexpr int kDB = 16 / NW;                      // 32-column latent blocks per wave
   constexpr int kPV = 2 * kDB * NW;                 // P · V products per tile (32)
   constexpr int kDma = kTileChunks / (NW * 64);     // copies per wave per tile
+  static_assert(kDma <= kKSteps, "copies are spread over the score K-steps");
   __shared__ __attribute__((aligned(16))) char ring[kSlots][kTileBytes];
   __shared__ Shared<NW> sh;
   static_assert(sizeof(ring) + sizeof(Shared<NW>) <= 160 * 1024, "LDS");
@@ -175,14 +176,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   const int l32 = lane & 31, hi = lane >> 5;
 
   // Absorbed queries of this wave's 32 heads as MFMA B operands, in registers for the whole
-  // split: lane -> head 32w + l32, K-step ks covers row elements [16 ks + 8 hi, +8).
+  // split: lane -> head 32w + l32, K-step ks covers row elements [16 ks + 8 hi, +8). Loaded
+  // after the first tile's copies are issued.
   bf16x8 qf[kKSteps];
-  {
-    const char* qp = reinterpret_cast<const char*>(q_abs) + (row0 + 32 * w + l32) * kRowBytes +
-                     hi * 16;
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
-  }
 
   // Per-lane byte offsets; the rest of every swizzled address is a compile-time constant.
   //  copies: LDS chunk p = (j NW + w) 64 + lane of a slot holds row p / 72, physical chunk
@@ -230,10 +226,15 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   // Block ids of the split, one per lane (lane i: block jbase + i of the sequence), so a
   // tile's id is a v_readlane instead of a scalar load waited on in the loop; reloaded when
   // the split moves past 64 blocks (tiles are visited in increasing order).
+  // The load is issued from asm with its own wait: a compiler-visible vector load in the loop
+  // would make the compiler wait for every copy in flight before each use of `ids`.
   int jbase = t0 / bs;
   auto load_ids = [&]() {
     const int jj = jbase + lane;
-    return jj < max_blocks ? table[static_cast<int64_t>(b) * max_blocks + jj] : -1;
+    const int32_t* src = table + static_cast<int64_t>(b) * max_blocks + (jj < max_blocks ? jj : 0);
+    int v;
+    asm volatile("global_load_dword %0, %1, off\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(src) : "memory");
+    return jj < max_blocks ? v : -1;
   };
   int ids = load_ids();
   // Cache address of the tile at pos0 (a multiple of 32 inside one block) and its number of
@@ -256,10 +257,16 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
 #pragma unroll
     for (int j = 0; j < kDma; ++j) dma16(src, doff[j], lbase + j * NW * 64 * 16);
   };
+  // Copy j of a tile issued from inside the score loop: the copies of the four waves then
+  // spread over the score phase instead of queueing at the vector-memory unit together.
+  auto issue_part = [&](const char* src, unsigned lbase, int j) __attribute__((always_inline)) {
+    if (src != nullptr) dma16(src, doff[j], lbase + j * NW * 64 * 16);
+  };
 
   // ---- scores S^T[position][head] of one tile over the 576-wide rows, each fragment read
   // kPre products ahead of its MFMA.
-  auto scores = [&](const char* cur) __attribute__((always_inline)) -> f32x16 {
+  auto scores = [&](const char* cur, const char* dsrc, unsigned dlds)
+                    __attribute__((always_inline)) -> f32x16 {
     f32x16 sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
@@ -273,6 +280,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       const int nx = ks + kPre;
       if (nx < kKSteps) af[ks % kPre] = lds16(cur + qb[nx & 3] + 128 * (nx >> 2));
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur, qf[ks], sc, 0, 0, 0);
+      // copies spread evenly over the K-steps (kDma <= kKSteps)
+      if ((ks * kDma) / kKSteps != ((ks + 1) * kDma) / kKSteps)
+        issue_part(dsrc, dlds, (ks * kDma) / kKSteps);
       __builtin_amdgcn_sched_barrier(0);
     }
     return sc;
@@ -389,6 +399,14 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   {
     int nv0;
     issue_tile(tile_src(t0, &nv0), ring[0]);
+    // vector memory completes in issue order: the query loads land before tiles 1 and 2, and
+    // the compiler's waits for them (which do not count the copies) stay conservative
+    {
+      const char* qp = reinterpret_cast<const char*>(q_abs) +
+                       (row0 + 32 * w + l32) * kRowBytes + hi * 16;
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+    }
     if (ntiles > 1) issue_tile(tile_src(t0 + kTileTok, &nv1), ring[1]);
     if (ntiles > 2) issue_tile(tile_src(t0 + 2 * kTileTok, &nv2), ring[2]);
     if (ntiles > 2)
@@ -398,7 +416,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     else
       wait_dma<0>();
     __syncthreads();
-    softmax_all(scores(ring[0]), nv0, 0);
+    softmax_all(scores(ring[0], nullptr, 0u), nv0, 0);
     if (nv0 < kTileTok) zero_tail(ring[0], nv0);
   }
 
@@ -414,14 +432,14 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       wait_dma<0>();
     __syncthreads();
     int nv3 = 0;
-    if (t + 3 < ntiles) issue_tile(tile_src(pos0 + 3 * kTileTok, &nv3), ring[(t + 3) & (kSlots - 1)]);
+    const char* src3 = t + 3 < ntiles ? tile_src(pos0 + 3 * kTileTok, &nv3) : nullptr;
     // One body for every iteration (separate paths would split the query registers' live
     // ranges): on the last tile the next slot holds stale data, and with no valid position
     // the mask turns every score into -inf, which leaves m_ref, l and the flag unchanged.
     const int nv_next = t + 1 < ntiles ? nv1 : 0;
     nv1 = nv2;
     nv2 = nv3;
-    f32x16 sc = scores(ring[nslot]);
+    f32x16 sc = scores(ring[nslot], src3, lds_addr(ring[(t + 3) & (kSlots - 1)]) + w * 64 * 16);
     if (nv_next < kTileTok) mask_tail(sc, nv_next);
     pv(ring[slot], t & 1, sc, (t + 1) & 1);
     // zeroed before the next barrier; other waves may still be reading these rows for their
