@@ -239,8 +239,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   int ids = load_ids();
   // Cache address of the tile at pos0 (a multiple of 32 inside one block) and its number of
   // valid positions (0 for a bad block id, whose rows are then never used).
-  auto tile_src = [&](int pos0, int* nvalid) -> const char* {
-    const int jb = pos0 / bs;
+  const int64_t blk_bytes = static_cast<int64_t>(bs) * kRowBytes;
+  // jb = pos0 / bs and off = pos0 - jb * bs are passed in (the loop tracks them incrementally)
+  auto tile_src_at = [&](int pos0, int jb, int off, int* nvalid) -> const char* {
     if (jb - jbase >= 64) {
       jbase = jb;
       ids = load_ids();
@@ -249,8 +250,11 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     const bool ok = id >= 0 && id < num_blocks;
     const int n = t1 - pos0 < kTileTok ? t1 - pos0 : kTileTok;
     *nvalid = ok ? n : 0;
-    return reinterpret_cast<const char*>(cache) +
-           (static_cast<int64_t>(ok ? id : 0) * bs + (pos0 - jb * bs)) * kRowBytes;
+    return reinterpret_cast<const char*>(cache) + (ok ? id : 0) * blk_bytes + off * kRowBytes;
+  };
+  auto tile_src = [&](int pos0, int* nvalid) -> const char* {
+    const int jb = pos0 / bs;
+    return tile_src_at(pos0, jb, pos0 - jb * bs, nvalid);
   };
   auto issue_tile = [&](const char* src, char* slot) __attribute__((always_inline)) {
     const unsigned lbase = lds_addr(slot) + w * 64 * 16;
@@ -294,7 +298,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   // numerators are left in P's LDS slot `par` as the A operand of the next P · V.
   // Split in pieces (compile-time numbers) so the unmasked case can be spread between the
   // P · V products.
-  constexpr int kSoftPieces = 18;
+  constexpr int kSoftPieces = 26;
   auto soft_piece = [&](int piece, f32x16& sc, SoftState& s, int par)
                         __attribute__((always_inline)) {
     if (piece == 0) {
@@ -315,16 +319,15 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       over = over || (mt > m_ref + kHead);
       s.neg = m_ref == -INFINITY ? 0.f : -m_ref;  // all masked so far: p = 0 anyway
       s.psum = 0.f;
-    } else if (piece <= 12) {
-      const int r = 2 * (piece - 5);
+    } else if (piece <= 20) {
+      // one transcendental per piece: it takes a quarter-rate VALU slot
+      const int r = piece - 5;
       // v_exp_f32: results below 2^-126 may flush to zero, negligible against l >= 1
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, s.neg));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[r + 1], scale_log2, s.neg));
-      s.psum += p0 + p1;
-      sc[r] = p0;
-      sc[r + 1] = p1;
-    } else if (piece <= 16) {
-      const int r = 4 * (piece - 13);
+      const float pr = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, s.neg));
+      s.psum += pr;
+      sc[r] = pr;
+    } else if (piece <= 24) {
+      const int r = 4 * (piece - 21);
 #pragma unroll
       for (int e = 0; e < 4; ++e) s.pf[r >> 3][(r & 7) + e] = static_cast<__bf16>(sc[r + e]);
     } else {
@@ -420,6 +423,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     if (nv0 < kTileTok) zero_tail(ring[0], nv0);
   }
 
+  // block and in-block offset of tile t+3, advanced by one tile per iteration
+  int jb3 = (t0 + 3 * kTileTok) / bs;
+  int off3 = t0 + 3 * kTileTok - jb3 * bs;
   for (int t = 0; t < ntiles; ++t) {
     const int slot = t & (kSlots - 1);
     const int nslot = (t + 1) & (kSlots - 1);
@@ -432,7 +438,13 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       wait_dma<0>();
     __syncthreads();
     int nv3 = 0;
-    const char* src3 = t + 3 < ntiles ? tile_src(pos0 + 3 * kTileTok, &nv3) : nullptr;
+    const char* src3 =
+        t + 3 < ntiles ? tile_src_at(pos0 + 3 * kTileTok, jb3, off3, &nv3) : nullptr;
+    off3 += kTileTok;
+    if (off3 >= bs) {
+      off3 -= bs;
+      ++jb3;
+    }
     // One body for every iteration (separate paths would split the query registers' live
     // ranges): on the last tile the next slot holds stale data, and with no valid position
     // the mask turns every score into -inf, which leaves m_ref, l and the flag unchanged.
