@@ -74,7 +74,7 @@ typedef struct mla_dims {
   int32_t d_model;     /* C: width of the hidden states appended to the cache */
   int32_t n_heads;     /* H: query heads */
   int32_t d_nope;      /* D: per-head content (non-rotary) query/key width */
-  int32_t d_v;         /* D_v: per-head value width (a multiple of 4) */
+  int32_t d_v;         /* D_v: per-head value width (a multiple of 8) */
   int32_t d_c;         /* d_c: latent width (a multiple of 8) */
   int32_t d_r;         /* d_r: shared rotary key width (even, may be 0) */
   int32_t n_groups;    /* G: groups indexing W_UK / W_UV; divides H; G == H is plain MLA */

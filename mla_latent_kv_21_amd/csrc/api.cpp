@@ -12,6 +12,9 @@ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Bytes per element of every float tensor, and of the split partial rows.
+int elt_of(const mla_dims& d) { return d.dtype == MLA_BF16 ? 2 : 4; }
+
 mla_status check_dims(const mla_dims* d) {
   if (d == nullptr) return MLA_ERR_NULL;
   if (d->dtype != MLA_F32 && d->dtype != MLA_BF16) return MLA_ERR_DTYPE;
@@ -20,7 +23,7 @@ mla_status check_dims(const mla_dims* d) {
     return MLA_ERR_SHAPE;
   if (d->n_heads % d->n_groups != 0) return MLA_ERR_SHAPE;
   if (d->d_c % 8 != 0) return MLA_ERR_SHAPE;  // 16-byte weight loads never straddle c and k_r
-  if (d->d_v % 4 != 0) return MLA_ERR_SHAPE;  // the merge reads partial rows as float4
+  if (d->d_v % 8 != 0) return MLA_ERR_SHAPE;  // the merge reads partial rows 16 bytes at a time
   // LDS budgets of the portable kernels: query row + value row + 2 KiB of per-pass state,
   // and 16 merged latent rows in the combine.
   if (d->d_c + d->d_r > 4096 || d->d_nope + d->d_r > 4096 || d->d_v > 1024 || d->d_c > 1024 ||
@@ -121,7 +124,7 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s
       n_split > MLA_MAX_SPLIT)
     return 0;
   const int ns = n_split == 0 ? resolve_split(*dims, batch, s_q, max_blocks) : n_split;
-  return mla::partials_bytes(batch, s_q, dims->n_heads, ns, dims->d_c);
+  return mla::partials_bytes(batch, s_q, dims->n_heads, ns, dims->d_c, elt_of(*dims));
 }
 
 }  // extern "C"
@@ -145,7 +148,7 @@ mla_status check_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const 
   if (!q_abs || !latent_cache || !block_table || !seq_lens) return MLA_ERR_NULL;
   if (!aligned16(q_abs) || !aligned16(latent_cache)) return MLA_ERR_ALIGN;
   *ns = n_split == 0 ? resolve_split(*dims, batch, s_q, max_blocks) : n_split;
-  const size_t need = mla::partials_bytes(batch, s_q, dims->n_heads, *ns, dims->d_c);
+  const size_t need = mla::partials_bytes(batch, s_q, dims->n_heads, *ns, dims->d_c, elt_of(*dims));
   if (workspace == nullptr || ws_bytes < need) return MLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MLA_ERR_ALIGN;
   return MLA_OK;
@@ -233,7 +236,7 @@ size_t gqla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t 
       n_split > MLA_MAX_SPLIT)
     return 0;
   const int ns = n_split == 0 ? resolve_split(*dims, batch, s_q, max_blocks) : n_split;
-  return mla::partials_bytes(batch, s_q, dims->n_heads, ns, dims->d_v);
+  return mla::partials_bytes(batch, s_q, dims->n_heads, ns, dims->d_v, elt_of(*dims));
 }
 
 mla_status gqla_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_nope,
@@ -256,7 +259,7 @@ mla_status gqla_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const v
   if (!aligned16(q_nope) || (q_pe && !aligned16(q_pe)) || !aligned16(gqa_cache) || !aligned16(out))
     return MLA_ERR_ALIGN;
   const int ns = n_split == 0 ? resolve_split(*dims, batch, s_q, max_blocks) : n_split;
-  const size_t need = mla::partials_bytes(batch, s_q, dims->n_heads, ns, dims->d_v);
+  const size_t need = mla::partials_bytes(batch, s_q, dims->n_heads, ns, dims->d_v, elt_of(*dims));
   if (workspace == nullptr || ws_bytes < need) return MLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MLA_ERR_ALIGN;
   return hip_status(mla::launch_gqa_decode(*dims, batch, s_q, q_nope, q_pe, q_pos, gqa_cache,

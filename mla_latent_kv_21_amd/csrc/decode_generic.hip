@@ -32,7 +32,7 @@ struct GenericArgs {
   float scale_log2, base;
   // Partials of split k for row r = (b s_q + i) H + h sit at [k * n_rows + r]: one split's rows
   // are contiguous (a workgroup writes one block), a row's splits are n_rows apart.
-  float* part_o;
+  void* part_o;  // partial rows, stored at the cache dtype T
   float* part_lse;
   int n_rows;    // batch * s_q * H
   int part_w;    // value width (latent: d_c; GQA: D_v)
@@ -113,7 +113,7 @@ __device__ void split_head(const GenericArgs& a, int b, int i, int k, int h, flo
   const bool any = l > 0.f;
   const float inv = any ? 1.0f / l : 0.f;
   for (int e = threadIdx.x; e < a.part_w; e += blockDim.x)
-    a.part_o[pidx * a.part_w + e] = os[e] * inv;
+    st(static_cast<T*>(a.part_o), pidx * a.part_w + e, os[e] * inv);
   if (threadIdx.x == 0) a.part_lse[pidx] = any ? m + log2f(l) : -INFINITY;
   __syncthreads();
 }
@@ -188,37 +188,37 @@ __global__ __launch_bounds__(kMergeThreads, 4) void merge_kernel(GenericArgs a,
                                                               const T* __restrict__ w_uv, int dv,
                                                               T* __restrict__ out,
                                                               float* lse_out) {
-  constexpr int kVec = 16 / static_cast<int>(sizeof(T));
+  constexpr int kVec = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte load
   extern __shared__ float smem[];
   __shared__ float red[16];
   __shared__ float wts[MLA_MAX_SPLIT];
   __shared__ __attribute__((aligned(16))) float o_s[kMaxMergeW];
-  __shared__ float4 mpart[kMergeThreads];
+  __shared__ float mpart[kMergeThreads * kVec];
   __shared__ float psum[kMergeThreads * kVec];
   __shared__ unsigned long long flagged[kMergeThreads / 64];
   const int n_split = a.n_split, pw = a.part_w, H = a.H;
   const int h = blockIdx.x, m = blockIdx.y;
   const int64_t rh = static_cast<int64_t>(m) * H + h;
   const int tid = threadIdx.x;
-  const float* P = a.part_o + rh * pw;             // split k at + k * n_rows * pw
+  const T* P = static_cast<const T*>(a.part_o) + rh * pw;  // split k at + k * n_rows * pw
   const int64_t kstride = static_cast<int64_t>(a.n_rows) * pw;
 
   // ---- everything this thread needs first is requested here
   float lk = tid < n_split ? a.part_lse[static_cast<int64_t>(tid) * a.n_rows + rh] : -INFINITY;
   const bool flag = redo != nullptr && tid < n_split &&
                     redo[static_cast<int64_t>(m) * n_split + tid] != 0;
-  const int nq = pw >> 2;  // pw % 4 == 0, nq <= kMergeThreads (checked on the host)
+  const int nq = pw / kVec;  // pw % 8 == 0 and pw <= 1024 (checked on the host)
   const int ngrp = min(16, kMergeThreads / nq);
   const int per = cdiv(n_split, ngrp);
   const int cq = tid % nq, grp = tid / nq;
   const bool pthread = grp < ngrp;
   const int k0 = pthread ? grp * per : 0, k1 = pthread ? min(n_split, k0 + per) : 0;
-  float4 v[kMergeU];
+  uint4 v[kMergeU];  // 16 raw bytes of a partial row per split, widened at use
   auto load_parts = [&](int kb) {
 #pragma unroll
     for (int u = 0; u < kMergeU; ++u)
-      v[u] = kb + u < k1 ? *reinterpret_cast<const float4*>(P + (kb + u) * kstride + 4 * cq)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[u] = kb + u < k1 ? *reinterpret_cast<const uint4*>(P + (kb + u) * kstride + kVec * cq)
+                         : make_uint4(0u, 0u, 0u, 0u);
   };
   load_parts(k0);
   const int g = h / (H / a.G);
@@ -279,27 +279,32 @@ __global__ __launch_bounds__(kMergeThreads, 4) void merge_kernel(GenericArgs a,
   __syncthreads();
 
   // ---- o_lat = sum_k w_k o_k into LDS (a split's weight 0 times its finite row adds 0)
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[kVec];
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) acc[e] = 0.f;
   for (int kb = k0; kb < k1; kb += kMergeU) {
     if (kb != k0) load_parts(kb);
 #pragma unroll
     for (int u = 0; u < kMergeU; ++u) {
       const float wk = kb + u < k1 ? wts[kb + u] : 0.f;
-      acc.x = fmaf(wk, v[u].x, acc.x);
-      acc.y = fmaf(wk, v[u].y, acc.y);
-      acc.z = fmaf(wk, v[u].z, acc.z);
-      acc.w = fmaf(wk, v[u].w, acc.w);
+      float f[kVec];
+      widen16<T>(v[u], f);
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) acc[e] = fmaf(wk, f[e], acc[e]);
     }
   }
-  if (pthread) mpart[grp * nq + cq] = acc;
+  if (pthread) {
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) mpart[(grp * nq + cq) * kVec + e] = acc[e];
+  }
   __syncthreads();
   if (tid < nq) {
-    float4 r = mpart[tid];
-    for (int q = 1; q < ngrp; ++q) {
-      const float4 t = mpart[q * nq + tid];
-      r.x += t.x; r.y += t.y; r.z += t.z; r.w += t.w;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      float r = mpart[tid * kVec + e];
+      for (int q = 1; q < ngrp; ++q) r += mpart[(q * nq + tid) * kVec + e];
+      o_s[kVec * tid + e] = r;
     }
-    *reinterpret_cast<float4*>(o_s + 4 * tid) = r;
   }
   __syncthreads();
   T* orow = out + rh * dv;
@@ -354,17 +359,17 @@ hipError_t run_combine(const GenericArgs& a, const int* redo, int batch, int dv,
 
 // Workspace views of one split-K decode.
 struct Partials {
-  float* o;
+  void* o;
   float* lse;
   int* redo;
 };
 
-Partials partials_of(void* ws, int batch, int s_q, int heads, int n_split, int width) {
+Partials partials_of(void* ws, int batch, int s_q, int heads, int n_split, int width, int elt) {
   const size_t rows = static_cast<size_t>(batch) * s_q * heads * n_split;
   char* base = static_cast<char*>(ws);
   Partials p;
-  p.o = reinterpret_cast<float*>(base);
-  base += (rows * width * sizeof(float) + 255) / 256 * 256;
+  p.o = base;
+  base += (rows * width * elt + 255) / 256 * 256;
   p.lse = reinterpret_cast<float*>(base);
   base += (rows * sizeof(float) + 255) / 256 * 256;
   p.redo = reinterpret_cast<int*>(base);
@@ -391,9 +396,9 @@ bool uses_mfma(const mla_dims& d) {
 
 }  // namespace
 
-size_t partials_bytes(int batch, int s_q, int heads, int n_split, int width) {
+size_t partials_bytes(int batch, int s_q, int heads, int n_split, int width, int elt) {
   const size_t rows = static_cast<size_t>(batch) * s_q * heads * n_split;
-  const size_t o = (rows * width * sizeof(float) + 255) / 256 * 256;
+  const size_t o = (rows * width * elt + 255) / 256 * 256;
   const size_t l = (rows * sizeof(float) + 255) / 256 * 256;
   const size_t f = (static_cast<size_t>(batch) * s_q * n_split * sizeof(int) + 255) / 256 * 256;
   return o + l + f;
@@ -403,7 +408,7 @@ hipError_t launch_decode_splitk(const mla_dims& d, int batch, int s_q, const voi
                                 const void* cache, int num_blocks, const int32_t* table,
                                 int max_blocks, const int32_t* seq_lens, int n_split, void* ws,
                                 hipStream_t s) {
-  const Partials p = partials_of(ws, batch, s_q, d.n_heads, n_split, d.d_c);
+  const Partials p = partials_of(ws, batch, s_q, d.n_heads, n_split, d.d_c, d.dtype == MLA_BF16 ? 2 : 4);
   if (uses_mfma(d))
     return launch_decode_mfma(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
                               seq_lens, n_split, p.o, p.lse, p.redo, s);
@@ -417,7 +422,7 @@ hipError_t launch_decode_merge(const mla_dims& d, int batch, int s_q, const void
                                const void* cache, int num_blocks, const int32_t* table,
                                int max_blocks, const int32_t* seq_lens, const void* w_uv,
                                int n_split, void* ws, void* out, float* lse, hipStream_t s) {
-  const Partials p = partials_of(ws, batch, s_q, d.n_heads, n_split, d.d_c);
+  const Partials p = partials_of(ws, batch, s_q, d.n_heads, n_split, d.d_c, d.dtype == MLA_BF16 ? 2 : 4);
   const GenericArgs a = latent_args(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
                                     seq_lens, n_split, p);
   // Only the MFMA kernel writes recompute flags; the portable kernel computes every split.
@@ -431,7 +436,7 @@ hipError_t launch_gqa_decode(const mla_dims& d, int batch, int s_q, const void* 
                              int num_blocks, const int32_t* table, int max_blocks,
                              const int32_t* seq_lens, int n_split, void* ws, void* out,
                              float* lse, hipStream_t s) {
-  const Partials p = partials_of(ws, batch, s_q, d.n_heads, n_split, d.d_v);
+  const Partials p = partials_of(ws, batch, s_q, d.n_heads, n_split, d.d_v, d.dtype == MLA_BF16 ? 2 : 4);
   GenericArgs a{};
   a.q = q_nope; a.q_pe = q_pe; a.q_pos = q_pos; a.cache = gqa; a.table = table;
   a.lens = seq_lens; a.num_blocks = num_blocks; a.max_blocks = max_blocks; a.bs = d.block_size;

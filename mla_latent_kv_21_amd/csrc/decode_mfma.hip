@@ -27,7 +27,7 @@
 //  * the loop body is scheduled by hand: the scores of tile t+1 run with their LDS reads
 //    several steps ahead, then P · V of tile t runs with the softmax of tile t+1 spread
 //    between its products, so the matrix cores are fed while the VALU and LDS work;
-//  * each split writes (O / l, m + log2 l) partials; the merge kernel combines the splits.
+//  * each split writes (O / l as bf16, m + log2 l) partials; the merge kernel combines them.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -113,6 +113,13 @@ __device__ __forceinline__ bf16x8 lds16(const char* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
+// two floats as a bf16 pair (round to nearest even), low element first
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(unsigned, v);
+}
+
 // max over the lane pair (lane, lane ^ 32), without going through LDS
 __device__ __forceinline__ float max_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ cache,
                         const int32_t* __restrict__ table, const int32_t* __restrict__ lens,
                         int num_blocks, int max_blocks, int bs, int s_q, int n_split,
-                        float scale_log2, float* __restrict__ part_o,
+                        float scale_log2, uint16_t* __restrict__ part_o,
                         float* __restrict__ part_lse, int* __restrict__ redo) {
   constexpr int H = NW * 32;
   constexpr int kDB = 16 / NW;                      // 32-column latent blocks per wave
@@ -167,8 +174,8 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
 
   if (t0 >= t1) {  // empty split: lse -inf (weight zero in the merge) and a zero partial row
     for (int h = threadIdx.x; h < H; h += blockDim.x) part_lse[prow0 + h] = -INFINITY;
-    for (int e = threadIdx.x; e < H * (kLat / 4); e += blockDim.x)
-      *reinterpret_cast<float4*>(part_o + prow0 * kLat + 4 * e) = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int e = threadIdx.x; e < H * (kLat / 8); e += blockDim.x)
+      *reinterpret_cast<uint4*>(part_o + prow0 * kLat + 8 * e) = make_uint4(0u, 0u, 0u, 0u);
     if (threadIdx.x == 0) redo[split_id] = 0;
     return;
   }
@@ -484,12 +491,12 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     redo[split_id] = any;
   }
   // O / l leaves through the ring one 32-head block at a time (rows padded by 32 bytes so the
-  // two half-waves' rows fall on different banks) and is written with 16-byte stores.
+  // two half-waves' rows fall on different banks) and is written as bf16 with 16-byte stores.
   constexpr int kStageRow = kLat * 4 + 32;
   char* stage = ring[0] + 1024;  // after the Tail
   static_assert(1024 + 32 * kStageRow <= kSlots * kTileBytes, "stage fits in the ring");
   static_assert(sizeof(Tail<NW>) <= 1024, "tail fits before the stage");
-  float* dst = part_o + prow0 * kLat;
+  uint16_t* dst = part_o + prow0 * kLat;
 #pragma unroll
   for (int hb = 0; hb < NW; ++hb) {
 #pragma unroll
@@ -502,10 +509,13 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
             o[hb * kDB + db][r] * il;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < 32 * (kLat / 4); e += NW * 64) {
-      const int row = e / (kLat / 4), c4 = e - row * (kLat / 4);
-      *reinterpret_cast<float4*>(dst + (32 * hb + row) * kLat + 4 * c4) =
-          *reinterpret_cast<const float4*>(stage + row * kStageRow + 16 * c4);
+    for (int e = threadIdx.x; e < 32 * (kLat / 8); e += NW * 64) {
+      const int row = e / (kLat / 8), c8 = e - row * (kLat / 8);
+      const float4 lo = *reinterpret_cast<const float4*>(stage + row * kStageRow + 32 * c8);
+      const float4 up = *reinterpret_cast<const float4*>(stage + row * kStageRow + 32 * c8 + 16);
+      *reinterpret_cast<uint4*>(dst + (32 * hb + row) * kLat + 8 * c8) =
+          make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w), pack_bf16x2(up.x, up.y),
+                     pack_bf16x2(up.z, up.w));
     }
     __syncthreads();
   }
@@ -521,14 +531,14 @@ bool mfma_decode_fits(const mla_dims& d) {
 hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void* q_abs,
                               const void* cache, int num_blocks, const int32_t* table,
                               int max_blocks, const int32_t* seq_lens, int n_split,
-                              float* part_o, float* part_lse, int* redo, hipStream_t s) {
+                              void* part_o, float* part_lse, int* redo, hipStream_t s) {
   const float scale_log2 = softmax_scale_of(d) * 1.4426950408889634f;
   const dim3 grid(n_split, s_q, batch);
 #define MLA_LAUNCH(NW_)                                                                      \
   hipLaunchKernelGGL(decode_mfma_kernel<NW_>, grid, dim3(64 * NW_), 0, s,                     \
                      static_cast<const uint16_t*>(q_abs), static_cast<const uint16_t*>(cache), \
                      table, seq_lens, num_blocks, max_blocks, d.block_size, s_q, n_split,      \
-                     scale_log2, part_o, part_lse, redo)
+                     scale_log2, static_cast<uint16_t*>(part_o), part_lse, redo)
   switch (d.n_heads) {
     case 128: MLA_LAUNCH(4); break;
     case 64: MLA_LAUNCH(2); break;

@@ -27,7 +27,7 @@ hipError_t launch_absorb(const mla_dims& d, int batch, int s_q, const void* q_no
 // Workspace of one split-K decode, each part 256-byte aligned: partial o [B, s_q, H, n_split,
 // width] fp32, partial lse2 [B, s_q, H, n_split] fp32 (log2 domain of scale*score), recompute
 // flags [B, s_q, n_split] int32, and the merged rows [B, s_q, H, width] fp32.
-size_t partials_bytes(int batch, int s_q, int heads, int n_split, int width);
+size_t partials_bytes(int batch, int s_q, int heads, int n_split, int width, int elt);
 
 // Split-K core: every (split, query, sequence) writes its partials (and recompute flag).
 hipError_t launch_decode_splitk(const mla_dims& d, int batch, int s_q, const void* q_abs,
@@ -56,7 +56,7 @@ bool mfma_decode_fits(const mla_dims& d);
 hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void* q_abs,
                               const void* cache, int num_blocks, const int32_t* table,
                               int max_blocks, const int32_t* seq_lens, int n_split,
-                              float* part_o, float* part_lse, int* redo, hipStream_t s);
+                              void* part_o, float* part_lse, int* redo, hipStream_t s);
 
 inline float softmax_scale_of(const mla_dims& d) {
   return d.softmax_scale > 0.f ? d.softmax_scale

@@ -44,7 +44,7 @@ def decode_ws_layout(c, n_split):
     w = c["w"]
     rows = w.batch * w.s_q * w.n_heads * n_split
     al = lambda x: (x + 255) // 256 * 256
-    off_flags = al(rows * w.d_c * 4) + al(rows * 4)
+    off_flags = al(rows * w.d_c * w.elt) + al(rows * 4)  # partial rows at the cache dtype
     return off_flags, w.batch * w.s_q * n_split
 
 

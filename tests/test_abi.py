@@ -66,7 +66,7 @@ def test_decode_validation(L):
     assert decode_call(L, dims(dtype=7)) == -3
     assert decode_call(L, dims(n_groups=3)) == -2          # 3 does not divide 128
     assert decode_call(L, dims(d_r=63)) == -2              # odd rotary width
-    assert decode_call(L, dims(d_v=126)) == -2             # value rows are merged as float4
+    assert decode_call(L, dims(d_v=124)) == -2             # value rows are merged 16 bytes at a time
     assert decode_call(L, dims(d_c=500)) == -2             # latent width not a multiple of 8
     assert decode_call(L, d, batch=0) == 0                 # empty batch: nothing to do
     assert decode_call(L, d, s_q=0) == -4
@@ -85,10 +85,10 @@ def test_workspace_sizes(L):
     n = L.mla_decode_workspace_bytes(ctypes.byref(d), 4, 1, 64, 2048)
     rows = 4 * 128 * 64
     al = lambda x: (x + 255) // 256 * 256
-    assert n == al(rows * 512 * 4) + al(rows * 4) + al(4 * 64 * 4)
+    assert n == al(rows * 512 * 2) + al(rows * 4) + al(4 * 64 * 4)  # bf16 partial rows
     g = L.gqla_decode_workspace_bytes(ctypes.byref(d), 4, 2, 8, 2048)
     rows = 4 * 2 * 128 * 8
-    assert g == al(rows * 128 * 4) + al(rows * 4) + al(4 * 2 * 8 * 4)
+    assert g == al(rows * 128 * 2) + al(rows * 4) + al(4 * 2 * 8 * 4)
     assert L.mla_decode_workspace_bytes(ctypes.byref(d), 4, 1, M.MLA_MAX_SPLIT + 1, 2048) == 0
     # auto split: never more splits than 64-position chunks of the longest sequence
     assert L.mla_auto_split(ctypes.byref(d), 1, 1, 1) == 1
