@@ -111,9 +111,9 @@ __global__ __launch_bounds__(256) void absorb_mfma(const uint16_t* __restrict__ 
       if (mm < M) q_abs[(static_cast<int64_t>(mm) * H + h) * row + j] = f32_to_bf16(acc[r]);
     }
   }
+  // rotary part: the (row, pair) items are shared out over the z-blocks of this head
   const int half = d_r / 2;
-  if (blockIdx.z != 0) return;
-  for (int e = threadIdx.x; e < 32 * half; e += blockDim.x) {
+  for (int e = threadIdx.x + blockIdx.z * blockDim.x; e < 32 * half; e += blockDim.x * gridDim.z) {
     const int r = e / half, jj = e % half;
     const int mm = m0 + r;
     if (mm >= M) continue;
