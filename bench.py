@@ -80,6 +80,84 @@ def cpu_baseline(w, lens, budget_s: float):
                       f"{w.n_heads} heads, {t:.1f} s; scaled by heads and by total length"}
 
 
+def _time_calls(fn, reps: int, torch):
+    """Median duration (ms) of fn() over reps launches, each bracketed by HIP events on the
+    current stream, after two warm-up calls."""
+    fn(); fn()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    stream = torch.cuda.current_stream()
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def measure_rows(dev, torch):
+    """The other rows of the path, each timed on its own workload: the absorbed decode on the
+    DeepSeek-shaped paged workload (64 sequences, lengths 1,024..8,192, random block table),
+    and on the GQLA workload (G = 8, 32 x 32,768) the absorbed decode, the GQA expansion and
+    the GQA decode. Rates use each call's algorithmic bytes against 8 TB/s."""
+    import workloads as W
+    from mla_latent_kv_21_amd import accounting as A
+    from mla_latent_kv_21_amd import binding as M
+    g = lambda a: (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
+    rows = {}
+
+    def absorbed(cfg):
+        w = W.CONFIGS[cfg]
+        lens = W.seq_lens(w)
+        table, nb = W.block_table(w, lens)
+        d = M.dims_of(w)
+        cache = W.cache_pool_device(w, nb, dev)
+        q_abs = g(W.absorbed_queries(w))
+        wts = {k: g(v) for k, v in W.weights(w).items()}
+        tab, lens_d = g(table), g(lens)
+        out = torch.empty(w.batch, w.s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=dev)
+        ns = M.mla_auto_split(d, w.batch, w.s_q, table.shape[1])
+        ws = torch.empty(M.mla_decode_workspace_bytes(d, w.batch, w.s_q, ns, table.shape[1]),
+                         dtype=torch.uint8, device=dev)
+        ms = _time_calls(lambda: M.mla_decode(d, q_abs, cache, tab, lens_d, wts["w_uv"], out,
+                                              n_split=ns, workspace=ws), 20, torch)
+        tr = A.decode_traffic(lens, w.s_q, w.n_heads, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt)
+        gbs = tr["bytes"] / (ms * 1e-3) / 1e9
+        return {"workload": w.name, "call": "mla_decode", "ms": ms,
+                "tokens_per_s": w.batch * w.s_q / (ms * 1e-3), "GBps": gbs,
+                "frac_hbm": gbs / HBM_PEAK_GBS, "n_split": ns}, (w, lens, table, nb, cache, tab,
+                                                                  lens_d, wts)
+
+    rows["absorbed_dsv3_paged"], _ = absorbed(3)
+    rows["absorbed_gqla_g8"], ctx = absorbed(5)
+    w, lens, table, nb, cache, tab, lens_d, wts = ctx
+    d = M.dims_of(w)
+    gqa = torch.empty(nb, w.block_size, w.n_groups * (w.d_nope + w.d_v) + w.d_r,
+                      dtype=w.torch_dtype, device=dev)
+    ms = _time_calls(lambda: M.gqla_expand(d, cache, tab, lens_d, wts["w_uk"], wts["w_uv"], gqa),
+                     5, torch)
+    L = int(np.sum(lens))
+    eb = L * (A.latent_row_bytes(w.d_c, w.d_r, w.elt) + A.gqa_row_bytes(w.n_groups, w.d_nope,
+                                                                        w.d_r, w.elt))
+    rows["gqla_expand"] = {"workload": w.name, "call": "gqla_expand", "ms": ms,
+                           "positions_per_s": L / (ms * 1e-3), "GBps": eb / (ms * 1e-3) / 1e9,
+                           "frac_hbm": eb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    q = {k: g(v) for k, v in W.queries(w).items()}
+    qpos = g(W.query_positions(w, lens))
+    out = torch.empty(w.batch, w.s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=dev)
+    ns = M.mla_auto_split(d, w.batch, w.s_q, table.shape[1])
+    ws = torch.empty(M.gqla_decode_workspace_bytes(d, w.batch, w.s_q, ns, table.shape[1]),
+                     dtype=torch.uint8, device=dev)
+    ms = _time_calls(lambda: M.gqla_decode(d, q["q_nope"], q["q_pe"], qpos, gqa, tab, lens_d, out,
+                                           n_split=ns, workspace=ws), 5, torch)
+    tr = A.gqa_decode_traffic(lens, w.s_q, w.n_heads, w.n_groups, w.d_nope, w.d_r, w.elt)
+    rows["gqla_decode"] = {"workload": w.name, "call": "gqla_decode", "ms": ms,
+                           "tokens_per_s": w.batch * w.s_q / (ms * 1e-3),
+                           "GBps": tr["bytes"] / (ms * 1e-3) / 1e9,
+                           "frac_hbm": tr["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -89,6 +167,8 @@ def main():
                     help="workload index (default 4: H=128, d_c=512, 4 x 131,072 context)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true",
+                    help="skip timing the path's other rows on their own workloads")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a bf16 buffer of this many MiB three "
                          "times (a plain copy of known size for scaling HBM byte counters)")
@@ -187,6 +267,8 @@ def main():
         "step_latent_cache_GBps": tr["cache_bytes"] / (ms_step * 1e-3) / 1e9,
         "wall_s": wall,
     }
+    if not args.no_rows:
+        rec["rows"] = measure_rows(dev, torch)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 2
         src = torch.randn(n, device=dev).to(torch.bfloat16)
