@@ -161,6 +161,33 @@ def test_gqla_expand_matches_oracle():
         assert np.isnan(got[:s]).all()                   # prefix left untouched
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gqla_expand_ragged_shapes(dtype):
+    """Expansion where the expanded width (3 groups x (24 + 16) = 120 columns) fills part of
+    a column tile, d_c = 128 spans two latent chunks, and the lengths leave ragged position
+    tiles (1, 255, 257 and 600 positions, block size 16); bf16 runs on the matrix cores, fp32 on
+    the portable kernel."""
+    w = W.CONFIGS[5].replace(n_groups=3, n_heads=6, d_nope=24, d_v=16, d_c=128, d_r=16,
+                             block_size=16, dtype=dtype)
+    c = decode_case(w, [1, 255, 257, 600], extra=23)
+    wts = W.weights(c["w"])
+    d = M.dims_of(c["w"])
+    g = gqa_cache_empty(w, c["nb"])
+    note(f"gqla_expand ragged shapes {dtype}")
+    M.gqla_expand(d, dev(c["pool"]), dev(c["table"]), dev(c["lens"]), dev(wts["w_uk"]),
+                  dev(wts["w_uv"]), g)
+    torch.cuda.synchronize()
+    g = g.cpu()
+    for b, L in enumerate(c["lens"]):
+        rows = O.gather_rows(c["pool"], c["table"], b, int(L))
+        ref = O.gqa_expand_rows(rows, wts["w_uk"], wts["w_uv"], w.n_groups, w.d_c, w.d_nope, w.d_v)
+        got = O.gather_rows(g, c["table"], b, int(L))
+        if dtype == "bf16":
+            assert ulp_close(got, ref, w.dtype) or rel_err(got, ref) <= 4e-3
+        else:
+            assert rel_err(got, ref) <= TOL["f32"]
+
+
 @pytest.mark.parametrize("s_q", [1, 2, 4])
 def test_gqla_paths_agree_with_oracle(s_q):
     """GQA path (expand once, then grouped decode) and absorbed path on the same weights and
