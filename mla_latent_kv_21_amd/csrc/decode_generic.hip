@@ -445,8 +445,13 @@ hipError_t launch_gqa_decode(const mla_dims& d, int batch, int s_q, const void* 
   a.d_c = d.d_c; a.d_r = d.d_r; a.D = d.d_nope; a.Dv = d.d_v;
   a.scale_log2 = softmax_scale_of(d) * kLog2e; a.base = d.rope_base;
   a.part_o = p.o; a.part_lse = p.lse; a.part_w = d.d_v; a.n_rows = batch * s_q * d.n_heads;
-  hipError_t e = d.dtype == MLA_BF16 ? run_generic<bf16, true>(a, batch, s)
-                                     : run_generic<float, true>(a, batch, s);
+  hipError_t e;
+  if (gqa_mfma_fits(d, s_q))
+    e = launch_gqa_mfma(d, batch, s_q, q_nope, q_pe, q_pos, gqa, num_blocks, table, max_blocks,
+                        seq_lens, n_split, p.o, p.lse, s);
+  else
+    e = d.dtype == MLA_BF16 ? run_generic<bf16, true>(a, batch, s)
+                            : run_generic<float, true>(a, batch, s);
   if (e != hipSuccess) return e;
   return d.dtype == MLA_BF16
              ? run_combine<bf16>(a, nullptr, batch, d.d_v, nullptr, out, lse, s)

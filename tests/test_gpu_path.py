@@ -221,3 +221,41 @@ def test_gqla_paths_agree_with_oracle(s_q):
         assert rel_err(out_a[b], ref) <= TOL["bf16"]
         assert np.max(np.abs(lse_g[b].cpu().double().numpy() - ref_lse)) <= TOL["bf16"]
     assert rel_err(out_g, out_a.double()) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("s_q,n_split,bs,generic", [(1, 0, 64, False), (3, 7, 32, False),
+                                                    (8, 64, 32, False), (2, 5, 32, True)])
+def test_gqa_decode_matches_oracle(s_q, n_split, bs, generic):
+    """gqla_decode alone, on an expanded cache written from the oracle's expansion (stored
+    as bf16), against the oracle's grouped-query decode of those same rows: lengths from
+    s_q to past several tiles and splits, few and many (mostly empty) splits, up to 64 query
+    rows per group (H / G = 8 heads x s_q = 8), block sizes 32 and 64, and the portable
+    kernel on the same case."""
+    w = W.CONFIGS[5].replace(n_heads=32, n_groups=4, block_size=bs, s_q=s_q)
+    c = decode_case(w, [s_q, 31 + s_q, 33, 700], s_q=s_q, extra=24)
+    wts = W.weights(c["w"])
+    q = W.queries(c["w"])
+    qpos = W.query_positions(c["w"], c["lens"])
+    d = M.dims_of(c["w"], generic=generic)
+    gw = w.n_groups * (w.d_nope + w.d_v) + w.d_r
+    g = torch.full((c["nb"] * bs, gw), float("nan"), dtype=torch.float64)
+    rows_of = []
+    for b, L in enumerate(c["lens"]):
+        rows = O.gather_rows(c["pool"], c["table"], b, int(L))
+        e = torch.from_numpy(O.gqa_expand_rows(rows, wts["w_uk"], wts["w_uv"], w.n_groups, w.d_c,
+                                               w.d_nope, w.d_v)).to(torch.bfloat16)
+        rows_of.append(e.double().numpy())
+        g[torch.from_numpy(O.seq_slots(c["table"], b, int(L), bs))] = e.double()
+    g = g.to(torch.bfloat16).view(c["nb"], bs, gw)
+    note(f"gqa decode s_q={s_q} n_split={n_split} bs={bs} generic={generic}")
+    out = torch.empty(c["w"].batch, s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=DEV)
+    lse = torch.empty(c["w"].batch, s_q, w.n_heads, dtype=torch.float32, device=DEV)
+    M.gqla_decode(d, dev(q["q_nope"]), dev(q["q_pe"]), dev(qpos), dev(g), dev(c["table"]),
+                  dev(c["lens"]), out, lse, n_split=n_split)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu().double().numpy()
+    for b in range(len(c["lens"])):
+        ref, ref_lse = O.decode_gqa(q["q_nope"][b], q["q_pe"][b], qpos[b], rows_of[b], w.n_groups,
+                                    w.d_v, BASE)
+        assert rel_err(out[b], ref) <= TOL["bf16"]
+        assert np.max(np.abs(lse[b] - ref_lse)) <= TOL["bf16"]
