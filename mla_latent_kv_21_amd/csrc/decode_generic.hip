@@ -9,6 +9,7 @@
 // merged latent through the head's group of W_UV once.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mfma_util.hpp"
 
 namespace mla {
 namespace {
@@ -340,6 +341,277 @@ __global__ __launch_bounds__(kMergeThreads, 4) void merge_kernel(GenericArgs a,
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Merge (+ W_UV) for bf16 partials, one workgroup per (head h, block of 32 query rows):
+//  * latent path (PW = d_c = 512, D_v = 128): the head's W_UV slice (512 x 128, 128 KiB) is
+//    read once for the block's rows instead of once per row, and the projection runs on
+//    matrix cores: out^T [128 x 32 rows] = W_UV^T · o_lat^T with v_mfma_f32_32x32x16_bf16,
+//    W_UV staged in LDS 256 rows at a time and read with transposing reads, o_lat (bf16 in
+//    LDS) read row-wise; wave w < 4 owns output columns 32 w .. 32 w + 31;
+//  * GQA path (PW = D_v = 128, no W_UV): the merged rows are the output.
+// The partial chunks are requested first, then the splits' lse values, then the W_UV slice.
+// Per row the weights 2^(lse_k - max) / sum go to LDS (one wave per row); the merged row is
+// o = sum_k w_k o_k. Splits the matrix-core decode flagged are recomputed exactly first
+// (split_head), as in merge_kernel.
+constexpr int kPjRows = 32, kPjThreads = 512;
+constexpr int kPjDv = 128;
+constexpr int kPjORow = 512 * 2 + 16;         // o_lat row in LDS: 1,040 B (rows spread banks)
+constexpr int kPjWRow = kPjDv * 2 + 64;       // W_UV row in LDS: 320 B (transposing reads spread)
+constexpr int kPjWHalf = 256 * kPjWRow;       // 256 W_UV rows staged at a time (80 KiB)
+constexpr int kPjWLoads = 512 * kPjDv * 2 / 16 / kPjThreads;  // 16-byte W loads per thread (16)
+
+template <int PW, bool kProj>
+__global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a,
+                                                                const int* __restrict__ redo,
+                                                                const uint16_t* __restrict__ w_uv,
+                                                                uint16_t* __restrict__ out,
+                                                                float* lse_out) {
+  typedef mfma::bf16x8 bf16x8;
+  typedef mfma::f32x16 f32x16;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  static_assert(!kProj || PW == 512, "the projection takes 512-wide latent rows");
+  constexpr int kPjL = kProj ? 16 : 32;  // partial chunks in flight per thread
+  __shared__ __attribute__((aligned(16))) char wbuf[kProj ? kPjWHalf : 16384];  // W half; scratch
+  __shared__ __attribute__((aligned(16))) char obuf[kProj ? kPjRows * kPjORow : 16];
+  __shared__ float wts[kPjRows][MLA_MAX_SPLIT];
+  __shared__ float red[16];
+  __shared__ int n_redo;
+  __shared__ int redo_list[256];
+  const int n_split = a.n_split, H = a.H;
+  const int h = blockIdx.x, m0 = blockIdx.y * kPjRows;
+  const int nrv = min(kPjRows, a.n_rows / H - m0);  // query rows of this block
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  auto prow = [&](int r, int k) {
+    return static_cast<int64_t>(k) * a.n_rows + static_cast<int64_t>(m0 + r) * H + h;
+  };
+
+  // ---- splits flagged for exact recomputation (rare)
+  if (tid == 0) n_redo = 0;
+  __syncthreads();
+  if (redo != nullptr) {
+    for (int e = tid; e < nrv * n_split; e += kPjThreads) {
+      const int r = e / n_split, k = e - r * n_split;
+      if (redo[static_cast<int64_t>(m0 + r) * n_split + k] != 0) {
+        const int slot = atomicAdd(&n_redo, 1);
+        if (slot < 256) redo_list[slot] = e;
+      }
+    }
+  }
+  __syncthreads();
+  if constexpr (kProj) {
+    const int nr = n_redo;
+    for (int qr = 0; qr < nr; ++qr) {
+      int e = -1;
+      if (qr < 256) {
+        e = redo_list[qr];
+      } else {  // more than 256 flags in this block: rescan for the qr-th one
+        int seen = 0;
+        for (int f = 0; f < nrv * n_split && e < 0; ++f) {
+          const int r = f / n_split, k = f - r * n_split;
+          if (redo[static_cast<int64_t>(m0 + r) * n_split + k] != 0 && seen++ == qr) e = f;
+        }
+      }
+      const int r = e / n_split, k = e - r * n_split;
+      float* qs = reinterpret_cast<float*>(wbuf);
+      float* ro = qs + a.q_w;
+      float* ps = ro + a.part_w;
+      int64_t* sl = reinterpret_cast<int64_t*>(ps + kTok);
+      const int mm = m0 + r;
+      split_head<bf16, false>(a, mm / a.s_q, mm % a.s_q, k, h, qs, ro, ps, sl, red);
+    }
+    __syncthreads();
+  }
+
+  // ---- this thread's partial chunks, requested before the weights are known. A pair is
+  //      (row, 8-column chunk). With few pairs (nq > 1), thread (pair, class q) takes splits
+  //      q, q + nq, ...; with few splits (at most 8), a thread takes up to kPjL / 8 pairs
+  //      t + 512 j and all their splits at once; otherwise pairs t + 512 j one after another.
+  const int n_pairs = nrv * (PW / 8);
+  const int nq = n_pairs >= kPjThreads ? 1 : kPjThreads / n_pairs;
+  const bool wide = nq == 1 && n_split <= 8 && n_pairs <= (kPjL / 8) * kPjThreads;
+  // byte offsets into the partial rows fit 32 bits (checked at launch): one uniform base
+  const char* P = static_cast<const char*>(a.part_o);
+  const uint32_t kstride_b = static_cast<uint32_t>(a.n_rows) * PW * 2;
+  u32x4 v[kPjL];
+  auto load_part = [&](int pr, int k) __attribute__((always_inline)) {
+    const int r = pr / (PW / 8), c8 = pr - r * (PW / 8);
+    const uint32_t off = static_cast<uint32_t>(k) * kstride_b +
+                         static_cast<uint32_t>((m0 + r) * H + h) * (PW * 2) + 16u * c8;
+    return *reinterpret_cast<const u32x4*>(P + off);
+  };
+  const int q = nq == 1 ? 0 : tid / n_pairs;
+  int pair = nq == 1 ? tid : tid % n_pairs;
+  bool live = nq == 1 ? pair < n_pairs : tid < n_pairs * nq;
+  int kb = q;
+  // one batch: kPjL splits kb + nq u of `pair`, or (wide) splits u % 8 of pairs pair + 512 (u / 8)
+  auto issue = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kPjL; ++u) {
+      const int pr = wide ? pair + kPjThreads * (u / 8) : pair;
+      const int k = wide ? u % 8 : kb + u * nq;
+      // past the end: some valid (finite) chunk, which gets weight 0
+      v[u] = load_part(min(pr, n_pairs - 1), min(k, n_split - 1));
+    }
+  };
+  if (live) issue();
+
+  // ---- weights of each row's splits (wave w: rows w, w + 8, ...)
+  for (int r = w; r < nrv; r += kPjThreads / 64) {
+    float lk[MLA_MAX_SPLIT / 64];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < MLA_MAX_SPLIT / 64; ++j) {
+      const int k = lane + 64 * j;
+      lk[j] = k < n_split ? a.part_lse[prow(r, k)] : -INFINITY;
+      mx = fmaxf(mx, lk[j]);
+    }
+    mx = wave_max(mx);
+    float ek[MLA_MAX_SPLIT / 64], sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < MLA_MAX_SPLIT / 64; ++j) {
+      ek[j] = (lane + 64 * j < n_split && mx != -INFINITY) ? exp2f(lk[j] - mx) : 0.f;
+      sum += ek[j];
+    }
+    sum = wave_sum(sum);
+    const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+#pragma unroll
+    for (int j = 0; j < MLA_MAX_SPLIT / 64; ++j)
+      if (lane + 64 * j < n_split) wts[r][lane + 64 * j] = ek[j] * inv;
+    if (lane == 0 && lse_out != nullptr)
+      lse_out[static_cast<int64_t>(m0 + r) * H + h] =
+          (mx == -INFINITY) ? -INFINITY : (mx + log2f(sum)) * kLn2;
+  }
+
+  // ---- W_UV[:, g D_v .. g D_v + 127], first 256 rows, into registers: thread t holds rows
+  //      t / 16 + 32 u, columns 8 (t % 16) .. +7 (the other half is requested after the merge)
+  u32x4 wr[kProj ? kPjWLoads / 2 : 1];
+  const uint16_t* wsrc = nullptr;
+  int64_t ldw = 0;
+  if constexpr (kProj) {
+    const int g = h / (H / a.G);
+    ldw = static_cast<int64_t>(a.G) * kPjDv;
+    wsrc = w_uv + static_cast<int64_t>(g) * kPjDv + 8 * (tid & 15) + (tid >> 4) * ldw;
+#pragma unroll
+    for (int u = 0; u < kPjWLoads / 2; ++u) wr[u] = *reinterpret_cast<const u32x4*>(wsrc + 32 * u * ldw);
+  }
+  __syncthreads();  // weights published
+
+  // ---- merged rows: o = sum_k w_k o_k (a split's weight 0 times its finite row adds 0)
+  float* part_sum = reinterpret_cast<float*>(wbuf);  // [nq][n_pairs][8] when nq > 1
+  auto finish = [&](int pr, const float* acc) __attribute__((always_inline)) {
+    const int r = pr / (PW / 8), c8 = pr - r * (PW / 8);
+    const u32x4 o = {mfma::pack_bf16x2(acc[0], acc[1]), mfma::pack_bf16x2(acc[2], acc[3]),
+                     mfma::pack_bf16x2(acc[4], acc[5]), mfma::pack_bf16x2(acc[6], acc[7])};
+    if constexpr (kProj)
+      *reinterpret_cast<u32x4*>(obuf + r * kPjORow + 16 * c8) = o;
+    else
+      *reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(m0 + r) * H + h) * PW + 8 * c8) = o;
+  };
+  auto fma8 = [&](float* acc, const u32x4& raw, float wk) __attribute__((always_inline)) {
+    float f[8];
+    widen16<bf16>(make_uint4(raw[0], raw[1], raw[2], raw[3]), f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(wk, f[e], acc[e]);
+  };
+  if (wide) {
+#pragma unroll
+    for (int j = 0; j < kPjL / 8; ++j) {
+      const int pr = pair + kPjThreads * j;
+      if (pr < n_pairs) {
+        const int r = pr / (PW / 8);
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) fma8(acc, v[8 * j + u], u < n_split ? wts[r][u] : 0.f);
+        finish(pr, acc);
+      }
+    }
+  } else {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    while (live) {
+      const int r = pair / (PW / 8);
+#pragma unroll
+      for (int u = 0; u < kPjL; ++u) {
+        const int k = kb + u * nq;
+        fma8(acc, v[u], k < n_split ? wts[r][k] : 0.f);
+      }
+      kb += kPjL * nq;
+      if (kb >= n_split) {  // this pair's splits are summed
+        if (nq == 1) {
+          finish(pair, acc);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            part_sum[(static_cast<int64_t>(q) * n_pairs + pair) * 8 + e] = acc[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        kb = q;
+        pair += kPjThreads;
+        live = nq == 1 && pair < n_pairs;
+      }
+      if (live) issue();
+    }
+  }
+  if (nq > 1) {
+    __syncthreads();
+    for (int pr = tid; pr < n_pairs; pr += kPjThreads) {
+      float sum8[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum8[e] = part_sum[pr * 8 + e];
+      for (int qq = 1; qq < nq; ++qq)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum8[e] += part_sum[(qq * n_pairs + pr) * 8 + e];
+      finish(pr, sum8);
+    }
+  }
+  if constexpr (kProj) {
+    // ---- out^T = W_UV^T · o_lat^T, two halves of 256 latent rows
+    const int l32 = lane & 31, hi = lane >> 5, G4 = lane >> 4, s16 = lane & 15;
+    f32x16 pacc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pacc[r] = 0.f;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      __syncthreads();  // o_lat is complete / the previous half is consumed
+#pragma unroll
+      for (int u = 0; u < kPjWLoads / 2; ++u)
+        *reinterpret_cast<u32x4*>(wbuf + ((tid >> 4) + 32 * u) * kPjWRow + 16 * (tid & 15)) = wr[u];
+      __syncthreads();
+      if (half == 0) {  // rows 256 .. 511 arrive while the first half is multiplied
+#pragma unroll
+        for (int u = 0; u < kPjWLoads / 2; ++u)
+          wr[u] = *reinterpret_cast<const u32x4*>(wsrc + (256 + 32 * u) * ldw);
+      }
+      if (w < kPjDv / 32) {
+        // transposing read: 16-lane group G4, source lane 4 kk + j -> W row 16 ks + 8 (G4 / 2)
+        // + kk (+4), columns 32 w + 16 (G4 % 2) + 4 j .. +3
+        const char* wp = wbuf + (8 * (G4 >> 1) + (s16 >> 2)) * kPjWRow +
+                         2 * (32 * w + 16 * (G4 & 1) + 4 * (s16 & 3));
+        const char* op = obuf + l32 * kPjORow + 2 * (256 * half + 8 * hi);
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks) {
+          const bf16x8 wa = mfma::lds_read_tr2(wp + 16 * ks * kPjWRow, wp + (16 * ks + 4) * kPjWRow);
+          const bf16x8 ob = mfma::lds16(op + 32 * ks);
+          pacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wa, ob, pacc, 0, 0, 0);
+        }
+      }
+    }
+    // register r holds output column 32 w + 8 (r / 4) + 4 hi + r % 4 of row m0 + l32
+    if (w < kPjDv / 32 && l32 < nrv) {
+      uint16_t* orow = out + (static_cast<int64_t>(m0 + l32) * H + h) * kPjDv + 32 * w + 4 * hi;
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        *reinterpret_cast<uint2*>(orow + 8 * qd) =
+            make_uint2(mfma::pack_bf16x2(pacc[4 * qd], pacc[4 * qd + 1]),
+                       mfma::pack_bf16x2(pacc[4 * qd + 2], pacc[4 * qd + 3]));
+    }
+  }
+}
+
 template <typename T, bool kGqa>
 hipError_t run_generic(const GenericArgs& a, int batch, hipStream_t s) {
   hipLaunchKernelGGL((decode_generic<T, kGqa>), dim3(a.n_split, a.s_q, batch), dim3(256),
@@ -351,6 +623,20 @@ template <typename T>
 hipError_t run_combine(const GenericArgs& a, const int* redo, int batch, int dv, const void* w_uv,
                        void* out, float* lse, hipStream_t s) {
   const int M = batch * a.s_q;
+  if constexpr (sizeof(T) == 2) {
+    const dim3 grid(a.H, cdiv(M, kPjRows));
+    const bool fits32 = static_cast<uint64_t>(a.n_split) * a.n_rows * a.part_w * 2 < (1ull << 32);
+    if (fits32 && w_uv != nullptr && a.part_w == 512 && dv == kPjDv) {
+      hipLaunchKernelGGL((merge_project_kernel<512, true>), grid, dim3(kPjThreads), 0, s, a, redo,
+                         static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out), lse);
+      return hipGetLastError();
+    }
+    if (fits32 && w_uv == nullptr && redo == nullptr && a.part_w == kPjDv && dv == kPjDv) {
+      hipLaunchKernelGGL((merge_project_kernel<kPjDv, false>), grid, dim3(kPjThreads), 0, s, a,
+                         redo, nullptr, static_cast<uint16_t*>(out), lse);
+      return hipGetLastError();
+    }
+  }
   const size_t lds = redo != nullptr ? split_head_lds(a) : 0;
   hipLaunchKernelGGL(merge_kernel<T>, dim3(a.H, M), dim3(kMergeThreads), lds, s, a, redo,
                      static_cast<const T*>(w_uv), dv, static_cast<T*>(out), lse);
