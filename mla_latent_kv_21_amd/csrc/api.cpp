@@ -123,6 +123,7 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s
   if (check_dims(dims) != MLA_OK || batch < 1 || s_q < 1 || max_blocks < 1 || n_split < 0 ||
       n_split > MLA_MAX_SPLIT)
     return 0;
+  if (n_split == 0 && mla::plan_applies(*dims, batch, s_q)) return mla::planned_workspace_bytes(*dims);
   const int ns = n_split == 0 ? resolve_split(*dims, batch, s_q, max_blocks) : n_split;
   return mla::partials_bytes(batch, s_q, dims->n_heads, ns, dims->d_c, elt_of(*dims));
 }
@@ -147,8 +148,13 @@ mla_status check_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const 
   if (batch == 0) return MLA_OK;
   if (!q_abs || !latent_cache || !block_table || !seq_lens) return MLA_ERR_NULL;
   if (!aligned16(q_abs) || !aligned16(latent_cache)) return MLA_ERR_ALIGN;
-  *ns = n_split == 0 ? resolve_split(*dims, batch, s_q, max_blocks) : n_split;
-  const size_t need = mla::partials_bytes(batch, s_q, dims->n_heads, *ns, dims->d_c, elt_of(*dims));
+  // n_split = 0: the length-balanced plan where it applies (*ns = 0 tells the launchers),
+  // else the uniform count the library picks
+  const bool planned = n_split == 0 && mla::plan_applies(*dims, batch, s_q);
+  *ns = planned ? 0 : n_split == 0 ? resolve_split(*dims, batch, s_q, max_blocks) : n_split;
+  const size_t need = planned ? mla::planned_workspace_bytes(*dims)
+                              : mla::partials_bytes(batch, s_q, dims->n_heads, *ns, dims->d_c,
+                                                    elt_of(*dims));
   if (workspace == nullptr || ws_bytes < need) return MLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MLA_ERR_ALIGN;
   return MLA_OK;

@@ -10,6 +10,7 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma_util.hpp"
+#include "plan.hpp"
 
 namespace mla {
 namespace {
@@ -37,6 +38,9 @@ struct GenericArgs {
   float* part_lse;
   int n_rows;    // batch * s_q * H
   int part_w;    // value width (latent: d_c; GQA: D_v)
+  // Length-balanced plan (in the workspace) or NULL: then split k of row m covers
+  // [k chunk, min((k+1) chunk, lim)) and its partial rows sit at [(first[m] + k) H + h].
+  const SplitPlan* plan;
 };
 
 // One (sequence b, query i, split k, head h) partial: online softmax over the split's positions
@@ -49,9 +53,18 @@ __device__ void split_head(const GenericArgs& a, int b, int i, int k, int h, flo
   const int capacity = a.max_blocks * a.bs;
   const int lim = visible_count(a.lens[b], a.s_q, i, capacity);
   int t0, t1;
-  split_range(lim, a.n_split, k, kSplitAlign, &t0, &t1);
-  const T* cache = static_cast<const T*>(a.cache);
   const int64_t qrow = (static_cast<int64_t>(b) * a.s_q + i) * a.H + h;
+  int64_t pidx;
+  if (a.plan != nullptr) {
+    const int chunk = a.plan->chunk;
+    t0 = min(k * chunk, lim);
+    t1 = min(t0 + chunk, lim);
+    pidx = static_cast<int64_t>(a.plan->first[b * a.s_q + i] + k) * a.H + h;
+  } else {
+    split_range(lim, a.n_split, k, kSplitAlign, &t0, &t1);
+    pidx = static_cast<int64_t>(k) * a.n_rows + qrow;
+  }
+  const T* cache = static_cast<const T*>(a.cache);
   const int g = h / (a.H / a.G);
   // key segments inside a cache row, and the value segment
   int ko1, kl1, ko2, vo;
@@ -110,7 +123,6 @@ __device__ void split_head(const GenericArgs& a, int b, int i, int k, int h, flo
     }
     __syncthreads();
   }
-  const int64_t pidx = static_cast<int64_t>(k) * a.n_rows + qrow;
   const bool any = l > 0.f;
   const float inv = any ? 1.0f / l : 0.f;
   for (int e = threadIdx.x; e < a.part_w; e += blockDim.x)
@@ -377,12 +389,29 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
   __shared__ float red[16];
   __shared__ int n_redo;
   __shared__ int redo_list[256];
-  const int n_split = a.n_split, H = a.H;
+  __shared__ int rfirst[kPjRows + 1];  // planned splits: first slot of each row
+  const int H = a.H;
   const int h = blockIdx.x, m0 = blockIdx.y * kPjRows;
   const int nrv = min(kPjRows, a.n_rows / H - m0);  // query rows of this block
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const SplitPlan* pl = a.plan;
+  if (pl != nullptr && tid <= nrv) rfirst[tid] = pl->first[m0 + tid];
+  __syncthreads();
+  // splits of row r (uniform: n_split; planned: its own count) and the most of any row here
+  auto nk = [&](int r) { return pl != nullptr ? rfirst[r + 1] - rfirst[r] : a.n_split; };
+  int n_split = a.n_split;
+  if (pl != nullptr) {
+    n_split = 0;
+    for (int r = 0; r < nrv; ++r) n_split = max(n_split, nk(r));
+  }
+  // partial row of split k of row r, and its recompute flag
   auto prow = [&](int r, int k) {
+    if (pl != nullptr) return static_cast<int64_t>(min(rfirst[r] + k, kPlanSlots - 1)) * H + h;
     return static_cast<int64_t>(k) * a.n_rows + static_cast<int64_t>(m0 + r) * H + h;
+  };
+  auto flag_at = [&](int r, int k) {
+    return pl != nullptr ? static_cast<int64_t>(rfirst[r] + k)
+                         : static_cast<int64_t>(m0 + r) * a.n_split + k;
   };
 
   // ---- splits flagged for exact recomputation (rare)
@@ -391,7 +420,7 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
   if (redo != nullptr) {
     for (int e = tid; e < nrv * n_split; e += kPjThreads) {
       const int r = e / n_split, k = e - r * n_split;
-      if (redo[static_cast<int64_t>(m0 + r) * n_split + k] != 0) {
+      if (k < nk(r) && redo[flag_at(r, k)] != 0) {
         const int slot = atomicAdd(&n_redo, 1);
         if (slot < 256) redo_list[slot] = e;
       }
@@ -408,7 +437,7 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
         int seen = 0;
         for (int f = 0; f < nrv * n_split && e < 0; ++f) {
           const int r = f / n_split, k = f - r * n_split;
-          if (redo[static_cast<int64_t>(m0 + r) * n_split + k] != 0 && seen++ == qr) e = f;
+          if (k < nk(r) && redo[flag_at(r, k)] != 0 && seen++ == qr) e = f;
         }
       }
       const int r = e / n_split, k = e - r * n_split;
@@ -431,12 +460,10 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
   const bool wide = nq == 1 && n_split <= 8 && n_pairs <= (kPjL / 8) * kPjThreads;
   // byte offsets into the partial rows fit 32 bits (checked at launch): one uniform base
   const char* P = static_cast<const char*>(a.part_o);
-  const uint32_t kstride_b = static_cast<uint32_t>(a.n_rows) * PW * 2;
   u32x4 v[kPjL];
   auto load_part = [&](int pr, int k) __attribute__((always_inline)) {
     const int r = pr / (PW / 8), c8 = pr - r * (PW / 8);
-    const uint32_t off = static_cast<uint32_t>(k) * kstride_b +
-                         static_cast<uint32_t>((m0 + r) * H + h) * (PW * 2) + 16u * c8;
+    const uint32_t off = static_cast<uint32_t>(prow(r, k)) * (PW * 2) + 16u * c8;
     return *reinterpret_cast<const u32x4*>(P + off);
   };
   const int q = nq == 1 ? 0 : tid / n_pairs;
@@ -449,8 +476,9 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
     for (int u = 0; u < kPjL; ++u) {
       const int pr = wide ? pair + kPjThreads * (u / 8) : pair;
       const int k = wide ? u % 8 : kb + u * nq;
-      // past the end: some valid (finite) chunk, which gets weight 0
-      v[u] = load_part(min(pr, n_pairs - 1), min(k, n_split - 1));
+      // past the end: some chunk inside the partials, which gets weight 0
+      const int prc = min(pr, n_pairs - 1);
+      v[u] = load_part(prc, max(min(k, nk(prc / (PW / 8)) - 1), 0));
     }
   };
   if (live) issue();
@@ -462,21 +490,21 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
 #pragma unroll
     for (int j = 0; j < MLA_MAX_SPLIT / 64; ++j) {
       const int k = lane + 64 * j;
-      lk[j] = k < n_split ? a.part_lse[prow(r, k)] : -INFINITY;
+      lk[j] = k < nk(r) ? a.part_lse[prow(r, k)] : -INFINITY;
       mx = fmaxf(mx, lk[j]);
     }
     mx = wave_max(mx);
     float ek[MLA_MAX_SPLIT / 64], sum = 0.f;
 #pragma unroll
     for (int j = 0; j < MLA_MAX_SPLIT / 64; ++j) {
-      ek[j] = (lane + 64 * j < n_split && mx != -INFINITY) ? exp2f(lk[j] - mx) : 0.f;
+      ek[j] = (lane + 64 * j < nk(r) && mx != -INFINITY) ? exp2f(lk[j] - mx) : 0.f;
       sum += ek[j];
     }
     sum = wave_sum(sum);
     const float inv = sum > 0.f ? 1.0f / sum : 0.f;
 #pragma unroll
     for (int j = 0; j < MLA_MAX_SPLIT / 64; ++j)
-      if (lane + 64 * j < n_split) wts[r][lane + 64 * j] = ek[j] * inv;
+      if (lane + 64 * j < n_split) wts[r][lane + 64 * j] = ek[j] * inv;  // 0 past nk(r)
     if (lane == 0 && lse_out != nullptr)
       lse_out[static_cast<int64_t>(m0 + r) * H + h] =
           (mx == -INFINITY) ? -INFINITY : (mx + log2f(sum)) * kLn2;
@@ -507,11 +535,13 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
     else
       *reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(m0 + r) * H + h) * PW + 8 * c8) = o;
   };
+  // a zero weight adds exactly nothing, whatever the chunk holds (a clamped load may read a
+  // slot that was never written)
   auto fma8 = [&](float* acc, const u32x4& raw, float wk) __attribute__((always_inline)) {
     float f[8];
     widen16<bf16>(make_uint4(raw[0], raw[1], raw[2], raw[3]), f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = fmaf(wk, f[e], acc[e]);
+    for (int e = 0; e < 8; ++e) acc[e] += wk != 0.f ? wk * f[e] : 0.f;
   };
   if (wide) {
 #pragma unroll
@@ -625,7 +655,8 @@ hipError_t run_combine(const GenericArgs& a, const int* redo, int batch, int dv,
   const int M = batch * a.s_q;
   if constexpr (sizeof(T) == 2) {
     const dim3 grid(a.H, cdiv(M, kPjRows));
-    const bool fits32 = static_cast<uint64_t>(a.n_split) * a.n_rows * a.part_w * 2 < (1ull << 32);
+    const bool fits32 = a.plan != nullptr ||
+                        static_cast<uint64_t>(a.n_split) * a.n_rows * a.part_w * 2 < (1ull << 32);
     if (fits32 && w_uv != nullptr && a.part_w == 512 && dv == kPjDv) {
       hipLaunchKernelGGL((merge_project_kernel<512, true>), grid, dim3(kPjThreads), 0, s, a, redo,
                          static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out), lse);
@@ -690,14 +721,32 @@ size_t partials_bytes(int batch, int s_q, int heads, int n_split, int width, int
   return o + l + f;
 }
 
+bool plan_applies(const mla_dims& d, int batch, int s_q) {
+  return uses_mfma(d) && d.d_v == kPjDv && batch >= 1 && s_q >= 1 &&
+         static_cast<int64_t>(batch) * s_q <= kPlanMaxRows;
+}
+
+size_t planned_workspace_bytes(const mla_dims& d) {
+  return kPlanBytes + partials_bytes(1, 1, d.n_heads, kPlanSlots, d.d_c, 2);
+}
+
+// n_split == 0 here means the length-balanced plan (the caller checked plan_applies): the
+// plan sits at the start of the workspace, the partials of the kPlanSlots slots after it.
 hipError_t launch_decode_splitk(const mla_dims& d, int batch, int s_q, const void* q_abs,
                                 const void* cache, int num_blocks, const int32_t* table,
                                 int max_blocks, const int32_t* seq_lens, int n_split, void* ws,
                                 hipStream_t s) {
+  if (n_split == 0) {
+    const Partials p = partials_of(static_cast<char*>(ws) + kPlanBytes, 1, 1, d.n_heads,
+                                   kPlanSlots, d.d_c, 2);
+    return launch_decode_mfma(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
+                              seq_lens, kPlanCap, p.o, p.lse, p.redo,
+                              static_cast<SplitPlan*>(ws), s);
+  }
   const Partials p = partials_of(ws, batch, s_q, d.n_heads, n_split, d.d_c, d.dtype == MLA_BF16 ? 2 : 4);
   if (uses_mfma(d))
     return launch_decode_mfma(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
-                              seq_lens, n_split, p.o, p.lse, p.redo, s);
+                              seq_lens, n_split, p.o, p.lse, p.redo, nullptr, s);
   const GenericArgs a = latent_args(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
                                     seq_lens, n_split, p);
   return d.dtype == MLA_BF16 ? run_generic<bf16, false>(a, batch, s)
@@ -708,6 +757,14 @@ hipError_t launch_decode_merge(const mla_dims& d, int batch, int s_q, const void
                                const void* cache, int num_blocks, const int32_t* table,
                                int max_blocks, const int32_t* seq_lens, const void* w_uv,
                                int n_split, void* ws, void* out, float* lse, hipStream_t s) {
+  if (n_split == 0) {  // length-balanced plan, as in launch_decode_splitk
+    const Partials p = partials_of(static_cast<char*>(ws) + kPlanBytes, 1, 1, d.n_heads,
+                                   kPlanSlots, d.d_c, 2);
+    GenericArgs a = latent_args(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
+                                seq_lens, kPlanCap, p);
+    a.plan = static_cast<const SplitPlan*>(ws);
+    return run_combine<bf16>(a, p.redo, batch, d.d_v, w_uv, out, lse, s);
+  }
   const Partials p = partials_of(ws, batch, s_q, d.n_heads, n_split, d.d_c, d.dtype == MLA_BF16 ? 2 : 4);
   const GenericArgs a = latent_args(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
                                     seq_lens, n_split, p);

@@ -30,6 +30,7 @@
 //  * each split writes (O / l as bf16, m + log2 l) partials; the merge kernel combines them.
 #include "common.hpp"
 #include "launch.hpp"
+#include "plan.hpp"
 
 namespace mla {
 namespace {
@@ -149,7 +150,8 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
                         const int32_t* __restrict__ table, const int32_t* __restrict__ lens,
                         int num_blocks, int max_blocks, int bs, int s_q, int n_split,
                         float scale_log2, uint16_t* __restrict__ part_o,
-                        float* __restrict__ part_lse, int* __restrict__ redo) {
+                        float* __restrict__ part_lse, int* __restrict__ redo, int batch,
+                        SplitPlan* __restrict__ plan_out) {
   constexpr int H = NW * 32;
   constexpr int kDB = 16 / NW;                      // 32-column latent blocks per wave
   constexpr int kPV = 2 * kDB * NW;                 // P · V products per tile (32)
@@ -161,16 +163,45 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int k = blockIdx.x, qi = blockIdx.y, b = blockIdx.z;
   const int capacity = max_blocks * bs;
-  const int lim = visible_count(lens[b], s_q, qi, capacity);
-  int t0, t1;
-  split_range(lim, n_split, k, kSplitAlign, &t0, &t1);
-  const int64_t row0 = (static_cast<int64_t>(b) * s_q + qi) * H;  // first (b, qi, h) row
-  const int64_t split_id = (static_cast<int64_t>(b) * s_q + qi) * n_split + k;
-  // partial rows of split k: [k * n_rows + row]; this workgroup's H rows are one block
-  const int64_t n_rows = static_cast<int64_t>(gridDim.z) * s_q * H;
-  const int64_t prow0 = k * n_rows + row0;
+  int k, qi, b, t0, t1;
+  int64_t split_id, prow0;
+  if (plan_out == nullptr) {
+    // uniform split: workgroup (k, qi, b); partial rows of split k at [k * n_rows + row]
+    k = blockIdx.x; qi = blockIdx.y; b = blockIdx.z;
+    const int lim = visible_count(lens[b], s_q, qi, capacity);
+    split_range(lim, n_split, k, kSplitAlign, &t0, &t1);
+    const int64_t m = static_cast<int64_t>(b) * s_q + qi;
+    split_id = m * n_split + k;
+    prow0 = k * (static_cast<int64_t>(batch) * s_q * H) + m * H;
+  } else {
+    // length-balanced plan: workgroup = split slot; partial rows of slot s at [s H + h]
+    SplitPlan* pl = reinterpret_cast<SplitPlan*>(ring[0]);
+    int* red = reinterpret_cast<int*>(ring[1]);
+    make_plan(lens, batch, s_q, capacity, pl, red);
+    const int slot = blockIdx.x;
+    if (slot >= pl->total) return;
+    const int rows = batch * s_q;
+    for (int m = threadIdx.x; m < rows; m += blockDim.x)
+      if (pl->first[m] <= slot && slot < pl->first[m + 1]) red[32] = m;
+    if (slot == 0) {
+      int* dst = reinterpret_cast<int*>(plan_out);
+      const int* src = reinterpret_cast<const int*>(pl);
+      for (int e = threadIdx.x; e < 2 + rows + 1; e += blockDim.x) dst[e] = src[e];
+    }
+    __syncthreads();
+    const int m = __builtin_amdgcn_readfirstlane(red[32]);
+    const int chunk = __builtin_amdgcn_readfirstlane(pl->chunk);
+    b = m / s_q; qi = m - b * s_q;
+    k = slot - __builtin_amdgcn_readfirstlane(pl->first[m]);
+    const int lim = visible_count(lens[b], s_q, qi, capacity);
+    t0 = k * chunk;
+    t1 = min(t0 + chunk, lim);
+    split_id = slot;
+    prow0 = static_cast<int64_t>(slot) * H;
+    __syncthreads();  // the plan is read before the ring takes tiles
+  }
+  const int64_t row0 = (static_cast<int64_t>(b) * s_q + qi) * H;  // first (b, qi, h) query row
 
   if (t0 >= t1) {  // empty split: lse -inf (weight zero in the merge) and a zero partial row
     for (int h = threadIdx.x; h < H; h += blockDim.x) part_lse[prow0 + h] = -INFINITY;
@@ -531,14 +562,15 @@ bool mfma_decode_fits(const mla_dims& d) {
 hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void* q_abs,
                               const void* cache, int num_blocks, const int32_t* table,
                               int max_blocks, const int32_t* seq_lens, int n_split,
-                              void* part_o, float* part_lse, int* redo, hipStream_t s) {
+                              void* part_o, float* part_lse, int* redo, SplitPlan* plan,
+                              hipStream_t s) {
   const float scale_log2 = softmax_scale_of(d) * 1.4426950408889634f;
-  const dim3 grid(n_split, s_q, batch);
+  const dim3 grid = plan != nullptr ? dim3(kPlanSlots) : dim3(n_split, s_q, batch);
 #define MLA_LAUNCH(NW_)                                                                      \
   hipLaunchKernelGGL(decode_mfma_kernel<NW_>, grid, dim3(64 * NW_), 0, s,                     \
                      static_cast<const uint16_t*>(q_abs), static_cast<const uint16_t*>(cache), \
                      table, seq_lens, num_blocks, max_blocks, d.block_size, s_q, n_split,      \
-                     scale_log2, static_cast<uint16_t*>(part_o), part_lse, redo)
+                     scale_log2, static_cast<uint16_t*>(part_o), part_lse, redo, batch, plan)
   switch (d.n_heads) {
     case 128: MLA_LAUNCH(4); break;
     case 64: MLA_LAUNCH(2); break;

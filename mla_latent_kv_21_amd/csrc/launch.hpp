@@ -53,10 +53,18 @@ hipError_t launch_gqa_decode(const mla_dims& d, int batch, int s_q, const void* 
 
 // Whether the MFMA decode kernel handles these dims (bf16, d_c 512, d_r 64, H % 32 == 0).
 bool mfma_decode_fits(const mla_dims& d);
+// With plan != NULL the splits follow the length-balanced plan (plan.hpp), which the kernel
+// computes and stores at *plan; else n_split uniform splits per (sequence, query).
+struct SplitPlan;
 hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void* q_abs,
                               const void* cache, int num_blocks, const int32_t* table,
                               int max_blocks, const int32_t* seq_lens, int n_split,
-                              void* part_o, float* part_lse, int* redo, hipStream_t s);
+                              void* part_o, float* part_lse, int* redo, SplitPlan* plan,
+                              hipStream_t s);
+// Whether n_split = 0 takes the length-balanced plan for these dims and rows, and the
+// workspace of a planned decode (the plan, then partials for every slot).
+bool plan_applies(const mla_dims& d, int batch, int s_q);
+size_t planned_workspace_bytes(const mla_dims& d);
 
 // Whether the MFMA GQA decode kernel handles these dims and query count (bf16, D = D_v = 128,
 // d_r = 64, block size a multiple of 32, (H / G) * s_q <= 64), and its launch: every

@@ -48,8 +48,21 @@ def decode_ws_layout(c, n_split):
     return off_flags, w.batch * w.s_q * n_split
 
 
-def run_decode(c, n_split=0, generic=False, gpu=None):
-    """mla_decode on the GPU; returns (out, lse, recompute flags) on the host."""
+PLAN_SLOTS, PLAN_BYTES = 256, 1024   # the length-balanced plan's slots and workspace reserve
+
+
+def planned_layout(c):
+    """(byte offset, count) of the recompute flags of a planned decode's workspace."""
+    w = c["w"]
+    rows = PLAN_SLOTS * w.n_heads
+    al = lambda x: (x + 255) // 256 * 256
+    return PLAN_BYTES + al(rows * w.d_c * w.elt) + al(rows * 4), PLAN_SLOTS
+
+
+def run_decode(c, n_split=0, generic=False, gpu=None, planned=False, ws_out=None):
+    """mla_decode on the GPU; returns (out, lse, recompute flags) on the host. planned: pass
+    n_split = 0 through, so that the library plans the splits from the lengths (the flags
+    returned are those of the plan's slots)."""
     w = c["w"]
     d = M.dims_of(w, generic=generic)
     g = gpu or {}
@@ -60,12 +73,16 @@ def run_decode(c, n_split=0, generic=False, gpu=None):
     wuv = dev(c["w_uv"])
     out = torch.empty(w.batch, w.s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=DEV)
     lse = torch.empty(w.batch, w.s_q, w.n_heads, dtype=torch.float32, device=DEV)
-    ns = n_split or M.mla_auto_split(d, w.batch, w.s_q, c["table"].shape[1])
-    ws = torch.empty(M.mla_decode_workspace_bytes(d, w.batch, w.s_q, ns, c["table"].shape[1]),
+    ns = 0 if planned else n_split or M.mla_auto_split(d, w.batch, w.s_q, c["table"].shape[1])
+    ws = torch.zeros(M.mla_decode_workspace_bytes(d, w.batch, w.s_q, ns, c["table"].shape[1]),
                      dtype=torch.uint8, device=DEV)
     M.mla_decode(d, q, pool, tab, lens, wuv, out, lse, n_split=ns, workspace=ws)
     torch.cuda.synchronize()
-    off, n = decode_ws_layout(c, ns)
+    if ws_out is not None:
+        ws_out.append(ws.cpu())
+    off, n = planned_layout(c) if planned else decode_ws_layout(c, ns)
+    if off + 4 * n > ws.numel():  # n_split = 0 took the uniform split: no planned flags
+        return out.cpu(), lse.cpu(), np.zeros(0, np.int32)
     flags = ws[off:off + 4 * n].view(torch.int32).cpu().numpy().copy()
     return out.cpu(), lse.cpu(), flags
 

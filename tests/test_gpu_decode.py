@@ -11,7 +11,8 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_cases import TOL, decode_case, note, oracle_decode, pick, rel_err, run_decode
+from gpu_cases import (PLAN_SLOTS, TOL, decode_case, note, oracle_decode, pick, rel_err,
+                       run_decode)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -132,3 +133,85 @@ def test_full_size_sampled(cfg, s_q):
     ref, ref_lse = oracle_decode(c, seqs=seqs, heads=heads)
     assert rel_err(pick(out, seqs, heads), ref) <= TOL["bf16"]
     assert np.max(np.abs(pick(lse, seqs, heads) - ref_lse)) <= TOL["bf16"]
+
+
+# ---- length-balanced split plan (n_split = 0 on the matrix-core path)
+
+def expected_plan(lens, s_q, capacity, slots=PLAN_SLOTS, cap=64, align=64):
+    """The plan's rule on the host: the smallest chunk (a multiple of `align`) for which the
+    rows (b, i) need at most `slots` splits in all and at most `cap` each; row m takes
+    ceil(lim_m / chunk) splits, numbered in row order."""
+    lims = [max(0, min(L - s_q + i + 1, capacity)) for L in lens for i in range(s_q)]
+    up = lambda x: -(-x // align) * align
+    chunk = up(max(-(-sum(lims) // slots), -(-max(lims) // cap), 1))
+    while sum(-(-l // chunk) for l in lims) > slots:
+        chunk += align
+    counts = [-(-l // chunk) for l in lims]
+    return chunk, sum(counts), np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+
+
+PLAN_CASES = [
+    # (name, config, lens, s_q)
+    ("c3-mixed", 3, [64, 33, 2600, 1, 5000, 1024], 1),
+    ("c3-one-long", 3, [8000, 1, 2, 3], 1),
+    ("c2-h32-mixed", 2, [1, 65, 1000, 4096], 1),
+    ("c5-g8-sq4", 5, [4, 257, 1030, 3000], 4),
+    ("c4-h128-long", 4, [20000, 300], 1),
+]
+
+
+@pytest.mark.parametrize("name,cfg,lens,s_q", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
+def test_planned_decode_matches_oracle(name, cfg, lens, s_q):
+    """n_split = 0: the library cuts mixed-length rows into chunks of one size chosen on the
+    device; outputs match the oracle, the stored plan matches the host rule exactly, and no
+    split needed the recompute."""
+    w = W.CONFIGS[cfg]
+    c = decode_case(w, lens, s_q=s_q, extra=40 + cfg)
+    note(f"planned decode {name} lens={lens} s_q={s_q}")
+    wss = []
+    out, lse, flags = run_decode(c, planned=True, ws_out=wss)
+    ref, ref_lse = oracle_decode(c)
+    assert rel_err(out, ref) <= TOL["bf16"]
+    assert np.max(np.abs(lse.double().numpy() - ref_lse)) <= TOL["bf16"]
+    plan = wss[0][:1024].view(torch.int32).numpy()
+    rows = len(lens) * s_q
+    chunk, total, first = expected_plan(c["lens"], s_q, c["table"].shape[1] * w.block_size)
+    assert plan[0] == chunk and plan[1] == total
+    assert np.array_equal(plan[2:2 + rows + 1], first)
+    assert total <= PLAN_SLOTS
+    assert not flags[:total].any()
+
+
+def test_planned_recompute_fallback():
+    """The recompute of a flagged split follows the plan's chunk and slot layout. The plan cuts
+    these rows into 64-position splits; position 1530 lies in the second tile of its split
+    (1472 .. 1535), after the tile that set the split's reference."""
+    w = W.CONFIGS[3]
+    c = decode_case(w, [2048, 300], extra=45, random_table=False, poison=False)
+    chunk, _, _ = expected_plan(c["lens"], 1, c["table"].shape[1] * w.block_size)
+    assert chunk == 64
+    q = c["q_abs"][0, 0].float()
+    c["pool"][1530 // 64, 1530 % 64] = (4.0 * q[5]).to(torch.bfloat16)
+    note("planned decode outgrown reference -> recompute")
+    out, lse, flags = run_decode(c, planned=True)
+    assert flags.any(), "expected the MFMA kernel to flag a split"
+    ref, ref_lse = oracle_decode(c)
+    assert rel_err(out, ref) <= TOL["bf16"]
+    assert np.max(np.abs(lse.double().numpy() - ref_lse)) <= TOL["bf16"]
+
+
+def test_planned_matches_uniform_and_falls_back_past_128_rows():
+    """Planned and uniform splits agree; a batch of more than 128 query rows takes the
+    uniform split even with n_split = 0."""
+    w = W.CONFIGS[3]
+    c = decode_case(w, [3000, 200, 64], extra=46)
+    note("planned vs uniform")
+    out_p, _, _ = run_decode(c, planned=True)
+    out_u, _, _ = run_decode(c, n_split=7)
+    assert rel_err(out_p, out_u.double()) <= TOL["bf16"]
+    lens = (np.arange(130) * 37) % 500 + 1
+    c2 = decode_case(w, lens, extra=47)
+    note("planned request with 130 rows")
+    out, _, _ = run_decode(c2, planned=True)
+    ref, _ = oracle_decode(c2, seqs=[0, 64, 129], heads=[0, 127])
+    assert rel_err(pick(out, [0, 64, 129], [0, 127]), ref) <= TOL["bf16"]
