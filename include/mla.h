@@ -133,8 +133,14 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, int32_t s_q, const 
  *  [batch] (device; s_q <= L_b <= max_blocks*bs expected: a query with no visible position
  *  gets out = 0 and lse = -inf); w_uv [d_c, G*D_v]; out [batch, s_q, H, D_v];
  *  lse fp32 [batch, s_q, H] or NULL.
- *  n_split: 1 .. MLA_MAX_SPLIT, or 0 to let the library pick from batch, s_q and max_blocks.
- *  workspace: mla_decode_workspace_bytes(dims, batch, s_q, n_split, max_blocks) bytes.
+ *  n_split: 1 .. MLA_MAX_SPLIT uniform chunks per (sequence, query), or 0 to let the library
+ *  choose. With 0, bf16 caches on the matrix-core path (d_c 512, d_r 64, D_v 128, block size
+ *  a multiple of 32) with batch * s_q <= 128 take a length-balanced plan made on the device
+ *  from seq_lens: every row is cut into chunks of one common size, the smallest multiple of 64
+ *  for which all rows need at most 256 chunks (at most 64 per row), so rows of mixed lengths
+ *  keep every CU busy; other cases take mla_auto_split(...) uniform chunks.
+ *  workspace: mla_decode_workspace_bytes(dims, batch, s_q, n_split, max_blocks) bytes (for
+ *  n_split = 0 the size of whichever scheme applies).
  */
 size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s_q,
                                   int32_t n_split, int32_t max_blocks);
@@ -193,7 +199,8 @@ mla_status gqla_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const v
                        const int32_t* seq_lens, int32_t n_split, void* workspace,
                        size_t ws_bytes, void* out, float* lse, hipStream_t stream);
 
-/* Split count n_split = 0 resolves to, for these sizes. */
+/* Uniform split count n_split = 0 resolves to for these sizes where the length-balanced plan
+ * of mla_decode does not apply (and the count gqla_decode uses for n_split = 0). */
 int32_t mla_auto_split(const mla_dims* dims, int32_t batch, int32_t s_q, int32_t max_blocks);
 
 /* Static, NUL-terminated description of a status. */
