@@ -372,7 +372,7 @@ constexpr int kPjWRow = kPjDv * 2 + 64;       // W_UV row in LDS: 320 B (transpo
 constexpr int kPjWHalf = 256 * kPjWRow;       // 256 W_UV rows staged at a time (80 KiB)
 constexpr int kPjWLoads = 512 * kPjDv * 2 / 16 / kPjThreads;  // 16-byte W loads per thread (16)
 
-template <int PW, bool kProj>
+template <int PW, bool kProj, bool kPlan>
 __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a,
                                                                 const int* __restrict__ redo,
                                                                 const uint16_t* __restrict__ w_uv,
@@ -394,24 +394,24 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
   const int h = blockIdx.x, m0 = blockIdx.y * kPjRows;
   const int nrv = min(kPjRows, a.n_rows / H - m0);  // query rows of this block
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const SplitPlan* pl = a.plan;
-  if (pl != nullptr && tid <= nrv) rfirst[tid] = pl->first[m0 + tid];
-  __syncthreads();
+  if constexpr (kPlan) {
+    if (tid <= nrv) rfirst[tid] = a.plan->first[m0 + tid];
+    __syncthreads();
+  }
   // splits of row r (uniform: n_split; planned: its own count) and the most of any row here
-  auto nk = [&](int r) { return pl != nullptr ? rfirst[r + 1] - rfirst[r] : a.n_split; };
+  auto nk = [&](int r) { return kPlan ? rfirst[r + 1] - rfirst[r] : a.n_split; };
   int n_split = a.n_split;
-  if (pl != nullptr) {
+  if constexpr (kPlan) {
     n_split = 0;
     for (int r = 0; r < nrv; ++r) n_split = max(n_split, nk(r));
   }
   // partial row of split k of row r, and its recompute flag
   auto prow = [&](int r, int k) {
-    if (pl != nullptr) return static_cast<int64_t>(min(rfirst[r] + k, kPlanSlots - 1)) * H + h;
+    if constexpr (kPlan) return static_cast<int64_t>(min(rfirst[r] + k, kPlanSlots - 1)) * H + h;
     return static_cast<int64_t>(k) * a.n_rows + static_cast<int64_t>(m0 + r) * H + h;
   };
   auto flag_at = [&](int r, int k) {
-    return pl != nullptr ? static_cast<int64_t>(rfirst[r] + k)
-                         : static_cast<int64_t>(m0 + r) * a.n_split + k;
+    return kPlan ? static_cast<int64_t>(rfirst[r] + k) : static_cast<int64_t>(m0 + r) * a.n_split + k;
   };
 
   // ---- splits flagged for exact recomputation (rare)
@@ -526,22 +526,24 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
 
   // ---- merged rows: o = sum_k w_k o_k (a split's weight 0 times its finite row adds 0)
   float* part_sum = reinterpret_cast<float*>(wbuf);  // [nq][n_pairs][8] when nq > 1
+  // a planned row with no split (nothing visible) merges to zero: its chunks were read from a
+  // slot that may never have been written
   auto finish = [&](int pr, const float* acc) __attribute__((always_inline)) {
     const int r = pr / (PW / 8), c8 = pr - r * (PW / 8);
-    const u32x4 o = {mfma::pack_bf16x2(acc[0], acc[1]), mfma::pack_bf16x2(acc[2], acc[3]),
-                     mfma::pack_bf16x2(acc[4], acc[5]), mfma::pack_bf16x2(acc[6], acc[7])};
+    u32x4 o = {mfma::pack_bf16x2(acc[0], acc[1]), mfma::pack_bf16x2(acc[2], acc[3]),
+               mfma::pack_bf16x2(acc[4], acc[5]), mfma::pack_bf16x2(acc[6], acc[7])};
+    if (kPlan && nk(r) == 0) o = u32x4{0u, 0u, 0u, 0u};
     if constexpr (kProj)
       *reinterpret_cast<u32x4*>(obuf + r * kPjORow + 16 * c8) = o;
     else
       *reinterpret_cast<u32x4*>(out + (static_cast<int64_t>(m0 + r) * H + h) * PW + 8 * c8) = o;
   };
-  // a zero weight adds exactly nothing, whatever the chunk holds (a clamped load may read a
-  // slot that was never written)
+  // chunks past a row's splits are other written chunks of the row, with weight 0
   auto fma8 = [&](float* acc, const u32x4& raw, float wk) __attribute__((always_inline)) {
     float f[8];
     widen16<bf16>(make_uint4(raw[0], raw[1], raw[2], raw[3]), f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += wk != 0.f ? wk * f[e] : 0.f;
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(wk, f[e], acc[e]);
   };
   if (wide) {
 #pragma unroll
@@ -658,13 +660,20 @@ hipError_t run_combine(const GenericArgs& a, const int* redo, int batch, int dv,
     const bool fits32 = a.plan != nullptr ||
                         static_cast<uint64_t>(a.n_split) * a.n_rows * a.part_w * 2 < (1ull << 32);
     if (fits32 && w_uv != nullptr && a.part_w == 512 && dv == kPjDv) {
-      hipLaunchKernelGGL((merge_project_kernel<512, true>), grid, dim3(kPjThreads), 0, s, a, redo,
-                         static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out), lse);
+      if (a.plan != nullptr)
+        hipLaunchKernelGGL((merge_project_kernel<512, true, true>), grid, dim3(kPjThreads), 0, s,
+                           a, redo, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out),
+                           lse);
+      else
+        hipLaunchKernelGGL((merge_project_kernel<512, true, false>), grid, dim3(kPjThreads), 0, s,
+                           a, redo, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out),
+                           lse);
       return hipGetLastError();
     }
-    if (fits32 && w_uv == nullptr && redo == nullptr && a.part_w == kPjDv && dv == kPjDv) {
-      hipLaunchKernelGGL((merge_project_kernel<kPjDv, false>), grid, dim3(kPjThreads), 0, s, a,
-                         redo, nullptr, static_cast<uint16_t*>(out), lse);
+    if (fits32 && a.plan == nullptr && w_uv == nullptr && redo == nullptr && a.part_w == kPjDv &&
+        dv == kPjDv) {
+      hipLaunchKernelGGL((merge_project_kernel<kPjDv, false, false>), grid, dim3(kPjThreads), 0,
+                         s, a, redo, nullptr, static_cast<uint16_t*>(out), lse);
       return hipGetLastError();
     }
   }
