@@ -453,11 +453,14 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
 
   // ---- this thread's partial chunks, requested before the weights are known. A pair is
   //      (row, 8-column chunk). With few pairs (nq > 1), thread (pair, class q) takes splits
-  //      q, q + nq, ...; with few splits (at most 8), a thread takes up to kPjL / 8 pairs
-  //      t + 512 j and all their splits at once; otherwise pairs t + 512 j one after another.
+  //      q, q + nq, ...; with few splits (at most 8, rounded up to S = 2^lgS), a thread takes
+  //      its pairs t + 512 j in groups of kPjL / S, all their splits at once; otherwise pairs
+  //      t + 512 j one after another.
   const int n_pairs = nrv * (PW / 8);
   const int nq = n_pairs >= kPjThreads ? 1 : kPjThreads / n_pairs;
-  const bool wide = nq == 1 && n_split <= 8 && n_pairs <= (kPjL / 8) * kPjThreads;
+  const bool wide = nq == 1 && n_split <= 8;
+  const int lgS = n_split <= 1 ? 0 : n_split <= 2 ? 1 : n_split <= 4 ? 2 : 3;
+  int jb = 0;  // wide: first pair group j of the batch
   // byte offsets into the partial rows fit 32 bits (checked at launch): one uniform base
   const char* P = static_cast<const char*>(a.part_o);
   u32x4 v[kPjL];
@@ -470,12 +473,13 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
   int pair = nq == 1 ? tid : tid % n_pairs;
   bool live = nq == 1 ? pair < n_pairs : tid < n_pairs * nq;
   int kb = q;
-  // one batch: kPjL splits kb + nq u of `pair`, or (wide) splits u % 8 of pairs pair + 512 (u / 8)
+  // one batch: kPjL splits kb + nq u of `pair`, or (wide) split u % S of pair
+  // pair + 512 (jb + u / S)
   auto issue = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kPjL; ++u) {
-      const int pr = wide ? pair + kPjThreads * (u / 8) : pair;
-      const int k = wide ? u % 8 : kb + u * nq;
+      const int pr = wide ? pair + kPjThreads * (jb + (u >> lgS)) : pair;
+      const int k = wide ? u & ((1 << lgS) - 1) : kb + u * nq;
       // past the end: some chunk inside the partials, which gets weight 0
       const int prc = min(pr, n_pairs - 1);
       v[u] = load_part(prc, max(min(k, nk(prc / (PW / 8)) - 1), 0));
@@ -483,21 +487,31 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
   };
   if (live) issue();
 
-  // ---- weights of each row's splits (wave w: rows w, w + 8, ...)
-  for (int r = w; r < nrv; r += kPjThreads / 64) {
-    float lk[MLA_MAX_SPLIT / 64];
-    float mx = -INFINITY;
+  // ---- weights of each row's splits (wave w: rows w, w + 8, ...): every lse value of the
+  //      wave's rows is requested before the first reduction waits
+  constexpr int kRowsPerWave = kPjRows / (kPjThreads / 64);  // 4
+  float lk[kRowsPerWave][MLA_MAX_SPLIT / 64];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int r = w + (kPjThreads / 64) * i;
 #pragma unroll
     for (int j = 0; j < MLA_MAX_SPLIT / 64; ++j) {
       const int k = lane + 64 * j;
-      lk[j] = k < nk(r) ? a.part_lse[prow(r, k)] : -INFINITY;
-      mx = fmaxf(mx, lk[j]);
+      lk[i][j] = (r < nrv && k < nk(r)) ? a.part_lse[prow(r, k)] : -INFINITY;
     }
+  }
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int r = w + (kPjThreads / 64) * i;
+    if (r >= nrv) break;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < MLA_MAX_SPLIT / 64; ++j) mx = fmaxf(mx, lk[i][j]);
     mx = wave_max(mx);
     float ek[MLA_MAX_SPLIT / 64], sum = 0.f;
 #pragma unroll
     for (int j = 0; j < MLA_MAX_SPLIT / 64; ++j) {
-      ek[j] = (lane + 64 * j < nk(r) && mx != -INFINITY) ? exp2f(lk[j] - mx) : 0.f;
+      ek[j] = (lane + 64 * j < nk(r) && mx != -INFINITY) ? exp2f(lk[i][j] - mx) : 0.f;
       sum += ek[j];
     }
     sum = wave_sum(sum);
@@ -546,18 +560,24 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
     for (int e = 0; e < 8; ++e) acc[e] = fmaf(wk, f[e], acc[e]);
   };
   if (wide) {
+    while (live) {
+      float acc[8];
 #pragma unroll
-    for (int j = 0; j < kPjL / 8; ++j) {
-      const int pr = pair + kPjThreads * j;
-      if (pr < n_pairs) {
-        const int r = pr / (PW / 8);
-        float acc[8];
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+      for (int u = 0; u < kPjL; ++u) {
+        const int pr = pair + kPjThreads * (jb + (u >> lgS));
+        const int k = u & ((1 << lgS) - 1);
+        if (pr < n_pairs) fma8(acc, v[u], k < n_split ? wts[pr / (PW / 8)][k] : 0.f);
+        if (k == (1 << lgS) - 1) {  // the pair's splits are summed
+          if (pr < n_pairs) finish(pr, acc);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) fma8(acc, v[8 * j + u], u < n_split ? wts[r][u] : 0.f);
-        finish(pr, acc);
+          for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+        }
       }
+      jb += kPjL >> lgS;
+      live = pair + kPjThreads * jb < n_pairs;
+      if (live) issue();
     }
   } else {
     float acc[8];
