@@ -259,3 +259,45 @@ def test_gqa_decode_matches_oracle(s_q, n_split, bs, generic):
                                     w.d_v, BASE)
         assert rel_err(out[b], ref) <= TOL["bf16"]
         assert np.max(np.abs(lse[b] - ref_lse)) <= TOL["bf16"]
+
+
+def test_gqla_full_size_sampled():
+    """The GQLA workload at full size (32 sequences x 32,768 positions, G = 8), in the launch
+    configuration the benchmark times (expansion of the whole cache, GQA decode with 8
+    splits): the expanded rows of sampled positions and the outputs of sampled sequences and
+    heads against the oracle, computed one sequence at a time."""
+    w = W.CONFIGS[5]
+    lens = W.seq_lens(w)
+    c = decode_case(w, lens, extra=25, poison=False)
+    wts = W.weights(c["w"])
+    q = W.queries(c["w"])
+    qpos = W.query_positions(c["w"], c["lens"])
+    d = M.dims_of(c["w"])
+    note(f"gqla full size B={w.batch} L={int(lens[0])}")
+    g = torch.empty(c["nb"], w.block_size, w.n_groups * (w.d_nope + w.d_v) + w.d_r,
+                    dtype=w.torch_dtype, device=DEV)
+    M.gqla_expand(d, dev(c["pool"]), dev(c["table"]), dev(c["lens"]), dev(wts["w_uk"]),
+                  dev(wts["w_uv"]), g)
+    out = torch.empty(w.batch, w.s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=DEV)
+    lse = torch.empty(w.batch, w.s_q, w.n_heads, dtype=torch.float32, device=DEV)
+    M.gqla_decode(d, dev(q["q_nope"]), dev(q["q_pe"]), dev(qpos), g, dev(c["table"]),
+                  dev(c["lens"]), out, lse, n_split=8)
+    torch.cuda.synchronize()
+    out, lse = out.cpu(), lse.cpu().double().numpy()
+    heads = [0, 77, w.n_heads - 1]
+    gflat = g.view(-1, g.shape[-1])
+    for b in (0, w.batch - 1):
+        L = int(c["lens"][b])
+        rows = O.gather_rows(c["pool"], c["table"], b, L)
+        slots = O.seq_slots(c["table"], b, L, w.block_size)
+        pick_pos = np.array([0, 1, 31, 32, 4095, L // 2, L - 1])
+        ref_rows = O.gqa_expand_rows(rows[pick_pos], wts["w_uk"], wts["w_uv"], w.n_groups, w.d_c,
+                                     w.d_nope, w.d_v)
+        got = gflat[torch.from_numpy(slots[pick_pos])].cpu()
+        assert ulp_close(got, ref_rows, w.dtype) or rel_err(got, ref_rows) <= 4e-3
+        # decode of the sampled heads over the GPU-expanded rows (isolates the decode error)
+        exp_rows = O.f64(gflat[torch.from_numpy(slots)].cpu())
+        ref, ref_lse = O.decode_gqa(q["q_nope"][b], q["q_pe"][b], qpos[b], exp_rows, w.n_groups,
+                                    w.d_v, BASE, heads=heads)
+        assert rel_err(out[b][:, heads], ref) <= TOL["bf16"]
+        assert np.max(np.abs(lse[b][:, heads] - ref_lse)) <= TOL["bf16"]
