@@ -10,9 +10,10 @@
 //    (sequence, split) are numbered so that they run on one XCD, where they share k_r in L2;
 //  * 32-position tiles of the group's K_g (256 B), V_g (256 B) and k_r (128 B) per position
 //    (20 KiB, always inside one cache block) stream HBM -> LDS with global_load_lds_dwordx4
-//    into a 4-slot ring, three tiles in flight; the 16-byte chunks of a row are XOR-swizzled
-//    by position so that the score reads and the transposing value reads are bank-conflict
-//    free;
+//    into a 2-slot ring: the next tile is in flight while one is used, and four workgroups
+//    share a CU (more waves issuing copies beat a deeper ring per wave); the 16-byte chunks
+//    of a row are XOR-swizzled by position so that the score reads and the transposing value
+//    reads are bank-conflict free;
 //  * S^T [32 positions x 32 rows] = [K_g | k_r] · Q^T with v_mfma_f32_32x32x16_bf16, the
 //    group's queries held in registers (q_pe rotated once, at the query position);
 //  * online softmax in the log2 domain, with the running maximum raised only when a tile
@@ -37,9 +38,10 @@ constexpr int kKBytes = kTok * kD * 2;             // 8 KiB of K_g rows (256 B e
 constexpr int kVBytes = kTok * kDv * 2;            // 8 KiB of V_g rows (256 B each)
 constexpr int kRBytes = kTok * kDr * 2;            // 4 KiB of k_r rows (128 B each)
 constexpr int kSlotBytes = kKBytes + kVBytes + kRBytes;
-constexpr int kSlots = 4;
+constexpr int kSlots = 2;                          // ring slots (40 KiB: 4 workgroups per CU)
 constexpr int kDmaK = kKBytes / 1024, kDmaV = kVBytes / 1024, kDmaR = kRBytes / 1024;
 constexpr int kDma = kDmaK + kDmaV + kDmaR;        // 1 KiB copies per tile (20)
+static_assert(kSlots >= 2 && kSlots <= 4, "ring depth the waits below cover");
 constexpr int kQSteps = (kD + kDr) / 16;           // score K-steps (12)
 constexpr int kDB = kDv / 32;                      // 32-wide value blocks (4)
 constexpr float kLazy = 8.0f;                      // log2 headroom before the max is raised
@@ -131,9 +133,9 @@ __global__ __launch_bounds__(64) void gqa_mfma_kernel(
       dma16(gbase, row + roff + 16u * (cr ^ swz128(p)), lbase + kKBytes + kVBytes + 1024 * i);
     }
   };
-  issue_tile(0, 0);
-  if (ntiles > 1) issue_tile(1, 1);
-  if (ntiles > 2) issue_tile(2, 2);
+#pragma unroll
+  for (int i = 0; i < kSlots - 1; ++i)
+    if (i < ntiles) issue_tile(i, i);
 
   // queries as the B operand of the scores: lane (n, hi) holds elements 16 ks + 8 hi .. +7 of
   // row n; q_pe is rotated at the query position (pairs (2j, 2j+1))
@@ -215,11 +217,16 @@ __global__ __launch_bounds__(64) void gqa_mfma_kernel(
   }
 
   for (int t = 0; t < ntiles; ++t) {
-    if (t + 2 < ntiles) wait_vm<2 * kDma>();
-    else if (t + 1 < ntiles) wait_vm<kDma>();
-    else wait_vm<0>();
-    if (t + 3 < ntiles) issue_tile(t + 3, (t + 3) & (kSlots - 1));
-    const char* slot = ring[t & (kSlots - 1)];
+    {
+      // tile t has landed when at most the copies of the tiles issued after it are in flight
+      const int later = min(kSlots - 2, ntiles - 1 - t);
+      if (later >= 2) wait_vm<2 * kDma>();
+      else if (later == 1) wait_vm<kDma>();
+      else wait_vm<0>();
+    }
+    // the next tile goes into the slot tile t-1 used
+    if (t + kSlots - 1 < ntiles) issue_tile(t + kSlots - 1, (t + kSlots - 1) % kSlots);
+    const char* slot = ring[t % kSlots];
     const int p0 = t0 + kTok * t;
     const int jb = p0 / bs;
     const int id_blk = table[static_cast<int64_t>(b) * max_blocks + jb];
