@@ -366,6 +366,7 @@ __global__ __launch_bounds__(kMergeThreads, 4) void merge_kernel(GenericArgs a,
 // o = sum_k w_k o_k. Splits the matrix-core decode flagged are recomputed exactly first
 // (split_head), as in merge_kernel.
 constexpr int kPjRows = 32, kPjThreads = 512;
+constexpr int kPjTargetWgs = 256;  // workgroups that fill the chip (one per CU)
 constexpr int kPjDv = 128;
 constexpr int kPjORow = 512 * 2 + 16;         // o_lat row in LDS: 1,040 B (rows spread banks)
 constexpr int kPjWRow = kPjDv * 2 + 64;       // W_UV row in LDS: 320 B (transposing reads spread)
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
                                                                 const int* __restrict__ redo,
                                                                 const uint16_t* __restrict__ w_uv,
                                                                 uint16_t* __restrict__ out,
-                                                                float* lse_out) {
+                                                                float* lse_out, int rpb) {
   typedef mfma::bf16x8 bf16x8;
   typedef mfma::f32x16 f32x16;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -391,8 +392,8 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
   __shared__ int redo_list[256];
   __shared__ int rfirst[kPjRows + 1];  // planned splits: first slot of each row
   const int H = a.H;
-  const int h = blockIdx.x, m0 = blockIdx.y * kPjRows;
-  const int nrv = min(kPjRows, a.n_rows / H - m0);  // query rows of this block
+  const int h = blockIdx.x, m0 = blockIdx.y * rpb;
+  const int nrv = min(rpb, a.n_rows / H - m0);  // query rows of this block (rpb <= kPjRows)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if constexpr (kPlan) {
     if (tid <= nrv) rfirst[tid] = a.plan->first[m0 + tid];
@@ -676,24 +677,29 @@ hipError_t run_combine(const GenericArgs& a, const int* redo, int batch, int dv,
                        void* out, float* lse, hipStream_t s) {
   const int M = batch * a.s_q;
   if constexpr (sizeof(T) == 2) {
-    const dim3 grid(a.H, cdiv(M, kPjRows));
+    // rows per workgroup: kPjRows, or 16 when that leaves CUs idle (the rows then spread over
+    // twice the workgroups, each reading the head's W_UV slice; fewer rows per workgroup
+    // measured slower: the merge of a handful of rows is latency-bound)
+    int rpb = kPjRows;
+    if (static_cast<int64_t>(a.H) * cdiv(M, rpb) < kPjTargetWgs) rpb = 16;
+    const dim3 grid(a.H, cdiv(M, rpb));
     const bool fits32 = a.plan != nullptr ||
                         static_cast<uint64_t>(a.n_split) * a.n_rows * a.part_w * 2 < (1ull << 32);
     if (fits32 && w_uv != nullptr && a.part_w == 512 && dv == kPjDv) {
       if (a.plan != nullptr)
         hipLaunchKernelGGL((merge_project_kernel<512, true, true>), grid, dim3(kPjThreads), 0, s,
                            a, redo, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out),
-                           lse);
+                           lse, rpb);
       else
         hipLaunchKernelGGL((merge_project_kernel<512, true, false>), grid, dim3(kPjThreads), 0, s,
                            a, redo, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out),
-                           lse);
+                           lse, rpb);
       return hipGetLastError();
     }
     if (fits32 && a.plan == nullptr && w_uv == nullptr && redo == nullptr && a.part_w == kPjDv &&
         dv == kPjDv) {
       hipLaunchKernelGGL((merge_project_kernel<kPjDv, false, false>), grid, dim3(kPjThreads), 0,
-                         s, a, redo, nullptr, static_cast<uint16_t*>(out), lse);
+                         s, a, redo, nullptr, static_cast<uint16_t*>(out), lse, rpb);
       return hipGetLastError();
     }
   }
