@@ -373,12 +373,13 @@ constexpr int kPjWRow = kPjDv * 2 + 64;       // W_UV row in LDS: 320 B (transpo
 constexpr int kPjWHalf = 256 * kPjWRow;       // 256 W_UV rows staged at a time (80 KiB)
 constexpr int kPjWLoads = 512 * kPjDv * 2 / 16 / kPjThreads;  // 16-byte W loads per thread (16)
 
-template <int PW, bool kProj, bool kPlan>
+template <int PW, bool kProj, bool kPlan, int kRpb>
 __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a,
                                                                 const int* __restrict__ redo,
                                                                 const uint16_t* __restrict__ w_uv,
                                                                 uint16_t* __restrict__ out,
-                                                                float* lse_out, int rpb) {
+                                                                float* lse_out) {
+  static_assert(kRpb == kPjRows || kRpb == kPjRows / 2, "rows per workgroup");
   typedef mfma::bf16x8 bf16x8;
   typedef mfma::f32x16 f32x16;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -392,8 +393,8 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
   __shared__ int redo_list[256];
   __shared__ int rfirst[kPjRows + 1];  // planned splits: first slot of each row
   const int H = a.H;
-  const int h = blockIdx.x, m0 = blockIdx.y * rpb;
-  const int nrv = min(rpb, a.n_rows / H - m0);  // query rows of this block (rpb <= kPjRows)
+  const int h = blockIdx.x, m0 = blockIdx.y * kRpb;
+  const int nrv = min(kRpb, a.n_rows / H - m0);  // query rows of this block
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if constexpr (kPlan) {
     if (tid <= nrv) rfirst[tid] = a.plan->first[m0 + tid];
@@ -677,29 +678,38 @@ hipError_t run_combine(const GenericArgs& a, const int* redo, int batch, int dv,
                        void* out, float* lse, hipStream_t s) {
   const int M = batch * a.s_q;
   if constexpr (sizeof(T) == 2) {
-    // rows per workgroup: kPjRows, or 16 when that leaves CUs idle (the rows then spread over
-    // twice the workgroups, each reading the head's W_UV slice; fewer rows per workgroup
-    // measured slower: the merge of a handful of rows is latency-bound)
-    int rpb = kPjRows;
-    if (static_cast<int64_t>(a.H) * cdiv(M, rpb) < kPjTargetWgs) rpb = 16;
-    const dim3 grid(a.H, cdiv(M, rpb));
+    // rows per workgroup of the latent merge: kPjRows, or 16 when that leaves CUs idle (the
+    // rows then spread over twice the workgroups, each reading the head's W_UV slice; fewer
+    // rows per workgroup measured slower, the merge of a handful of rows being latency-bound).
+    // A compile-time count: as a run-time one it made the GQA merge twice as slow.
+    const bool proj = w_uv != nullptr;
+    const bool half = proj && static_cast<int64_t>(a.H) * cdiv(M, kPjRows) < kPjTargetWgs &&
+                      cdiv(M, kPjRows / 2) > cdiv(M, kPjRows);
+    const dim3 grid(a.H, cdiv(M, half ? kPjRows / 2 : kPjRows));
     const bool fits32 = a.plan != nullptr ||
                         static_cast<uint64_t>(a.n_split) * a.n_rows * a.part_w * 2 < (1ull << 32);
-    if (fits32 && w_uv != nullptr && a.part_w == 512 && dv == kPjDv) {
-      if (a.plan != nullptr)
-        hipLaunchKernelGGL((merge_project_kernel<512, true, true>), grid, dim3(kPjThreads), 0, s,
-                           a, redo, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out),
-                           lse, rpb);
+    if (fits32 && proj && a.part_w == 512 && dv == kPjDv) {
+      const uint16_t* wp = static_cast<const uint16_t*>(w_uv);
+      uint16_t* op = static_cast<uint16_t*>(out);
+      if (a.plan != nullptr && half)
+        hipLaunchKernelGGL((merge_project_kernel<512, true, true, kPjRows / 2>), grid,
+                           dim3(kPjThreads), 0, s, a, redo, wp, op, lse);
+      else if (a.plan != nullptr)
+        hipLaunchKernelGGL((merge_project_kernel<512, true, true, kPjRows>), grid,
+                           dim3(kPjThreads), 0, s, a, redo, wp, op, lse);
+      else if (half)
+        hipLaunchKernelGGL((merge_project_kernel<512, true, false, kPjRows / 2>), grid,
+                           dim3(kPjThreads), 0, s, a, redo, wp, op, lse);
       else
-        hipLaunchKernelGGL((merge_project_kernel<512, true, false>), grid, dim3(kPjThreads), 0, s,
-                           a, redo, static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out),
-                           lse, rpb);
+        hipLaunchKernelGGL((merge_project_kernel<512, true, false, kPjRows>), grid,
+                           dim3(kPjThreads), 0, s, a, redo, wp, op, lse);
       return hipGetLastError();
     }
-    if (fits32 && a.plan == nullptr && w_uv == nullptr && redo == nullptr && a.part_w == kPjDv &&
+    if (fits32 && a.plan == nullptr && !proj && redo == nullptr && a.part_w == kPjDv &&
         dv == kPjDv) {
-      hipLaunchKernelGGL((merge_project_kernel<kPjDv, false, false>), grid, dim3(kPjThreads), 0,
-                         s, a, redo, nullptr, static_cast<uint16_t*>(out), lse, rpb);
+      hipLaunchKernelGGL((merge_project_kernel<kPjDv, false, false, kPjRows>), grid,
+                         dim3(kPjThreads), 0, s, a, redo, nullptr, static_cast<uint16_t*>(out),
+                         lse);
       return hipGetLastError();
     }
   }
