@@ -31,14 +31,14 @@ def kernel_hash() -> str:
     return hashlib.sha256(open(SPLITK_SRC, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(config: int):
+def measured_traffic(workload: str):
     """HBM bytes per launch of the split-K kernel from committed rocprofv3 counter runs, or
     None when they were taken on different kernel source or another workload."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("kernel_sha256_16") != kernel_hash() or t.get("config") != config:
+    if t.get("kernel_sha256_16") != kernel_hash() or t.get("workload") != workload:
         return None
     return t.get("bytes_per_launch")
 
@@ -106,8 +106,8 @@ def measure_rows(dev, torch):
     g = lambda a: (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
     rows = {}
 
-    def absorbed(cfg):
-        w = W.CONFIGS[cfg]
+    def absorbed(name):
+        w = W.WORKLOADS[name]
         lens = W.seq_lens(w)
         table, nb = W.block_table(w, lens)
         d = M.dims_of(w)
@@ -128,8 +128,8 @@ def measure_rows(dev, torch):
                 "frac_hbm": gbs / HBM_PEAK_GBS, "n_split": "planned"}, (w, lens, table, nb, cache, tab,
                                                                   lens_d, wts)
 
-    rows["absorbed_dsv3_paged"], _ = absorbed(3)
-    rows["absorbed_gqla_g8"], ctx = absorbed(5)
+    rows["absorbed_dsv3_paged"], _ = absorbed("dsv3-paged")
+    rows["absorbed_gqla_g8"], ctx = absorbed("gqla-g8")
     w, lens, table, nb, cache, tab, lens_d, wts = ctx
     d = M.dims_of(w)
     gqa = torch.empty(nb, w.block_size, w.n_groups * (w.d_nope + w.d_v) + w.d_r,
@@ -163,8 +163,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=4,
-                    help="workload index (default 4: H=128, d_c=512, 4 x 131,072 context)")
+    ap.add_argument("--workload", default="long-128k",
+                    help="workload name (default long-128k: H=128, d_c=512, 4 x 131,072 context)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
@@ -188,7 +188,7 @@ def main():
         from mla_latent_kv_21_amd.build import build
         build()
     dev = torch.device("cuda:0")
-    w = W.CONFIGS[args.config]
+    w = W.WORKLOADS[args.workload]
     lens = W.seq_lens(w)
     table, nb = W.block_table(w, lens)
     B, s_q, H = w.batch, w.s_q, w.n_heads
@@ -251,7 +251,7 @@ def main():
     tr = A.decode_traffic(lens, s_q, H, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt)
     core_bytes = tr["core_bytes"]
     achieved = core_bytes / (core_ms * 1e-3) / 1e9
-    traffic = measured_traffic(args.config)
+    traffic = measured_traffic(w.name)
     tokens_per_s = B * s_q / (ms_step * 1e-3)
     rec = {
         "metric": "MLA decode tokens/s, latent-cache GB/s & % roofline (H=128, d_c=512)",

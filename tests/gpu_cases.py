@@ -15,6 +15,11 @@ def note(msg: str):
     print(f"[case] {msg}", flush=True)
 
 
+def stream_tag(w) -> int:
+    """A small per-workload number that keeps the case generators' random streams apart."""
+    return w.seed % 100
+
+
 def rel_err(y, ref) -> float:
     """Normwise error max|y - ref| / max|ref| over a whole tensor."""
     y, ref = O.f64(y), O.f64(ref)

@@ -12,30 +12,30 @@ import torch
 
 import workloads as W
 from gpu_cases import (PLAN_SLOTS, TOL, decode_case, note, oracle_decode, pick, rel_err,
-                       run_decode)
+                       run_decode, stream_tag)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 CASES = [
-    # (name, config, lens, s_q, n_split)
-    ("c1-f32", 1, [512], 1, 0),
-    ("c1-f32-ragged", 1, [1, 77, 300], 1, 3),
-    ("c2-h32", 2, [1, 65, 1000], 1, 0),
-    ("c2-h32-split7", 2, [700, 2049], 1, 7),
-    ("c3-h128-ragged", 3, [64, 33, 2600], 1, 0),
-    ("c3-h128-split1", 3, [1500], 1, 1),
-    ("c4-h128-many-splits", 4, [4096, 100], 1, 64),
-    ("c5-g8-sq2", 5, [2, 300], 2, 0),
-    ("c5-g8-sq4", 5, [4, 257, 1030], 4, 5),
+    # (name, workload, lens, s_q, n_split)
+    ("smallem-f32", "smallem-fp32", [512], 1, 0),
+    ("smallem-f32-ragged", "smallem-fp32", [1, 77, 300], 1, 3),
+    ("mid-h32", "mid-bf16", [1, 65, 1000], 1, 0),
+    ("mid-h32-split7", "mid-bf16", [700, 2049], 1, 7),
+    ("paged-h128-ragged", "dsv3-paged", [64, 33, 2600], 1, 0),
+    ("paged-h128-split1", "dsv3-paged", [1500], 1, 1),
+    ("long-h128-many-splits", "long-128k", [4096, 100], 1, 64),
+    ("gqla-g8-sq2", "gqla-g8", [2, 300], 2, 0),
+    ("gqla-g8-sq4", "gqla-g8", [4, 257, 1030], 4, 5),
 ]
 
 
-@pytest.mark.parametrize("name,cfg,lens,s_q,n_split", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("name,wl,lens,s_q,n_split", CASES, ids=[c[0] for c in CASES])
 @pytest.mark.parametrize("generic", [False, True], ids=["mfma", "portable"])
-def test_decode_matches_oracle(name, cfg, lens, s_q, n_split, generic):
-    w = W.CONFIGS[cfg]
-    c = decode_case(w, lens, s_q=s_q, extra=cfg)
+def test_decode_matches_oracle(name, wl, lens, s_q, n_split, generic):
+    w = W.WORKLOADS[wl]
+    c = decode_case(w, lens, s_q=s_q, extra=stream_tag(w))
     note(f"decode {name} generic={generic} lens={lens} s_q={s_q} n_split={n_split}")
     out, lse, flags = run_decode(c, n_split=n_split, generic=generic)
     ref, ref_lse = oracle_decode(c)
@@ -47,7 +47,7 @@ def test_decode_matches_oracle(name, cfg, lens, s_q, n_split, generic):
 
 
 def test_split_count_invariance():
-    w = W.CONFIGS[3]
+    w = W.WORKLOADS["dsv3-paged"]
     c = decode_case(w, [3000, 200], extra=11)
     ref, _ = oracle_decode(c)
     outs = []
@@ -62,7 +62,7 @@ def test_split_count_invariance():
 
 def test_block_permutation_is_bit_exact():
     """Renumbering physical blocks (same logical content) leaves every output bit unchanged."""
-    w = W.CONFIGS[3]
+    w = W.WORKLOADS["dsv3-paged"]
     c = decode_case(w, [1000, 257, 64], extra=12, poison=False)
     note("decode block permutation (original ids)")
     out_a, lse_a, _ = run_decode(c, n_split=5)
@@ -83,7 +83,7 @@ def test_block_permutation_is_bit_exact():
 def test_recompute_fallback_for_outgrown_reference():
     """A late position whose score beats the split's first tile by far more than 2^64 (log2)
     is flagged by the MFMA kernel and recomputed exactly by the portable kernel."""
-    w = W.CONFIGS[3]
+    w = W.WORKLOADS["dsv3-paged"]
     c = decode_case(w, [2048], extra=13, random_table=False, poison=False)
     q = c["q_abs"][0, 0].float()
     # position 1500 of sequence 0 (identity table, block 23, row 28): 4x the query of head 5
@@ -98,10 +98,10 @@ def test_recompute_fallback_for_outgrown_reference():
 
 def test_single_position_and_minimum_lengths():
     """L = 1 (out = that position's value projection) and L = s_q for multi-token steps."""
-    for cfg, lens, s_q in ((3, [1, 1], 1), (5, [4, 4], 4), (2, [2], 2)):
-        w = W.CONFIGS[cfg]
+    for wl, lens, s_q in (("dsv3-paged", [1, 1], 1), ("gqla-g8", [4, 4], 4), ("mid-bf16", [2], 2)):
+        w = W.WORKLOADS[wl]
         c = decode_case(w, lens, s_q=s_q, extra=14)
-        note(f"decode minimum lengths cfg={cfg} lens={lens} s_q={s_q}")
+        note(f"decode minimum lengths {wl} lens={lens} s_q={s_q}")
         out, lse, _ = run_decode(c)
         ref, ref_lse = oracle_decode(c)
         assert rel_err(out, ref) <= TOL[w.dtype]
@@ -109,7 +109,7 @@ def test_single_position_and_minimum_lengths():
 
 def test_unused_table_entries_and_spare_capacity():
     """max_blocks larger than any sequence needs; entries past ceil(L/bs) hold -1."""
-    w = W.CONFIGS[3]
+    w = W.WORKLOADS["dsv3-paged"]
     c = decode_case(w, [130, 64], extra=15, max_blocks=40)
     assert (c["table"][:, 3:] == -1).all()
     note("decode spare table capacity")
@@ -118,14 +118,14 @@ def test_unused_table_entries_and_spare_capacity():
     assert rel_err(out, ref) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("cfg,s_q", [(3, 1), (4, 1), (5, 1), (5, 4)])
-def test_full_size_sampled(cfg, s_q):
+@pytest.mark.parametrize("wl,s_q", [("dsv3-paged", 1), ("long-128k", 1), ("gqla-g8", 1), ("gqla-g8", 4)])
+def test_full_size_sampled(wl, s_q):
     """Full workload shapes, in the launch configuration the benchmark times, checked on a
     sample of sequences and heads that the oracle computes one by one."""
-    w = W.CONFIGS[cfg].replace(s_q=s_q)
+    w = W.WORKLOADS[wl].replace(s_q=s_q)
     lens = W.seq_lens(w)
     c = decode_case(w, lens, s_q=s_q, extra=16, poison=False)
-    note(f"decode full size cfg={cfg} s_q={s_q} B={w.batch} sum(L)={int(lens.sum())}")
+    note(f"decode full size {wl} s_q={s_q} B={w.batch} sum(L)={int(lens.sum())}")
     out, lse, flags = run_decode(c, n_split=w.n_split)
     assert not flags.any()
     seqs = sorted({0, w.batch - 1, int(np.argmax(lens))})
@@ -151,22 +151,22 @@ def expected_plan(lens, s_q, capacity, slots=PLAN_SLOTS, cap=64, align=64):
 
 
 PLAN_CASES = [
-    # (name, config, lens, s_q)
-    ("c3-mixed", 3, [64, 33, 2600, 1, 5000, 1024], 1),
-    ("c3-one-long", 3, [8000, 1, 2, 3], 1),
-    ("c2-h32-mixed", 2, [1, 65, 1000, 4096], 1),
-    ("c5-g8-sq4", 5, [4, 257, 1030, 3000], 4),
-    ("c4-h128-long", 4, [20000, 300], 1),
+    # (name, workload, lens, s_q)
+    ("paged-mixed", "dsv3-paged", [64, 33, 2600, 1, 5000, 1024], 1),
+    ("paged-one-long", "dsv3-paged", [8000, 1, 2, 3], 1),
+    ("mid-h32-mixed", "mid-bf16", [1, 65, 1000, 4096], 1),
+    ("gqla-g8-sq4", "gqla-g8", [4, 257, 1030, 3000], 4),
+    ("long-h128", "long-128k", [20000, 300], 1),
 ]
 
 
-@pytest.mark.parametrize("name,cfg,lens,s_q", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
-def test_planned_decode_matches_oracle(name, cfg, lens, s_q):
+@pytest.mark.parametrize("name,wl,lens,s_q", PLAN_CASES, ids=[c[0] for c in PLAN_CASES])
+def test_planned_decode_matches_oracle(name, wl, lens, s_q):
     """n_split = 0: the library cuts mixed-length rows into chunks of one size chosen on the
     device; outputs match the oracle, the stored plan matches the host rule exactly, and no
     split needed the recompute."""
-    w = W.CONFIGS[cfg]
-    c = decode_case(w, lens, s_q=s_q, extra=40 + cfg)
+    w = W.WORKLOADS[wl]
+    c = decode_case(w, lens, s_q=s_q, extra=40 + stream_tag(w))
     note(f"planned decode {name} lens={lens} s_q={s_q}")
     wss = []
     out, lse, flags = run_decode(c, planned=True, ws_out=wss)
@@ -186,7 +186,7 @@ def test_planned_recompute_fallback():
     """The recompute of a flagged split follows the plan's chunk and slot layout. The plan cuts
     these rows into 64-position splits; position 1530 lies in the second tile of its split
     (1472 .. 1535), after the tile that set the split's reference."""
-    w = W.CONFIGS[3]
+    w = W.WORKLOADS["dsv3-paged"]
     c = decode_case(w, [2048, 300], extra=45, random_table=False, poison=False)
     chunk, _, _ = expected_plan(c["lens"], 1, c["table"].shape[1] * w.block_size)
     assert chunk == 64
@@ -203,7 +203,7 @@ def test_planned_recompute_fallback():
 def test_planned_matches_uniform_and_falls_back_past_128_rows():
     """Planned and uniform splits agree; a batch of more than 128 query rows takes the
     uniform split even with n_split = 0."""
-    w = W.CONFIGS[3]
+    w = W.WORKLOADS["dsv3-paged"]
     c = decode_case(w, [3000, 200, 64], extra=46)
     note("planned vs uniform")
     out_p, _, _ = run_decode(c, planned=True)

@@ -59,11 +59,12 @@ def gpu_append(w, a, chunks=1):
     return cache.cpu()
 
 
-@pytest.mark.parametrize("cfg,lens", [(1, [512]), (2, [40, 130]), (3, [3, 70]), (5, [65])])
-def test_append_matches_oracle(cfg, lens):
-    w = W.CONFIGS[cfg]
+@pytest.mark.parametrize("wl,lens", [("smallem-fp32", [512]), ("mid-bf16", [40, 130]),
+                                     ("dsv3-paged", [3, 70]), ("gqla-g8", [65])])
+def test_append_matches_oracle(wl, lens):
+    w = W.WORKLOADS[wl]
     a = append_case(w, lens)
-    note(f"append cfg={cfg} lens={lens}")
+    note(f"append {wl} lens={lens}")
     cache = gpu_append(w, a)
     ref = O.latent_rows(a["x"], a["wts"]["w_dkv"], a["wts"]["gamma"], a["wts"]["w_kr"], a["pos"],
                         BASE, EPS)
@@ -80,7 +81,7 @@ def test_append_matches_oracle(cfg, lens):
 
 
 def test_chunked_append_is_bit_exact():
-    w = W.CONFIGS[3]
+    w = W.WORKLOADS["dsv3-paged"]
     a = append_case(w, [100, 37])
     note("append bulk vs 3 chunks")
     one = gpu_append(w, a, chunks=1)
@@ -88,29 +89,30 @@ def test_chunked_append_is_bit_exact():
     assert torch.equal(one.view(torch.int16), three.view(torch.int16))
 
 
-@pytest.mark.parametrize("cfg,s_q", [(1, 1), (2, 1), (3, 1), (5, 4)])
-def test_absorb_matches_oracle(cfg, s_q):
-    w = W.CONFIGS[cfg].replace(batch=3, s_q=s_q)
+@pytest.mark.parametrize("wl,s_q", [("smallem-fp32", 1), ("mid-bf16", 1), ("dsv3-paged", 1),
+                                    ("gqla-g8", 4)])
+def test_absorb_matches_oracle(wl, s_q):
+    w = W.WORKLOADS[wl].replace(batch=3, s_q=s_q)
     q = W.queries(w)
     lens = np.array([5000, 17, 131000], np.int32)[:w.batch]
     qpos = W.query_positions(w, lens)
     wts = W.weights(w)
     d = M.dims_of(w)
     out = torch.empty(w.batch, s_q, w.n_heads, w.row, dtype=w.torch_dtype, device=DEV)
-    note(f"absorb cfg={cfg} s_q={s_q}")
+    note(f"absorb {wl} s_q={s_q}")
     M.mla_absorb_q(d, dev(q["q_nope"]), dev(q["q_pe"]), dev(qpos), dev(wts["w_uk"]), out)
     torch.cuda.synchronize()
     ref = O.absorb_query(q["q_nope"], q["q_pe"], qpos, wts["w_uk"], w.n_groups, BASE)
     assert rel_err(out.cpu(), ref) <= (1e-5 if w.dtype == "f32" else 4e-3)
 
 
-@pytest.mark.parametrize("cfg,lens,s_q", [(1, [512], 1), (2, [300, 45], 1), (5, [200], 2),
-                                          (3, [129, 1], 1)])
-def test_end_to_end_matches_reconstructed_oracle(cfg, lens, s_q):
+@pytest.mark.parametrize("wl,lens,s_q", [("smallem-fp32", [512], 1), ("mid-bf16", [300, 45], 1),
+                                         ("gqla-g8", [200], 2), ("dsv3-paged", [129, 1], 1)])
+def test_end_to_end_matches_reconstructed_oracle(wl, lens, s_q):
     """x -> append -> absorb -> decode on the GPU versus keys and values rebuilt explicitly."""
-    w = W.CONFIGS[cfg].replace(batch=len(lens), s_q=s_q)
+    w = W.WORKLOADS[wl].replace(batch=len(lens), s_q=s_q)
     a = append_case(w, lens)
-    note(f"end to end cfg={cfg} lens={lens} s_q={s_q}")
+    note(f"end to end {wl} lens={lens} s_q={s_q}")
     cache = gpu_append(w, a)
     q = W.queries(w)
     qpos = W.query_positions(w, a["lens"])
@@ -141,7 +143,7 @@ def gqa_cache_empty(w, nb):
 
 
 def test_gqla_expand_matches_oracle():
-    w = W.CONFIGS[5]
+    w = W.WORKLOADS["gqla-g8"]
     c = decode_case(w, [70, 129], extra=21)
     wts = W.weights(c["w"])
     start = np.array([0, 64], np.int32)   # second sequence: only positions 64.. are expanded
@@ -167,7 +169,7 @@ def test_gqla_expand_ragged_shapes(dtype):
     a column tile, d_c = 128 spans two latent chunks, and the lengths leave ragged position
     tiles (1, 255, 257 and 600 positions, block size 16); bf16 runs on the matrix cores, fp32 on
     the portable kernel."""
-    w = W.CONFIGS[5].replace(n_groups=3, n_heads=6, d_nope=24, d_v=16, d_c=128, d_r=16,
+    w = W.WORKLOADS["gqla-g8"].replace(n_groups=3, n_heads=6, d_nope=24, d_v=16, d_c=128, d_r=16,
                              block_size=16, dtype=dtype)
     c = decode_case(w, [1, 255, 257, 600], extra=23)
     wts = W.weights(c["w"])
@@ -192,7 +194,7 @@ def test_gqla_expand_ragged_shapes(dtype):
 def test_gqla_paths_agree_with_oracle(s_q):
     """GQA path (expand once, then grouped decode) and absorbed path on the same weights and
     latents: both match the reconstructed oracle and each other."""
-    w = W.CONFIGS[5].replace(s_q=s_q)
+    w = W.WORKLOADS["gqla-g8"].replace(s_q=s_q)
     c = decode_case(w, [s_q, 333, 1100], s_q=s_q, extra=22)
     wts = W.weights(c["w"])
     q = W.queries(c["w"])
@@ -231,7 +233,7 @@ def test_gqa_decode_matches_oracle(s_q, n_split, bs, generic):
     s_q to past several tiles and splits, few and many (mostly empty) splits, up to 64 query
     rows per group (H / G = 8 heads x s_q = 8), block sizes 32 and 64, and the portable
     kernel on the same case."""
-    w = W.CONFIGS[5].replace(n_heads=32, n_groups=4, block_size=bs, s_q=s_q)
+    w = W.WORKLOADS["gqla-g8"].replace(n_heads=32, n_groups=4, block_size=bs, s_q=s_q)
     c = decode_case(w, [s_q, 31 + s_q, 33, 700], s_q=s_q, extra=24)
     wts = W.weights(c["w"])
     q = W.queries(c["w"])
@@ -266,7 +268,7 @@ def test_gqla_full_size_sampled():
     configuration the benchmark times (expansion of the whole cache, GQA decode with 8
     splits): the expanded rows of sampled positions and the outputs of sampled sequences and
     heads against the oracle, computed one sequence at a time."""
-    w = W.CONFIGS[5]
+    w = W.WORKLOADS["gqla-g8"]
     lens = W.seq_lens(w)
     c = decode_case(w, lens, extra=25, poison=False)
     wts = W.weights(c["w"])

@@ -72,22 +72,22 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads of this method, seed 21000 + k for workload k.
-CONFIGS = {
-    1: Workload("smallem-fp32", "f32", batch=1, s_q=1, d_model=512, n_heads=8, d_nope=64,
-                d_v=64, d_c=128, d_r=32, n_groups=8, block_size=64, ctx=512, seed=21001),
-    2: Workload("mid-bf16", "bf16", batch=16, s_q=1, d_model=4096, n_heads=32, d_nope=128,
-                d_v=128, d_c=512, d_r=64, n_groups=32, block_size=64, ctx=4096, seed=21002),
-    3: Workload("dsv3-paged", "bf16", batch=64, s_q=1, d_model=7168, n_heads=128, d_nope=128,
-                d_v=128, d_c=512, d_r=64, n_groups=128, block_size=64, ctx=8192,
-                ctx_min=1024, random_table=True, seed=21003),
-    4: Workload("long-128k", "bf16", batch=4, s_q=1, d_model=7168, n_heads=128, d_nope=128,
-                d_v=128, d_c=512, d_r=64, n_groups=128, block_size=64, ctx=131072,
-                n_split=64, seed=21004),
-    5: Workload("gqla-g8", "bf16", batch=32, s_q=1, d_model=7168, n_heads=128, d_nope=128,
-                d_v=128, d_c=512, d_r=64, n_groups=8, block_size=64, ctx=32768,
-                random_table=True, seed=21005),
-}
+# The five workloads of this method by name, each with its own seed.
+WORKLOADS = {w.name: w for w in (
+    Workload("smallem-fp32", "f32", batch=1, s_q=1, d_model=512, n_heads=8, d_nope=64,
+             d_v=64, d_c=128, d_r=32, n_groups=8, block_size=64, ctx=512, seed=21001),
+    Workload("mid-bf16", "bf16", batch=16, s_q=1, d_model=4096, n_heads=32, d_nope=128,
+             d_v=128, d_c=512, d_r=64, n_groups=32, block_size=64, ctx=4096, seed=21002),
+    Workload("dsv3-paged", "bf16", batch=64, s_q=1, d_model=7168, n_heads=128, d_nope=128,
+             d_v=128, d_c=512, d_r=64, n_groups=128, block_size=64, ctx=8192,
+             ctx_min=1024, random_table=True, seed=21003),
+    Workload("long-128k", "bf16", batch=4, s_q=1, d_model=7168, n_heads=128, d_nope=128,
+             d_v=128, d_c=512, d_r=64, n_groups=128, block_size=64, ctx=131072,
+             n_split=64, seed=21004),
+    Workload("gqla-g8", "bf16", batch=32, s_q=1, d_model=7168, n_heads=128, d_nope=128,
+             d_v=128, d_c=512, d_r=64, n_groups=8, block_size=64, ctx=32768,
+             random_table=True, seed=21005),
+)}
 
 
 def rng(w: Workload, stream: int, extra: int = 0) -> np.random.Generator:
