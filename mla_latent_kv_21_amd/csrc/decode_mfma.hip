@@ -177,24 +177,21 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   } else {
     // length-balanced plan: workgroup = split slot; partial rows of slot s at [s H + h]
     SplitPlan* pl = reinterpret_cast<SplitPlan*>(ring[0]);
-    int* red = reinterpret_cast<int*>(ring[1]);
-    make_plan(lens, batch, s_q, capacity, pl, red);
+    int* row_of = reinterpret_cast<int*>(ring[1]);
     const int slot = blockIdx.x;
+    make_plan(lens, batch, s_q, capacity, slot, pl, row_of);
     if (slot >= pl->total) return;
     const int rows = batch * s_q;
-    for (int m = threadIdx.x; m < rows; m += blockDim.x)
-      if (pl->first[m] <= slot && slot < pl->first[m + 1]) red[32] = m;
     if (slot == 0) {
       int* dst = reinterpret_cast<int*>(plan_out);
       const int* src = reinterpret_cast<const int*>(pl);
       for (int e = threadIdx.x; e < 2 + rows + 1; e += blockDim.x) dst[e] = src[e];
     }
-    __syncthreads();
-    const int m = __builtin_amdgcn_readfirstlane(red[32]);
+    const int m = __builtin_amdgcn_readfirstlane(row_of[0]);
     const int chunk = __builtin_amdgcn_readfirstlane(pl->chunk);
     b = m / s_q; qi = m - b * s_q;
     k = slot - __builtin_amdgcn_readfirstlane(pl->first[m]);
-    const int lim = visible_count(lens[b], s_q, qi, capacity);
+    const int lim = __builtin_amdgcn_readfirstlane(row_of[1]);
     t0 = k * chunk;
     t1 = min(t0 + chunk, lim);
     split_id = slot;

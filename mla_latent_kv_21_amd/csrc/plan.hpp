@@ -9,8 +9,8 @@
 //  * row m = b s_q + i takes splits first[m] .. first[m+1]-1; split slot s covers positions
 //    [k chunk, min((k+1) chunk, lim_m)) of its row, k = s - first[m];
 //  * partials are indexed by slot: row s H + h of the partial rows, flag s of the flags.
-// Every split workgroup computes the same plan from the lengths; slot 0 also stores it in the
-// workspace, where the merge reads it.
+// Every split workgroup computes the same plan from the lengths (one wave, no block-wide
+// reductions); slot 0 also stores it in the workspace, where the merge reads it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -33,92 +33,99 @@ struct SplitPlan {
 };
 static_assert(sizeof(SplitPlan) <= kPlanBytes, "plan fits its workspace reserve");
 
-// Sum and max over the thread block (blockDim.x a multiple of 64, at most 1024); `red` holds
-// 32 ints of LDS.
-__device__ __forceinline__ int64_t plan_block_sum(int64_t v, int* red) {
+// Wave-wide sum and max (64 lanes).
+__device__ __forceinline__ int64_t plan_wave_sum(int64_t v) {
   long long s = v;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) {
-    red[2 * w] = static_cast<int>(s & 0xffffffff);
-    red[2 * w + 1] = static_cast<int>(s >> 32);
-  }
-  __syncthreads();
-  int64_t t = 0;
-  for (int i = 0; i < nw; ++i)
-    t += static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(red[2 * i + 1])) << 32) |
-                              static_cast<uint32_t>(red[2 * i]));
-  return t;
+  return s;
 }
-
-__device__ __forceinline__ int plan_block_max(int v, int* red) {
+__device__ __forceinline__ int plan_wave_sum32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int plan_wave_max(int v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
-  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
-  int t = red[0];
-  for (int i = 1; i < nw; ++i) t = max(t, red[i]);
-  return t;
+  return v;
+}
+// inclusive prefix sum over the wave's lanes
+__device__ __forceinline__ int plan_wave_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
 }
 
-// The plan for `rows` = batch * s_q <= kPlanMaxRows query rows, computed by the whole thread
-// block into *p (LDS); `red` is 32 ints of LDS scratch.
+// The plan for `rows` = batch * s_q <= kPlanMaxRows query rows into *p (LDS), and in row_of[0]
+// the row that split slot `slot` belongs to (-1 past the last split), in row_of[1] that row's
+// visible length. Wave 0 computes it alone
+// (lane l holds rows l and l + 64), with wave-level reductions only; the one barrier at the end
+// publishes it to the whole block, which must call this together.
 __device__ inline void make_plan(const int32_t* __restrict__ lens, int batch, int s_q,
-                                 int capacity, SplitPlan* p, int* red) {
+                                 int capacity, int slot, SplitPlan* p, int* row_of) {
   const int rows = batch * s_q;
-  // row lengths (visible positions) go through p->first as scratch
-  int64_t wsum = 0;
-  int lmax = 0;
-  for (int m = threadIdx.x; m < rows; m += blockDim.x) {
-    const int lim = visible_count(lens[m / s_q], s_q, m % s_q, capacity);
-    p->first[m] = lim;
-    wsum += lim;
-    lmax = max(lmax, lim);
-  }
-  const int64_t W = plan_block_sum(wsum, red);
-  lmax = plan_block_max(lmax, red);
-  const int64_t a = kSplitAlign;
-  auto up = [&](int64_t x) { return (x + a - 1) / a * a; };
-  int64_t lo = up(max(max((W + kPlanSlots - 1) / kPlanSlots, static_cast<int64_t>(lmax + kPlanCap - 1) / kPlanCap),
-                      static_cast<int64_t>(1)));
-  // with chunk >= W / (kPlanSlots - rows), the rows need at most W / chunk + rows <= kPlanSlots
-  int64_t hi = max(lo, up((W + (kPlanSlots - rows) - 1) / (kPlanSlots - rows)));
-  // smallest chunk in [lo, hi] (multiples of kSplitAlign) whose split count fits: the count
-  // never grows with the chunk
-  while (lo < hi) {
-    const int64_t mid = lo + (hi - lo) / (2 * a) * a;
-    int64_t cnt = 0;
-    for (int m = threadIdx.x; m < rows; m += blockDim.x) cnt += (p->first[m] + mid - 1) / mid;
-    if (plan_block_sum(cnt, red) <= kPlanSlots)
-      hi = mid;
-    else
-      lo = mid + a;
-  }
-  const int chunk = static_cast<int>(lo);
-  __syncthreads();
-  // first[] as the exclusive prefix of the per-row split counts, by wave 0 in 64-row pieces
   if (threadIdx.x < 64) {
-    int carry = 0;
-    for (int base = 0; base < rows; base += 64) {
-      const int m = base + static_cast<int>(threadIdx.x);
-      const int n = m < rows ? (p->first[m] + chunk - 1) / chunk : 0;
-      int incl = n;
+    const int lane = threadIdx.x;
+    int lim[2];
+    int64_t wsum = 0;
+    int lmax = 0;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o, 64);
-        if (static_cast<int>(threadIdx.x) >= o) incl += t;
-      }
-      if (m < rows) p->first[m] = carry + incl - n;
-      carry += __shfl(incl, 63, 64);
+    for (int j = 0; j < 2; ++j) {
+      const int m = lane + 64 * j;
+      lim[j] = m < rows ? visible_count(lens[m / s_q], s_q, m % s_q, capacity) : 0;
+      wsum += lim[j];
+      lmax = max(lmax, lim[j]);
     }
-    if (threadIdx.x == 0) {
-      p->first[rows] = carry;
-      p->total = carry;
+    const int64_t W = plan_wave_sum(wsum);
+    lmax = plan_wave_max(lmax);
+    const int64_t a = kSplitAlign;
+    auto up = [&](int64_t x) { return (x + a - 1) / a * a; };
+    int64_t lo = up(max(max((W + kPlanSlots - 1) / kPlanSlots,
+                            static_cast<int64_t>(lmax + kPlanCap - 1) / kPlanCap),
+                        static_cast<int64_t>(1)));
+    // with chunk >= W / (kPlanSlots - rows), the rows need at most W / chunk + rows <= kPlanSlots
+    int64_t hi = max(lo, up((W + (kPlanSlots - rows) - 1) / (kPlanSlots - rows)));
+    // smallest chunk in [lo, hi] (multiples of kSplitAlign) whose split count fits: the count
+    // never grows with the chunk. With rows <= 128, hi is at most the longest row rounded up,
+    // so 32-bit unsigned divisions hold every quotient.
+    while (lo < hi) {
+      const int64_t mid = lo + (hi - lo) / (2 * a) * a;
+      const unsigned um = static_cast<unsigned>(mid);
+      const int c = static_cast<int>((static_cast<unsigned>(lim[0]) + um - 1) / um +
+                                     (static_cast<unsigned>(lim[1]) + um - 1) / um);
+      const int cnt = plan_wave_sum32(c);
+      if (cnt <= kPlanSlots)
+        hi = mid;
+      else
+        lo = mid + a;
+    }
+    const int chunk = static_cast<int>(lo);
+    // first[] as the exclusive prefix of the per-row split counts, rows in order
+    const unsigned uc = static_cast<unsigned>(chunk);
+    const int n0 = static_cast<int>((static_cast<unsigned>(lim[0]) + uc - 1) / uc);
+    const int n1 = static_cast<int>((static_cast<unsigned>(lim[1]) + uc - 1) / uc);
+    const int i0 = plan_wave_scan(n0, lane);
+    const int carry = __shfl(i0, 63, 64);
+    const int i1 = plan_wave_scan(n1, lane);
+    const int total = carry + __shfl(i1, 63, 64);
+    const int f0 = i0 - n0, f1 = carry + i1 - n1;
+    if (lane < rows) p->first[lane] = f0;
+    if (lane + 64 < rows) p->first[lane + 64] = f1;
+    // the row of `slot`: the one whose splits [first, first + n) hold it
+    const bool h0 = lane < rows && f0 <= slot && slot < f0 + n0;
+    const bool h1 = lane + 64 < rows && f1 <= slot && slot < f1 + n1;
+    if (h0) row_of[1] = lim[0];
+    if (h1) row_of[1] = lim[1];
+    const unsigned long long b0 = __ballot(h0), b1 = __ballot(h1);
+    if (lane == 0) {
+      p->first[rows] = total;
+      p->total = total;
       p->chunk = chunk;
+      *row_of = b0 ? __builtin_ctzll(b0) : b1 ? 64 + __builtin_ctzll(b1) : -1;
     }
   }
   __syncthreads();
