@@ -3,11 +3,11 @@
 // section 2, "Chemin GQA": the latent is expanded once, and decode then runs plain GQA with no
 // expansion per step).
 //
-// bf16 caches whose widths are multiples of 8 (d_c of 64) run on the matrix cores
-// (expand_mfma: 256 positions x 256 columns per workgroup). Everything else takes the portable
-// kernel: a tiled product over 64 positions x 64 output columns per workgroup with fp32
-// arithmetic, latents gathered through the block table into LDS. In both, the workgroups of
-// column tile 0 also copy k_r.
+// bf16 caches whose widths are multiples of 8 (d_c of 32) run on the matrix cores
+// (expand_mfma: 128 positions x 256 columns per workgroup, two workgroups per CU). Everything
+// else takes the portable kernel: a tiled product over 64 positions x 64 output columns per
+// workgroup with fp32 arithmetic, latents gathered through the block table into LDS. In both,
+// the workgroups of column tile 0 also copy k_r.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -97,15 +97,9 @@ typedef short __attribute__((ext_vector_type(4))) i16x4;
 typedef __attribute__((address_space(3))) char lds_char_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-constexpr int kXPos = 256;                      // positions per workgroup (128 per wave)
 constexpr int kXCols = 256;                     // expanded columns per workgroup (128 per wave)
-constexpr int kXK = 64;                         // latent rows per LDS chunk (4 K-steps of 16)
-constexpr int kXARow = kXK * 2 + 16;            // staged latent row: 144 B, b128 reads spread
 constexpr int kXWRow = kXCols * 2 + 64;         // staged W row: 576 B, transposing reads spread
-constexpr int kXABytes = kXPos * kXARow;        // 36 KiB of latents per chunk
-constexpr int kXBuf = kXABytes + kXK * kXWRow;  // + 36 KiB of W per chunk
 constexpr int kXORow = 128 * 2 + 16;            // staged output row of a wave: 272 B
-constexpr int kXSlots = 2 * kXBuf;              // cache slots of the tile's positions (int64)
 
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef float __attribute__((ext_vector_type(2))) f32x2_t;
@@ -116,25 +110,38 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
-// bf16 expansion on matrix cores. A workgroup computes 256 positions x 256 expanded columns
-// over the whole latent width, in chunks of 64 latent rows that are staged, double-buffered,
-// in LDS: the gathered latent rows (row-major) and the matching rows of W = [W_UK | W_UV].
-// Wave w owns positions 128 (w % 2) .. +127 and columns 128 (w / 2) .. +127 as 4 x 4 blocks
-// of 32 x 32. Each block is computed transposed, out^T = W^T C^T: the W fragment (matrix A)
-// comes from a transposing LDS read that gives each lane 8 consecutive latent rows of one
-// column, the latent fragment (matrix B) is 16 contiguous bytes of one position's row, and
-// each lane ends up with 4 consecutive columns of one position per register quad, stored as
-// 8 bytes. Workgroups are numbered so that the column tiles of a position tile run on one XCD
-// (blocks are handed to the 8 XCDs in turn), where its latent rows stay in L2; the workgroups
-// of column tile 0 also copy k_r.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// bf16 expansion on matrix cores. A workgroup computes 128 positions x 256 expanded columns
+// over the whole latent width, in chunks of 32 latent rows staged, double-buffered, in LDS:
+// the gathered latent rows and the matching rows of W = [W_UK | W_UV]. Wave w owns positions
+// 64 (w % 2) .. +63 and columns 128 (w / 2) .. +127 as 2 x 4 blocks of 32 x 32: 128
+// accumulators, so two workgroups share a CU and one wave's LDS traffic and waits overlap the
+// other's products on the same SIMD.
+//  * Each block is computed transposed, out^T = W^T C^T: the W fragment (matrix A) comes from
+//    a transposing LDS read that gives each lane 8 consecutive latent rows of one column, the
+//    latent fragment (matrix B) is 16 contiguous bytes of one position's row, and each lane
+//    ends up with 4 consecutive columns of one position per register quad.
+//  * A staged latent row is 64 bytes with its four 16-byte pieces XOR-swizzled by
+//    (row / 4) % 4, so the staging writes (4 rows x 4 pieces per 16 lanes) and the fragment
+//    reads (16 rows x one piece) touch distinct banks; W rows are padded to 576 bytes.
+//  * The global loads of a chunk are issued two chunks ahead into one of two register sets.
+//  * Outputs go through LDS, 32 positions of a wave at a time, as whole 256-byte row pieces.
+//  * Workgroups are numbered so that the column tiles of a position tile run on one XCD
+//    (blocks are handed to the 8 XCDs in turn), where its latent rows stay in L2; the
+//    workgroups of column tile 0 also copy k_r.
+constexpr int kXPos = 128;                       // positions per workgroup
+constexpr int kXK = 32;                          // latent rows per chunk (2 K-steps)
+constexpr int kXARow = kXK * 2;                  // staged latent row: 64 B, pieces swizzled
+constexpr int kXABytes = kXPos * kXARow;         // 8 KiB
+constexpr int kXBuf = kXABytes + kXK * kXWRow;   // + 18 KiB of W
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void expand_mfma(const uint16_t* __restrict__ latent, int num_blocks,
-                 const int32_t* __restrict__ table, int max_blocks, const int32_t* __restrict__ lens,
-                 const int32_t* __restrict__ start_pos, int bs, int d_c, int d_r, int G, int D,
-                 int Dv, const uint16_t* __restrict__ w_uk, const uint16_t* __restrict__ w_uv,
-                 uint16_t* __restrict__ gqa, int ptiles_per_seq, int n_ptiles, int n_ctiles) {
+                  const int32_t* __restrict__ table, int max_blocks,
+                  const int32_t* __restrict__ lens, const int32_t* __restrict__ start_pos,
+                  int bs, int d_c, int d_r, int G, int D, int Dv,
+                  const uint16_t* __restrict__ w_uk, const uint16_t* __restrict__ w_uv,
+                  uint16_t* __restrict__ gqa, int ptiles_per_seq, int n_ptiles, int n_ctiles) {
   __shared__ __attribute__((aligned(16))) char lds[2 * kXBuf + kXPos * 8];
-  static_assert(4 * 128 * kXORow <= 2 * kXBuf, "output staging fits in the chunk buffers");
+  static_assert(4 * 32 * kXORow <= 2 * kXBuf, "half-block output staging fits");
   const int id = blockIdx.x;
   const int j = id >> 3;
   const int ct = j % n_ctiles;
@@ -158,58 +165,56 @@ void expand_mfma(const uint16_t* __restrict__ latent, int num_blocks,
   const int nuk = G * D, nuv = G * Dv, ncol = nuk + nuv;
   const int64_t gw = ncol + d_r;
 
-  // cache slot of each of the tile's positions (-1: not expanded)
-  int64_t* slot_of = reinterpret_cast<int64_t*>(lds + kXSlots);
-  {
+  int64_t* slot_of = reinterpret_cast<int64_t*>(lds + 2 * kXBuf);
+  if (tid < kXPos) {
     const int p = p0 + tid;
     slot_of[tid] = (p >= P0 && p < L) ? cache_slot(table, max_blocks, bs, num_blocks, b, p) : -1;
   }
   __syncthreads();
-  // staging: thread tid moves 16 bytes of latent rows tid / 8 + 32 u and of W rows tid / 32 + 8 u.
-  // Rows of positions that are not expanded, and columns past the end, read some valid row
-  // instead (slot 0, the last 8 columns): their products are never stored.
-  const int c16 = tid & 7;
-  const uint16_t* asrc[8];
+  // staging: thread tid moves 16 bytes of latent rows tid / 4 + 64 u (u < 2) and of W rows
+  // tid / 32 + 8 u (u < 4); rows of positions that are not expanded, and columns past the end,
+  // read some valid row instead (never stored)
+  const int c4 = tid & 3;
+  const uint16_t* asrc[2];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int64_t sl = slot_of[(tid >> 3) + 32 * u];
-    asrc[u] = latent + (sl >= 0 ? sl * row_w : 0) + 8 * c16;
+  for (int u = 0; u < 2; ++u) {
+    const int64_t sl = slot_of[(tid >> 2) + 64 * u];
+    asrc[u] = latent + (sl >= 0 ? sl * row_w : 0) + 8 * c4;
   }
   const int wcol = min(c0 + 8 * (tid & 31), ncol - 8);
   const int64_t wstride = wcol < nuk ? nuk : nuv;
   const uint16_t* wsrc = (wcol < nuk ? w_uk + wcol : w_uv + (wcol - nuk)) + (tid >> 5) * wstride;
-  u32x4_t ra[8], rw[8];
-  auto load_chunk = [&](int kk) __attribute__((always_inline)) {
+  // two chunks in registers ahead of the one being multiplied (sets 0 and 1, alternating)
+  u32x4_t ra[2][2], rw[2][4];
+  auto load_chunk = [&](int kk, u32x4_t (&ra_)[2], u32x4_t (&rw_)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) ra[u] = *reinterpret_cast<const u32x4_t*>(asrc[u] + kk);
+    for (int u = 0; u < 2; ++u) ra_[u] = *reinterpret_cast<const u32x4_t*>(asrc[u] + kk);
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      rw[u] = *reinterpret_cast<const u32x4_t*>(wsrc + (kk + 8 * u) * wstride);
+    for (int u = 0; u < 4; ++u)
+      rw_[u] = *reinterpret_cast<const u32x4_t*>(wsrc + (kk + 8 * u) * wstride);
   };
-  auto store_chunk = [&](char* buf) __attribute__((always_inline)) {
+  auto store_chunk = [&](char* buf, const u32x4_t (&ra_)[2], const u32x4_t (&rw_)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      *reinterpret_cast<u32x4_t*>(buf + ((tid >> 3) + 32 * u) * kXARow + 16 * c16) = ra[u];
+    for (int u = 0; u < 2; ++u) {
+      const int row = (tid >> 2) + 64 * u;
+      *reinterpret_cast<u32x4_t*>(buf + row * kXARow + 16 * (c4 ^ ((row >> 2) & 3))) = ra_[u];
+    }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      *reinterpret_cast<u32x4_t*>(buf + kXABytes + ((tid >> 5) + 8 * u) * kXWRow + 16 * (tid & 31)) = rw[u];
+    for (int u = 0; u < 4; ++u)
+      *reinterpret_cast<u32x4_t*>(buf + kXABytes + ((tid >> 5) + 8 * u) * kXWRow + 16 * (tid & 31)) = rw_[u];
   };
-
-  // fragment addresses: latent row 128 wp + 32 pn + l32 at K offset 8 hi; transposing W read of
-  // 16-lane group G4, source lane 4 k' + j: latent row 8 (G4 / 2) + k' (+4), columns
-  // 128 wc + 16 (G4 % 2) + 4 j .. +3 of the block
   const int wp = w & 1, wc = w >> 1;
   const int G4 = lane >> 4, s16 = lane & 15;
-  const int a_off = (128 * wp + l32) * kXARow + 16 * hi;
+  // row 64 wp + 32 pn + l32 keeps the swizzle of l32: piece (2 ks + hi) ^ ((l32 / 4) % 4)
+  const int a_off = (64 * wp + l32) * kXARow;
+  const int a_piece[2] = {16 * ((0 + hi) ^ ((l32 >> 2) & 3)), 16 * ((2 + hi) ^ ((l32 >> 2) & 3))};
   const int w_off = kXABytes + (8 * (G4 >> 1) + (s16 >> 2)) * kXWRow +
                     2 * (128 * wc + 16 * (G4 & 1) + 4 * (s16 & 3));
-  // the latent fragments first: the first products of a K-step need all four of them and
-  // the first W fragment
-  auto read_frags = [&](const char* buf, int ks, bf16x8 (&wf)[4], bf16x8 (&cf)[4])
+  auto read_frags = [&](const char* buf, int ks, bf16x8 (&wf)[4], bf16x8 (&cf)[2])
       __attribute__((always_inline)) {
 #pragma unroll
-    for (int pn = 0; pn < 4; ++pn)
-      cf[pn] = *reinterpret_cast<const bf16x8*>(buf + a_off + 32 * pn * kXARow + 32 * ks);
+    for (int pn = 0; pn < 2; ++pn)
+      cf[pn] = *reinterpret_cast<const bf16x8*>(buf + a_off + 32 * pn * kXARow + a_piece[ks]);
 #pragma unroll
     for (int cm = 0; cm < 4; ++cm) {
       const char* bp = buf + w_off + 16 * ks * kXWRow + 64 * cm;
@@ -220,81 +225,71 @@ void expand_mfma(const uint16_t* __restrict__ latent, int num_blocks,
     }
   };
 
-  f32x16 acc[16];
+  f32x16 acc[8];
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-  load_chunk(0);
-  for (int kk = 0; kk < d_c; kk += kXK) {
-    // chunk kk goes from registers into buffer (kk / 64) % 2, last read two chunks ago: the
-    // barrier of the previous chunk has seen every wave finish that read. One barrier per chunk.
+  // chunk kk: stored from its register set into buffer (kk / 32) % 2 (last read two chunks
+  // ago, behind the previous chunk's barrier), then the set is refilled with chunk kk + 64 (the
+  // last chunks reload themselves)
+  auto chunk = [&](int kk, u32x4_t (&ra_)[2], u32x4_t (&rw_)[4]) __attribute__((always_inline)) {
     char* cur = lds + ((kk / kXK) & 1) * kXBuf;
-    store_chunk(cur);
+    store_chunk(cur, ra_, rw_);
     __syncthreads();
-    // the next chunk's loads overlap this chunk's products (the last chunk reloads itself)
-    load_chunk(kk + kXK < d_c ? kk + kXK : kk);
-    bf16x8 wf[2][4], cf[2][4];
+    load_chunk(kk + 2 * kXK < d_c ? kk + 2 * kXK : kk, ra_, rw_);
+    bf16x8 wf[2][4], cf[2][2];
     read_frags(cur, 0, wf[0], cf[0]);
+    read_frags(cur, 1, wf[1], cf[1]);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      // fragments of the next K-step are read while this one's 16 products run
-      if (ks < 3) read_frags(cur, ks + 1, wf[(ks + 1) & 1], cf[(ks + 1) & 1]);
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int cm = 0; cm < 4; ++cm)
 #pragma unroll
-        for (int pn = 0; pn < 4; ++pn)
-          acc[4 * cm + pn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks & 1][cm], cf[ks & 1][pn],
-                                                                      acc[4 * cm + pn], 0, 0, 0);
-    }
-    // order after the barrier: the next chunk's global loads, the first K-step's fragments,
-    // then each K-step's products with the next K-step's reads threaded between them
-    __builtin_amdgcn_sched_group_barrier(0x020, 16, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);
-#pragma unroll
-    for (int ks = 0; ks < 3; ++ks) {
-#pragma unroll
-      for (int i = 0; i < 6; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 10, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+        for (int pn = 0; pn < 2; ++pn)
+          acc[2 * cm + pn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks][cm], cf[ks][pn],
+                                                                      acc[2 * cm + pn], 0, 0, 0);
+  };
+  load_chunk(0, ra[0], rw[0]);
+  load_chunk(kXK < d_c ? kXK : 0, ra[1], rw[1]);
+  for (int kk = 0; kk < d_c; kk += 2 * kXK) {
+    chunk(kk, ra[0], rw[0]);
+    if (kk + kXK < d_c) chunk(kk + kXK, ra[1], rw[1]);
   }
 
-  // the accumulators go through LDS so that the stores are whole rows: wave w stages its
-  // 128 x 128 outputs as bf16, position-major; register r of block (cm, pn) holds column
-  // 32 cm + 8 (r / 4) + 4 hi + r % 4 of the wave's columns for position 32 pn + l32
+  // outputs through LDS, 32 positions of each wave at a time, as whole 256-byte row pieces
   __syncthreads();  // every wave is done with the chunk buffers
-  char* stage = lds + w * 128 * kXORow;
+  {
+    char* stage = lds + w * 32 * kXORow;
+    const int seg = lane & 15;
+    const int col = c0 + 128 * wc + 8 * seg;
 #pragma unroll
-  for (int cm = 0; cm < 4; ++cm)
+    for (int pn = 0; pn < 2; ++pn) {
 #pragma unroll
-    for (int pn = 0; pn < 4; ++pn)
+      for (int cm = 0; cm < 4; ++cm)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x16& a = acc[4 * cm + pn];
-        *reinterpret_cast<uint2*>(stage + (32 * pn + l32) * kXORow + 2 * (32 * cm + 8 * g + 4 * hi)) =
-            make_uint2(pack2_bf16(a[4 * g], a[4 * g + 1]), pack2_bf16(a[4 * g + 2], a[4 * g + 3]));
+        for (int g = 0; g < 4; ++g) {
+          const f32x16& a = acc[2 * cm + pn];
+          *reinterpret_cast<uint2*>(stage + l32 * kXORow + 2 * (32 * cm + 8 * g + 4 * hi)) =
+              make_uint2(pack2_bf16(a[4 * g], a[4 * g + 1]), pack2_bf16(a[4 * g + 2], a[4 * g + 3]));
+        }
+      // a wave's LDS accesses complete in order: its rows are in place for its reads
+      if (col < ncol) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int row = 4 * i + (lane >> 4);
+          const int64_t sl = slot_of[64 * wp + 32 * pn + row];
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + row * kXORow + 16 * seg);
+          if (sl >= 0) *reinterpret_cast<u32x4_t*>(gqa + sl * gw + col) = v;
+        }
       }
-  __syncthreads();
-  // 16 lanes per position, 16 bytes each: 4 positions per store
-  const int seg = lane & 15;
-  const int col = c0 + 128 * wc + 8 * seg;
-  if (col < ncol) {
-#pragma unroll 8
-    for (int i = 0; i < 32; ++i) {
-      const int row = 4 * i + (lane >> 4);
-      const int64_t sl = slot_of[128 * wp + row];
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + row * kXORow + 16 * seg);
-      if (sl >= 0) *reinterpret_cast<u32x4_t*>(gqa + sl * gw + col) = v;
     }
   }
   if (ct == 0) {  // k_r of each expanded position, copied as is
+    const int c16 = tid & 7;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < 4; ++u) {
       const int64_t sl = slot_of[(tid >> 3) + 32 * u];
       if (sl < 0) continue;
       for (int q = c16; q < d_r / 8; q += 8)
@@ -303,7 +298,6 @@ void expand_mfma(const uint16_t* __restrict__ latent, int num_blocks,
     }
   }
 }
-
 
 }  // namespace
 
