@@ -354,7 +354,8 @@ __global__ __launch_bounds__(kMergeThreads, 4) void merge_kernel(GenericArgs a,
 }
 
 // ---------------------------------------------------------------------------------------
-// Merge (+ W_UV) for bf16 partials, one workgroup per (head h, block of 32 query rows):
+// Merge (+ W_UV) for bf16 partials, one workgroup per (head h, block of kRpb = 32 or 16 query
+// rows; the launch takes 16 when that gives the chip more workgroups):
 //  * latent path (PW = d_c = 512, D_v = 128): the head's W_UV slice (512 x 128, 128 KiB) is
 //    read once for the block's rows instead of once per row, and the projection runs on
 //    matrix cores: out^T [128 x 32 rows] = W_UV^T · o_lat^T with v_mfma_f32_32x32x16_bf16,
