@@ -160,7 +160,42 @@ def measure_rows(dev, torch):
                            "tokens_per_s": w.batch * w.s_q / (ms * 1e-3),
                            "GBps": tr["bytes"] / (ms * 1e-3) / 1e9,
                            "frac_hbm": tr["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    rows["path_select"] = select_paths(dev, torch, w, lens, table, cache, gqa, tab, lens_d, wts)
     return rows
+
+
+def select_paths(dev, torch, w, lens, table, cache, gqa, tab, lens_d, wts):
+    """Both decode paths of the GQLA workload timed at s_q = 1, 2, 4 (the absorbed one with
+    planned splits, the GQA one with the automatic split count), beside mla_select_path's
+    choice and model times for MI355X: the choice should be the faster measured path."""
+    import workloads as W
+    from mla_latent_kv_21_amd import binding as M
+    g = lambda a: (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
+    res = []
+    for s_q in (1, 2, 4):
+        ws_ = w.replace(s_q=s_q)
+        d = M.dims_of(ws_)
+        q_abs = g(W.absorbed_queries(ws_))
+        out = torch.empty(w.batch, s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=dev)
+        wsa = torch.empty(M.mla_decode_workspace_bytes(d, w.batch, s_q, 0, table.shape[1]),
+                          dtype=torch.uint8, device=dev)
+        ms_abs = _time_calls(lambda: M.mla_decode(d, q_abs, cache, tab, lens_d, wts["w_uv"], out,
+                                                  n_split=0, workspace=wsa), 10, torch)
+        q = {k: g(v) for k, v in W.queries(ws_).items()}
+        qpos = g(W.query_positions(ws_, lens))
+        ns = M.mla_auto_split(d, w.batch, s_q, table.shape[1])
+        wsg = torch.empty(M.gqla_decode_workspace_bytes(d, w.batch, s_q, ns, table.shape[1]),
+                          dtype=torch.uint8, device=dev)
+        ms_gqa = _time_calls(lambda: M.gqla_decode(d, q["q_nope"], q["q_pe"], qpos, gqa, tab,
+                                                   lens_d, out, n_split=ns, workspace=wsg),
+                             5, torch)
+        path, ta, tg = M.mla_select_path(d, s_q, int(np.max(lens)))
+        chosen = "gqa" if path == M.MLA_PATH_GQA else "absorbed"
+        res.append({"s_q": s_q, "absorbed_ms": ms_abs, "gqa_ms": ms_gqa,
+                    "model_absorbed_ms": ta * w.batch * 1e3, "model_gqa_ms": tg * w.batch * 1e3,
+                    "selected": chosen,
+                    "selected_is_faster": (ms_abs <= ms_gqa) == (chosen == "absorbed")})
+    return {"workload": w.name, "call": "mla_select_path", "cases": res}
 
 
 def main():

@@ -203,6 +203,36 @@ mla_status gqla_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const v
  * of mla_decode does not apply (and the count gqla_decode uses for n_split = 0). */
 int32_t mla_auto_split(const mla_dims* dims, int32_t batch, int32_t s_q, int32_t max_blocks);
 
+/*
+ * mla_select_path -- choose the decode path of a GQLA layer for a target device from the
+ * roofline of each path ([GQLA] section 2, "Sélection du chemin": the absorbed MQA path on
+ * hardware whose compute/bandwidth ridge sits above its intensity, the GQA path where the
+ * ridge is low; section 1 gives the ridges, section 4 the projected throughputs this model
+ * reproduces). Per query step of one sequence with `context` cached positions:
+ *     absorbed: bytes = context * (d_c + d_r) * elt
+ *               FLOPs = context * s_q * (2 H (d_c + d_r) + 2 H d_c)
+ *     GQA:      bytes = context * (G (D + D_v) + d_r) * elt
+ *               FLOPs = context * s_q * (2 H (D + d_r) + 2 H D_v)
+ *     time = max(bytes / hbm_bytes_per_s, FLOPs / flops_per_s)
+ *  The path with the smaller time is returned (the absorbed path on a tie). The query,
+ *  output and up-projection work around the attention, and the one-off expansion of the GQA
+ *  cache, are not counted.
+ *  hbm_bytes_per_s, flops_per_s: the target's rates; both 0 selects MI355X as measured here
+ *  (MLA_MI355X_HBM_BYTES_PER_S, MLA_MI355X_BF16_FLOPS). t_absorbed, t_gqa: nullable outputs,
+ *  the two times in seconds. Returns MLA_PATH_ABSORBED or MLA_PATH_GQA; otherwise a negative
+ *  mla_status: the dims checks of the other calls, MLA_ERR_RANGE for s_q < 1, context < 1 or
+ *  rates that are not both positive (or both 0). Host only: launches nothing.
+ */
+typedef enum { MLA_PATH_ABSORBED = 0, MLA_PATH_GQA = 1 } mla_path;
+/* MI355X rates used by default: a stream read by 256 workgroups reaches 6.0e12 B/s; the
+ * bf16 matrix cores' 2.5e15 FLOP/s peak at 2.4 GHz scales to 2.03e15 at the 1.95 GHz the
+ * decode kernels sustain. */
+#define MLA_MI355X_HBM_BYTES_PER_S 6.0e12
+#define MLA_MI355X_BF16_FLOPS 2.03e15
+int32_t mla_select_path(const mla_dims* dims, int32_t s_q, int64_t context,
+                        double hbm_bytes_per_s, double flops_per_s, double* t_absorbed,
+                        double* t_gqa);
+
 /* Static, NUL-terminated description of a status. */
 const char* mla_status_string(mla_status status);
 

@@ -25,7 +25,8 @@ STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTY
 EXPORTS = ["mla_cache_append_workspace_bytes", "mla_cache_append", "mla_absorb_q",
            "mla_decode_workspace_bytes", "mla_decode", "mla_decode_splitk", "mla_decode_merge",
            "gqla_expand",
-           "gqla_decode_workspace_bytes", "gqla_decode", "mla_auto_split", "mla_status_string",
+           "gqla_decode_workspace_bytes", "gqla_decode", "mla_auto_split", "mla_select_path",
+           "mla_status_string",
            "mla_validate_block_table"]
 
 
@@ -82,6 +83,9 @@ def lib() -> ctypes.CDLL:
             "gqla_decode_workspace_bytes": (S, [D, I, I, I, I]),
             "gqla_decode": (I, [D, I, I, P, P, P, P, I, P, I, P, I, P, S, P, P, P]),
             "mla_auto_split": (I, [D, I, I, I]),
+            "mla_select_path": (I, [D, I, ctypes.c_int64, ctypes.c_double, ctypes.c_double,
+                                    ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_double)]),
             "mla_status_string": (ctypes.c_char_p, [I]),
             "mla_validate_block_table": (I, [D, P, I, I, P, I]),
         }
@@ -139,6 +143,19 @@ def mla_absorb_q(dims, q_nope, q_pe, q_pos, w_uk, q_abs):
 
 def mla_auto_split(dims, batch, s_q, max_blocks) -> int:
     return lib().mla_auto_split(ctypes.byref(dims), batch, s_q, max_blocks)
+
+
+MLA_PATH_ABSORBED, MLA_PATH_GQA = 0, 1
+
+
+def mla_select_path(dims, s_q, context, hbm_bytes_per_s=0.0, flops_per_s=0.0):
+    """(path, t_absorbed, t_gqa): the cheaper decode path by the roofline of each, and both
+    times in seconds per query step of one sequence. Rates 0, 0 mean MI355X."""
+    ta, tg = ctypes.c_double(), ctypes.c_double()
+    r = lib().mla_select_path(ctypes.byref(dims), s_q, context, hbm_bytes_per_s, flops_per_s,
+                              ctypes.byref(ta), ctypes.byref(tg))
+    _check(r if r < 0 else 0, "mla_select_path")
+    return r, ta.value, tg.value
 
 
 def mla_decode_workspace_bytes(dims, batch, s_q, n_split, max_blocks) -> int:

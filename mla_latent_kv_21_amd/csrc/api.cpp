@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "launch.hpp"
 #include "mla.h"
 
@@ -69,6 +71,31 @@ const char* mla_status_string(mla_status s) {
 int32_t mla_auto_split(const mla_dims* dims, int32_t batch, int32_t s_q, int32_t max_blocks) {
   if (check_dims(dims) != MLA_OK || batch < 1 || s_q < 1 || max_blocks < 1) return 0;
   return resolve_split(*dims, batch, s_q, max_blocks);
+}
+
+int32_t mla_select_path(const mla_dims* dims, int32_t s_q, int64_t context,
+                        double hbm_bytes_per_s, double flops_per_s, double* t_absorbed,
+                        double* t_gqa) {
+  const mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (s_q < 1 || context < 1) return MLA_ERR_RANGE;
+  if (hbm_bytes_per_s == 0.0 && flops_per_s == 0.0) {
+    hbm_bytes_per_s = MLA_MI355X_HBM_BYTES_PER_S;
+    flops_per_s = MLA_MI355X_BF16_FLOPS;
+  }
+  if (!(hbm_bytes_per_s > 0.0) || !(flops_per_s > 0.0)) return MLA_ERR_RANGE;
+  const mla_dims& d = *dims;
+  const double elt = d.dtype == MLA_BF16 ? 2.0 : 4.0;
+  const double H = d.n_heads, G = d.n_groups, L = static_cast<double>(context), q = s_q;
+  const double abs_bytes = L * (d.d_c + d.d_r) * elt;
+  const double abs_flops = L * q * (2.0 * H * (d.d_c + d.d_r) + 2.0 * H * d.d_c);
+  const double gqa_bytes = L * (G * (d.d_nope + d.d_v) + d.d_r) * elt;
+  const double gqa_flops = L * q * (2.0 * H * (d.d_nope + d.d_r) + 2.0 * H * d.d_v);
+  const double ta = std::max(abs_bytes / hbm_bytes_per_s, abs_flops / flops_per_s);
+  const double tg = std::max(gqa_bytes / hbm_bytes_per_s, gqa_flops / flops_per_s);
+  if (t_absorbed) *t_absorbed = ta;
+  if (t_gqa) *t_gqa = tg;
+  return tg < ta ? MLA_PATH_GQA : MLA_PATH_ABSORBED;
 }
 
 size_t mla_cache_append_workspace_bytes(const mla_dims* dims, int32_t n_tok) {

@@ -1,0 +1,80 @@
+"""mla_select_path (host only, no GPU): its roofline model of the two GQLA decode paths is
+pinned to the throughputs the GQLA summary projects (section 4, "Résultats"), and its choices
+follow the summary's path selection (section 2, "Sélection du chemin")."""
+import json
+import os
+
+import pytest
+
+import workloads as W
+from mla_latent_kv_21_amd import binding as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLD = json.load(open(os.path.join(ROOT, "tests", "golden", "closed_forms.json")))
+P = GOLD["gqla_projections"]
+H100 = (P["assumed_h100_bw"], 989e12)
+H20 = (P["assumed_h20_bw"], P["assumed_h20_flops"])
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    if not os.path.exists(M.LIB_PATH):
+        from mla_latent_kv_21_amd.build import build
+        build()
+    return M.lib()
+
+
+def dims(g, **kw):
+    return M.dims_of(W.WORKLOADS["gqla-g8"].replace(n_groups=g, **kw))
+
+
+def test_model_reproduces_the_projected_throughputs():
+    L, tol = P["assumed_ctx"], P["approx_rel"]
+    _, ta, _ = M.mla_select_path(dims(8), 1, L, *H100)
+    assert abs(1 / ta / P["h100_absorbed"] - 1) < tol
+    _, ta, _ = M.mla_select_path(dims(8), 1, L, *H20)
+    assert abs(1 / ta / P["h20_mla"] - 1) < tol
+    _, _, tg = M.mla_select_path(dims(8), 2, L, *H20)
+    assert abs(2 / tg / P["h20_gqa_g8_sq2"] - 1) < tol
+
+
+def test_choices_follow_the_summary():
+    L = P["assumed_ctx"]
+    # H100: the absorbed path at s_q = 1
+    assert M.mla_select_path(dims(8), 1, L, *H100)[0] == M.MLA_PATH_ABSORBED
+    # H20: the GQA path, g = 8 with s_q = 2 or g = 4 with s_q = 1
+    assert M.mla_select_path(dims(8), 2, L, *H20)[0] == M.MLA_PATH_GQA
+    assert M.mla_select_path(dims(4), 1, L, *H20)[0] == M.MLA_PATH_GQA
+    # MI355X (defaults): absorbed for g = 8 up to s_q = 4, GQA from s_q = 8 on
+    for s_q in (1, 2, 4):
+        assert M.mla_select_path(dims(8), s_q, L)[0] == M.MLA_PATH_ABSORBED
+    assert M.mla_select_path(dims(8), 8, L)[0] == M.MLA_PATH_GQA
+
+
+def test_degenerate_group_counts():
+    L = 4096
+    # G = H: the "GQA" cache holds every head's keys and values, never cheaper
+    for s_q in (1, 4, 16):
+        assert M.mla_select_path(dims(128), s_q, L)[0] == M.MLA_PATH_ABSORBED
+    # G = 1 (MQA): fewer bytes and fewer FLOPs than the absorbed path
+    _, ta, tg = M.mla_select_path(dims(1), 1, L)
+    assert tg < ta
+    assert M.mla_select_path(dims(1), 1, L)[0] == M.MLA_PATH_GQA
+
+
+def test_times_scale_with_context_and_rates():
+    _, a1, g1 = M.mla_select_path(dims(8), 1, 1000, 1e12, 1e15)
+    _, a2, g2 = M.mla_select_path(dims(8), 1, 2000, 1e12, 1e15)
+    assert a2 == pytest.approx(2 * a1) and g2 == pytest.approx(2 * g1)
+    _, a3, _ = M.mla_select_path(dims(8), 1, 1000, 2e12, 2e15)
+    assert a3 == pytest.approx(a1 / 2)
+
+
+def test_invalid_arguments(lib):
+    import ctypes
+    d = dims(8)
+    t = ctypes.c_double()
+    assert lib.mla_select_path(ctypes.byref(d), 1, 0, 0.0, 0.0, None, None) == -4
+    assert lib.mla_select_path(ctypes.byref(d), 0, 10, 0.0, 0.0, None, None) == -4
+    assert lib.mla_select_path(ctypes.byref(d), 1, 10, 1e12, 0.0, None, None) == -4
+    assert lib.mla_select_path(None, 1, 10, 0.0, 0.0, ctypes.byref(t), None) == -1
