@@ -59,14 +59,16 @@ __global__ __launch_bounds__(64) void gqa_mfma_kernel(
     const int32_t* __restrict__ q_pos, const uint16_t* __restrict__ gqa,
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int num_blocks,
     int max_blocks, int bs, int H, int G, int s_q, int n_split, int n_units, int n_rows,
-    float scale_log2, float rope_base, uint16_t* __restrict__ part_o,
+    int nrb, float scale_log2, float rope_base, uint16_t* __restrict__ part_o,
     float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) char ring[kSlots][kSlotBytes];
   // work item: blocks are handed to the 8 XCDs in turn; the G groups of unit (sequence,
-  // split) take consecutive turns on one XCD
+  // split), and the nrb workgroups that share a group's query rows (32 NRB rows each), take
+  // consecutive turns on one XCD, where the tiles they all read stay in L2
   const int id = blockIdx.x, jx = id >> 3;
-  const int g = jx % G;
-  const int unit = (jx / G) * 8 + (id & 7);
+  const int gr = jx % (G * nrb);
+  const int g = gr / nrb, rbw = gr - g * nrb;
+  const int unit = (jx / (G * nrb)) * 8 + (id & 7);
   if (unit >= n_units) return;
   const int b = unit / n_split, k = unit - b * n_split;
   const int lane = threadIdx.x, l32 = lane & 31, hi = lane >> 5;
@@ -78,13 +80,13 @@ __global__ __launch_bounds__(64) void gqa_mfma_kernel(
   split_range(lim_all, n_split, k, kSplitAlign, &t0, &t1);
   const int ntiles = t1 > t0 ? cdiv(t1 - t0, kTok) : 0;
 
-  // rows of this lane: n = 32 rb + l32 -> (query i, head g hg + n % hg)
+  // rows of this lane: n = 32 (NRB rbw + rb) + l32 -> (query i, head g hg + n % hg)
   int64_t pidx[NRB];
   int lim[NRB];
   bool valid[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    const int n = 32 * rb + l32;
+    const int n = 32 * (NRB * rbw + rb) + l32;
     valid[rb] = n < R;
     const int i = valid[rb] ? n / hg : 0;
     const int64_t qrow = (static_cast<int64_t>(b) * s_q + i) * H + g * hg + (valid[rb] ? n % hg : 0);
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(64) void gqa_mfma_kernel(
   bf16x8 qf[NRB][kQSteps];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
-    const int n = 32 * rb + l32;
+    const int n = 32 * (NRB * rbw + rb) + l32;
     const int i = valid[rb] ? n / hg : 0;
     const int64_t qrow = pidx[rb] - static_cast<int64_t>(k) * n_rows;
 #pragma unroll
@@ -334,18 +336,22 @@ hipError_t launch_gqa_mfma(const mla_dims& d, int batch, int s_q, const void* q_
                            hipStream_t s) {
   const float scale_log2 = softmax_scale_of(d) * 1.4426950408889634f;
   const int n_units = batch * n_split;
-  const int64_t n_wg = 8 * static_cast<int64_t>(d.n_groups) * cdiv(n_units, 8);
-  if (n_wg > INT32_MAX) return hipErrorInvalidConfiguration;
   const int n_rows = batch * s_q * d.n_heads;
   const int R = (d.n_heads / d.n_groups) * s_q;
+  // a group's query rows go to workgroups of 32 rows each (one row block per wave), which read
+  // the same tiles through L2: at 64 rows (s_q = 4, G = 8) this measured 1.21 ms against
+  // 1.35 ms for both row blocks in one wave (NRB = 2)
+  const int nrb = cdiv(R, 32);
+  const int64_t n_wg = 8 * static_cast<int64_t>(d.n_groups) * nrb * cdiv(n_units, 8);
+  if (n_wg > INT32_MAX) return hipErrorInvalidConfiguration;
 #define MLA_LAUNCH(NRB_)                                                                    \
   hipLaunchKernelGGL(gqa_mfma_kernel<NRB_>, dim3(static_cast<unsigned>(n_wg)), dim3(64), 0, s, \
                      static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_pe),  \
                      q_pos, static_cast<const uint16_t*>(gqa), table, seq_lens, num_blocks,     \
                      max_blocks, d.block_size, d.n_heads, d.n_groups, s_q, n_split, n_units,    \
-                     n_rows, scale_log2, d.rope_base, static_cast<uint16_t*>(part_o), part_lse)
-  if (R <= 32) MLA_LAUNCH(1);
-  else MLA_LAUNCH(2);
+                     n_rows, nrb, scale_log2, d.rope_base, static_cast<uint16_t*>(part_o),     \
+                     part_lse)
+  MLA_LAUNCH(1);
 #undef MLA_LAUNCH
   return hipGetLastError();
 }
