@@ -204,6 +204,37 @@ mla_status gqla_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const v
 int32_t mla_auto_split(const mla_dims* dims, int32_t batch, int32_t s_q, int32_t max_blocks);
 
 /*
+ * mla_query_project -- the query side of the layer, before mla_absorb_q ([Smallem] "Le code":
+ * query_down, query_norm, query_up and query_rope; "L'obstacle : RoPE": the queries' rotary
+ * part comes from their own latent c_q):
+ *     c_q    = RMSNorm(x · W_DQ) * gamma_q        [d_q]   (rounded once to the dtype)
+ *     q_nope = c_q · W_UQ                         [H, D]
+ *     q_pe   = c_q · W_QR                         [H, d_r] (not rotated: mla_absorb_q rotates)
+ *  x [n_tok, C]; w_dq [C, d_q]; gamma_q [d_q]; w_uq [d_q, H*D]; w_qr [d_q, H*d_r] (NULL when
+ *  d_r = 0); q_nope [n_tok, H, D] and q_pe [n_tok, H, d_r] (outputs, q_pe NULL when d_r = 0).
+ *  RMSNorm as in mla_cache_append (dims->rms_eps). n_tok == 0 enqueues nothing.
+ *  workspace: at least mla_query_project_workspace_bytes(dims, n_tok, d_q) bytes.
+ */
+size_t mla_query_project_workspace_bytes(const mla_dims* dims, int32_t n_tok, int32_t d_q);
+mla_status mla_query_project(const mla_dims* dims, int32_t n_tok, int32_t d_q, const void* x,
+                             const void* w_dq, const void* gamma_q, const void* w_uq,
+                             const void* w_qr, void* q_nope, void* q_pe, void* workspace,
+                             size_t ws_bytes, hipStream_t stream);
+
+/*
+ * mla_output_project -- the layer's output projection, after mla_decode ([Smallem] "Le code",
+ * proj, a linear layer with bias):
+ *     y = o · W_O + b_O
+ *  o [n_tok, H*D_v] (mla_decode's out, heads in order); w_o [H*D_v, C]; b_o [C] (NULL: no
+ *  bias); y [n_tok, C] (output). n_tok == 0 enqueues nothing.
+ *  workspace: at least mla_output_project_workspace_bytes(dims, n_tok) bytes.
+ */
+size_t mla_output_project_workspace_bytes(const mla_dims* dims, int32_t n_tok);
+mla_status mla_output_project(const mla_dims* dims, int32_t n_tok, const void* o,
+                              const void* w_o, const void* b_o, void* y, void* workspace,
+                              size_t ws_bytes, hipStream_t stream);
+
+/*
  * mla_select_path -- choose the decode path of a GQLA layer for a target device from the
  * roofline of each path ([GQLA] section 2, "Sélection du chemin": the absorbed MQA path on
  * hardware whose compute/bandwidth ridge sits above its intensity, the GQA path where the

@@ -23,6 +23,8 @@ STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTY
           -4: "MLA_ERR_RANGE", -5: "MLA_ERR_WORKSPACE", -6: "MLA_ERR_ALIGN", -7: "MLA_ERR_HIP",
           -8: "MLA_ERR_BLOCK_TABLE"}
 EXPORTS = ["mla_cache_append_workspace_bytes", "mla_cache_append", "mla_absorb_q",
+           "mla_query_project_workspace_bytes", "mla_query_project",
+           "mla_output_project_workspace_bytes", "mla_output_project",
            "mla_decode_workspace_bytes", "mla_decode", "mla_decode_splitk", "mla_decode_merge",
            "gqla_expand",
            "gqla_decode_workspace_bytes", "gqla_decode", "mla_auto_split", "mla_select_path",
@@ -75,6 +77,10 @@ def lib() -> ctypes.CDLL:
             "mla_cache_append_workspace_bytes": (S, [D, I]),
             "mla_cache_append": (I, [D, I, P, P, P, P, P, P, P, I, I, I, P, P, S, P]),
             "mla_absorb_q": (I, [D, I, I, P, P, P, P, P, P]),
+            "mla_query_project_workspace_bytes": (S, [D, I, I]),
+            "mla_query_project": (I, [D, I, I, P, P, P, P, P, P, P, P, S, P]),
+            "mla_output_project_workspace_bytes": (S, [D, I]),
+            "mla_output_project": (I, [D, I, P, P, P, P, P, S, P]),
             "mla_decode_workspace_bytes": (S, [D, I, I, I, I]),
             "mla_decode": (I, [D, I, I, P, P, I, P, I, P, P, I, P, S, P, P, P]),
             "mla_decode_splitk": (I, [D, I, I, P, P, I, P, I, P, I, P, S, P]),
@@ -132,6 +138,27 @@ def mla_cache_append(dims, x, seq_idx, pos, w_dkv, gamma, w_kr, block_table, num
                                 block_table.shape[0], block_table.shape[1], num_blocks,
                                 _ptr(latent_cache), _ptr(workspace), workspace.numel(), _stream())
     _check(st, "mla_cache_append")
+
+
+def mla_query_project(dims, x, w_dq, gamma_q, w_uq, w_qr, q_nope, q_pe, workspace=None):
+    n_tok, d_q = x.shape[0], w_dq.shape[1]
+    if workspace is None:
+        workspace = _workspace(lib().mla_query_project_workspace_bytes(ctypes.byref(dims), n_tok,
+                                                                       d_q), x.device)
+    st = lib().mla_query_project(ctypes.byref(dims), n_tok, d_q, _ptr(x), _ptr(w_dq),
+                                 _ptr(gamma_q), _ptr(w_uq), _ptr(w_qr), _ptr(q_nope), _ptr(q_pe),
+                                 _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "mla_query_project")
+
+
+def mla_output_project(dims, o, w_o, b_o, y, workspace=None):
+    n_tok = o.shape[0]
+    if workspace is None:
+        workspace = _workspace(lib().mla_output_project_workspace_bytes(ctypes.byref(dims), n_tok),
+                               o.device)
+    st = lib().mla_output_project(ctypes.byref(dims), n_tok, _ptr(o), _ptr(w_o), _ptr(b_o),
+                                  _ptr(y), _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "mla_output_project")
 
 
 def mla_absorb_q(dims, q_nope, q_pe, q_pos, w_uk, q_abs):

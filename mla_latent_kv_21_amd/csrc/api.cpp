@@ -145,6 +145,54 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, int32_t s_q, const 
   return hip_status(mla::launch_absorb(*dims, batch, s_q, q_nope, q_pe, q_pos, w_uk, q_abs, stream));
 }
 
+size_t mla_query_project_workspace_bytes(const mla_dims* dims, int32_t n_tok, int32_t d_q) {
+  if (check_dims(dims) != MLA_OK || n_tok < 1 || d_q < 1) return 0;
+  return mla::query_project_ws_bytes(*dims, n_tok, d_q);
+}
+
+mla_status mla_query_project(const mla_dims* dims, int32_t n_tok, int32_t d_q, const void* x,
+                             const void* w_dq, const void* gamma_q, const void* w_uq,
+                             const void* w_qr, void* q_nope, void* q_pe, void* workspace,
+                             size_t ws_bytes, hipStream_t stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_tok < 0 || d_q < 1) return MLA_ERR_RANGE;
+  if (n_tok == 0) return MLA_OK;
+  const bool rope = dims->d_r > 0;
+  if (!x || !w_dq || !gamma_q || !w_uq || !q_nope || (rope && (!w_qr || !q_pe)))
+    return MLA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_dq) || !aligned16(gamma_q) || !aligned16(w_uq) ||
+      !aligned16(q_nope) || (rope && (!aligned16(w_qr) || !aligned16(q_pe))))
+    return MLA_ERR_ALIGN;
+  if (workspace == nullptr || ws_bytes < mla_query_project_workspace_bytes(dims, n_tok, d_q))
+    return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_query_project(*dims, n_tok, d_q, x, w_dq, gamma_q, w_uq,
+                                              rope ? w_qr : nullptr, q_nope,
+                                              rope ? q_pe : nullptr, workspace, stream));
+}
+
+size_t mla_output_project_workspace_bytes(const mla_dims* dims, int32_t n_tok) {
+  if (check_dims(dims) != MLA_OK || n_tok < 1) return 0;
+  return mla::output_project_ws_bytes(*dims, n_tok);
+}
+
+mla_status mla_output_project(const mla_dims* dims, int32_t n_tok, const void* o,
+                              const void* w_o, const void* b_o, void* y, void* workspace,
+                              size_t ws_bytes, hipStream_t stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_tok < 0) return MLA_ERR_RANGE;
+  if (n_tok == 0) return MLA_OK;
+  if (!o || !w_o || !y) return MLA_ERR_NULL;
+  if (!aligned16(o) || !aligned16(w_o) || (b_o && !aligned16(b_o)) || !aligned16(y))
+    return MLA_ERR_ALIGN;
+  if (workspace == nullptr || ws_bytes < mla_output_project_workspace_bytes(dims, n_tok))
+    return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_output_project(*dims, n_tok, o, w_o, b_o, y, workspace, stream));
+}
+
 size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s_q,
                                   int32_t n_split, int32_t max_blocks) {
   if (check_dims(dims) != MLA_OK || batch < 1 || s_q < 1 || max_blocks < 1 || n_split < 0 ||

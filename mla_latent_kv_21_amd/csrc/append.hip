@@ -36,9 +36,9 @@ __device__ __forceinline__ uint4 load16(const T* src, int n_avail) {
 
 template <typename T>
 __global__ __launch_bounds__(256) void append_project(const T* __restrict__ x,
-                                                      const T* __restrict__ w_dkv,
-                                                      const T* __restrict__ w_kr, int n_tok,
-                                                      int C, int d_c, int d_r, int k_chunk,
+                                                      const T* __restrict__ w_a,
+                                                      const T* __restrict__ w_b, int n_tok,
+                                                      int C, int n_a, int n_b, int k_chunk,
                                                       float* __restrict__ y_part) {
   // One workgroup: 64 output columns x one k_chunk-wide range of C x up to 16 tokens. Weights
   // and activations are staged through LDS with 16-byte loads issued together; thread (column
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void append_project(const T* __restrict__ x,
   __shared__ __attribute__((aligned(16))) T xs[kTokTile][kKStage];
   __shared__ __attribute__((aligned(16))) T wsm[kKStage][kColTile];
   __shared__ float part[4][kTokTile][kColTile];
-  const int ncols = d_c + d_r;
+  const int ncols = n_a + n_b;
   const int c0 = blockIdx.x * kColTile;
   const int ks = blockIdx.y;
   const int n0 = blockIdx.z * kTokTile;
@@ -73,10 +73,10 @@ __global__ __launch_bounds__(256) void append_project(const T* __restrict__ x,
     const int kg = k0 + k, cg = c0 + cv;
     if (k >= kn || cg >= ncols)
       wr[i] = make_uint4(0u, 0u, 0u, 0u);
-    else if (cg < d_c)
-      wr[i] = load16(w_dkv + static_cast<int64_t>(kg) * d_c + cg, d_c - cg);
+    else if (cg < n_a)
+      wr[i] = load16(w_a + static_cast<int64_t>(kg) * n_a + cg, n_a - cg);
     else
-      wr[i] = load16(w_kr + static_cast<int64_t>(kg) * d_r + (cg - d_c), ncols - cg);
+      wr[i] = load16(w_b + static_cast<int64_t>(kg) * n_b + (cg - n_a), ncols - cg);
   }
 #pragma unroll
   for (int i = 0; i < kXIt; ++i) {
@@ -120,6 +120,10 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 
 constexpr int kWtStride = kKStage * 2 + 16;  // bytes per transposed weight column in LDS
 
+// The two projection kernels compute the split-K partial sums of y = x · [W_a | W_b] (columns
+// 0 .. n_a - 1 from W_a [K, n_a], then n_b from W_b [K, n_b]; W_b may be absent with n_b = 0):
+// the append's [W_DKV | W_KR], and the decode layer's query and output projections.
+//
 // bf16 projection on matrix cores, same partial sums as append_project (fixed 256-wide
 // ranges of C, so a row's bits do not depend on the other tokens appended with it). One
 // workgroup per (64 output columns, 256-wide range of C, 32 tokens); wave w computes the
@@ -129,13 +133,13 @@ constexpr int kWtStride = kKStage * 2 + 16;  // bytes per transposed weight colu
 //  * B operand (k x columns): the weight tile is staged in LDS transposed (column-major, rows
 //    padded to 528 bytes), so each lane's 8 consecutive k of one column are one 16-byte read.
 __global__ __launch_bounds__(256) void append_project_mfma(const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ w_dkv,
-                                                           const uint16_t* __restrict__ w_kr,
-                                                           int n_tok, int C, int d_c, int d_r,
+                                                           const uint16_t* __restrict__ w_a,
+                                                           const uint16_t* __restrict__ w_b,
+                                                           int n_tok, int C, int n_a, int n_b,
                                                            float* __restrict__ y_part) {
   __shared__ __attribute__((aligned(16))) char wt[kColTile * kWtStride];
   __shared__ float half1[2][16][64];
-  const int ncols = d_c + d_r;
+  const int ncols = n_a + n_b;
   const int c0 = blockIdx.x * kColTile;
   const int ks = blockIdx.y;
   const int n0 = blockIdx.z * 32;
@@ -163,8 +167,8 @@ __global__ __launch_bounds__(256) void append_project_mfma(const uint16_t* __res
     const int kg = k0 + k, cg = c0 + cv;
     wr[i] = make_uint4(0u, 0u, 0u, 0u);
     if (kg < C && cg < ncols) {
-      const uint16_t* src = cg < d_c ? w_dkv + static_cast<int64_t>(kg) * d_c + cg
-                                     : w_kr + static_cast<int64_t>(kg) * d_r + (cg - d_c);
+      const uint16_t* src = cg < n_a ? w_a + static_cast<int64_t>(kg) * n_a + cg
+                                     : w_b + static_cast<int64_t>(kg) * n_b + (cg - n_a);
       wr[i] = *reinterpret_cast<const uint4*>(src);
     }
   }
@@ -248,6 +252,30 @@ __global__ __launch_bounds__(1024) void append_finalize(
 }
 
 }  // namespace
+
+int projection_ksplit(int K) { return cdiv(K, kKChunk); }
+
+hipError_t launch_projection_partials(int dt, bool mfma, int n_tok, int K, const void* x,
+                                      const void* w_a, int n_a, const void* w_b, int n_b,
+                                      float* y_part, hipStream_t s) {
+  const int ncols = n_a + n_b;
+  const int n_ksplit = projection_ksplit(K);
+  if (dt == MLA_BF16 && mfma) {
+    hipLaunchKernelGGL(append_project_mfma, dim3(cdiv(ncols, kColTile), n_ksplit, cdiv(n_tok, 32)),
+                       dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(w_a), static_cast<const uint16_t*>(w_b), n_tok,
+                       K, n_a, n_b, y_part);
+  } else if (dt == MLA_BF16) {
+    hipLaunchKernelGGL(append_project<bf16>, dim3(cdiv(ncols, kColTile), n_ksplit, cdiv(n_tok, kTokTile)),
+                       dim3(256), 0, s, static_cast<const bf16*>(x), static_cast<const bf16*>(w_a),
+                       static_cast<const bf16*>(w_b), n_tok, K, n_a, n_b, kKChunk, y_part);
+  } else {
+    hipLaunchKernelGGL(append_project<float>, dim3(cdiv(ncols, kColTile), n_ksplit, cdiv(n_tok, kTokTile)),
+                       dim3(256), 0, s, static_cast<const float*>(x), static_cast<const float*>(w_a),
+                       static_cast<const float*>(w_b), n_tok, K, n_a, n_b, kKChunk, y_part);
+  }
+  return hipGetLastError();
+}
 
 AppendPlan append_plan(const mla_dims& d, int n_tok) {
   // Fixed 256-wide ranges of C per partial sum, added in a fixed order: a row's result does

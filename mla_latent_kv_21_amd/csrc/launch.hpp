@@ -20,6 +20,24 @@ hipError_t launch_append(const mla_dims& d, int n_tok, const void* x, const int3
                          const void* w_kr, const int32_t* table, int batch, int max_blocks,
                          int num_blocks, void* cache, void* ws, hipStream_t s);
 
+// Split-K partial sums of y = x · [W_a | W_b] for n_tok tokens (K-wide rows of x):
+// y_part[k][n][c] over C range [256 k, 256 k + 256), k < projection_ksplit(K). The matrix-core
+// kernel needs bf16, K, n_a and n_b multiples of 8 and 16-byte aligned operands.
+int projection_ksplit(int K);
+hipError_t launch_projection_partials(int dt, bool mfma, int n_tok, int K, const void* x,
+                                      const void* w_a, int n_a, const void* w_b, int n_b,
+                                      float* y_part, hipStream_t s);
+// Decode-layer projections around the path (project.hip); ws as sized by the matching
+// *_workspace_bytes call of the C ABI.
+size_t query_project_ws_bytes(const mla_dims& d, int n_tok, int d_q);
+hipError_t launch_query_project(const mla_dims& d, int n_tok, int d_q, const void* x,
+                                const void* w_dq, const void* gamma_q, const void* w_uq,
+                                const void* w_qr, void* q_nope, void* q_pe, void* ws,
+                                hipStream_t s);
+size_t output_project_ws_bytes(const mla_dims& d, int n_tok);
+hipError_t launch_output_project(const mla_dims& d, int n_tok, const void* o, const void* w_o,
+                                 const void* b_o, void* y, void* ws, hipStream_t s);
+
 hipError_t launch_absorb(const mla_dims& d, int batch, int s_q, const void* q_nope,
                          const void* q_pe, const int32_t* q_pos, const void* w_uk, void* q_abs,
                          hipStream_t s);

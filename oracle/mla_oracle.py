@@ -45,6 +45,7 @@ import math
 import numpy as np
 
 __all__ = [
+    "query_project", "output_project",
     "f64", "round_bf16", "round_storage", "slot", "seq_slots", "gather_rows", "owned_slot_mask",
     "rms_norm", "rope", "latent_rows", "group_of", "softmax_scale",
     "attend", "decode_reconstructed", "absorb_query", "decode_absorbed_latent",
@@ -341,3 +342,28 @@ def decode_gqa(q_nope, q_pe, q_pos, gqa_rows, n_groups: int, d_v: int, base: flo
             n = lim[i]
             out[i, j], lse[i, j] = attend(q, K[:n], V[:n], scale)
     return out, lse
+
+
+# ------------------------------------------------------------------ the layer around the path
+def query_project(x, w_dq, gamma_q, w_uq, w_qr, eps: float, round_cq=None):
+    """(q_nope [n, H*D], q_pe [n, H*d_r]) of the layer's query side, f64.
+
+    [Smallem] "Le code": query_down (C -> d_q), query_norm, query_up (d_q -> H*D) and
+    query_rope (d_q -> H*d_r); "L'obstacle : RoPE": the queries' rotary part is taken from
+    their own latent c_q, and rotated by the same rule as the keys (done by absorb_query).
+    c_q = RMSNorm(x · W_DQ) * gamma_q; round_cq, when given, is the storage rounding applied to
+    c_q between the two products.
+    """
+    c_q = rms_norm(f64(x) @ f64(w_dq), f64(gamma_q), eps)
+    if round_cq is not None:
+        c_q = round_cq(c_q)
+    return c_q @ f64(w_uq), c_q @ f64(w_qr)
+
+
+def output_project(o, w_o, b_o=None):
+    """y [n, C] = o · W_O + b_O, f64: the layer's proj, a linear layer with bias ([Smallem]
+    "Le code"), applied to the heads' outputs o [n, H*D_v] in head order."""
+    y = f64(o) @ f64(w_o)
+    if b_o is not None:
+        y = y + f64(b_o)
+    return y

@@ -72,3 +72,20 @@ def decode(q_nope, q_pe, q_pos, hist, w_uk, w_uv, n_groups, d_c, d_v, base):
             out[i][h] = o
             lse[i][h] = top + math.log(total)
     return out, lse
+
+
+def query_project(x, w_dq, gamma_q, w_uq, w_qr, eps):
+    """Loops for one token: c_q = RMSNorm(x W_DQ) gamma_q, then c_q W_UQ and c_q W_QR."""
+    d_q = len(gamma_q)
+    y = _vec_mat(x, w_dq, 0, d_q)
+    ms = sum(t * t for t in y) / d_q
+    c = [y[j] / math.sqrt(ms + eps) * gamma_q[j] for j in range(d_q)]
+    q_nope = _vec_mat(c, w_uq, 0, len(w_uq[0]))
+    q_pe = _vec_mat(c, w_qr, 0, len(w_qr[0]) if w_qr and w_qr[0] else 0)
+    return q_nope, q_pe
+
+
+def output_project(o, w_o, b_o):
+    """Loops for one token: o W_O + b_O."""
+    y = _vec_mat(o, w_o, 0, len(w_o[0]))
+    return [y[j] + (b_o[j] if b_o is not None else 0.0) for j in range(len(y))]

@@ -30,6 +30,7 @@ import torch
 # stream ids of default_rng([seed, stream]); one per tensor kind
 S_W_DKV, S_GAMMA, S_W_KR, S_W_UK, S_W_UV, S_X, S_Q_NOPE, S_Q_PE, S_LENS, S_TABLE = range(10)
 S_CACHE_C, S_CACHE_KR, S_Q_ABS, S_X_NEW, S_POS_SHIFT = 10, 11, 12, 13, 14
+S_W_DQ, S_GAMMA_Q, S_W_UQ, S_W_QR, S_W_O, S_B_O, S_O = 15, 16, 17, 18, 19, 20, 21
 
 
 @dataclasses.dataclass(frozen=True)
@@ -62,6 +63,12 @@ class Workload:
     @property
     def elt(self) -> int:
         return 4 if self.dtype == "f32" else 2
+
+    @property
+    def d_q(self) -> int:
+        """Width of the query latent: 3 d_c (wider than the key-value latent; 1,536 at
+        d_c = 512)."""
+        return 3 * self.d_c
 
     @property
     def row(self) -> int:
@@ -126,6 +133,27 @@ def weights(w: Workload, random_gamma: bool = False) -> dict:
     else:
         out["gamma"] = to_storage(np.ones((w.d_c,), np.float32), w)
     return out
+
+
+def layer_weights(w: Workload) -> dict:
+    """The query-side and output weights of the layer: W_DQ [C, d_q], gamma_q [d_q] (random
+    around 1), W_UQ [d_q, H*D], W_QR [d_q, H*d_r], W_O [H*D_v, C], b_O [C]."""
+    C, H, dq = w.d_model, w.n_heads, w.d_q
+    g = 1.0 + 0.25 * rng(w, S_GAMMA_Q).standard_normal(size=(dq,), dtype=np.float32)
+    b = 0.1 * rng(w, S_B_O).standard_normal(size=(C,), dtype=np.float32)
+    return {
+        "w_dq": normal(w, S_W_DQ, (C, dq), std=C ** -0.5),
+        "gamma_q": to_storage(g, w),
+        "w_uq": normal(w, S_W_UQ, (dq, H * w.d_nope), std=dq ** -0.5),
+        "w_qr": normal(w, S_W_QR, (dq, H * w.d_r), std=dq ** -0.5),
+        "w_o": normal(w, S_W_O, (H * w.d_v, C), std=(H * w.d_v) ** -0.5),
+        "b_o": to_storage(b, w),
+    }
+
+
+def head_outputs(w: Workload, n_tok: int) -> torch.Tensor:
+    """[n_tok, H*D_v] ~ N(0, 1): stand-in for the attention outputs fed to the projection."""
+    return normal(w, S_O, (n_tok, w.n_heads * w.d_v))
 
 
 # ----------------------------------------------------------------------------- lengths / paging
