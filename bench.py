@@ -164,6 +164,43 @@ def measure_rows(dev, torch):
     return rows
 
 
+def measure_layer(w, d, step, x_new, dev, torch):
+    """The whole decode layer on the bench workload: the query side (mla_query_project) and
+    the output projection (mla_output_project) around the step, each call's weight bytes
+    against 8 TB/s, and the layer's tokens/s."""
+    import workloads as W
+    from mla_latent_kv_21_amd import binding as M
+    g = lambda a: (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
+    n = w.batch * w.s_q
+    lw = {k: g(v) for k, v in W.layer_weights(w).items()}
+    x = x_new[:n]
+    q_nope = torch.empty(n, w.n_heads, w.d_nope, dtype=w.torch_dtype, device=dev)
+    q_pe = torch.empty(n, w.n_heads, w.d_r, dtype=w.torch_dtype, device=dev)
+    o = g(W.head_outputs(w, n))
+    y = torch.empty(n, w.d_model, dtype=w.torch_dtype, device=dev)
+    wsq = torch.empty(M.mla_query_project_workspace_bytes(d, n, w.d_q), dtype=torch.uint8,
+                      device=dev)
+    wso = torch.empty(M.mla_output_project_workspace_bytes(d, n), dtype=torch.uint8, device=dev)
+    qp = lambda: M.mla_query_project(d, x, lw["w_dq"], lw["gamma_q"], lw["w_uq"], lw["w_qr"],
+                                     q_nope, q_pe, workspace=wsq)
+    op = lambda: M.mla_output_project(d, o, lw["w_o"], lw["b_o"], y, workspace=wso)
+    ms_q = _time_calls(qp, 20, torch)
+    ms_o = _time_calls(op, 20, torch)
+
+    def layer():
+        qp()
+        step()
+        op()
+    ms_l = _time_calls(layer, 20, torch)
+    e = w.elt
+    bq = (w.d_model * w.d_q + w.d_q + w.d_q * w.n_heads * (w.d_nope + w.d_r)) * e
+    bo = (w.n_heads * w.d_v * w.d_model + w.d_model) * e
+    return {"workload": w.name, "calls": "mla_query_project, then the step, then mla_output_project",
+            "d_q": w.d_q, "ms": ms_l, "tokens_per_s": n / (ms_l * 1e-3),
+            "query_project_ms": ms_q, "query_project_weight_GBps": bq / (ms_q * 1e-3) / 1e9,
+            "output_project_ms": ms_o, "output_project_weight_GBps": bo / (ms_o * 1e-3) / 1e9}
+
+
 def select_paths(dev, torch, w, lens, table, cache, gqa, tab, lens_d, wts):
     """Both decode paths of the GQLA workload timed at s_q = 1, 2, 4 (the absorbed one with
     planned splits, the GQA one with the automatic split count), beside mla_select_path's
@@ -313,6 +350,7 @@ def main():
     }
     if not args.no_rows:
         rec["rows"] = measure_rows(dev, torch)
+        rec["rows"]["decode_layer"] = measure_layer(w, d, step, x_new, dev, torch)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 2
         src = torch.randn(n, device=dev).to(torch.bfloat16)

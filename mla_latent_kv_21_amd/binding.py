@@ -140,11 +140,18 @@ def mla_cache_append(dims, x, seq_idx, pos, w_dkv, gamma, w_kr, block_table, num
     _check(st, "mla_cache_append")
 
 
+def mla_query_project_workspace_bytes(dims, n_tok, d_q) -> int:
+    return lib().mla_query_project_workspace_bytes(ctypes.byref(dims), n_tok, d_q)
+
+
+def mla_output_project_workspace_bytes(dims, n_tok) -> int:
+    return lib().mla_output_project_workspace_bytes(ctypes.byref(dims), n_tok)
+
+
 def mla_query_project(dims, x, w_dq, gamma_q, w_uq, w_qr, q_nope, q_pe, workspace=None):
     n_tok, d_q = x.shape[0], w_dq.shape[1]
     if workspace is None:
-        workspace = _workspace(lib().mla_query_project_workspace_bytes(ctypes.byref(dims), n_tok,
-                                                                       d_q), x.device)
+        workspace = _workspace(mla_query_project_workspace_bytes(dims, n_tok, d_q), x.device)
     st = lib().mla_query_project(ctypes.byref(dims), n_tok, d_q, _ptr(x), _ptr(w_dq),
                                  _ptr(gamma_q), _ptr(w_uq), _ptr(w_qr), _ptr(q_nope), _ptr(q_pe),
                                  _ptr(workspace), workspace.numel(), _stream())
@@ -154,8 +161,7 @@ def mla_query_project(dims, x, w_dq, gamma_q, w_uq, w_qr, q_nope, q_pe, workspac
 def mla_output_project(dims, o, w_o, b_o, y, workspace=None):
     n_tok = o.shape[0]
     if workspace is None:
-        workspace = _workspace(lib().mla_output_project_workspace_bytes(ctypes.byref(dims), n_tok),
-                               o.device)
+        workspace = _workspace(mla_output_project_workspace_bytes(dims, n_tok), o.device)
     st = lib().mla_output_project(ctypes.byref(dims), n_tok, _ptr(o), _ptr(w_o), _ptr(b_o),
                                   _ptr(y), _ptr(workspace), workspace.numel(), _stream())
     _check(st, "mla_output_project")

@@ -18,16 +18,18 @@ namespace mla {
 namespace {
 
 constexpr int kProjTok = 32;      // tokens per pass
-constexpr int kFinCols = 2048;    // columns per finalize workgroup when nothing couples them
-constexpr int kFinThreads = 256;
+constexpr int kFinCols = 256;     // columns per finalize workgroup when nothing couples them
+constexpr int kFinThreads = 256;  // ... one column per thread
+constexpr int kNormThreads = 1024;  // a normalised row: one workgroup per token
 
 // Workgroup (token n, column chunk j) of one pass: y_c = sum_k y_part[k][n][c], k = 0, 1, ...
+// (sixteen partial sums of a column requested at once: the sum is a chain of round trips).
 // With n_norm > 0 the workgroup holds the whole row (one chunk) and applies
 // y_c / sqrt(mean_{c' < n_norm} y_c'^2 + eps) * gamma_c to the first n_norm columns. bias
 // (nullable) is added after. Columns c < n_a go to out_a (rows of n_a), the rest to out_b (rows
 // of ncols - n_a).
 template <typename T>
-__global__ __launch_bounds__(kFinThreads) void project_finalize(
+__global__ __launch_bounds__(kNormThreads) void project_finalize(
     const float* __restrict__ y_part, int n_ksplit, int n_tok, int ncols, int n_norm,
     const T* __restrict__ gamma, float eps, const T* __restrict__ bias, T* __restrict__ out_a,
     int n_a, T* __restrict__ out_b) {
@@ -38,15 +40,15 @@ __global__ __launch_bounds__(kFinThreads) void project_finalize(
   const int c1 = n_norm > 0 ? ncols : min(ncols, c0 + kFinCols);
   const int n_b = ncols - n_a;
   auto sum_col = [&](int c) {
-    // the partial sums of column c in the fixed order k = 0, 1, ...; eight loads in flight
+    // the partial sums of column c in the fixed order k = 0, 1, ...
     float y = 0.f;
-    for (int k = 0; k < n_ksplit; k += 8) {
-      float v[8];
+    for (int k = 0; k < n_ksplit; k += 16) {
+      float v[16];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 16; ++u)
         v[u] = k + u < n_ksplit ? y_part[(static_cast<int64_t>(k + u) * n_tok + n) * ncols + c] : 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 16; ++u)
         if (k + u < n_ksplit) y += v[u];
     }
     return y;
@@ -80,7 +82,8 @@ hipError_t finalize(const float* y_part, int n_ksplit, int n, int ncols, int n_n
                     void* out_b, hipStream_t s) {
   const dim3 grid(n, n_norm > 0 ? 1 : cdiv(ncols, kFinCols));
   const size_t lds = n_norm > 0 ? static_cast<size_t>(ncols) * sizeof(float) : 0;
-  hipLaunchKernelGGL(project_finalize<T>, grid, dim3(kFinThreads), lds, s, y_part, n_ksplit, n,
+  hipLaunchKernelGGL(project_finalize<T>, grid, dim3(n_norm > 0 ? kNormThreads : kFinThreads), lds,
+                     s, y_part, n_ksplit, n,
                      ncols, n_norm, static_cast<const T*>(gamma), eps, static_cast<const T*>(bias),
                      static_cast<T*>(out_a), n_a, static_cast<T*>(out_b));
   return hipGetLastError();
