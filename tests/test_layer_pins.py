@@ -79,7 +79,18 @@ def _no_norm(x, w_dq, g, w_uq, w_qr, eps, round_cq=None):
     return c @ w_uq, c @ w_qr
 
 
-@pytest.mark.parametrize("bad", [_transposed_up, _no_norm])
+def _no_gain(x, w_dq, g, w_uq, w_qr, eps, round_cq=None):
+    c = O.rms_norm(x @ w_dq, np.ones_like(g), eps)
+    return c @ w_uq, c @ w_qr
+
+
+def _norm_width_off_by_one(x, w_dq, g, w_uq, w_qr, eps, round_cq=None):
+    y = x @ w_dq
+    c = y / np.sqrt(np.sum(y * y, axis=-1, keepdims=True) / (y.shape[-1] - 1) + eps) * g
+    return c @ w_uq, c @ w_qr
+
+
+@pytest.mark.parametrize("bad", [_transposed_up, _no_norm, _no_gain, _norm_width_off_by_one])
 def test_planted_mistakes_are_caught(bad):
     rng = np.random.default_rng(36)
     C, d_q, H, D = 5, 4, 1, 4
@@ -88,3 +99,11 @@ def test_planted_mistakes_are_caught(bad):
     qn, _ = bad(x, w_dq, g, w_uq, w_qr, EPS)
     bn, _ = BF.query_project(list(x[0]), w_dq.tolist(), list(g), w_uq.tolist(), w_qr.tolist(), EPS)
     assert np.max(np.abs(qn[0] - np.array(bn))) > 1e-6
+
+
+def test_planted_missing_bias_is_caught():
+    rng = np.random.default_rng(37)
+    o, w_o, b = rand(rng, 1, 6), rand(rng, 6, 5), rand(rng, 5)
+    ref = BF.output_project(list(o[0]), w_o.tolist(), list(b))
+    assert np.max(np.abs(O.output_project(o, w_o, None)[0] - np.array(ref))) > 1e-6
+    assert np.max(np.abs(O.output_project(o, w_o, b)[0] - np.array(ref))) <= 1e-12
