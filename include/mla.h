@@ -199,6 +199,36 @@ mla_status gqla_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const v
                        const int32_t* seq_lens, int32_t n_split, void* workspace,
                        size_t ws_bytes, void* out, float* lse, hipStream_t stream);
 
+/*
+ * mla_prefill -- attention of many new tokens per sequence over the latent cache, in the
+ * expanded form that the no-cache (training) pass uses ([Smallem] "Le code": keys and values
+ * of every head are key_up and value_up of the latent; "Deux produits ou une concaténation ?":
+ * one score product over the concatenation [k_nope ; k_r] and [q_nope ; q_r]):
+ *     K_h(p) = c_p · W_UK[:, g(h)],  V_h(p) = c_p · W_UV[:, g(h)]   for every visible p
+ *     out_h(i) = softmax_p(([q_nope,h ; RoPE(q_pe,h, q_pos)] · [K_h(p) ; k_r(p)]) * scale) · V_h
+ *  with the causal visibility of mla_decode (query i of a sequence of length L sees positions
+ *  0 .. L - s_q + i). G = H is MLA (one key and value per head); G < H is the GQLA grouping.
+ *  Arguments as in mla_decode (q_nope [batch, s_q, H, D], q_pe [batch, s_q, H, d_r], q_pos,
+ *  latent_cache [num_blocks, bs, d_c + d_r], block_table, seq_lens) and gqla_expand (w_uk,
+ *  w_uv [d_c, G * D] and [d_c, G * D_v]); out [batch, s_q, H, D_v]; lse as in mla_decode
+ *  (nullable). The rows of the new tokens must already be in the cache (mla_cache_append).
+ *  The call expands positions 0 .. seq_lens[b] - 1 of every sequence into the workspace
+ *  (laid out as a GQA cache of num_blocks blocks under the same block table), then runs the
+ *  grouped-query attention over it; a chunked prefill that keeps its expanded cache between
+ *  chunks calls gqla_expand (start_pos = the chunk) and gqla_decode itself instead.
+ *  workspace: at least mla_prefill_workspace_bytes(dims, batch, s_q, num_blocks, max_blocks)
+ *  bytes (num_blocks * block_size * (G * (D + D_v) + d_r) elements, then gqla_decode's).
+ *  Errors: as gqla_expand and gqla_decode; nothing is enqueued when a check fails.
+ */
+size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                   int32_t num_blocks, int32_t max_blocks);
+mla_status mla_prefill(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_nope,
+                       const void* q_pe, const int32_t* q_pos, const void* latent_cache,
+                       int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                       const int32_t* seq_lens, const void* w_uk, const void* w_uv,
+                       void* workspace, size_t ws_bytes, void* out, float* lse,
+                       hipStream_t stream);
+
 /* Uniform split count n_split = 0 resolves to for these sizes where the length-balanced plan
  * of mla_decode does not apply (and the count gqla_decode uses for n_split = 0). */
 int32_t mla_auto_split(const mla_dims* dims, int32_t batch, int32_t s_q, int32_t max_blocks);

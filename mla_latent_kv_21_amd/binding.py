@@ -27,7 +27,8 @@ EXPORTS = ["mla_cache_append_workspace_bytes", "mla_cache_append", "mla_absorb_q
            "mla_output_project_workspace_bytes", "mla_output_project",
            "mla_decode_workspace_bytes", "mla_decode", "mla_decode_splitk", "mla_decode_merge",
            "gqla_expand",
-           "gqla_decode_workspace_bytes", "gqla_decode", "mla_auto_split", "mla_select_path",
+           "gqla_decode_workspace_bytes", "gqla_decode",
+           "mla_prefill_workspace_bytes", "mla_prefill", "mla_auto_split", "mla_select_path",
            "mla_status_string",
            "mla_validate_block_table"]
 
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
             "gqla_expand": (I, [D, I, P, I, P, I, P, P, P, P, P, P]),
             "gqla_decode_workspace_bytes": (S, [D, I, I, I, I]),
             "gqla_decode": (I, [D, I, I, P, P, P, P, I, P, I, P, I, P, S, P, P, P]),
+            "mla_prefill_workspace_bytes": (S, [D, I, I, I, I]),
+            "mla_prefill": (I, [D, I, I, P, P, P, P, I, P, I, P, P, P, P, S, P, P, P]),
             "mla_auto_split": (I, [D, I, I, I]),
             "mla_select_path": (I, [D, I, ctypes.c_int64, ctypes.c_double, ctypes.c_double,
                                     ctypes.POINTER(ctypes.c_double),
@@ -252,6 +255,24 @@ def gqla_decode(dims, q_nope, q_pe, q_pos, gqa_cache, block_table, seq_lens, out
                            _ptr(seq_lens), n_split, _ptr(workspace), workspace.numel(),
                            _ptr(out), _ptr(lse), _stream())
     _check(st, "gqla_decode")
+
+
+def mla_prefill_workspace_bytes(dims, batch, s_q, num_blocks, max_blocks) -> int:
+    return lib().mla_prefill_workspace_bytes(ctypes.byref(dims), batch, s_q, num_blocks,
+                                             max_blocks)
+
+
+def mla_prefill(dims, q_nope, q_pe, q_pos, latent_cache, block_table, seq_lens, w_uk, w_uv,
+                out, lse=None, workspace=None):
+    B, s_q = q_nope.shape[0], q_nope.shape[1]
+    nb, mb = latent_cache.shape[0], block_table.shape[1]
+    if workspace is None:
+        workspace = _workspace(mla_prefill_workspace_bytes(dims, B, s_q, nb, mb), q_nope.device)
+    st = lib().mla_prefill(ctypes.byref(dims), B, s_q, _ptr(q_nope), _ptr(q_pe), _ptr(q_pos),
+                           _ptr(latent_cache), nb, _ptr(block_table), mb, _ptr(seq_lens),
+                           _ptr(w_uk), _ptr(w_uv), _ptr(workspace), workspace.numel(),
+                           _ptr(out), _ptr(lse), _stream())
+    _check(st, "mla_prefill")
 
 
 def mla_validate_block_table(dims, table_host: torch.Tensor, seq_lens_host: torch.Tensor,

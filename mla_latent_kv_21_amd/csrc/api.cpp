@@ -49,6 +49,13 @@ int resolve_split(const mla_dims& d, int batch, int s_q, int max_blocks) {
 
 mla_status hip_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_HIP; }
 
+// the expanded rows of a prefill: [K_0 .. K_{G-1} || V_0 .. V_{G-1} || k_r] per cached slot
+size_t prefill_kv_bytes(const mla_dims& d, int num_blocks) {
+  const size_t row = static_cast<size_t>(d.n_groups) * (d.d_nope + d.d_v) + d.d_r;
+  const size_t b = static_cast<size_t>(num_blocks) * d.block_size * row * elt_of(d);
+  return (b + 255) / 256 * 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -346,6 +353,49 @@ mla_status gqla_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const v
   return hip_status(mla::launch_gqa_decode(*dims, batch, s_q, q_nope, q_pe, q_pos, gqa_cache,
                                            num_blocks, block_table, max_blocks, seq_lens, ns,
                                            workspace, out, lse, stream));
+}
+
+size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                   int32_t num_blocks, int32_t max_blocks) {
+  if (check_dims(dims) != MLA_OK || batch < 1 || s_q < 1 || num_blocks < 1 || max_blocks < 1)
+    return 0;
+  const size_t dec = gqla_decode_workspace_bytes(dims, batch, s_q, 0, max_blocks);
+  return dec == 0 ? 0 : prefill_kv_bytes(*dims, num_blocks) + dec;
+}
+
+mla_status mla_prefill(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_nope,
+                       const void* q_pe, const int32_t* q_pos, const void* latent_cache,
+                       int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
+                       const int32_t* seq_lens, const void* w_uk, const void* w_uv,
+                       void* workspace, size_t ws_bytes, void* out, float* lse,
+                       hipStream_t stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || s_q < 1 || max_blocks < 1 || num_blocks < 1) return MLA_ERR_RANGE;
+  if (batch == 0) return MLA_OK;
+  const size_t need = mla_prefill_workspace_bytes(dims, batch, s_q, num_blocks, max_blocks);
+  if (need == 0) return MLA_ERR_RANGE;
+  if (workspace == nullptr || ws_bytes < need) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  // the checks of both calls below, made before either enqueues anything
+  if (batch > 65535 || s_q > 65535 || static_cast<int64_t>(batch) * s_q > 65535 ||
+      static_cast<int64_t>(max_blocks) * dims->block_size > INT32_MAX)
+    return MLA_ERR_RANGE;
+  if (!q_nope || !q_pos || !out || (dims->d_r > 0 && !q_pe) || !latent_cache || !block_table ||
+      !seq_lens || !w_uk || !w_uv)
+    return MLA_ERR_NULL;
+  if (!aligned16(q_nope) || (q_pe && !aligned16(q_pe)) || !aligned16(out) ||
+      !aligned16(latent_cache) || !aligned16(w_uk) || !aligned16(w_uv))
+    return MLA_ERR_ALIGN;
+  // every head's (or group's) keys and values of the sequences' positions, then attention
+  // over them
+  const size_t kv = prefill_kv_bytes(*dims, num_blocks);
+  char* dec_ws = static_cast<char*>(workspace) + kv;
+  st = gqla_expand(dims, batch, latent_cache, num_blocks, block_table, max_blocks, seq_lens,
+                   nullptr, w_uk, w_uv, workspace, stream);
+  if (st != MLA_OK) return st;
+  return gqla_decode(dims, batch, s_q, q_nope, q_pe, q_pos, workspace, num_blocks, block_table,
+                     max_blocks, seq_lens, 0, dec_ws, ws_bytes - kv, out, lse, stream);
 }
 
 mla_status mla_validate_block_table(const mla_dims* dims, const int32_t* host_table,

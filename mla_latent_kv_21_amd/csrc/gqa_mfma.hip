@@ -1,5 +1,6 @@
 // Split-K grouped-query decode over the expanded GQA cache on gfx950 matrix cores: bf16,
-// D = D_v = 128, d_r = 64, up to 64 query rows (heads of one group x query tokens).
+// D = D_v = 128, d_r = 64, any number of query rows (heads of one group x query tokens) in
+// workgroups of 32: decode steps and, with the expanded cache of every head, prefill.
 //
 // What is computed is the GQA path of the GQLA summary (section 2, "Chemin GQA"): head h of
 // group g scores [q_nope_h ; rotation(q_pe_h)] against the cached [K_g ; k_r] rows, takes the
@@ -45,6 +46,7 @@ static_assert(kSlots >= 2 && kSlots <= 4, "ring depth the waits below cover");
 constexpr int kQSteps = (kD + kDr) / 16;           // score K-steps (12)
 constexpr int kDB = kDv / 32;                      // 32-wide value blocks (4)
 constexpr float kLazy = 8.0f;                      // log2 headroom before the max is raised
+constexpr int kMaxRows = 1 << 20;                  // query rows per group (heads x tokens)
 
 // Physical 16-byte chunk of logical chunk c in a 256-byte row p is c ^ swz256(p): a bijection
 // of p's low four bits, so 16 consecutive rows read at one logical chunk hit 16 distinct
@@ -59,17 +61,30 @@ __global__ __launch_bounds__(64) void gqa_mfma_kernel(
     const int32_t* __restrict__ q_pos, const uint16_t* __restrict__ gqa,
     const int32_t* __restrict__ table, const int32_t* __restrict__ lens, int num_blocks,
     int max_blocks, int bs, int H, int G, int s_q, int n_split, int n_units, int n_rows,
-    int nrb, float scale_log2, float rope_base, uint16_t* __restrict__ part_o,
-    float* __restrict__ part_lse) {
+    int nrb, int spread, float scale_log2, float lse_scale, float rope_base,
+    uint16_t* __restrict__ part_o, float* __restrict__ part_lse) {
   __shared__ __attribute__((aligned(16))) char ring[kSlots][kSlotBytes];
-  // work item: blocks are handed to the 8 XCDs in turn; the G groups of unit (sequence,
-  // split), and the nrb workgroups that share a group's query rows (32 NRB rows each), take
-  // consecutive turns on one XCD, where the tiles they all read stay in L2
+  // work item: blocks are handed to the 8 XCDs in turn. Without spread, the G groups of unit
+  // (sequence, split), and the nrb workgroups that share a group's query rows (32 NRB rows
+  // each), take consecutive turns on one XCD, where the tiles they all read stay in L2. With
+  // spread (fewer units than XCDs: a prefill), the (unit, group) lines go to the XCDs in turn,
+  // each line's row blocks on its XCD, the latest query rows (the longest causal range) first.
   const int id = blockIdx.x, jx = id >> 3;
-  const int gr = jx % (G * nrb);
-  const int g = gr / nrb, rbw = gr - g * nrb;
-  const int unit = (jx / (G * nrb)) * 8 + (id & 7);
-  if (unit >= n_units) return;
+  int g, rbw, unit;
+  if (spread) {
+    const int lj = jx / nrb;
+    const int line = 8 * lj + (id & 7);
+    if (line >= n_units * G) return;
+    rbw = nrb - 1 - (jx - lj * nrb);
+    unit = line / G;
+    g = line - unit * G;
+  } else {
+    const int gr = jx % (G * nrb);
+    g = gr / nrb;
+    rbw = gr - g * nrb;
+    unit = (jx / (G * nrb)) * 8 + (id & 7);
+    if (unit >= n_units) return;
+  }
   const int b = unit / n_split, k = unit - b * n_split;
   const int lane = threadIdx.x, l32 = lane & 31, hi = lane >> 5;
   const int hg = H / G, R = hg * s_q;
@@ -78,7 +93,6 @@ __global__ __launch_bounds__(64) void gqa_mfma_kernel(
   const int lim_all = visible_count(Lb, s_q, s_q - 1, capacity);  // the last query sees most
   int t0, t1;
   split_range(lim_all, n_split, k, kSplitAlign, &t0, &t1);
-  const int ntiles = t1 > t0 ? cdiv(t1 - t0, kTok) : 0;
 
   // rows of this lane: n = 32 (NRB rbw + rb) + l32 -> (query i, head g hg + n % hg)
   int64_t pidx[NRB];
@@ -93,12 +107,23 @@ __global__ __launch_bounds__(64) void gqa_mfma_kernel(
     pidx[rb] = static_cast<int64_t>(k) * n_rows + qrow;
     lim[rb] = valid[rb] ? visible_count(Lb, s_q, i, capacity) : 0;
   }
+  {
+    // the split's range ends at the workgroup's last visible position (the wave-wide maximum
+    // over its rows): row blocks of early queries in a multi-token step skip later tiles
+    int me = 0;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) me = max(me, lim[rb]);
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) me = max(me, __shfl_xor(me, sh, 64));
+    t1 = min(t1, __builtin_amdgcn_readfirstlane(me));
+  }
+  const int ntiles = t1 > t0 ? cdiv(t1 - t0, kTok) : 0;
 
   if (ntiles == 0) {  // nothing of this split is visible: an empty partial
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       if (!valid[rb]) continue;
-      if (hi == 0) part_lse[pidx[rb]] = -INFINITY;
+      if (hi == 0 && part_lse != nullptr) part_lse[pidx[rb]] = -INFINITY;
       uint4* dst = reinterpret_cast<uint4*>(part_o + pidx[rb] * kDv);
       for (int e = hi; e < kDv / 8; e += 2) dst[e] = make_uint4(0u, 0u, 0u, 0u);
     }
@@ -308,7 +333,8 @@ __global__ __launch_bounds__(64) void gqa_mfma_kernel(
     const float l_tot = sum_xor32(l_part[rb]);
     if (!valid[rb]) continue;
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    if (hi == 0) part_lse[pidx[rb]] = l_tot > 0.f ? m_run[rb] + log2f(l_tot) : -INFINITY;
+    if (hi == 0 && part_lse != nullptr)
+      part_lse[pidx[rb]] = l_tot > 0.f ? (m_run[rb] + log2f(l_tot)) * lse_scale : -INFINITY;
     uint16_t* dst = part_o + pidx[rb] * kDv;
 #pragma unroll
     for (int db = 0; db < kDB; ++db)
@@ -326,14 +352,14 @@ bool gqa_mfma_fits(const mla_dims& d, int s_q) {
   if (d.dtype != MLA_BF16 || (d.flags & MLA_FLAG_GENERIC_KERNELS)) return false;
   if (d.d_nope != kD || d.d_v != kDv || d.d_r != kDr || d.block_size % kTok != 0) return false;
   if (d.n_groups < 1 || d.n_heads % d.n_groups != 0) return false;
-  return (d.n_heads / d.n_groups) * s_q <= 64;
+  return static_cast<int64_t>(d.n_heads / d.n_groups) * s_q <= kMaxRows;
 }
 
 hipError_t launch_gqa_mfma(const mla_dims& d, int batch, int s_q, const void* q_nope,
                            const void* q_pe, const int32_t* q_pos, const void* gqa,
                            int num_blocks, const int32_t* table, int max_blocks,
                            const int32_t* seq_lens, int n_split, void* part_o, float* part_lse,
-                           hipStream_t s) {
+                           bool direct, hipStream_t s) {
   const float scale_log2 = softmax_scale_of(d) * 1.4426950408889634f;
   const int n_units = batch * n_split;
   const int n_rows = batch * s_q * d.n_heads;
@@ -342,15 +368,19 @@ hipError_t launch_gqa_mfma(const mla_dims& d, int batch, int s_q, const void* q_
   // the same tiles through L2: at 64 rows (s_q = 4, G = 8) this measured 1.21 ms against
   // 1.35 ms for both row blocks in one wave (NRB = 2)
   const int nrb = cdiv(R, 32);
-  const int64_t n_wg = 8 * static_cast<int64_t>(d.n_groups) * nrb * cdiv(n_units, 8);
+  const int spread = n_units < 8;
+  const int64_t n_wg = spread ? 8 * static_cast<int64_t>(nrb) * cdiv(n_units * d.n_groups, 8)
+                              : 8 * static_cast<int64_t>(d.n_groups) * nrb * cdiv(n_units, 8);
+  // direct: one split, written as the final output (O / l) and natural-log lse
+  const float lse_scale = direct ? 0.6931471805599453f : 1.0f;
   if (n_wg > INT32_MAX) return hipErrorInvalidConfiguration;
 #define MLA_LAUNCH(NRB_)                                                                    \
   hipLaunchKernelGGL(gqa_mfma_kernel<NRB_>, dim3(static_cast<unsigned>(n_wg)), dim3(64), 0, s, \
                      static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_pe),  \
                      q_pos, static_cast<const uint16_t*>(gqa), table, seq_lens, num_blocks,     \
                      max_blocks, d.block_size, d.n_heads, d.n_groups, s_q, n_split, n_units,    \
-                     n_rows, nrb, scale_log2, d.rope_base, static_cast<uint16_t*>(part_o),     \
-                     part_lse)
+                     n_rows, nrb, spread, scale_log2, lse_scale, d.rope_base,                  \
+                     static_cast<uint16_t*>(part_o), part_lse)
   MLA_LAUNCH(1);
 #undef MLA_LAUNCH
   return hipGetLastError();

@@ -85,14 +85,15 @@ bool plan_applies(const mla_dims& d, int batch, int s_q);
 size_t planned_workspace_bytes(const mla_dims& d);
 
 // Whether the MFMA GQA decode kernel handles these dims and query count (bf16, D = D_v = 128,
-// d_r = 64, block size a multiple of 32, (H / G) * s_q <= 64), and its launch: every
-// (sequence, split, group) writes the partials of its heads.
+// d_r = 64, block size a multiple of 32), and its launch: every (sequence, split, group,
+// 32 query rows) writes the partials of its rows, or with direct (n_split = 1) the final
+// output and natural-log lse (lse may then be null).
 bool gqa_mfma_fits(const mla_dims& d, int s_q);
 hipError_t launch_gqa_mfma(const mla_dims& d, int batch, int s_q, const void* q_nope,
                            const void* q_pe, const int32_t* q_pos, const void* gqa,
                            int num_blocks, const int32_t* table, int max_blocks,
                            const int32_t* seq_lens, int n_split, void* part_o, float* part_lse,
-                           hipStream_t s);
+                           bool direct, hipStream_t s);
 
 inline float softmax_scale_of(const mla_dims& d) {
   return d.softmax_scale > 0.f ? d.softmax_scale

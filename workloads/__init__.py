@@ -79,7 +79,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads of this method by name, each with its own seed.
+# The workloads of this method by name, each with its own seed.
 WORKLOADS = {w.name: w for w in (
     Workload("smallem-fp32", "f32", batch=1, s_q=1, d_model=512, n_heads=8, d_nope=64,
              d_v=64, d_c=128, d_r=32, n_groups=8, block_size=64, ctx=512, seed=21001),
@@ -94,6 +94,10 @@ WORKLOADS = {w.name: w for w in (
     Workload("gqla-g8", "bf16", batch=32, s_q=1, d_model=7168, n_heads=128, d_nope=128,
              d_v=128, d_c=512, d_r=64, n_groups=8, block_size=64, ctx=32768,
              random_table=True, seed=21005),
+    # a prefill: every position of two 4,096-token prompts is a query (s_q = L)
+    Workload("prefill-4k", "bf16", batch=2, s_q=4096, d_model=7168, n_heads=128, d_nope=128,
+             d_v=128, d_c=512, d_r=64, n_groups=128, block_size=64, ctx=4096,
+             random_table=True, seed=21006),
 )}
 
 
