@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 SPLITK_SRC = os.path.join(ROOT, "mla_latent_kv_21_amd", "csrc", "decode_mfma.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_traffic.json")
 
@@ -161,7 +162,59 @@ def measure_rows(dev, torch):
                            "GBps": tr["bytes"] / (ms * 1e-3) / 1e9,
                            "frac_hbm": tr["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
     rows["path_select"] = select_paths(dev, torch, w, lens, table, cache, gqa, tab, lens_d, wts)
+    del cache, gqa
+    rows["prefill"] = measure_prefill(dev, torch)
     return rows
+
+
+def measure_prefill(dev, torch):
+    """Prefill of two 4,096-token prompts (every position a query, H = 128, one key and value
+    per head): mla_prefill, and its two parts (gqla_expand of the latents into every head's
+    K and V, then the concatenated-score attention) timed alone. Rates in FLOP: the
+    expansion's 2 d_c G (D + D_v) per position and the attention's 2 (D + d_r) + 2 D_v per
+    head per visible (query, position) pair, against the bf16 matrix-core peak."""
+    import workloads as W
+    from mla_latent_kv_21_amd import binding as M
+    w = W.WORKLOADS["prefill-4k"]
+    lens = W.seq_lens(w)
+    table, nb = W.block_table(w, lens)
+    d = M.dims_of(w)
+    g = lambda a: (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
+    cache = W.cache_pool_device(w, nb, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    shp = (w.batch, w.s_q, w.n_heads)
+    q_nope = torch.randn(shp + (w.d_nope,), generator=gen, device=dev).to(w.torch_dtype)
+    q_pe = torch.randn(shp + (w.d_r,), generator=gen, device=dev).to(w.torch_dtype)
+    qpos = g(W.query_positions(w, lens))
+    wts = {k: g(v) for k, v in W.weights(w).items()}
+    tab, lens_d = g(table), g(lens)
+    out = torch.empty(shp + (w.d_v,), dtype=w.torch_dtype, device=dev)
+    ws = torch.empty(M.mla_prefill_workspace_bytes(d, w.batch, w.s_q, nb, table.shape[1]),
+                     dtype=torch.uint8, device=dev)
+    ms = _time_calls(lambda: M.mla_prefill(d, q_nope, q_pe, qpos, cache, tab, lens_d,
+                                           wts["w_uk"], wts["w_uv"], out, workspace=ws),
+                     10, torch)
+    kv = ws[:nb * w.block_size * (w.n_groups * (w.d_nope + w.d_v) + w.d_r) * w.elt]
+    kv = kv.view(w.torch_dtype).view(nb, w.block_size, -1)
+    ms_x = _time_calls(lambda: M.gqla_expand(d, cache, tab, lens_d, wts["w_uk"], wts["w_uv"], kv),
+                       10, torch)
+    dws = torch.empty(M.gqla_decode_workspace_bytes(d, w.batch, w.s_q, 0, table.shape[1]),
+                      dtype=torch.uint8, device=dev)
+    ms_a = _time_calls(lambda: M.gqla_decode(d, q_nope, q_pe, qpos, kv, tab, lens_d, out,
+                                             workspace=dws), 10, torch)
+    L = lens.astype(np.int64)
+    pairs = int(np.sum(w.s_q * (L - w.s_q) + w.s_q * (w.s_q + 1) // 2))
+    f_attn = pairs * w.n_heads * (2 * (w.d_nope + w.d_r) + 2 * w.d_v)
+    f_exp = int(L.sum()) * 2 * w.d_c * w.n_groups * (w.d_nope + w.d_v)
+    tf = lambda f, t: f / (t * 1e-3) / 1e12
+    return {"workload": w.name, "call": "mla_prefill", "ms": ms,
+            "tokens_per_s": w.batch * w.s_q / (ms * 1e-3),
+            "flop": f_attn + f_exp, "TFLOPs": tf(f_attn + f_exp, ms),
+            "frac_mfma": tf(f_attn + f_exp, ms) / BF16_PEAK_TFLOPS,
+            "expand_ms": ms_x, "expand_TFLOPs": tf(f_exp, ms_x),
+            "attention_ms": ms_a, "attention_TFLOPs": tf(f_attn, ms_a),
+            "attention_frac_mfma": tf(f_attn, ms_a) / BF16_PEAK_TFLOPS}
 
 
 def measure_layer(w, d, step, x_new, dev, torch):

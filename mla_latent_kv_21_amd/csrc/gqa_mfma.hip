@@ -367,8 +367,11 @@ hipError_t launch_gqa_mfma(const mla_dims& d, int batch, int s_q, const void* q_
   // a group's query rows go to workgroups of 32 rows each (one row block per wave), which read
   // the same tiles through L2: at 64 rows (s_q = 4, G = 8) this measured 1.21 ms against
   // 1.35 ms for both row blocks in one wave (NRB = 2)
-  const int nrb = cdiv(R, 32);
+  // With few (sequence, split) units and many rows (a prefill, bound by the matrix cores
+  // rather than HBM) each wave takes two row blocks, halving the tile copies per product.
   const int spread = n_units < 8;
+  const bool two = spread && R > 64;
+  const int nrb = cdiv(R, two ? 64 : 32);
   const int64_t n_wg = spread ? 8 * static_cast<int64_t>(nrb) * cdiv(n_units * d.n_groups, 8)
                               : 8 * static_cast<int64_t>(d.n_groups) * nrb * cdiv(n_units, 8);
   // direct: one split, written as the final output (O / l) and natural-log lse
@@ -381,7 +384,10 @@ hipError_t launch_gqa_mfma(const mla_dims& d, int batch, int s_q, const void* q_
                      max_blocks, d.block_size, d.n_heads, d.n_groups, s_q, n_split, n_units,    \
                      n_rows, nrb, spread, scale_log2, lse_scale, d.rope_base,                  \
                      static_cast<uint16_t*>(part_o), part_lse)
-  MLA_LAUNCH(1);
+  if (two)
+    MLA_LAUNCH(2);
+  else
+    MLA_LAUNCH(1);
 #undef MLA_LAUNCH
   return hipGetLastError();
 }
