@@ -30,9 +30,11 @@ def run_prefill(c, q, qpos, wts):
 # (workload, lengths, s_q): a full prefill beside a chunk appended to 53 cached positions
 # (MLA, one key and value per head); the GQLA grouping (G = 8) with two chunks of 260 over
 # 300 and 260 positions; the Smallem shape (fp32, H 8, D 64, d_r 32, portable kernels) at
-# 128 new tokens; and single-token steps (one query row per head, split-K partials merged)
+# 128 new tokens; single-token steps (one query row per head, split-K partials merged); and
+# 200 new tokens per head (a full and a ragged block of 128 query rows in the prefill kernel)
 CASES = [("dsv3-paged", [150, 97], 97), ("gqla-g8", [300, 260], 260),
-         ("smallem-fp32", [128, 200], 128), ("dsv3-paged", [5, 300], 1)]
+         ("smallem-fp32", [128, 200], 128), ("dsv3-paged", [5, 300], 1),
+         ("dsv3-paged", [300, 200], 200)]
 
 
 @pytest.mark.parametrize("wl,lens,s_q", CASES)
