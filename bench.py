@@ -299,8 +299,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip timing the path's other rows on their own workloads")
-    ap.add_argument("--rows", choices=("all", "layer", "none"), default="all",
-                    help="rows timed after the step: all of them, only the decode layer, or none")
+    ap.add_argument("--rows", choices=("all", "layer", "prefill", "none"), default="all",
+                    help="rows timed after the step: all of them, only the decode layer, only "
+                         "the prefill, or none")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a bf16 buffer of this many MiB three "
                          "times (a plain copy of known size for scaling HBM byte counters)")
@@ -406,7 +407,10 @@ def main():
     rows = "none" if args.no_rows else args.rows
     if rows != "none":
         rec["rows"] = measure_rows(dev, torch) if rows == "all" else {}
-        rec["rows"]["decode_layer"] = measure_layer(w, d, step, x_new, dev, torch)
+        if rows == "prefill":
+            rec["rows"]["prefill"] = measure_prefill(dev, torch)
+        else:
+            rec["rows"]["decode_layer"] = measure_layer(w, d, step, x_new, dev, torch)
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 2
         src = torch.randn(n, device=dev).to(torch.bfloat16)

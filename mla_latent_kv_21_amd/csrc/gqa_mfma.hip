@@ -293,7 +293,8 @@ __global__ __launch_bounds__(64) void gqa_mfma_kernel(
       mt = max_xor32(mt);
       const bool raise = mt > m_run[rb] + kLazy;
       if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-        const float alpha = raise ? (m_run[rb] == -INFINITY ? 0.f : exp2f(m_run[rb] - mt)) : 1.f;
+        const float alpha =
+            raise ? (m_run[rb] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run[rb] - mt)) : 1.f;
         if (raise) m_run[rb] = mt;
         l_part[rb] *= alpha;
 #pragma unroll
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(64) void gqa_mfma_kernel(
       float ls = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        p[r] = exp2f(s[r] - mu);
+        p[r] = __builtin_amdgcn_exp2f(s[r] - mu);  // exp2(-inf) = 0
         ls += p[r];
       }
       l_part[rb] += ls;

@@ -219,24 +219,23 @@ void prefill_mfma_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __
     for (int ks = 0; ks < kQSteps; ++ks)
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds16(slot + s_off[ks]), qf[ks], sc, 0, 0, 0);
 
-    // register r holds position p0 + 8 (r / 4) + 4 hi + r % 4 of row l32
-    float s[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = sc[r] * scale_log2;
+    // register r holds position p0 + 8 (r / 4) + 4 hi + r % 4 of row l32; the scale (> 0) is
+    // applied inside the exponent, so the raw scores are masked and their maximum scaled
     if (masked) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int p = p0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (!tile_ok || p >= lim) s[r] = -INFINITY;
+        if (!tile_ok || p >= lim) sc[r] = -INFINITY;
       }
     }
-    float mt = s[0];
+    float mt = sc[0];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, s[r]);
-    mt = max_xor32(mt);
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+    mt = max_xor32(mt) * scale_log2;
     const bool raise = mt > m_run + kLazy;
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float alpha = raise ? (m_run == -INFINITY ? 0.f : exp2f(m_run - mt)) : 1.f;
+      const float alpha =
+          raise ? (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mt)) : 1.f;
       if (raise) m_run = mt;
       l_part *= alpha;
 #pragma unroll
@@ -244,12 +243,12 @@ void prefill_mfma_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
-    const float mu = m_run == -INFINITY ? 0.f : m_run;
+    const float nmu = m_run == -INFINITY ? 0.f : -m_run;
     float p[16];
     float ls = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      p[r] = exp2f(s[r] - mu);
+      p[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], scale_log2, nmu));  // exp2(-inf) = 0
       ls += p[r];
     }
     l_part += ls;
