@@ -222,10 +222,12 @@ void prefill_mfma_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __
     // register r holds position p0 + 8 (r / 4) + 4 hi + r % 4 of row l32; the scale (> 0) is
     // applied inside the exponent, so the raw scores are masked and their maximum scaled
     if (masked) {
+      // (the empty asm keeps this branch a branch: speculated, it costs every tile 60 VALU)
+      asm volatile("" ::: "memory");
+      const int d = lim - p0 - 4 * hi;  // element r is past this row's end when its offset >= d
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int p = p0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (!tile_ok || p >= lim) sc[r] = -INFINITY;
+        if (!tile_ok || 8 * (r >> 2) + (r & 3) >= d) sc[r] = -INFINITY;
       }
     }
     float mt = sc[0];
