@@ -24,6 +24,7 @@
 //    overlaps the other's products on each SIMD;
 //  * the output O / l (bf16) and the natural-log lse are written directly.
 #include <climits>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -196,22 +197,9 @@ void prefill_mfma_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float m_run = -INFINITY, l_part = 0.f;
 
-  for (int t = 0; t < ntiles; ++t) {
-    // tile t has landed (for this wave's copies) once only tile t + 1's may be in flight
-    if (t + 1 < ntiles)
-      wait_vm<kCopiesPerWave>();
-    else
-      wait_vm<0>();
-    __syncthreads();  // every wave's copies of tile t are in; tile t - 1's slot is free
-    if (t + 2 < ntiles) issue_tile(t + 2, (t + 2) % kSlots);
-    const int p0 = kTok * t;
-    if (p0 >= wave_end) continue;  // past every row of this wave (it still takes the barriers)
-    const char* slot = ring[t % kSlots];
-    const int jb = p0 / bs;
-    const int id_blk = table[static_cast<int64_t>(b) * max_blocks + jb];
-    const bool tile_ok = id_blk >= 0 && id_blk < num_blocks;
-    const bool masked = !tile_ok || p0 + kTok > mask_from;
-
+  // one tile of this wave's rows from the slot at `slot`
+  auto tile_body = [&](const char* slot, int p0, bool tile_ok, bool masked)
+                       __attribute__((always_inline)) {
     f32x16 sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
@@ -265,6 +253,31 @@ void prefill_mfma_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __
       const bf16x8 va = lds_read_tr2(slot + v_off[0][db] + 4096, slot + v_off[1][db] + 4096);
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb1, o[db], 0, 0, 0);
     }
+  };
+
+  // tile t of the loop; the loop is unrolled by the ring depth so that every slot's LDS address
+  // is a constant (the operand reads then take it as an immediate offset)
+  auto step = [&](int t, auto kSlot) __attribute__((always_inline)) {
+    constexpr int S = decltype(kSlot)::value;
+    // tile t has landed (for this wave's copies) once only tile t + 1's may be in flight
+    if (t + 1 < ntiles)
+      wait_vm<kCopiesPerWave>();
+    else
+      wait_vm<0>();
+    __syncthreads();  // every wave's copies of tile t are in; tile t - 1's slot is free
+    if (t + 2 < ntiles) issue_tile(t + 2, (S + 2) % kSlots);
+    const int p0 = kTok * t;
+    if (p0 >= wave_end) return;  // past every row of this wave (it still takes the barriers)
+    const int jb = p0 / bs;
+    const int id_blk = table[static_cast<int64_t>(b) * max_blocks + jb];
+    const bool tile_ok = id_blk >= 0 && id_blk < num_blocks;
+    tile_body(ring[S], p0, tile_ok, !tile_ok || p0 + kTok > mask_from);
+  };
+  static_assert(kSlots == 3, "the unrolled loop below");
+  for (int t = 0; t < ntiles; t += kSlots) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 2 < ntiles) step(t + 2, std::integral_constant<int, 2>{});
   }
 
   // O^T register r of block db holds value column 32 db + 8 (r / 4) + 4 hi + r % 4 of row
