@@ -146,3 +146,52 @@ def test_validate_block_table(L):
     assert M.mla_validate_block_table(d, big, blens, 200_000) == 0
     big[63, 2047] = big[0, 0]
     assert M.mla_validate_block_table(d, big, blens, 200_000) == -8
+
+
+def prefill_call(L, d, batch=2, s_q=300, q=FAKE, qpe=FAKE, qpos=FAKE, cache=FAKE, nb=16,
+                 table=FAKE, mb=8, lens=FAKE, wuk=FAKE, wuv=FAKE, ws=None, ws_bytes=0, out=FAKE):
+    dp = ctypes.byref(d) if d is not None else None
+    return L.mla_prefill(dp, batch, s_q, P(q), P(qpe), P(qpos), P(cache), nb, P(table), mb,
+                         P(lens), P(wuk), P(wuv), P(ws), ws_bytes, P(out), None, None)
+
+
+def test_prefill_validation_and_workspace(L):
+    """mla_prefill checks everything before the expansion is enqueued: a failing check leaves
+    nothing launched (a half-done call would expand and then stop)."""
+    d = dims()
+    bd = ctypes.byref(d)
+    need = L.mla_prefill_workspace_bytes(bd, 2, 300, 16, 8)
+    al = lambda x: (x + 255) // 256 * 256
+    kv = al(16 * 64 * (128 * (128 + 128) + 64) * 2)       # the expanded rows of 16 blocks
+    assert need == kv + L.gqla_decode_workspace_bytes(bd, 2, 300, 0, 8)
+    ok = dict(ws=FAKE, ws_bytes=need)
+    assert prefill_call(L, None) == -1
+    assert prefill_call(L, d, batch=0) == 0
+    assert prefill_call(L, d, s_q=0, **ok) == -4
+    assert prefill_call(L, d, ws=None) == -5
+    assert prefill_call(L, d, ws=FAKE, ws_bytes=need - 1) == -5
+    assert prefill_call(L, d, batch=300, s_q=300, **ok) == -5        # workspace sized for 2
+    assert prefill_call(L, d, q=0, **ok) == -1
+    assert prefill_call(L, d, wuv=0, **ok) == -1
+    assert prefill_call(L, d, q=FAKE + 2, **ok) == -6
+    assert prefill_call(L, d, out=FAKE + 8, **ok) == -6
+    big = L.mla_prefill_workspace_bytes(bd, 300, 300, 16, 8)
+    assert prefill_call(L, d, batch=300, s_q=300, ws=FAKE, ws_bytes=big) == -4  # B s_q > 65535
+
+
+def test_layer_projection_validation(L):
+    d = dims()
+    bd = ctypes.byref(d)
+    nq = L.mla_query_project_workspace_bytes(bd, 4, 1536)
+    no = L.mla_output_project_workspace_bytes(bd, 4)
+    assert nq > 0 and no > 0
+    assert L.mla_query_project(bd, 0, 1536, None, None, None, None, None, None, None, None, 0,
+                               None) == 0
+    assert L.mla_query_project(bd, 4, 1536, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                               P(FAKE), P(FAKE), P(FAKE), nq - 1, None) == -5
+    assert L.mla_query_project(bd, 4, 1536, None, P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                               P(FAKE), P(FAKE), P(FAKE), nq, None) == -1
+    assert L.mla_output_project(bd, 4, P(FAKE), P(FAKE), None, P(FAKE), P(FAKE), no - 1,
+                                None) == -5
+    assert L.mla_output_project(bd, 4, P(FAKE + 2), P(FAKE), None, P(FAKE), P(FAKE), no,
+                                None) == -6
