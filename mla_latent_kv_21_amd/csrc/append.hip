@@ -218,6 +218,10 @@ __global__ __launch_bounds__(1024) void append_finalize(
   __shared__ float red[16];
   const int n = blockIdx.x;
   const int ncols = d_c + d_r;
+  // the row's slot first: its dependent loads (sequence, position, block table) overlap the
+  // partial sums below
+  const int b = seq_idx[n], p = pos[n];
+  const int64_t slot = (b < 0 || b >= batch) ? -1 : cache_slot(table, max_blocks, bs, num_blocks, b, p);
   float ss = 0.f;
   for (int c = threadIdx.x; c < ncols; c += blockDim.x) {
     // partial sums added in the fixed order k = 0, 1, ...; sixteen loads in flight
@@ -235,9 +239,6 @@ __global__ __launch_bounds__(1024) void append_finalize(
     if (c < d_c) ss += y * y;
   }
   ss = block_sum(ss, red);  // also orders the ys writes before the reads below
-  const int b = seq_idx[n], p = pos[n];
-  if (b < 0 || b >= batch) return;
-  const int64_t slot = cache_slot(table, max_blocks, bs, num_blocks, b, p);
   if (slot < 0) return;
   const float inv = 1.0f / sqrtf(ss / static_cast<float>(d_c) + eps);
   T* row = cache + slot * ncols;
