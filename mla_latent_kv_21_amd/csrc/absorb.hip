@@ -93,25 +93,20 @@ __global__ __launch_bounds__(256) void absorb_mfma(const uint16_t* __restrict__ 
                                                 16 * ks + 8 * hi);
   }
   const int64_t ldw = static_cast<int64_t>(G) * D;
-  for (int nb = 4 * blockIdx.z + w; nb < d_c / 32 && nb < 4 * blockIdx.z + 4; nb += 4) {
-    const int j = nb * 32 + l32;
-    const uint16_t* wr = w_uk + j * ldw + static_cast<int64_t>(g) * D + 8 * hi;
-    // all B fragments of this column block are requested before the first MFMA
-    bf16x8 bv[16];
+  // B fragments of one 32-column block: all requested before the first MFMA
+  bf16x8 bv[16];
+  auto load_b = [&](int nb) __attribute__((always_inline)) {
+    const uint16_t* wr = w_uk + (nb * 32 + l32) * ldw + static_cast<int64_t>(g) * D + 8 * hi;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks)
       bv[ks] = ks < ksteps ? *reinterpret_cast<const bf16x8*>(wr + 16 * ks) : zero;
-    f32x16 acc = {};
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks)
-      if (ks < ksteps) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], bv[ks], acc, 0, 0, 0);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int mm = m0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (mm < M) q_abs[(static_cast<int64_t>(mm) * H + h) * row + j] = f32_to_bf16(acc[r]);
-    }
-  }
-  // rotary part: the (row, pair) items are shared out over the z-blocks of this head
+  };
+  int nb = 4 * blockIdx.z + w;
+  const int nb_end = min(d_c / 32, 4 * static_cast<int>(blockIdx.z) + 4);
+  if (nb < nb_end) load_b(nb);
+
+  // rotary part, while the first block's fragments are in flight: the (row, pair) items are
+  // shared out over the z-blocks of this head
   const int half = d_r / 2;
   for (int e = threadIdx.x + blockIdx.z * blockDim.x; e < 32 * half; e += blockDim.x * gridDim.z) {
     const int r = e / half, jj = e % half;
@@ -124,6 +119,21 @@ __global__ __launch_bounds__(256) void absorb_mfma(const uint16_t* __restrict__ 
     const int64_t dst = (static_cast<int64_t>(mm) * H + h) * row + d_c + 2 * jj;
     q_abs[dst] = f32_to_bf16(x0 * cs - x1 * sn);
     q_abs[dst + 1] = f32_to_bf16(x0 * sn + x1 * cs);
+  }
+
+  while (nb < nb_end) {
+    const int j = nb * 32 + l32;
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks)
+      if (ks < ksteps) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], bv[ks], acc, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int mm = m0 + 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (mm < M) q_abs[(static_cast<int64_t>(mm) * H + h) * row + j] = f32_to_bf16(acc[r]);
+    }
+    nb += 4;
+    if (nb < nb_end) load_b(nb);
   }
 }
 
