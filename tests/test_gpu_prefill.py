@@ -103,3 +103,23 @@ def test_prefill_equals_expand_then_grouped_decode():
                   dev(c["lens"]), out2)
     torch.cuda.synchronize()
     assert torch.equal(out, out2.cpu())
+
+
+def test_prefill_kernel_block_size_32_and_eight_heads_per_group():
+    """The prefill kernel (one split: B s_q >= 256) with 32-position cache blocks, so every tile
+    is a whole block, and 8 heads per group, so a 32-row block mixes query tokens and heads
+    (row n -> token n / 8, head n % 8); lengths leave ragged last blocks."""
+    w = W.WORKLOADS["gqla-g8"].replace(n_heads=32, n_groups=4, block_size=32, s_q=100)
+    c = decode_case(w, [100, 177, 300], s_q=100, extra=44)
+    wts = W.weights(c["w"])
+    q = W.queries(c["w"])
+    qpos = W.query_positions(c["w"], c["lens"])
+    note("mla_prefill bs 32, H 32, G 4, s_q 100")
+    out, lse = run_prefill(c, q, qpos, wts)
+    for b, L in enumerate(c["lens"]):
+        rows = O.gather_rows(c["pool"], c["table"], b, int(L))
+        ref, ref_lse = O.decode_reconstructed(q["q_nope"][b], q["q_pe"][b], qpos[b], rows,
+                                              wts["w_uk"], wts["w_uv"], w.n_groups, w.d_c,
+                                              w.d_v, BASE)
+        assert rel_err(out[b], ref) <= TOL[w.dtype]
+        assert np.max(np.abs(lse[b].double().numpy() - ref_lse)) <= TOL[w.dtype]
