@@ -24,6 +24,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+SELECT_HBM_BPS = 6.0e12           # stream-read rate reached on the chip
+SELECT_SUSTAINED_FLOPS = 1.0e15   # bf16 rate the absorbed split-K core sustains
 SPLITK_SRC = os.path.join(ROOT, "mla_latent_kv_21_amd", "csrc", "decode_mfma.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_traffic.json")
 
@@ -255,14 +257,14 @@ def measure_layer(w, d, step, x_new, dev, torch):
 
 
 def select_paths(dev, torch, w, lens, table, cache, gqa, tab, lens_d, wts):
-    """Both decode paths of the GQLA workload timed at s_q = 1, 2, 4 (the absorbed one with
+    """Both decode paths of the GQLA workload timed at s_q = 1, 2, 4, 8 (the absorbed one with
     planned splits, the GQA one with the automatic split count), beside mla_select_path's
     choice and model times for MI355X: the choice should be the faster measured path."""
     import workloads as W
     from mla_latent_kv_21_amd import binding as M
     g = lambda a: (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
     res = []
-    for s_q in (1, 2, 4):
+    for s_q in (1, 2, 4, 8):
         ws_ = w.replace(s_q=s_q)
         d = M.dims_of(ws_)
         q_abs = g(W.absorbed_queries(ws_))
@@ -281,10 +283,17 @@ def select_paths(dev, torch, w, lens, table, cache, gqa, tab, lens_d, wts):
                              5, torch)
         path, ta, tg = M.mla_select_path(d, s_q, int(np.max(lens)))
         chosen = "gqa" if path == M.MLA_PATH_GQA else "absorbed"
+        # the same model at the rate the absorbed split-K core's matrix cores sustain (its
+        # MFMA-busy counters: ~0.96 PFLOP/s) instead of the chip's peak
+        path_c, _, _ = M.mla_select_path(d, s_q, int(np.max(lens)), SELECT_HBM_BPS,
+                                         SELECT_SUSTAINED_FLOPS)
+        chosen_c = "gqa" if path_c == M.MLA_PATH_GQA else "absorbed"
         res.append({"s_q": s_q, "absorbed_ms": ms_abs, "gqa_ms": ms_gqa,
                     "model_absorbed_ms": ta * w.batch * 1e3, "model_gqa_ms": tg * w.batch * 1e3,
                     "selected": chosen,
-                    "selected_is_faster": (ms_abs <= ms_gqa) == (chosen == "absorbed")})
+                    "selected_is_faster": (ms_abs <= ms_gqa) == (chosen == "absorbed"),
+                    "selected_sustained_rate": chosen_c,
+                    "sustained_rate_is_faster": (ms_abs <= ms_gqa) == (chosen_c == "absorbed")})
     return {"workload": w.name, "call": "mla_select_path", "cases": res}
 
 
