@@ -835,13 +835,18 @@ hipError_t launch_gqa_decode(const mla_dims& d, int batch, int s_q, const void* 
   a.scale_log2 = softmax_scale_of(d) * kLog2e; a.base = d.rope_base;
   a.part_o = p.o; a.part_lse = p.lse; a.part_w = d.d_v; a.n_rows = batch * s_q * d.n_heads;
   hipError_t e;
-  if (n_split == 1 && prefill_mfma_fits(d, s_q))  // many rows per group: the prefill kernel
+  // many rows per group: four waves share each tile (one split: the kernel writes out and lse)
+  const bool shared = prefill_mfma_fits(d, s_q);
+  if (shared && n_split == 1)
     return launch_prefill_mfma(d, batch, s_q, q_nope, q_pe, q_pos, gqa, num_blocks, table,
-                               max_blocks, seq_lens, out, lse, s);
-  if (gqa_mfma_fits(d, s_q) && n_split == 1)  // one split: the kernel writes out and lse itself
+                               max_blocks, seq_lens, 1, out, lse, true, s);
+  if (!shared && gqa_mfma_fits(d, s_q) && n_split == 1)
     return launch_gqa_mfma(d, batch, s_q, q_nope, q_pe, q_pos, gqa, num_blocks, table,
                            max_blocks, seq_lens, 1, out, lse, true, s);
-  if (gqa_mfma_fits(d, s_q))
+  if (shared)
+    e = launch_prefill_mfma(d, batch, s_q, q_nope, q_pe, q_pos, gqa, num_blocks, table,
+                            max_blocks, seq_lens, n_split, p.o, p.lse, false, s);
+  else if (gqa_mfma_fits(d, s_q))
     e = launch_gqa_mfma(d, batch, s_q, q_nope, q_pe, q_pos, gqa, num_blocks, table, max_blocks,
                         seq_lens, n_split, p.o, p.lse, false, s);
   else

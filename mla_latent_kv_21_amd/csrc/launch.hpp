@@ -89,13 +89,15 @@ size_t planned_workspace_bytes(const mla_dims& d);
 // 32 query rows) writes the partials of its rows, or with direct (n_split = 1) the final
 // output and natural-log lse (lse may then be null).
 bool gqa_mfma_fits(const mla_dims& d, int s_q);
-// The prefill kernel (one split, at least 128 query rows per group, same shape limits as the
-// GQA kernel): out and natural-log lse (nullable) written directly.
+// The shared-tile kernel (at least 64 query rows per group, same shape limits as the GQA
+// kernel): with direct (n_split = 1) out and natural-log lse (nullable) written directly,
+// otherwise every split's partials as the GQA kernel writes them.
 bool prefill_mfma_fits(const mla_dims& d, int s_q);
 hipError_t launch_prefill_mfma(const mla_dims& d, int batch, int s_q, const void* q_nope,
                                const void* q_pe, const int32_t* q_pos, const void* gqa,
                                int num_blocks, const int32_t* table, int max_blocks,
-                               const int32_t* seq_lens, void* out, float* lse, hipStream_t s);
+                               const int32_t* seq_lens, int n_split, void* out, float* lse,
+                               bool direct, hipStream_t s);
 hipError_t launch_gqa_mfma(const mla_dims& d, int batch, int s_q, const void* q_nope,
                            const void* q_pe, const int32_t* q_pos, const void* gqa,
                            int num_blocks, const int32_t* table, int max_blocks,

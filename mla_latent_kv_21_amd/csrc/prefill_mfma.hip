@@ -72,34 +72,52 @@ void prefill_mfma_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __
                          const int32_t* __restrict__ q_pos, const uint16_t* __restrict__ gqa,
                          const int32_t* __restrict__ table, const int32_t* __restrict__ lens,
                          int num_blocks, int max_blocks, int bs, int H, int G, int s_q,
-                         int batch, int nrb, float scale_log2, float rope_base,
+                         int batch, int n_split, int n_rows, int nrb, int spread,
+                         float scale_log2, float lse_scale, float rope_base,
                          uint16_t* __restrict__ out, float* __restrict__ lse) {
   __shared__ __attribute__((aligned(1024))) char ring[kSlots][kSlotBytes];
-  // work item: (sequence, group) lines go to the 8 XCDs in turn, a line's nrb row blocks on
-  // its XCD, the last row block first
+  // work item (unit = (sequence, split), group, row block). With spread (fewer units than
+  // XCDs: a prefill) the (unit, group) lines go to the 8 XCDs in turn, a line's row blocks on
+  // its XCD, the last row block first; otherwise the groups and row blocks of a unit take
+  // consecutive turns on one XCD, where the k_r rows they all read stay in L2.
   const int id = blockIdx.x, jx = id >> 3;
-  const int lj = jx / nrb;
-  const int line = 8 * lj + (id & 7);
-  if (line >= batch * G) return;
-  const int rbw = nrb - 1 - (jx - lj * nrb);
-  const int b = line / G, g = line - b * G;
+  const int n_units = batch * n_split;
+  int unit, g, rbw;
+  if (spread) {
+    const int lj = jx / nrb;
+    const int line = 8 * lj + (id & 7);
+    if (line >= n_units * G) return;
+    rbw = nrb - 1 - (jx - lj * nrb);
+    unit = line / G;
+    g = line - unit * G;
+  } else {
+    const int gr = jx % (G * nrb);
+    g = gr / nrb;
+    rbw = gr - g * nrb;
+    unit = (jx / (G * nrb)) * 8 + (id & 7);
+    if (unit >= n_units) return;
+  }
+  const int b = unit / n_split, k = unit - b * n_split;
   const int lane = threadIdx.x & 63, l32 = lane & 31, hi = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hg = H / G, R = hg * s_q;
   const int capacity = max_blocks * bs;
   const int Lb = lens[b];
+  // this split's positions [t0, t1) of those the last query sees
+  int t0, t1;
+  split_range(visible_count(Lb, s_q, s_q - 1, capacity), n_split, k, kSplitAlign, &t0, &t1);
 
   // this lane's row: n = 128 rbw + 32 w + l32 -> (query i = n / hg, head g hg + n % hg)
   const int n = kRows * rbw + 32 * w + l32;
   const bool valid = n < R;
   const int i = valid ? n / hg : 0;
   const int64_t qrow = (static_cast<int64_t>(b) * s_q + i) * H + g * hg + (valid ? n % hg : 0);
-  const int lim = valid ? visible_count(Lb, s_q, i, capacity) : 0;
+  const int lim = valid ? min(visible_count(Lb, s_q, i, capacity), t1) : 0;
   // the workgroup streams positions up to its last row's end; a wave computes up to its own
   // rows' largest end and masks from their smallest
   const int n_last = min(R - 1, kRows * rbw + kRows - 1);
-  const int wg_end = max(0, visible_count(Lb, s_q, n_last / hg, capacity));
-  const int ntiles = cdiv(wg_end, kTok);
+  const int wg_end = min(t1, max(0, visible_count(Lb, s_q, n_last / hg, capacity)));
+  const int ntiles = wg_end > t0 ? cdiv(wg_end - t0, kTok) : 0;
   const int wave_end = wave_max(lim);
   const int mask_from = wave_min(valid ? lim : INT_MAX);
 
@@ -143,7 +161,7 @@ void prefill_mfma_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __
   const int pk = lane >> 4, ck = lane & 15;
   const int pr = lane >> 3, cr = lane & 7;
   auto issue_tile = [&](int t, int slot) __attribute__((always_inline)) {
-    const int p0 = kTok * t;
+    const int p0 = t0 + kTok * t;
     const int jb = p0 / bs;
     int id_blk = table[static_cast<int64_t>(b) * max_blocks + jb];
     id_blk = (id_blk < 0 || id_blk >= num_blocks) ? 0 : id_blk;  // masked below, read in bounds
@@ -266,7 +284,7 @@ void prefill_mfma_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __
       wait_vm<0>();
     __syncthreads();  // every wave's copies of tile t are in; tile t - 1's slot is free
     if (t + 2 < ntiles) issue_tile(t + 2, (S + 2) % kSlots);
-    const int p0 = kTok * t;
+    const int p0 = t0 + kTok * t;
     if (p0 >= wave_end) return;  // past every row of this wave (it still takes the barriers)
     const int jb = p0 / bs;
     const int id_blk = table[static_cast<int64_t>(b) * max_blocks + jb];
@@ -285,9 +303,11 @@ void prefill_mfma_kernel(const uint16_t* __restrict__ q_nope, const uint16_t* __
   const float l_tot = sum_xor32(l_part);
   if (!valid) return;
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  // the row's output (one split, natural-log lse) or split k's partial (log2-sum-exp)
+  const int64_t oidx = static_cast<int64_t>(k) * n_rows + qrow;
   if (hi == 0 && lse != nullptr)
-    lse[qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
-  uint16_t* dst = out + qrow * kDv;
+    lse[oidx] = l_tot > 0.f ? (m_run + log2f(l_tot)) * lse_scale : -INFINITY;
+  uint16_t* dst = out + oidx * kDv;
 #pragma unroll
   for (int db = 0; db < kDB; ++db)
 #pragma unroll
@@ -303,23 +323,30 @@ bool prefill_mfma_fits(const mla_dims& d, int s_q) {
   if (d.dtype != MLA_BF16 || (d.flags & MLA_FLAG_GENERIC_KERNELS)) return false;
   if (d.d_nope != kD || d.d_v != kDv || d.d_r != kDr || d.block_size % kTok != 0) return false;
   if (d.n_groups < 1 || d.n_heads % d.n_groups != 0) return false;
-  return static_cast<int64_t>(d.n_heads / d.n_groups) * s_q >= kRows;
+  return static_cast<int64_t>(d.n_heads / d.n_groups) * s_q >= kRows / 2;
 }
 
 hipError_t launch_prefill_mfma(const mla_dims& d, int batch, int s_q, const void* q_nope,
                                const void* q_pe, const int32_t* q_pos, const void* gqa,
                                int num_blocks, const int32_t* table, int max_blocks,
-                               const int32_t* seq_lens, void* out, float* lse, hipStream_t s) {
+                               const int32_t* seq_lens, int n_split, void* out, float* lse,
+                               bool direct, hipStream_t s) {
   const float scale_log2 = softmax_scale_of(d) * 1.4426950408889634f;
   const int64_t R = static_cast<int64_t>(d.n_heads / d.n_groups) * s_q;
   const int nrb = static_cast<int>((R + kRows - 1) / kRows);
-  const int64_t n_wg = 8 * static_cast<int64_t>(nrb) * cdiv(batch * d.n_groups, 8);
+  const int n_units = batch * n_split;
+  const int spread = n_units < 8;
+  const int64_t n_wg = spread ? 8 * static_cast<int64_t>(nrb) * cdiv(n_units * d.n_groups, 8)
+                              : 8 * static_cast<int64_t>(d.n_groups) * nrb * cdiv(n_units, 8);
   if (n_wg > INT32_MAX) return hipErrorInvalidConfiguration;
+  const int n_rows = batch * s_q * d.n_heads;
+  const float lse_scale = direct ? 0.6931471805599453f : 1.0f;
   hipLaunchKernelGGL(prefill_mfma_kernel, dim3(static_cast<unsigned>(n_wg)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_pe),
                      q_pos, static_cast<const uint16_t*>(gqa), table, seq_lens, num_blocks,
-                     max_blocks, d.block_size, d.n_heads, d.n_groups, s_q, batch, nrb,
-                     scale_log2, d.rope_base, static_cast<uint16_t*>(out), lse);
+                     max_blocks, d.block_size, d.n_heads, d.n_groups, s_q, batch, n_split,
+                     n_rows, nrb, spread, scale_log2, lse_scale, d.rope_base,
+                     static_cast<uint16_t*>(out), lse);
   return hipGetLastError();
 }
 
