@@ -28,7 +28,8 @@
  *    arithmetic accumulates in fp32; bf16 results round to nearest, ties to even. lse is fp32.
  *  - Ownership: the caller owns every buffer (device memory unless noted) and the stream.
  *    The library allocates nothing, frees nothing, never synchronises and keeps no state, so
- *    calls are reentrant. Work is enqueued on `stream` (NULL = the default stream) and the
+ *    calls are reentrant (the one exception, mla_decode_noalloc, keeps its partials in a
+ *    device array of its own). Work is enqueued on `stream` (NULL = the default stream) and the
  *    call returns at once. Device pointers must be 16-byte aligned.
  *  - Errors: the status is decided on the host before anything is enqueued, except
  *    MLA_ERR_HIP, which reports a failed launch. Nothing is printed and nothing aborts.
@@ -172,6 +173,28 @@ mla_status mla_decode_merge(const mla_dims* dims, int32_t batch, int32_t s_q, co
                             const int32_t* seq_lens, const void* w_uv, int32_t n_split,
                             void* workspace, size_t ws_bytes, void* out, float* lse,
                             hipStream_t stream);
+
+/*
+ * mla_decode_noalloc -- mla_decode for callers that cannot allocate device memory: code under
+ *  HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Arguments, results
+ *  and errors are mla_decode's, without workspace and ws_bytes: the split-K partials live in a
+ *  file-scope device array of MLA_NOALLOC_SCRATCH_BYTES inside the library. Each GPU the call
+ *  runs on holds its own copy until the process ends (its device address is looked up on the
+ *  first call made with that device current); the call itself allocates and frees nothing.
+ *  Limits: a batch whose mla_decode_workspace_bytes(dims, batch, s_q, n_split, max_blocks)
+ *  exceeds MLA_NOALLOC_SCRATCH_BYTES is rejected with MLA_ERR_WORKSPACE (36 MiB holds the
+ *  length-balanced plan of any batch, and uniform splits of up to 32,768 query rows x heads x
+ *  splits with d_c = 512 in bf16). All calls on one GPU share its array, which keeps the last
+ *  call's contents: calls that overlap on one GPU (two streams or two threads) race and must
+ *  be ordered by the caller. Nothing in the array needs clearing between calls. MLA_ERR_HIP
+ *  also reports a failed lookup of the array.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)36 << 20)
+mla_status mla_decode_noalloc(const mla_dims* dims, int32_t batch, int32_t s_q,
+                              const void* q_abs, const void* latent_cache, int32_t num_blocks,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* seq_lens, const void* w_uv, int32_t n_split,
+                              void* out, float* lse, hipStream_t stream);
 
 /*
  * gqla_expand -- expand latent rows into the GQA cache once ([GQLA] "Chemin GQA"):

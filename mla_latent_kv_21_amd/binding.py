@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 MLA_F32, MLA_BF16 = 0, 1
 MLA_FLAG_GENERIC_KERNELS = 1
 MLA_MAX_SPLIT = 256
+MLA_NOALLOC_SCRATCH_BYTES = 36 << 20
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTYPE",
           -4: "MLA_ERR_RANGE", -5: "MLA_ERR_WORKSPACE", -6: "MLA_ERR_ALIGN", -7: "MLA_ERR_HIP",
           -8: "MLA_ERR_BLOCK_TABLE"}
@@ -26,6 +27,7 @@ EXPORTS = ["mla_cache_append_workspace_bytes", "mla_cache_append", "mla_absorb_q
            "mla_query_project_workspace_bytes", "mla_query_project",
            "mla_output_project_workspace_bytes", "mla_output_project",
            "mla_decode_workspace_bytes", "mla_decode", "mla_decode_splitk", "mla_decode_merge",
+           "mla_decode_noalloc",
            "gqla_expand",
            "gqla_decode_workspace_bytes", "gqla_decode",
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_auto_split", "mla_select_path",
@@ -86,6 +88,7 @@ def lib() -> ctypes.CDLL:
             "mla_decode": (I, [D, I, I, P, P, I, P, I, P, P, I, P, S, P, P, P]),
             "mla_decode_splitk": (I, [D, I, I, P, P, I, P, I, P, I, P, S, P]),
             "mla_decode_merge": (I, [D, I, I, P, P, I, P, I, P, P, I, P, S, P, P, P]),
+            "mla_decode_noalloc": (I, [D, I, I, P, P, I, P, I, P, P, I, P, P, P]),
             "gqla_expand": (I, [D, I, P, I, P, I, P, P, P, P, P, P]),
             "gqla_decode_workspace_bytes": (S, [D, I, I, I, I]),
             "gqla_decode": (I, [D, I, I, P, P, P, P, I, P, I, P, I, P, S, P, P, P]),
@@ -209,6 +212,17 @@ def mla_decode(dims, q_abs, latent_cache, block_table, seq_lens, w_uv, out, lse=
                           _ptr(w_uv), n_split, _ptr(workspace), workspace.numel(), _ptr(out),
                           _ptr(lse), _stream())
     _check(st, "mla_decode")
+
+
+def mla_decode_noalloc(dims, q_abs, latent_cache, block_table, seq_lens, w_uv, out, lse=None,
+                       n_split=0):
+    """mla_decode with its partials in the library's own device array (no workspace)."""
+    B, s_q = q_abs.shape[0], q_abs.shape[1]
+    st = lib().mla_decode_noalloc(ctypes.byref(dims), B, s_q, _ptr(q_abs), _ptr(latent_cache),
+                                  latent_cache.shape[0], _ptr(block_table), block_table.shape[1],
+                                  _ptr(seq_lens), _ptr(w_uv), n_split, _ptr(out), _ptr(lse),
+                                  _stream())
+    _check(st, "mla_decode_noalloc")
 
 
 def mla_decode_splitk(dims, q_abs, latent_cache, block_table, seq_lens, n_split, workspace):

@@ -195,3 +195,27 @@ def test_layer_projection_validation(L):
                                 None) == -5
     assert L.mla_output_project(bd, 4, P(FAKE + 2), P(FAKE), None, P(FAKE), P(FAKE), no,
                                 None) == -6
+
+
+def noalloc_call(L, d, batch=2, s_q=1, mb=4, n_split=0):
+    dp = ctypes.byref(d) if d is not None else None
+    return L.mla_decode_noalloc(dp, batch, s_q, P(FAKE), P(FAKE), 8, P(FAKE), mb, P(FAKE),
+                                P(FAKE), n_split, P(FAKE), None, None)
+
+
+def test_decode_noalloc_host_checks(L):
+    """The no-workspace decode rejects what mla_decode rejects, and any batch whose partials
+    would not fit its fixed device array, before it touches a device."""
+    L.mla_decode_noalloc.restype = ctypes.c_int32
+    d = dims()
+    assert noalloc_call(L, None) == -1
+    assert noalloc_call(L, d, batch=0) == 0
+    assert noalloc_call(L, d, s_q=0) == -4
+    assert noalloc_call(L, dims(n_groups=3)) == -2
+    # 16 sequences x 128 heads x 64 uniform splits of bf16 partials: 134 MB > 36 MiB
+    need = L.mla_decode_workspace_bytes(ctypes.byref(d), 16, 1, 64, 4096)
+    assert need > M.MLA_NOALLOC_SCRATCH_BYTES
+    assert noalloc_call(L, d, batch=16, mb=4096, n_split=64) == -5
+    # the largest workload shapes fit: long context (4 x 64 splits) and the balanced plan
+    assert L.mla_decode_workspace_bytes(ctypes.byref(d), 4, 1, 64, 2048) <= M.MLA_NOALLOC_SCRATCH_BYTES
+    assert L.mla_decode_workspace_bytes(ctypes.byref(d), 32, 4, 0, 512) <= M.MLA_NOALLOC_SCRATCH_BYTES
