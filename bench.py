@@ -24,8 +24,6 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
-SELECT_HBM_BPS = 6.0e12           # stream-read rate reached on the chip
-SELECT_SUSTAINED_FLOPS = 1.0e15   # bf16 rate the absorbed split-K core sustains
 SPLITK_SRC = os.path.join(ROOT, "mla_latent_kv_21_amd", "csrc", "decode_mfma.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_traffic.json")
 
@@ -88,81 +86,123 @@ def cpu_baseline(w, lens, budget_s: float):
                       f"all {w.n_heads} heads of all {w.batch} sequences by positions"}
 
 
-def _time_calls(fn, reps: int, torch):
-    """Median duration (ms) of fn() over reps launches, each bracketed by HIP events on the
-    current stream, after two warm-up calls."""
-    fn(); fn()
+def _time_calls(fn, reps: int, torch, stats: bool = False):
+    """Duration (ms) of fn(i) over reps launches, each bracketed by HIP events on the current
+    stream, after two warm-up calls: the median, or with stats the mean, median, p10 and p90.
+    fn receives the call's index (callers rotate over copies of their inputs with it)."""
+    fn(0); fn(1)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     stream = torch.cuda.current_stream()
-    for a, b in evs:
+    for i, (a, b) in enumerate(evs):
         a.record(stream)
-        fn()
+        fn(i)
         b.record(stream)
     torch.cuda.synchronize()
-    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    if not stats:
+        return float(np.median(ms))
+    return {"mean_ms": float(np.mean(ms)), "median_ms": float(np.median(ms)),
+            "p10_ms": float(np.percentile(ms, 10)), "p90_ms": float(np.percentile(ms, 90)),
+            "launches": reps}
 
 
-def measure_rows(dev, torch):
-    """The other rows of the path, each timed on its own workload: the absorbed decode on the
-    DeepSeek-shaped paged workload (64 sequences, lengths 1,024..8,192, random block table),
-    and on the GQLA workload (G = 8, 32 x 32,768) the absorbed decode, the GQA expansion and
-    the GQA decode. Rates use each call's algorithmic bytes against 8 TB/s."""
+ROTATE_BYTES = 1 << 30   # caches smaller than the 256 MB MALL are rotated over >= 1 GiB
+
+
+def _copies(cache_bytes: int) -> int:
+    """Independent cache copies to rotate through so that >= 1 GiB separates two reads of one
+    copy (none needed for caches of 1 GiB or more)."""
+    return max(1, -(-ROTATE_BYTES // cache_bytes))
+
+
+def absorbed_row(dev, torch, w, planned=True, reps=20):
+    """mla_decode (split-K core + merge + W_UV) on workload w, timed with HIP events over
+    reps calls that rotate over enough cache copies to keep the MALL from serving them, with
+    the call's algorithmic bytes and FLOPs priced against the binding roofline."""
     import workloads as W
     from mla_latent_kv_21_amd import accounting as A
     from mla_latent_kv_21_amd import binding as M
     g = lambda a: (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
-    rows = {}
-
-    def absorbed(name):
-        w = W.WORKLOADS[name]
-        lens = W.seq_lens(w)
-        table, nb = W.block_table(w, lens)
-        d = M.dims_of(w)
-        cache = W.cache_pool_device(w, nb, dev)
-        q_abs = g(W.absorbed_queries(w))
-        wts = {k: g(v) for k, v in W.weights(w).items()}
-        tab, lens_d = g(table), g(lens)
-        out = torch.empty(w.batch, w.s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=dev)
-        ns = 0  # the library plans the splits from the lengths
-        ws = torch.empty(M.mla_decode_workspace_bytes(d, w.batch, w.s_q, ns, table.shape[1]),
-                         dtype=torch.uint8, device=dev)
-        ms = _time_calls(lambda: M.mla_decode(d, q_abs, cache, tab, lens_d, wts["w_uv"], out,
-                                              n_split=ns, workspace=ws), 20, torch)
-        tr = A.decode_traffic(lens, w.s_q, w.n_heads, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt)
-        gbs = tr["bytes"] / (ms * 1e-3) / 1e9
-        return {"workload": w.name, "call": "mla_decode", "ms": ms,
-                "tokens_per_s": w.batch * w.s_q / (ms * 1e-3), "GBps": gbs,
-                "frac_hbm": gbs / HBM_PEAK_GBS, "n_split": "planned"}, (w, lens, table, nb, cache, tab,
-                                                                  lens_d, wts)
-
-    rows["absorbed_dsv3_paged"], _ = absorbed("dsv3-paged")
-    rows["absorbed_gqla_g8"], ctx = absorbed("gqla-g8")
-    w, lens, table, nb, cache, tab, lens_d, wts = ctx
+    lens = W.seq_lens(w)
+    table, nb = W.block_table(w, lens)
     d = M.dims_of(w)
+    n_copies = _copies(nb * w.block_size * w.row * w.elt)
+    caches = [W.cache_pool_device(w, nb, dev, extra=k) for k in range(n_copies)]
+    q_abs = g(W.absorbed_queries(w))
+    wts = {k: g(v) for k, v in W.weights(w).items()}
+    tab, lens_d = g(table), g(lens)
+    out = torch.empty(w.batch, w.s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=dev)
+    ns = 0 if planned else (w.n_split or M.mla_auto_split(d, w.batch, w.s_q, table.shape[1]))
+    ws = torch.empty(M.mla_decode_workspace_bytes(d, w.batch, w.s_q, ns, table.shape[1]),
+                     dtype=torch.uint8, device=dev)
+    ms = _time_calls(lambda i: M.mla_decode(d, q_abs, caches[i % n_copies], tab, lens_d,
+                                            wts["w_uv"], out, n_split=ns, workspace=ws),
+                     reps, torch)
+    tr = A.decode_traffic(lens, w.s_q, w.n_heads, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt)
+    row = {"workload": w.name, "call": "mla_decode", "batch": w.batch, "s_q": w.s_q,
+           "heads": w.n_heads, "context_max": int(lens.max()), "ms": ms,
+           "tokens_per_s": w.batch * w.s_q / (ms * 1e-3),
+           "GBps": tr["bytes"] / (ms * 1e-3) / 1e9,
+           "latent_cache_GBps": tr["cache_bytes"] / (ms * 1e-3) / 1e9,
+           "n_split": "planned" if planned else ns, "cache_copies_rotated": n_copies}
+    row.update(A.binding_roofline(tr["bytes"], tr["flops"], ms))
+    del caches
+    return row, (lens, table, nb, tab, lens_d, wts)
+
+
+def measure_rows(dev, torch):
+    """The other rows of the path, each timed on its own workload: the absorbed decode on the
+    mid-size (H = 32, 16 x 4,096) and DeepSeek-shaped paged workloads (64 sequences, lengths
+    1,024..8,192, random block table), an H = 128 context sweep (8K, 32K, 128K positions per
+    sequence at 524,288 cached positions in all), and on the GQLA workload (G = 8,
+    32 x 32,768) the absorbed decode, the GQA expansion and the GQA decode. Every row carries
+    its binding roofline: the larger of its HBM and bf16 matrix-core times at the published
+    peaks."""
+    import workloads as W
+    from mla_latent_kv_21_amd import accounting as A
+    from mla_latent_kv_21_amd import binding as M
+    rows = {}
+    rows["absorbed_mid_bf16"], _ = absorbed_row(dev, torch, W.WORKLOADS["mid-bf16"])
+    rows["absorbed_dsv3_paged"], _ = absorbed_row(dev, torch, W.WORKLOADS["dsv3-paged"])
+    sweep = []
+    base = W.WORKLOADS["long-128k"]
+    for B, L in ((64, 8192), (16, 32768), (4, 131072)):
+        r, _ = absorbed_row(dev, torch, base.replace(name=f"h128-ctx{L // 1024}k", batch=B,
+                                                     ctx=L, n_split=0))
+        sweep.append(r)
+    rows["absorbed_h128_context_sweep"] = sweep
+    w = W.WORKLOADS["gqla-g8"]
+    rows["absorbed_gqla_g8"], ctx = absorbed_row(dev, torch, w)
+    lens, table, nb, tab, lens_d, wts = ctx
+    d = M.dims_of(w)
+    cache = W.cache_pool_device(w, nb, dev)
     gqa = torch.empty(nb, w.block_size, w.n_groups * (w.d_nope + w.d_v) + w.d_r,
                       dtype=w.torch_dtype, device=dev)
-    ms = _time_calls(lambda: M.gqla_expand(d, cache, tab, lens_d, wts["w_uk"], wts["w_uv"], gqa),
+    ms = _time_calls(lambda i: M.gqla_expand(d, cache, tab, lens_d, wts["w_uk"], wts["w_uv"], gqa),
                      5, torch)
     L = int(np.sum(lens))
     eb = L * (A.latent_row_bytes(w.d_c, w.d_r, w.elt) + A.gqa_row_bytes(w.n_groups, w.d_nope,
                                                                         w.d_r, w.elt))
+    ef = L * 2 * w.d_c * w.n_groups * (w.d_nope + w.d_v)
     rows["gqla_expand"] = {"workload": w.name, "call": "gqla_expand", "ms": ms,
                            "positions_per_s": L / (ms * 1e-3), "GBps": eb / (ms * 1e-3) / 1e9,
-                           "frac_hbm": eb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                           "TFLOPs": ef / (ms * 1e-3) / 1e12}
+    rows["gqla_expand"].update(A.binding_roofline(eb, ef, ms))
+    g = lambda a: (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
     q = {k: g(v) for k, v in W.queries(w).items()}
     qpos = g(W.query_positions(w, lens))
     out = torch.empty(w.batch, w.s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=dev)
     ns = M.mla_auto_split(d, w.batch, w.s_q, table.shape[1])
     ws = torch.empty(M.gqla_decode_workspace_bytes(d, w.batch, w.s_q, ns, table.shape[1]),
                      dtype=torch.uint8, device=dev)
-    ms = _time_calls(lambda: M.gqla_decode(d, q["q_nope"], q["q_pe"], qpos, gqa, tab, lens_d, out,
-                                           n_split=ns, workspace=ws), 5, torch)
+    ms = _time_calls(lambda i: M.gqla_decode(d, q["q_nope"], q["q_pe"], qpos, gqa, tab, lens_d,
+                                             out, n_split=ns, workspace=ws), 5, torch)
     tr = A.gqa_decode_traffic(lens, w.s_q, w.n_heads, w.n_groups, w.d_nope, w.d_r, w.elt)
     rows["gqla_decode"] = {"workload": w.name, "call": "gqla_decode", "ms": ms,
                            "tokens_per_s": w.batch * w.s_q / (ms * 1e-3),
-                           "GBps": tr["bytes"] / (ms * 1e-3) / 1e9,
-                           "frac_hbm": tr["bytes"] / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+                           "GBps": tr["bytes"] / (ms * 1e-3) / 1e9}
+    rows["gqla_decode"].update(A.binding_roofline(tr["bytes"], tr["flops"], ms))
     rows["path_select"] = select_paths(dev, torch, w, lens, table, cache, gqa, tab, lens_d, wts)
     del cache, gqa
     rows["prefill"] = measure_prefill(dev, torch)
@@ -194,16 +234,16 @@ def measure_prefill(dev, torch):
     out = torch.empty(shp + (w.d_v,), dtype=w.torch_dtype, device=dev)
     ws = torch.empty(M.mla_prefill_workspace_bytes(d, w.batch, w.s_q, nb, table.shape[1]),
                      dtype=torch.uint8, device=dev)
-    ms = _time_calls(lambda: M.mla_prefill(d, q_nope, q_pe, qpos, cache, tab, lens_d,
+    ms = _time_calls(lambda i: M.mla_prefill(d, q_nope, q_pe, qpos, cache, tab, lens_d,
                                            wts["w_uk"], wts["w_uv"], out, workspace=ws),
                      10, torch)
     kv = ws[:nb * w.block_size * (w.n_groups * (w.d_nope + w.d_v) + w.d_r) * w.elt]
     kv = kv.view(w.torch_dtype).view(nb, w.block_size, -1)
-    ms_x = _time_calls(lambda: M.gqla_expand(d, cache, tab, lens_d, wts["w_uk"], wts["w_uv"], kv),
+    ms_x = _time_calls(lambda i: M.gqla_expand(d, cache, tab, lens_d, wts["w_uk"], wts["w_uv"], kv),
                        10, torch)
     dws = torch.empty(M.gqla_decode_workspace_bytes(d, w.batch, w.s_q, 0, table.shape[1]),
                       dtype=torch.uint8, device=dev)
-    ms_a = _time_calls(lambda: M.gqla_decode(d, q_nope, q_pe, qpos, kv, tab, lens_d, out,
+    ms_a = _time_calls(lambda i: M.gqla_decode(d, q_nope, q_pe, qpos, kv, tab, lens_d, out,
                                              workspace=dws), 10, torch)
     L = lens.astype(np.int64)
     pairs = int(np.sum(w.s_q * (L - w.s_q) + w.s_q * (w.s_q + 1) // 2))
@@ -239,14 +279,14 @@ def measure_layer(w, d, step, x_new, dev, torch):
     qp = lambda: M.mla_query_project(d, x, lw["w_dq"], lw["gamma_q"], lw["w_uq"], lw["w_qr"],
                                      q_nope, q_pe, workspace=wsq)
     op = lambda: M.mla_output_project(d, o, lw["w_o"], lw["b_o"], y, workspace=wso)
-    ms_q = _time_calls(qp, 20, torch)
-    ms_o = _time_calls(op, 20, torch)
+    ms_q = _time_calls(lambda i: qp(), 20, torch)
+    ms_o = _time_calls(lambda i: op(), 20, torch)
 
     def layer():
         qp()
         step()
         op()
-    ms_l = _time_calls(layer, 20, torch)
+    ms_l = _time_calls(lambda i: layer(), 20, torch)
     e = w.elt
     bq = (w.d_model * w.d_q + w.d_q + w.d_q * w.n_heads * (w.d_nope + w.d_r)) * e
     bo = (w.n_heads * w.d_v * w.d_model + w.d_model) * e
@@ -259,8 +299,11 @@ def measure_layer(w, d, step, x_new, dev, torch):
 def select_paths(dev, torch, w, lens, table, cache, gqa, tab, lens_d, wts):
     """Both decode paths of the GQLA workload timed at s_q = 1, 2, 4, 8 (the absorbed one with
     planned splits, the GQA one with the automatic split count), beside mla_select_path's
-    choice and model times for MI355X: the choice should be the faster measured path."""
+    default choice and model times for MI355X (the rates its kernels sustain): the choice
+    should be the faster measured path. Each path's binding roofline fraction is reported,
+    and the choice the model would make at the chip's published peak rates."""
     import workloads as W
+    from mla_latent_kv_21_amd import accounting as A
     from mla_latent_kv_21_amd import binding as M
     g = lambda a: (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
     res = []
@@ -271,29 +314,32 @@ def select_paths(dev, torch, w, lens, table, cache, gqa, tab, lens_d, wts):
         out = torch.empty(w.batch, s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=dev)
         wsa = torch.empty(M.mla_decode_workspace_bytes(d, w.batch, s_q, 0, table.shape[1]),
                           dtype=torch.uint8, device=dev)
-        ms_abs = _time_calls(lambda: M.mla_decode(d, q_abs, cache, tab, lens_d, wts["w_uv"], out,
+        ms_abs = _time_calls(lambda i: M.mla_decode(d, q_abs, cache, tab, lens_d, wts["w_uv"], out,
                                                   n_split=0, workspace=wsa), 10, torch)
         q = {k: g(v) for k, v in W.queries(ws_).items()}
         qpos = g(W.query_positions(ws_, lens))
         ns = M.mla_auto_split(d, w.batch, s_q, table.shape[1])
         wsg = torch.empty(M.gqla_decode_workspace_bytes(d, w.batch, s_q, ns, table.shape[1]),
                           dtype=torch.uint8, device=dev)
-        ms_gqa = _time_calls(lambda: M.gqla_decode(d, q["q_nope"], q["q_pe"], qpos, gqa, tab,
+        ms_gqa = _time_calls(lambda i: M.gqla_decode(d, q["q_nope"], q["q_pe"], qpos, gqa, tab,
                                                    lens_d, out, n_split=ns, workspace=wsg),
                              5, torch)
         path, ta, tg = M.mla_select_path(d, s_q, int(np.max(lens)))
         chosen = "gqa" if path == M.MLA_PATH_GQA else "absorbed"
-        # the same model at the rate the absorbed split-K core's matrix cores sustain (its
-        # MFMA-busy counters: ~0.96 PFLOP/s) instead of the chip's peak
-        path_c, _, _ = M.mla_select_path(d, s_q, int(np.max(lens)), SELECT_HBM_BPS,
-                                         SELECT_SUSTAINED_FLOPS)
-        chosen_c = "gqa" if path_c == M.MLA_PATH_GQA else "absorbed"
+        # the same model at the chip's published peaks (8 TB/s, 2.5 PFLOP/s bf16)
+        path_p, _, _ = M.mla_select_path(d, s_q, int(np.max(lens)), HBM_PEAK_GBS * 1e9,
+                                         BF16_PEAK_TFLOPS * 1e12)
+        tra = A.decode_traffic(lens, s_q, w.n_heads, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt)
+        trg = A.gqa_decode_traffic(lens, s_q, w.n_heads, w.n_groups, w.d_nope, w.d_r, w.elt)
+        ra = A.binding_roofline(tra["bytes"], tra["flops"], ms_abs)
+        rg = A.binding_roofline(trg["bytes"], trg["flops"], ms_gqa)
         res.append({"s_q": s_q, "absorbed_ms": ms_abs, "gqa_ms": ms_gqa,
+                    "absorbed_bound": ra["bound"], "absorbed_frac": ra["frac"],
+                    "gqa_bound": rg["bound"], "gqa_frac": rg["frac"],
                     "model_absorbed_ms": ta * w.batch * 1e3, "model_gqa_ms": tg * w.batch * 1e3,
                     "selected": chosen,
                     "selected_is_faster": (ms_abs <= ms_gqa) == (chosen == "absorbed"),
-                    "selected_sustained_rate": chosen_c,
-                    "sustained_rate_is_faster": (ms_abs <= ms_gqa) == (chosen_c == "absorbed")})
+                    "selected_at_peak_rates": "gqa" if path_p == M.MLA_PATH_GQA else "absorbed"})
     return {"workload": w.name, "call": "mla_select_path", "cases": res}
 
 
@@ -356,22 +402,12 @@ def main():
                          dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     n_steps = args.steps
-    # The split-K core is bracketed by events on every kCoreEvery-th timed step only: each
-    # event record is a barrier packet on the stream that costs the step a few microseconds.
-    kCoreEvery = 8
-    core_steps = set(range(0, n_steps, kCoreEvery))
-    ev_core = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for i in core_steps}
 
-    def step(i=None):
+    def step():
         M.mla_cache_append(d, x_new, seq_idx, pos_new, wts["w_dkv"], wts["gamma"], wts["w_kr"],
                            tab, nb, cache, workspace=ws_app)
         M.mla_absorb_q(d, q["q_nope"], q["q_pe"], q_pos, wts["w_uk"], q_abs)
-        if i in core_steps:
-            ev_core[i][0].record(stream)
         M.mla_decode_splitk(d, q_abs, cache, tab, lens_d, ns, ws)
-        if i in core_steps:
-            ev_core[i][1].record(stream)
         M.mla_decode_merge(d, q_abs, cache, tab, lens_d, wts["w_uv"], out, lse, ns, ws)
 
     for _ in range(args.warmup):
@@ -381,14 +417,19 @@ def main():
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(n_steps):
-        step(i)
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / n_steps
-    core_ms = float(np.mean([a.elapsed_time(b) for a, b in ev_core.values()]))
     if not torch.isfinite(out.float()).all():
         raise RuntimeError("non-finite decode output")
+    # The split-K core (the dominant kernel) in a loop of its own, every launch bracketed by
+    # HIP events on the stream it runs on (an event pair inside the step would add its own
+    # barrier packets to the step time).
+    core = _time_calls(lambda i: M.mla_decode_splitk(d, q_abs, cache, tab, lens_d, ns, ws),
+                       max(20, n_steps), torch, stats=True)
+    core_ms = core["mean_ms"]
 
     tr = A.decode_traffic(lens, s_q, H, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt)
     core_bytes = tr["core_bytes"]
@@ -408,7 +449,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "decode_mfma_kernel (split-K core)", "launch_ms": core_ms,
-                     "algorithmic_bytes_per_launch": core_bytes},
+                     "launch_stats": core,
+                     "algorithmic_bytes_per_launch": core_bytes,
+                     "algorithmic_flops_per_launch": tr["core_flops"],
+                     "frac_mfma": tr["core_flops"] / (core_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
+        "step_outside_core_ms": ms_step - core_ms,
         "latent_cache_GBps": tr["cache_bytes"] / (core_ms * 1e-3) / 1e9,
         "step_latent_cache_GBps": tr["cache_bytes"] / (ms_step * 1e-3) / 1e9,
         "wall_s": wall,

@@ -62,7 +62,10 @@ typedef enum {
   MLA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than the *_workspace_bytes() size */
   MLA_ERR_ALIGN = -6,       /* a device pointer is not 16-byte aligned */
   MLA_ERR_HIP = -7,         /* a kernel launch failed */
-  MLA_ERR_BLOCK_TABLE = -8  /* mla_validate_block_table(): bad or shared block id */
+  MLA_ERR_BLOCK_TABLE = -8, /* mla_validate_block_table(): bad or shared block id */
+  MLA_STATUS_INT32_ = 0x7fffffff /* not a status: gives the type the range of an int32, so
+                                    that any int a caller passes (mla_status_string) is a
+                                    valid value of it */
 } mla_status;
 
 /* dims->flags bits */
@@ -301,18 +304,21 @@ mla_status mla_output_project(const mla_dims* dims, int32_t n_tok, const void* o
  *  The path with the smaller time is returned (the absorbed path on a tie). The query,
  *  output and up-projection work around the attention, and the one-off expansion of the GQA
  *  cache, are not counted.
- *  hbm_bytes_per_s, flops_per_s: the target's rates; both 0 selects MI355X as measured here
- *  (MLA_MI355X_HBM_BYTES_PER_S, MLA_MI355X_BF16_FLOPS). t_absorbed, t_gqa: nullable outputs,
+ *  hbm_bytes_per_s, flops_per_s: the target's rates; both 0 selects the rates this library's
+ *  kernels sustain on MI355X (MLA_MI355X_HBM_BYTES_PER_S, MLA_MI355X_BF16_FLOPS), so that the
+ *  choice is the faster of the two measured paths. t_absorbed, t_gqa: nullable outputs,
  *  the two times in seconds. Returns MLA_PATH_ABSORBED or MLA_PATH_GQA; otherwise a negative
  *  mla_status: the dims checks of the other calls, MLA_ERR_RANGE for s_q < 1, context < 1 or
  *  rates that are not both positive (or both 0). Host only: launches nothing.
  */
 typedef enum { MLA_PATH_ABSORBED = 0, MLA_PATH_GQA = 1 } mla_path;
-/* MI355X rates used by default: a stream read by 256 workgroups reaches 6.0e12 B/s; the
- * bf16 matrix cores' 2.5e15 FLOP/s peak at 2.4 GHz scales to 2.03e15 at the 1.95 GHz the
- * decode kernels sustain. */
+/* MI355X rates used by default, as measured: a stream read by 256 workgroups reaches
+ * 6.0e12 B/s; the absorbed split-K decode sustains 1.0e15 bf16 FLOP/s (146 GFLOP in about
+ * 0.15 ms on 4 x 131,072 positions at H = 128). The chip's dense bf16 peak is 2.5e15, but
+ * under a sustained matrix-core load it holds about 1.75e15 (the clock falls to ~1.7 GHz),
+ * and the decode's matrix cores are busy about half of its launch. */
 #define MLA_MI355X_HBM_BYTES_PER_S 6.0e12
-#define MLA_MI355X_BF16_FLOPS 2.03e15
+#define MLA_MI355X_BF16_FLOPS 1.0e15
 int32_t mla_select_path(const mla_dims* dims, int32_t s_q, int64_t context,
                         double hbm_bytes_per_s, double flops_per_s, double* t_absorbed,
                         double* t_gqa);

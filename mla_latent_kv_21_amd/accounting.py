@@ -92,3 +92,17 @@ def gqa_decode_traffic(lens, s_q: int, n_heads: int, n_groups: int, d_h: int, d_
     b = rows * gqa_row_bytes(n_groups, d_h, d_r, elt) + B * s_q * n_heads * (2 * d_h + d_r) * elt
     return {"bytes": b, "flops": vis * gqa_flops_per_pos(n_heads, d_h, d_r),
             "cache_bytes": rows * gqa_row_bytes(n_groups, d_h, d_r, elt)}
+
+
+def binding_roofline(nbytes: float, flops: float, ms: float,
+                     hbm_gbs: float = HBM_PEAK_GBS,
+                     mfma_tflops: float = MFMA_BF16_PEAK_TFLOPS) -> dict:
+    """The binding roofline of a launch that moves nbytes and does flops in ms: the larger of
+    its HBM time (nbytes at the HBM peak) and its matrix-core time (flops at the bf16 peak),
+    and the fraction of that bound achieved, beside both fractions."""
+    t_hbm = nbytes / (hbm_gbs * 1e9)
+    t_mfma = flops / (mfma_tflops * 1e12)
+    t = ms * 1e-3
+    return {"bound": "hbm" if t_hbm >= t_mfma else "mfma",
+            "frac": max(t_hbm, t_mfma) / t, "frac_hbm": t_hbm / t, "frac_mfma": t_mfma / t,
+            "roofline_ms": max(t_hbm, t_mfma) * 1e3}

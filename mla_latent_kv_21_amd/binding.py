@@ -14,7 +14,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmla.so")
+# MLA_LIB overrides the library path (the host-sanitizer test loads an instrumented build).
+LIB_PATH = os.environ.get("MLA_LIB") or os.path.join(_HERE, "libmla.so")
 
 MLA_F32, MLA_BF16 = 0, 1
 MLA_FLAG_GENERIC_KERNELS = 1

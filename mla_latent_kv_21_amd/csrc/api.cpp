@@ -71,6 +71,7 @@ const char* mla_status_string(mla_status s) {
     case MLA_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
     case MLA_ERR_HIP: return "a kernel launch failed";
     case MLA_ERR_BLOCK_TABLE: return "block table holds a bad or shared block id";
+    case MLA_STATUS_INT32_: break;
   }
   return "unknown status";
 }

@@ -30,14 +30,13 @@
 //  * each split writes (O / l as bf16, m + log2 l) partials; the merge kernel combines them.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mfma_util.hpp"
 #include "plan.hpp"
 
 namespace mla {
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-typedef short __attribute__((ext_vector_type(4))) i16x4;
+using namespace mfma;
 
 constexpr int kRowElems = 576;            // d_c + d_r
 constexpr int kRowBytes = kRowElems * 2;  // 1,152
@@ -52,9 +51,6 @@ constexpr int kPre = 10;                          // score fragments read ahead 
 constexpr int kVPre = 2;                          // P · V steps whose V fragments are in flight
 constexpr int kSlots = 4;                         // ring slots: two tiles in flight
 
-typedef __attribute__((address_space(3))) char lds_char_t;
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
-
 // Physical 16-byte chunk of logical chunk c in tile row t is c ^ swz(t). swz is a linear map
 // of the row's low four bits into three bits (a row's 72 chunks stay in their groups of 8).
 // It is chosen so that the score reads (16 bytes per lane, 32 rows x one chunk pair) and the
@@ -64,36 +60,6 @@ __host__ __device__ constexpr int swz(int t) {
   return ((t & 1) ? 3 : 0) ^ ((t & 2) ? 4 : 0) ^ ((t & 4) ? 2 : 0) ^ ((t & 8) ? 1 : 0);
 }
 
-// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane i's 16 bytes from
-// gbase + off land at LDS byte address lds + 16 i. Issued from asm so that the compiler does
-// not order later LDS reads of *other* ring slots behind it; the kernel waits for these
-// copies itself (vmcnt) before the barrier that publishes a tile. M0 is restored afterwards.
-__device__ __forceinline__ void dma16(const char* gbase, unsigned off, unsigned lds) {
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
-      "s_nop 0\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(off), "s"(gbase)
-      : "memory");
-}
-
-__device__ __forceinline__ unsigned lds_addr(const char* p) {
-  return static_cast<unsigned>(reinterpret_cast<size_t>((lds_char_t*)p));
-}
-
-// s_waitcnt immediate that waits for vmcnt <= n only (expcnt and lgkmcnt at their maxima).
-constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
-// Wait until at most `later` global -> LDS copies issued by this wave are still in flight:
-// copies complete in issue order, so everything issued before them has landed.
-template <int kLater>
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(vmcnt_imm(kLater)); }
-
 // O += A · B with O held in accumulation registers (AGPRs). The score products use the
 // compiler's MFMA in its VGPR form (this file is built with MFMA results in VGPRs), so that
 // O (256 AGPRs) and the score accumulator never compete for one register file. The compiler
@@ -102,30 +68,6 @@ __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(vmcnt_im
 // only after the explicit wait that follows the main loop.
 __device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& a, const bf16x8& b) {
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
-}
-
-// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane i receives
-// element (i % 4) of the 8 bytes addressed by lanes 4k + i/4, for k = 0..3.
-__device__ __forceinline__ i16x4 lds_read_tr(const char* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)((lds_char_t*)p));
-}
-
-__device__ __forceinline__ bf16x8 lds16(const char* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
-}
-
-// two floats as a bf16 pair (round to nearest even), low element first
-__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
-  return __builtin_bit_cast(unsigned, v);
-}
-
-// max over the lane pair (lane, lane ^ 32), without going through LDS
-__device__ __forceinline__ float max_xor32(float v) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 template <int NW>
@@ -448,11 +390,11 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     if (ntiles > 1) issue_tile(tile_src(t0 + kTileTok, &nv1), ring[1]);
     if (ntiles > 2) issue_tile(tile_src(t0 + 2 * kTileTok, &nv2), ring[2]);
     if (ntiles > 2)
-      wait_dma<2 * kDma>();
+      wait_vm<2 * kDma>();
     else if (ntiles > 1)
-      wait_dma<kDma>();
+      wait_vm<kDma>();
     else
-      wait_dma<0>();
+      wait_vm<0>();
     __syncthreads();
     softmax_all(scores(ring[0], nullptr, 0u), nv0, 0);
     if (nv0 < kTileTok) zero_tail(ring[0], nv0);
@@ -468,9 +410,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     // tile t+1 has landed (tile t+2 may still be in flight); after the barrier P(t) and the
     // zeroed tail of tile t are visible to every wave and the slot of tile t-1 is free
     if (t + 2 < ntiles)
-      wait_dma<kDma>();
+      wait_vm<kDma>();
     else
-      wait_dma<0>();
+      wait_vm<0>();
     __syncthreads();
     int nv3 = 0;
     const char* src3 =

@@ -1,5 +1,7 @@
 """Shared builders for the GPU parity tests: seeded inputs (workloads), library calls through
 the C ABI (binding) and expected values from the oracle, on the same input bits."""
+import os
+
 import numpy as np
 import torch
 
@@ -26,6 +28,45 @@ def rel_err(y, ref) -> float:
     assert y.shape == ref.shape, (y.shape, ref.shape)
     assert np.all(np.isfinite(y)), "non-finite values in the GPU result"
     return float(np.max(np.abs(y - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def row_errors(y, ref) -> np.ndarray:
+    """Per-row error max_j|y_j - ref_j| / max_j|ref_j| over the last axis (one row per query
+    and head of an output, or per position of cache rows)."""
+    y, ref = O.f64(y), O.f64(ref)
+    num = np.max(np.abs(y - ref), axis=-1)
+    den = np.maximum(np.max(np.abs(ref), axis=-1), 1e-30)
+    return num / den
+
+
+def check(y, ref, tol: float, what: str = "") -> float:
+    """Assert the normwise error of y against ref is within tol, and print it with the worst
+    row's error and index so that the margin under the bound is on record."""
+    err = rel_err(y, ref)
+    rows = row_errors(y, ref)
+    worst = np.unravel_index(int(np.argmax(rows)), rows.shape) if rows.size else ()
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    print(f"[err] {test} {what} normwise={err:.3e} worst_row={float(np.max(rows)):.3e} "
+          f"at {tuple(int(i) for i in worst)} tol={tol:.0e}", flush=True)
+    assert err <= tol, f"{what}: normwise error {err:.3e} > {tol}"
+    return err
+
+
+def check_lse(got, ref, tol: float, what: str = "lse") -> float:
+    """Absolute error of log-sum-exps (natural log), printed and held to tol."""
+    got, ref = O.f64(got), O.f64(ref)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    err = float(np.max(np.abs(got - ref)))
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    print(f"[err] {test} {what} abs={err:.3e} tol={tol:.0e}", flush=True)
+    assert err <= tol, f"{what}: error {err:.3e} > {tol}"
+    return err
+
+
+def check_per_seq(y, ref, tol: float, what: str = "out"):
+    """check() on each sequence (axis 0) of a batch separately."""
+    for b in range(len(ref)):
+        check(y[b], ref[b], tol, f"{what}[seq {b}]")
 
 
 def dev(t):

@@ -7,7 +7,7 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_cases import DEV, TOL, dev, note, rel_err
+from gpu_cases import (DEV, TOL, check, dev, note)
 from mla_latent_kv_21_amd import binding as M
 
 pytestmark = pytest.mark.gpu
@@ -40,8 +40,8 @@ def test_query_project_matches_oracle(wl, n_tok):
     torch.cuda.synchronize()
     rn, rp = O.query_project(x, lw["w_dq"], lw["gamma_q"], lw["w_uq"], lw["w_qr"], EPS,
                              round_cq=lambda a: store(a, w))
-    assert rel_err(q_nope.cpu().view(n_tok, -1), rn) <= TOL[w.dtype]
-    assert rel_err(q_pe.cpu().view(n_tok, -1), rp) <= TOL[w.dtype]
+    check(q_nope.cpu().view(n_tok, -1), rn, TOL[w.dtype])
+    check(q_pe.cpu().view(n_tok, -1), rp, TOL[w.dtype])
 
 
 @pytest.mark.parametrize("wl", ["smallem-fp32", "mid-bf16", "dsv3-paged"])
@@ -56,7 +56,7 @@ def test_output_project_matches_oracle(wl, n_tok, bias):
     note(f"output project {wl} n_tok={n_tok} bias={bias}")
     M.mla_output_project(d, dev(o), dev(lw["w_o"]), None if b is None else dev(b), y)
     torch.cuda.synchronize()
-    assert rel_err(y.cpu(), O.output_project(o, lw["w_o"], b)) <= TOL[w.dtype]
+    check(y.cpu(), O.output_project(o, lw["w_o"], b), TOL[w.dtype])
 
 
 @pytest.mark.parametrize("wl,lens,s_q", [("smallem-fp32", [40, 17], 1), ("dsv3-paged", [70, 33], 1),
@@ -104,4 +104,4 @@ def test_decode_layer_matches_reconstructed_oracle(wl, lens, s_q):
         heads.append(store(o_b, w).reshape(s_q, -1))
         k += L
     ref = O.output_project(np.concatenate(heads), lw["w_o"], lw["b_o"])
-    assert rel_err(y.cpu(), ref) <= TOL[w.dtype]
+    check(y.cpu(), ref, TOL[w.dtype])

@@ -2,13 +2,12 @@
 in the expanded, concatenated-score form of the no-cache pass (Smallem article 13, "Le code"
 and "Deux produits ou une concaténation ?"), against the oracle's reconstructed attention
 (every head's K and V rebuilt from the latents), which is the prefill written out."""
-import numpy as np
 import pytest
 import torch
 
 import oracle as O
 import workloads as W
-from gpu_cases import DEV, TOL, decode_case, dev, note, rel_err
+from gpu_cases import (DEV, TOL, check, check_lse, decode_case, dev, note)
 from mla_latent_kv_21_amd import binding as M
 
 pytestmark = pytest.mark.gpu
@@ -51,8 +50,8 @@ def test_prefill_matches_reconstructed_oracle(wl, lens, s_q):
         ref, ref_lse = O.decode_reconstructed(q["q_nope"][b], q["q_pe"][b], qpos[b], rows,
                                               wts["w_uk"], wts["w_uv"], w.n_groups, w.d_c,
                                               w.d_v, BASE)
-        assert rel_err(out[b], ref) <= TOL[w.dtype]
-        assert np.max(np.abs(lse[b].double().numpy() - ref_lse)) <= TOL[w.dtype]
+        check(out[b], ref, TOL[w.dtype])
+        check_lse(lse[b].double().numpy(), ref_lse, TOL[w.dtype])
 
 
 def test_prefill_4k_sampled_rows():
@@ -79,8 +78,8 @@ def test_prefill_4k_sampled_rows():
                                                   wts["w_uv"], w.n_groups, w.d_c, w.d_v, BASE,
                                                   heads=heads)
             got = out[b, i, heads]
-            assert rel_err(got, ref[0]) <= TOL[w.dtype], (b, i)
-            assert np.max(np.abs(lse[b, i, heads].double().numpy() - ref_lse[0])) <= TOL[w.dtype]
+            check(got, ref[0], TOL[w.dtype], f"(b, i) = {(b, i)}")
+            check_lse(lse[b, i, heads].double().numpy(), ref_lse[0], TOL[w.dtype])
 
 
 def test_prefill_equals_expand_then_grouped_decode():
@@ -121,5 +120,5 @@ def test_prefill_kernel_block_size_32_and_eight_heads_per_group():
         ref, ref_lse = O.decode_reconstructed(q["q_nope"][b], q["q_pe"][b], qpos[b], rows,
                                               wts["w_uk"], wts["w_uv"], w.n_groups, w.d_c,
                                               w.d_v, BASE)
-        assert rel_err(out[b], ref) <= TOL[w.dtype]
-        assert np.max(np.abs(lse[b].double().numpy() - ref_lse)) <= TOL[w.dtype]
+        check(out[b], ref, TOL[w.dtype])
+        check_lse(lse[b].double().numpy(), ref_lse, TOL[w.dtype])

@@ -45,10 +45,17 @@ def test_choices_follow_the_summary():
     # H20: the GQA path, g = 8 with s_q = 2 or g = 4 with s_q = 1
     assert M.mla_select_path(dims(8), 2, L, *H20)[0] == M.MLA_PATH_GQA
     assert M.mla_select_path(dims(4), 1, L, *H20)[0] == M.MLA_PATH_GQA
-    # MI355X (defaults): absorbed for g = 8 up to s_q = 4, GQA from s_q = 8 on
-    for s_q in (1, 2, 4):
+
+
+def test_default_rates_pick_the_measured_faster_path():
+    """MI355X defaults (the rates the kernels sustain) at H = 128, G = 8 and 32,768 cached
+    positions: the absorbed path for s_q = 1 and 2, the GQA path for s_q = 4 and 8, which is
+    what timing both paths on the chip shows."""
+    L = 32768
+    for s_q in (1, 2):
         assert M.mla_select_path(dims(8), s_q, L)[0] == M.MLA_PATH_ABSORBED
-    assert M.mla_select_path(dims(8), 8, L)[0] == M.MLA_PATH_GQA
+    for s_q in (4, 8):
+        assert M.mla_select_path(dims(8), s_q, L)[0] == M.MLA_PATH_GQA
 
 
 def test_degenerate_group_counts():

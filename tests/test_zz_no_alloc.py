@@ -3,12 +3,12 @@ against mla_decode with a caller workspace, through the C ABI: two calls in a ro
 with a smaller input, so that the array still holds the first call's larger contents. Both run
 the same kernels with the same split plan, so the outputs must be bit-identical; each is also
 held to the oracle's bound."""
-import numpy as np
 import pytest
 import torch
 
 import workloads as W
-from gpu_cases import TOL, decode_case, dev, note, oracle_decode, rel_err, run_decode, stream_tag
+from gpu_cases import (TOL, check_lse, check_per_seq, decode_case, dev, note, oracle_decode,
+                       run_decode, stream_tag)
 from mla_latent_kv_21_amd import binding as M
 
 pytestmark = [pytest.mark.gpu,
@@ -47,7 +47,5 @@ def test_noalloc_matches_workspace_decode(wl, lens1, lens2, s_q, n_split):
         assert torch.equal(got, ref_out), "differs from mla_decode with a caller workspace"
         assert torch.equal(got_lse, ref_lse)
         oracle_out, oracle_lse = oracle_decode(c)
-        err = rel_err(got, oracle_out)
-        note(f"  rel_err vs oracle {err:.3e}")
-        assert err <= TOL[w.dtype]
-        assert np.max(np.abs(got_lse.double().numpy() - oracle_lse)) <= TOL[w.dtype]
+        check_per_seq(got, oracle_out, TOL[w.dtype])
+        check_lse(got_lse.double().numpy(), oracle_lse, TOL[w.dtype])
