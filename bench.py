@@ -2,9 +2,10 @@
 """Benchmark of one absorbed MLA decode step on one MI355X.
 
 A step is one pass of the whole decode path over one batch: append the step's new positions to
-the paged latent cache (W_DKV projection, RMSNorm, RoPE on k_r), carry the queries into latent
-space (W_UK absorption + RoPE), the split-K attention core over [c || k_r], and the log-sum-exp
-merge with the W_UV projection. Inputs are seeded synthetic tensors already resident in HBM.
+the paged latent cache (W_DKV projection, RMSNorm, RoPE on k_r) and carry the queries into latent
+space (W_UK absorption + RoPE), the absorption sharing the projection's launch; the split-K
+attention core over [c || k_r];
+and the log-sum-exp merge with the W_UV projection. Inputs are seeded synthetic tensors already resident in HBM.
 
 Prints one JSON line: tokens/s (query tokens per second, one layer), the dominant kernel's
 roofline (the split-K core, timed with HIP events on the stream it runs on) and the CPU
@@ -114,6 +115,62 @@ def _copies(cache_bytes: int) -> int:
     """Independent cache copies to rotate through so that >= 1 GiB separates two reads of one
     copy (none needed for caches of 1 GiB or more)."""
     return max(1, -(-ROTATE_BYTES // cache_bytes))
+
+
+def _smi_sample():
+    """(socket power W, mean gfx clock MHz) from one amd-smi reading, or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "-p", "-c", "--json"],
+                           capture_output=True, text=True, timeout=5)
+        j = json.loads(r.stdout)
+        g = j["gpu_data"][0] if isinstance(j, dict) else j[0]
+        pw = float(g["power"]["socket_power"]["value"])
+        clks = [float(v["clk"]["value"]) for k, v in g["clock"].items()
+                if k.startswith("gfx") and isinstance(v, dict) and "clk" in v]
+        return pw, (sum(clks) / len(clks) if clks else None)
+    except Exception:  # amd-smi missing or its output changed: no reading
+        return None
+
+
+def power_sample(fn, seconds: float, torch):
+    """Board power and shader clock while fn() (the split-K core) runs back to back for about
+    `seconds`, from amd-smi readings taken every ~50 ms by a helper thread, beside the idle
+    reading before it. The core's mean launch time over the window comes from two events."""
+    import threading
+    idle = [x for x in (_smi_sample() for _ in range(3)) if x]
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            x = _smi_sample()
+            if x:
+                samples.append(x)
+            time.sleep(0.05)
+    fn(); torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    th = threading.Thread(target=sampler)
+    th.start()
+    time.sleep(0.2)
+    n, t0 = 0, time.perf_counter()
+    a.record(torch.cuda.current_stream())
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            fn()
+        n += 50
+        torch.cuda.synchronize()
+    b.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    busy = samples[len(samples) // 4:]   # readings lag the load by a few samples
+    if not idle or not busy:
+        return None
+    return {"idle_W": float(np.mean([x[0] for x in idle])),
+            "busy_W": float(np.mean([x[0] for x in busy])),
+            "busy_gfx_clock_MHz": float(np.mean([x[1] for x in busy if x[1]])),
+            "launches": n, "mean_launch_ms": a.elapsed_time(b) / n,
+            "readings": len(busy), "source": "amd-smi metric -p -c, every ~50 ms"}
 
 
 def absorbed_row(dev, torch, w, planned=True, reps=20):
@@ -350,6 +407,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long-128k",
                     help="workload name (default long-128k: H=128, d_c=512, 4 x 131,072 context)")
+    ap.add_argument("--s-q", type=int, default=0,
+                    help="query tokens per sequence in the step (default: the workload's)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
@@ -357,6 +416,9 @@ def main():
     ap.add_argument("--rows", choices=("all", "layer", "prefill", "none"), default="all",
                     help="rows timed after the step: all of them, only the decode layer, only "
                          "the prefill, or none")
+    ap.add_argument("--power-seconds", type=float, default=2.0,
+                    help="run the split-K core back to back for this long while sampling board "
+                         "power and shader clock with amd-smi (0: skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the timed steps, copy a bf16 buffer of this many MiB three "
                          "times (a plain copy of known size for scaling HBM byte counters)")
@@ -377,6 +439,8 @@ def main():
         build()
     dev = torch.device("cuda:0")
     w = W.WORKLOADS[args.workload]
+    if args.s_q > 0:
+        w = w.replace(s_q=args.s_q)
     lens = W.seq_lens(w)
     table, nb = W.block_table(w, lens)
     B, s_q, H = w.batch, w.s_q, w.n_heads
@@ -395,7 +459,9 @@ def main():
     q_abs = torch.empty(B, s_q, H, w.row, dtype=w.torch_dtype, device=dev)
     out = torch.empty(B, s_q, H, w.d_v, dtype=w.torch_dtype, device=dev)
     lse = torch.empty(B, s_q, H, dtype=torch.float32, device=dev)
-    ns = w.n_split or M.mla_auto_split(d, B, s_q, table.shape[1])
+    # the workload's split count, else 0: the library's choice (the length-balanced plan
+    # where it applies, as the rows below time it)
+    ns = w.n_split
     ws = torch.empty(M.mla_decode_workspace_bytes(d, B, s_q, ns, table.shape[1]),
                      dtype=torch.uint8, device=dev)
     ws_app = torch.empty(max(M.mla_cache_append_workspace_bytes(d, B * s_q), 256),
@@ -404,9 +470,9 @@ def main():
     n_steps = args.steps
 
     def step():
-        M.mla_cache_append(d, x_new, seq_idx, pos_new, wts["w_dkv"], wts["gamma"], wts["w_kr"],
-                           tab, nb, cache, workspace=ws_app)
-        M.mla_absorb_q(d, q["q_nope"], q["q_pe"], q_pos, wts["w_uk"], q_abs)
+        M.mla_cache_append_absorb_q(d, x_new, seq_idx, pos_new, wts["w_dkv"], wts["gamma"],
+                                    wts["w_kr"], tab, nb, cache, q["q_nope"], q["q_pe"], q_pos,
+                                    wts["w_uk"], q_abs, workspace=ws_app)
         M.mla_decode_splitk(d, q_abs, cache, tab, lens_d, ns, ws)
         M.mla_decode_merge(d, q_abs, cache, tab, lens_d, wts["w_uv"], out, lse, ns, ws)
 
@@ -445,7 +511,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "s_q": s_q, "heads": H, "groups": w.n_groups,
                    "d_c": w.d_c, "d_r": w.d_r, "context": int(lens.max()),
                    "context_total": int(lens.sum()), "block_size": w.block_size,
-                   "n_split": ns, "d_model": w.d_model},
+                   "n_split": ns if ns else "planned", "d_model": w.d_model},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "decode_mfma_kernel (split-K core)", "launch_ms": core_ms,
@@ -458,6 +524,10 @@ def main():
         "step_latent_cache_GBps": tr["cache_bytes"] / (ms_step * 1e-3) / 1e9,
         "wall_s": wall,
     }
+    if args.power_seconds > 0:
+        rec["roofline"]["power"] = power_sample(
+            lambda: M.mla_decode_splitk(d, q_abs, cache, tab, lens_d, ns, ws), args.power_seconds,
+            torch)
     rows = "none" if args.no_rows else args.rows
     if rows != "none":
         rec["rows"] = measure_rows(dev, torch) if rows == "all" else {}

@@ -125,6 +125,24 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, int32_t s_q, const 
                         hipStream_t stream);
 
 /*
+ * mla_cache_append_absorb_q -- mla_cache_append(dims, n_tok, x, ..., workspace, ws_bytes)
+ *  followed by mla_absorb_q(dims, batch, s_q, q_nope, q_pe, q_pos, w_uk, q_abs), the two
+ *  independent calls that open a decode step. On the matrix-core path (bf16) the absorption
+ *  runs in the same launch as the append's projection (two launches for both instead of
+ *  three); otherwise the two calls run in order. batch is both the block table's row count and
+ *  the number of query sequences. Arguments, results, errors and the workspace are those of
+ *  the two calls.
+ */
+mla_status mla_cache_append_absorb_q(const mla_dims* dims, int32_t n_tok, const void* x,
+                                     const int32_t* seq_idx, const int32_t* pos,
+                                     const void* w_dkv, const void* rms_gamma, const void* w_kr,
+                                     const int32_t* block_table, int32_t batch,
+                                     int32_t max_blocks, int32_t num_blocks, void* latent_cache,
+                                     void* workspace, size_t ws_bytes, int32_t s_q,
+                                     const void* q_nope, const void* q_pe, const int32_t* q_pos,
+                                     const void* w_uk, void* q_abs, hipStream_t stream);
+
+/*
  * mla_decode -- absorbed decode over the latent cache ([Smallem] "Ce que DeepSeek fait de plus";
  * [GQLA] "Chemin MQA-Absorbé"): for every sequence b, query i and head h,
  *     z_t = scale * (q_abs[b,i,h] . row_t)          for visible positions t

@@ -25,6 +25,7 @@ STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTY
           -4: "MLA_ERR_RANGE", -5: "MLA_ERR_WORKSPACE", -6: "MLA_ERR_ALIGN", -7: "MLA_ERR_HIP",
           -8: "MLA_ERR_BLOCK_TABLE"}
 EXPORTS = ["mla_cache_append_workspace_bytes", "mla_cache_append", "mla_absorb_q",
+           "mla_cache_append_absorb_q",
            "mla_query_project_workspace_bytes", "mla_query_project",
            "mla_output_project_workspace_bytes", "mla_output_project",
            "mla_decode_workspace_bytes", "mla_decode", "mla_decode_splitk", "mla_decode_merge",
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
             "mla_cache_append_workspace_bytes": (S, [D, I]),
             "mla_cache_append": (I, [D, I, P, P, P, P, P, P, P, I, I, I, P, P, S, P]),
             "mla_absorb_q": (I, [D, I, I, P, P, P, P, P, P]),
+            "mla_cache_append_absorb_q": (I, [D, I, P, P, P, P, P, P, P, I, I, I, P, P, S, I, P,
+                                              P, P, P, P, P]),
             "mla_query_project_workspace_bytes": (S, [D, I, I]),
             "mla_query_project": (I, [D, I, I, P, P, P, P, P, P, P, P, S, P]),
             "mla_output_project_workspace_bytes": (S, [D, I]),
@@ -145,6 +148,24 @@ def mla_cache_append(dims, x, seq_idx, pos, w_dkv, gamma, w_kr, block_table, num
                                 block_table.shape[0], block_table.shape[1], num_blocks,
                                 _ptr(latent_cache), _ptr(workspace), workspace.numel(), _stream())
     _check(st, "mla_cache_append")
+
+
+def mla_cache_append_absorb_q(dims, x, seq_idx, pos, w_dkv, gamma, w_kr, block_table,
+                              num_blocks, latent_cache, q_nope, q_pe, q_pos, w_uk, q_abs,
+                              workspace=None):
+    """mla_cache_append then mla_absorb_q (the absorption in the projection's launch)."""
+    n_tok = x.shape[0]
+    B, s_q = q_nope.shape[0], q_nope.shape[1]
+    if block_table.shape[0] != B:
+        raise ValueError("the block table's rows and the query batch must agree")
+    if workspace is None:
+        workspace = _workspace(mla_cache_append_workspace_bytes(dims, n_tok), x.device)
+    st = lib().mla_cache_append_absorb_q(
+        ctypes.byref(dims), n_tok, _ptr(x), _ptr(seq_idx), _ptr(pos), _ptr(w_dkv), _ptr(gamma),
+        _ptr(w_kr), _ptr(block_table), B, block_table.shape[1], num_blocks, _ptr(latent_cache),
+        _ptr(workspace), workspace.numel(), s_q, _ptr(q_nope), _ptr(q_pe), _ptr(q_pos),
+        _ptr(w_uk), _ptr(q_abs), _stream())
+    _check(st, "mla_cache_append_absorb_q")
 
 
 def mla_query_project_workspace_bytes(dims, n_tok, d_q) -> int:

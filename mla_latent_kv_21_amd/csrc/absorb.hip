@@ -5,6 +5,7 @@
 // bf16 runs on matrix cores (absorb_mfma); the portable kernel (fp32, or other shapes) uses
 // one workgroup per (head, 16 query rows): the head's d_c x D slice of W_UK is read once per
 // 16 rows and every thread produces whole latent columns for all 16 rows.
+#include "absorb_tile.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -63,92 +64,39 @@ __global__ __launch_bounds__(256) void absorb_kernel(const T* __restrict__ q_nop
   }
 }
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
-
-// bf16 absorption on matrix cores: per head, Q_lat[32 rows x d_c] = q_nope[32 x D] ·
-// W_UK[:, g]^T, i.e. a product whose operands are both contiguous along the contraction
-// (rows of q_nope and rows of W_UK), so MFMA fragments load straight from memory. One
-// workgroup per (head, 32 rows, 128 latent columns); wave w computes one 32-column block.
-__global__ __launch_bounds__(256) void absorb_mfma(const uint16_t* __restrict__ q_nope,
-                                                   const uint16_t* __restrict__ q_pe,
-                                                   const int32_t* __restrict__ q_pos,
-                                                   const uint16_t* __restrict__ w_uk, int M,
-                                                   int H, int G, int D, int d_c, int d_r,
-                                                   float base, uint16_t* __restrict__ q_abs) {
-  const int h = blockIdx.x, m0 = blockIdx.y * 32;
-  const int g = h / (H / G);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int row = d_c + d_r;
-  const int ksteps = D / 16;  // at most 16 (D <= 256)
-  const int m = m0 + l32;
-  bf16x8 af[16];
-  const bf16x8 zero = {};
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
-    af[ks] = zero;
-    if (ks < ksteps && m < M)
-      af[ks] = *reinterpret_cast<const bf16x8*>(q_nope + (static_cast<int64_t>(m) * H + h) * D +
-                                                16 * ks + 8 * hi);
-  }
-  const int64_t ldw = static_cast<int64_t>(G) * D;
-  // B fragments of one 32-column block: all requested before the first MFMA
-  bf16x8 bv[16];
-  auto load_b = [&](int nb) __attribute__((always_inline)) {
-    const uint16_t* wr = w_uk + (nb * 32 + l32) * ldw + static_cast<int64_t>(g) * D + 8 * hi;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks)
-      bv[ks] = ks < ksteps ? *reinterpret_cast<const bf16x8*>(wr + 16 * ks) : zero;
-  };
-  int nb = 4 * blockIdx.z + w;
-  const int nb_end = min(d_c / 32, 4 * static_cast<int>(blockIdx.z) + 4);
-  if (nb < nb_end) load_b(nb);
-
-  // rotary part, while the first block's fragments are in flight: the (row, pair) items are
-  // shared out over the z-blocks of this head
-  const int half = d_r / 2;
-  for (int e = threadIdx.x + blockIdx.z * blockDim.x; e < 32 * half; e += blockDim.x * gridDim.z) {
-    const int r = e / half, jj = e % half;
-    const int mm = m0 + r;
-    if (mm >= M) continue;
-    float cs, sn;
-    rope_cos_sin(q_pos[mm], jj, d_r, base, &cs, &sn);
-    const int64_t src = (static_cast<int64_t>(mm) * H + h) * d_r + 2 * jj;
-    const float x0 = bf16_to_f32(q_pe[src]), x1 = bf16_to_f32(q_pe[src + 1]);
-    const int64_t dst = (static_cast<int64_t>(mm) * H + h) * row + d_c + 2 * jj;
-    q_abs[dst] = f32_to_bf16(x0 * cs - x1 * sn);
-    q_abs[dst + 1] = f32_to_bf16(x0 * sn + x1 * cs);
-  }
-
-  while (nb < nb_end) {
-    const int j = nb * 32 + l32;
-    f32x16 acc = {};
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks)
-      if (ks < ksteps) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], bv[ks], acc, 0, 0, 0);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int mm = m0 + 8 * (r >> 2) + 4 * hi + (r & 3);
-      if (mm < M) q_abs[(static_cast<int64_t>(mm) * H + h) * row + j] = f32_to_bf16(acc[r]);
-    }
-    nb += 4;
-    if (nb < nb_end) load_b(nb);
-  }
+// One workgroup per absorb tile (absorb_tile.hpp).
+__global__ __launch_bounds__(256) void absorb_mfma(AbsorbArgs q) {
+  absorb_tile_mfma(q, blockIdx.x, blockIdx.y * 32, blockIdx.z, gridDim.z);
 }
 
 }  // namespace
+
+bool absorb_mfma_fits(const mla_dims& d) {
+  return d.dtype == MLA_BF16 && !(d.flags & MLA_FLAG_GENERIC_KERNELS) && d.d_c % 32 == 0 &&
+         d.d_nope % 16 == 0 && d.d_nope <= 256;
+}
+
+AbsorbArgs absorb_args(const mla_dims& d, int M, const void* q_nope, const void* q_pe,
+                       const int32_t* q_pos, const void* w_uk, void* q_abs) {
+  AbsorbArgs q;
+  q.q_nope = static_cast<const uint16_t*>(q_nope);
+  q.q_pe = static_cast<const uint16_t*>(q_pe);
+  q.q_pos = q_pos;
+  q.w_uk = static_cast<const uint16_t*>(w_uk);
+  q.M = M; q.H = d.n_heads; q.G = d.n_groups; q.D = d.d_nope; q.d_c = d.d_c; q.d_r = d.d_r;
+  q.base = d.rope_base;
+  q.q_abs = static_cast<uint16_t*>(q_abs);
+  return q;
+}
 
 hipError_t launch_absorb(const mla_dims& d, int batch, int s_q, const void* q_nope,
                          const void* q_pe, const int32_t* q_pos, const void* w_uk, void* q_abs,
                          hipStream_t s) {
   const int M = batch * s_q;
-  if (d.dtype == MLA_BF16 && !(d.flags & MLA_FLAG_GENERIC_KERNELS) && d.d_c % 32 == 0 &&
-      d.d_nope % 16 == 0 && d.d_nope <= 256) {
-    hipLaunchKernelGGL(absorb_mfma, dim3(d.n_heads, cdiv(M, 32), cdiv(d.d_c / 32, 4)), dim3(256), 0, s,
-                       static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_pe),
-                       q_pos, static_cast<const uint16_t*>(w_uk), M, d.n_heads, d.n_groups,
-                       d.d_nope, d.d_c, d.d_r, d.rope_base, static_cast<uint16_t*>(q_abs));
+  if (absorb_mfma_fits(d)) {
+    const AbsorbArgs q = absorb_args(d, M, q_nope, q_pe, q_pos, w_uk, q_abs);
+    hipLaunchKernelGGL(absorb_mfma, dim3(d.n_heads, cdiv(M, 32), cdiv(d.d_c / 32, 4)), dim3(256), 0,
+                       s, q);
     return hipGetLastError();
   }
   const dim3 grid(d.n_heads, cdiv(M, kRows));

@@ -108,19 +108,20 @@ int32_t mla_select_path(const mla_dims* dims, int32_t s_q, int64_t context,
 
 size_t mla_cache_append_workspace_bytes(const mla_dims* dims, int32_t n_tok) {
   if (check_dims(dims) != MLA_OK || n_tok < 0) return 0;
-  const mla::AppendPlan p = mla::append_plan(*dims, n_tok);
-  const size_t n = n_tok < 2048 ? n_tok : 2048;  // tokens per pass
-  return static_cast<size_t>(p.n_ksplit) * n * (dims->d_c + dims->d_r) * sizeof(float);
+  return mla::append_ws_bytes(*dims, n_tok);
 }
 
-mla_status mla_cache_append(const mla_dims* dims, int32_t n_tok, const void* x,
-                            const int32_t* seq_idx, const int32_t* pos, const void* w_dkv,
-                            const void* rms_gamma, const void* w_kr, const int32_t* block_table,
-                            int32_t batch, int32_t max_blocks, int32_t num_blocks,
-                            void* latent_cache, void* workspace, size_t ws_bytes,
-                            hipStream_t stream) {
-  mla_status st = check_dims(dims);
-  if (st != MLA_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// Host checks of mla_cache_append (dims already checked); MLA_OK with n_tok == 0 means
+// nothing to do.
+mla_status check_append(const mla_dims* dims, int32_t n_tok, const void* x,
+                        const int32_t* seq_idx, const int32_t* pos, const void* w_dkv,
+                        const void* rms_gamma, const void* w_kr, const int32_t* block_table,
+                        int32_t batch, int32_t max_blocks, int32_t num_blocks,
+                        const void* latent_cache, const void* workspace, size_t ws_bytes) {
   if (n_tok < 0 || batch < 0 || max_blocks < 1 || num_blocks < 1) return MLA_ERR_RANGE;
   if (n_tok == 0) return MLA_OK;
   if (!x || !seq_idx || !pos || !w_dkv || !rms_gamma || !block_table || !latent_cache ||
@@ -134,6 +135,38 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t n_tok, const void* x,
   const size_t need = mla_cache_append_workspace_bytes(dims, n_tok);
   if (workspace == nullptr || ws_bytes < need) return MLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MLA_ERR_ALIGN;
+  return MLA_OK;
+}
+
+// Host checks of mla_absorb_q (dims already checked); MLA_OK with batch == 0 means nothing
+// to do.
+mla_status check_absorb(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_nope,
+                        const void* q_pe, const int32_t* q_pos, const void* w_uk,
+                        const void* q_abs) {
+  if (batch < 0 || s_q < 1) return MLA_ERR_RANGE;
+  if (batch == 0) return MLA_OK;
+  if (!q_nope || !q_pos || !w_uk || !q_abs || (dims->d_r > 0 && !q_pe)) return MLA_ERR_NULL;
+  if (static_cast<int64_t>(batch) * s_q > 65535 * 16) return MLA_ERR_RANGE;
+  if (!aligned16(q_nope) || (q_pe && !aligned16(q_pe)) || !aligned16(w_uk) || !aligned16(q_abs))
+    return MLA_ERR_ALIGN;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_cache_append(const mla_dims* dims, int32_t n_tok, const void* x,
+                            const int32_t* seq_idx, const int32_t* pos, const void* w_dkv,
+                            const void* rms_gamma, const void* w_kr, const int32_t* block_table,
+                            int32_t batch, int32_t max_blocks, int32_t num_blocks,
+                            void* latent_cache, void* workspace, size_t ws_bytes,
+                            hipStream_t stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  st = check_append(dims, n_tok, x, seq_idx, pos, w_dkv, rms_gamma, w_kr, block_table, batch,
+                    max_blocks, num_blocks, latent_cache, workspace, ws_bytes);
+  if (st != MLA_OK || n_tok == 0) return st;
   return hip_status(mla::launch_append(*dims, n_tok, x, seq_idx, pos, w_dkv, rms_gamma, w_kr,
                                        block_table, batch, max_blocks, num_blocks, latent_cache,
                                        workspace, stream));
@@ -144,13 +177,34 @@ mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, int32_t s_q, const 
                         hipStream_t stream) {
   mla_status st = check_dims(dims);
   if (st != MLA_OK) return st;
-  if (batch < 0 || s_q < 1) return MLA_ERR_RANGE;
-  if (batch == 0) return MLA_OK;
-  if (!q_nope || !q_pos || !w_uk || !q_abs || (dims->d_r > 0 && !q_pe)) return MLA_ERR_NULL;
-  if (static_cast<int64_t>(batch) * s_q > 65535 * 16) return MLA_ERR_RANGE;
-  if (!aligned16(q_nope) || (q_pe && !aligned16(q_pe)) || !aligned16(w_uk) || !aligned16(q_abs))
-    return MLA_ERR_ALIGN;
+  st = check_absorb(dims, batch, s_q, q_nope, q_pe, q_pos, w_uk, q_abs);
+  if (st != MLA_OK || batch == 0) return st;
   return hip_status(mla::launch_absorb(*dims, batch, s_q, q_nope, q_pe, q_pos, w_uk, q_abs, stream));
+}
+
+mla_status mla_cache_append_absorb_q(const mla_dims* dims, int32_t n_tok, const void* x,
+                                     const int32_t* seq_idx, const int32_t* pos,
+                                     const void* w_dkv, const void* rms_gamma, const void* w_kr,
+                                     const int32_t* block_table, int32_t batch,
+                                     int32_t max_blocks, int32_t num_blocks, void* latent_cache,
+                                     void* workspace, size_t ws_bytes, int32_t s_q,
+                                     const void* q_nope, const void* q_pe, const int32_t* q_pos,
+                                     const void* w_uk, void* q_abs, hipStream_t stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  st = check_append(dims, n_tok, x, seq_idx, pos, w_dkv, rms_gamma, w_kr, block_table, batch,
+                    max_blocks, num_blocks, latent_cache, workspace, ws_bytes);
+  if (st != MLA_OK) return st;
+  st = check_absorb(dims, batch, s_q, q_nope, q_pe, q_pos, w_uk, q_abs);
+  if (st != MLA_OK) return st;
+  if (n_tok == 0 && batch == 0) return MLA_OK;
+  if (n_tok == 0)
+    return hip_status(mla::launch_absorb(*dims, batch, s_q, q_nope, q_pe, q_pos, w_uk, q_abs,
+                                         stream));
+  return hip_status(mla::launch_append_absorb(*dims, n_tok, x, seq_idx, pos, w_dkv, rms_gamma,
+                                              w_kr, block_table, batch, max_blocks, num_blocks,
+                                              latent_cache, workspace, batch, s_q, q_nope, q_pe,
+                                              q_pos, w_uk, q_abs, stream));
 }
 
 size_t mla_query_project_workspace_bytes(const mla_dims* dims, int32_t n_tok, int32_t d_q) {

@@ -6,6 +6,7 @@
 // projection is bound by reading the 2*C*(d_c+d_r)-byte weights, so it is spread over many
 // workgroups even for a handful of tokens), then one workgroup per token that sums the
 // partials in a fixed order, normalises, rotates and stores the row at its slot.
+#include "absorb_tile.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -132,17 +133,15 @@ constexpr int kWtStride = kKStage * 2 + 16;  // bytes per transposed weight colu
 //  * A operand (tokens x k): rows of x, 16 bytes per lane straight from memory;
 //  * B operand (k x columns): the weight tile is staged in LDS transposed (column-major, rows
 //    padded to 528 bytes), so each lane's 8 consecutive k of one column are one 16-byte read.
-__global__ __launch_bounds__(256) void append_project_mfma(const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ w_a,
-                                                           const uint16_t* __restrict__ w_b,
-                                                           int n_tok, int C, int n_a, int n_b,
-                                                           float* __restrict__ y_part) {
+__device__ inline void project_tile_mfma(const uint16_t* __restrict__ x,
+                                         const uint16_t* __restrict__ w_a,
+                                         const uint16_t* __restrict__ w_b, int n_tok, int C,
+                                         int n_a, int n_b, float* __restrict__ y_part, int cbk,
+                                         int ks, int n0) {
   __shared__ __attribute__((aligned(16))) char wt[kColTile * kWtStride];
   __shared__ float half1[2][16][64];
   const int ncols = n_a + n_b;
-  const int c0 = blockIdx.x * kColTile;
-  const int ks = blockIdx.y;
-  const int n0 = blockIdx.z * 32;
+  const int c0 = cbk * kColTile;
   const int k0 = ks * kKStage;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
@@ -208,6 +207,15 @@ __global__ __launch_bounds__(256) void append_project_mfma(const uint16_t* __res
   }
 }
 
+__global__ __launch_bounds__(256) void append_project_mfma(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ w_a,
+                                                           const uint16_t* __restrict__ w_b,
+                                                           int n_tok, int C, int n_a, int n_b,
+                                                           float* __restrict__ y_part) {
+  project_tile_mfma(x, w_a, w_b, n_tok, C, n_a, n_b, y_part, blockIdx.x, blockIdx.y,
+                    blockIdx.z * 32);
+}
+
 template <typename T>
 __global__ __launch_bounds__(1024) void append_finalize(
     const float* __restrict__ y_part, int n_ksplit, int n_tok, const T* __restrict__ gamma,
@@ -215,30 +223,42 @@ __global__ __launch_bounds__(1024) void append_finalize(
     const int32_t* __restrict__ table, int batch, int max_blocks, int num_blocks, int bs,
     int d_c, int d_r, float eps, float base, T* __restrict__ cache) {
   extern __shared__ float ys[];  // [d_c + d_r]
-  __shared__ float red[16];
+  __shared__ float red[64];
   const int n = blockIdx.x;
   const int ncols = d_c + d_r;
   // the row's slot first: its dependent loads (sequence, position, block table) overlap the
   // partial sums below
   const int b = seq_idx[n], p = pos[n];
   const int64_t slot = (b < 0 || b >= batch) ? -1 : cache_slot(table, max_blocks, bs, num_blocks, b, p);
-  float ss = 0.f;
   for (int c = threadIdx.x; c < ncols; c += blockDim.x) {
-    // partial sums added in the fixed order k = 0, 1, ...; sixteen loads in flight
+    // partial sums added in the fixed order k = 0, 1, ...; up to 32 loads in flight
     float y = 0.f;
-    for (int k = 0; k < n_ksplit; k += 16) {
-      float v[16];
+    for (int k = 0; k < n_ksplit; k += 32) {
+      float v[32];
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
+      for (int u = 0; u < 32; ++u)
         v[u] = k + u < n_ksplit ? y_part[(static_cast<int64_t>(k + u) * n_tok + n) * ncols + c] : 0.f;
 #pragma unroll
-      for (int u = 0; u < 16; ++u)
+      for (int u = 0; u < 32; ++u)
         if (k + u < n_ksplit) y += v[u];
     }
     ys[c] = y;
-    if (c < d_c) ss += y * y;
   }
-  ss = block_sum(ss, red);  // also orders the ys writes before the reads below
+  __syncthreads();
+  // sum of squares of the latent part: each 64-column block in column order, then the blocks
+  // in order (a fixed order, independent of the block size)
+  const int lat_blocks = cdiv(d_c, kColTile);
+  if (static_cast<int>(threadIdx.x) < lat_blocks) {
+    float s2 = 0.f;
+    for (int cc = 0; cc < kColTile; ++cc) {
+      const int c = threadIdx.x * kColTile + cc;
+      s2 += c < d_c ? ys[c] * ys[c] : 0.f;
+    }
+    red[threadIdx.x] = s2;
+  }
+  __syncthreads();
+  float ss = 0.f;
+  for (int j = 0; j < lat_blocks; ++j) ss += red[j];
   if (slot < 0) return;
   const float inv = 1.0f / sqrtf(ss / static_cast<float>(d_c) + eps);
   T* row = cache + slot * ncols;
@@ -250,6 +270,34 @@ __global__ __launch_bounds__(1024) void append_finalize(
     st(row, d_c + 2 * j, a * cs - q * sn);
     st(row, d_c + 2 * j + 1, a * sn + q * cs);
   }
+}
+
+
+// ---- the append's projection and the query absorption of a decode step in one launch.
+//
+// Both are weight streams with no dependency on each other (W_DKV | W_KR for the new tokens,
+// W_UK for the queries), each too small to fill the chip for long: run as one grid, the
+// absorb tiles fill the CUs the projection leaves idle and the step saves a launch. The
+// append's finalize (sum of the partials in k order, RMSNorm, RoPE, store) follows as before.
+__global__ __launch_bounds__(256) void project_absorb(const uint16_t* __restrict__ x,
+                                                      const uint16_t* __restrict__ w_a,
+                                                      const uint16_t* __restrict__ w_b,
+                                                      int n_tok, int C, int n_a, int n_b,
+                                                      float* __restrict__ y_part, int col_blocks,
+                                                      int n_ksplit, AbsorbArgs q, int absorb_rb,
+                                                      int absorb_zb) {
+  const int n_proj = col_blocks * n_ksplit * cdiv(n_tok, 32);
+  if (static_cast<int>(blockIdx.x) >= n_proj) {
+    // an absorb tile: z fastest, then the 32-row block, then the head
+    int t = blockIdx.x - n_proj;
+    const int z = t % absorb_zb;
+    t /= absorb_zb;
+    absorb_tile_mfma(q, t / absorb_rb, (t % absorb_rb) * 32, z, absorb_zb);
+    return;
+  }
+  const int t = blockIdx.x;
+  const int cb = t % col_blocks, ks = (t / col_blocks) % n_ksplit, nt = t / (col_blocks * n_ksplit);
+  project_tile_mfma(x, w_a, w_b, n_tok, C, n_a, n_b, y_part, cb, ks, 32 * nt);
 }
 
 }  // namespace
@@ -292,10 +340,28 @@ AppendPlan append_plan(const mla_dims& d, int n_tok) {
   return p;
 }
 
+size_t append_ws_bytes(const mla_dims& d, int n_tok) {
+  const AppendPlan p = append_plan(d, n_tok);
+  const size_t n = n_tok < kMaxTok ? n_tok : kMaxTok;
+  return static_cast<size_t>(p.n_ksplit) * n * (d.d_c + d.d_r) * sizeof(float);
+}
+
 hipError_t launch_append(const mla_dims& d, int n_tok, const void* x, const int32_t* seq_idx,
                          const int32_t* pos, const void* w_dkv, const void* gamma,
                          const void* w_kr, const int32_t* table, int batch, int max_blocks,
                          int num_blocks, void* cache, void* ws, hipStream_t s) {
+  return launch_append_absorb(d, n_tok, x, seq_idx, pos, w_dkv, gamma, w_kr, table, batch,
+                              max_blocks, num_blocks, cache, ws, 0, 0, nullptr, nullptr, nullptr,
+                              nullptr, nullptr, s);
+}
+
+hipError_t launch_append_absorb(const mla_dims& d, int n_tok, const void* x,
+                                const int32_t* seq_idx, const int32_t* pos, const void* w_dkv,
+                                const void* gamma, const void* w_kr, const int32_t* table,
+                                int batch, int max_blocks, int num_blocks, void* cache, void* ws,
+                                int q_batch, int s_q, const void* q_nope, const void* q_pe,
+                                const int32_t* q_pos, const void* w_uk, void* q_abs,
+                                hipStream_t s) {
   float* y_part = static_cast<float*>(ws);
   const size_t lds = static_cast<size_t>(d.d_c + d.d_r) * sizeof(float);
   const size_t elt = d.dtype == MLA_BF16 ? 2 : 4;
@@ -303,23 +369,38 @@ hipError_t launch_append(const mla_dims& d, int n_tok, const void* x, const int3
   const dim3 fin_block(ncols >= 1024 ? 1024 : (ncols + 63) / 64 * 64);
   // matrix-core projection: every 16-byte weight and activation load stays inside one row
   // and one of the two weight matrices (16-byte-aligned base pointers are a library rule)
-  const bool mfma_ok = !(d.flags & MLA_FLAG_GENERIC_KERNELS) && d.d_model % 8 == 0 &&
-                       d.d_c % 8 == 0 && d.d_r % 8 == 0;
+  const bool mfma_ok = d.dtype == MLA_BF16 && !(d.flags & MLA_FLAG_GENERIC_KERNELS) &&
+                       d.d_model % 8 == 0 && d.d_c % 8 == 0 && d.d_r % 8 == 0;
+  const int M = q_batch * s_q;
+  // the absorption rides along with the first pass of the projection where both run on the
+  // matrix cores; otherwise it is launched on its own after the append
+  bool absorb_pending = M > 0;
   for (int t0 = 0; t0 < n_tok; t0 += kMaxTok) {
     const int n = n_tok - t0 < kMaxTok ? n_tok - t0 : kMaxTok;
     const AppendPlan p = append_plan(d, n);
     const dim3 g1(p.col_blocks, p.n_ksplit, p.tok_tiles);
     const void* xc = static_cast<const char*>(x) + static_cast<size_t>(t0) * d.d_model * elt;
     if (d.dtype == MLA_BF16) {
-      if (mfma_ok)
+      if (mfma_ok && absorb_pending && absorb_mfma_fits(d)) {
+        const AbsorbArgs q = absorb_args(d, M, q_nope, q_pe, q_pos, w_uk, q_abs);
+        int rb = 1, zb = 1;
+        const int tiles = absorb_tiles(q, &rb, &zb);
+        const int proj = p.col_blocks * p.n_ksplit * cdiv(n, 32);
+        hipLaunchKernelGGL(project_absorb, dim3(proj + tiles), dim3(256), 0, s,
+                           static_cast<const uint16_t*>(xc), static_cast<const uint16_t*>(w_dkv),
+                           static_cast<const uint16_t*>(w_kr), n, d.d_model, d.d_c, d.d_r, y_part,
+                           p.col_blocks, p.n_ksplit, q, rb, zb);
+        absorb_pending = false;
+      } else if (mfma_ok) {
         hipLaunchKernelGGL(append_project_mfma, dim3(p.col_blocks, p.n_ksplit, cdiv(n, 32)),
                            dim3(256), 0, s, static_cast<const uint16_t*>(xc),
                            static_cast<const uint16_t*>(w_dkv), static_cast<const uint16_t*>(w_kr),
                            n, d.d_model, d.d_c, d.d_r, y_part);
-      else
+      } else {
         hipLaunchKernelGGL(append_project<bf16>, g1, dim3(256), 0, s, static_cast<const bf16*>(xc),
                            static_cast<const bf16*>(w_dkv), static_cast<const bf16*>(w_kr), n,
                            d.d_model, d.d_c, d.d_r, p.k_chunk, y_part);
+      }
       hipLaunchKernelGGL(append_finalize<bf16>, dim3(n), fin_block, lds, s, y_part, p.n_ksplit,
                          n, static_cast<const bf16*>(gamma), seq_idx + t0, pos + t0, table,
                          batch, max_blocks, num_blocks, d.block_size, d.d_c, d.d_r, d.rms_eps,
@@ -337,6 +418,7 @@ hipError_t launch_append(const mla_dims& d, int n_tok, const void* x, const int3
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (absorb_pending) return launch_absorb(d, q_batch, s_q, q_nope, q_pe, q_pos, w_uk, q_abs, s);
   return hipSuccess;
 }
 

@@ -120,7 +120,12 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     // length-balanced plan: workgroup = split slot; partial rows of slot s at [s H + h]
     SplitPlan* pl = reinterpret_cast<SplitPlan*>(ring[0]);
     int* row_of = reinterpret_cast<int*>(ring[1]);
-    const int slot = blockIdx.x;
+    // Workgroup x runs on XCD x % 8 (workgroups are dealt to the XCDs in turn), so XCD c takes
+    // the contiguous slots [32 c, 32 c + 32): the s_q query rows of one sequence, whose slots
+    // are adjacent, then stream the same cache tiles through one L2, which serves all but the
+    // first read of each tile.
+    static_assert(kPlanSlots % 8 == 0, "one slot range per XCD");
+    const int slot = (blockIdx.x & 7) * (kPlanSlots / 8) + (blockIdx.x >> 3);
     make_plan(lens, batch, s_q, capacity, slot, pl, row_of);
     if (slot >= pl->total) return;
     const int rows = batch * s_q;

@@ -15,10 +15,21 @@ struct AppendPlan {
 };
 AppendPlan append_plan(const mla_dims& d, int n_tok);
 
+// Workspace of an append of n_tok tokens: the split-K partial sums.
+size_t append_ws_bytes(const mla_dims& d, int n_tok);
 hipError_t launch_append(const mla_dims& d, int n_tok, const void* x, const int32_t* seq_idx,
                          const int32_t* pos, const void* w_dkv, const void* gamma,
                          const void* w_kr, const int32_t* table, int batch, int max_blocks,
                          int num_blocks, void* cache, void* ws, hipStream_t s);
+// The append, then the absorption of q_batch x s_q queries (none when q_batch * s_q == 0). On
+// the matrix cores the absorption shares a launch with the append's projection.
+hipError_t launch_append_absorb(const mla_dims& d, int n_tok, const void* x,
+                                const int32_t* seq_idx, const int32_t* pos, const void* w_dkv,
+                                const void* gamma, const void* w_kr, const int32_t* table,
+                                int batch, int max_blocks, int num_blocks, void* cache, void* ws,
+                                int q_batch, int s_q, const void* q_nope, const void* q_pe,
+                                const int32_t* q_pos, const void* w_uk, void* q_abs,
+                                hipStream_t s);
 
 // Split-K partial sums of y = x · [W_a | W_b] for n_tok tokens (K-wide rows of x):
 // y_part[k][n][c] over C range [256 k, 256 k + 256), k < projection_ksplit(K). The matrix-core

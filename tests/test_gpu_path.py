@@ -89,6 +89,94 @@ def test_chunked_append_is_bit_exact():
     assert torch.equal(one.view(torch.int16), three.view(torch.int16))
 
 
+APPEND_SHAPES = [
+    ("dsv3-paged", {}),
+    # latent width 160: the third 64-column block holds latent and rotary columns
+    ("gqla-g8", dict(d_model=512, d_c=160, d_r=32, n_groups=8)),
+]
+
+
+@pytest.mark.parametrize("wl,kw", APPEND_SHAPES, ids=[s[0] + ("-dc160" if s[1] else "")
+                                                     for s in APPEND_SHAPES])
+def test_appends_of_any_size_write_the_same_bytes(wl, kw):
+    """Appending 20 tokens one call at a time, then 13 and 7 at a time, through one reused
+    workspace, writes exactly the bytes that one call with all 20 writes (a row depends only
+    on its own token: fixed split-K ranges summed in a fixed order, and the sum of squares of
+    the latent part taken per 64-column block in a fixed order), and those are within one
+    storage ulp of the oracle's rows."""
+    w = W.WORKLOADS[wl].replace(**kw)
+    a = append_case(w, [12, 8])
+    d = M.dims_of(w)
+    n = len(a["seq"])
+    assert n == 20
+    bulk = gpu_append(w, a)
+    ws = torch.empty(M.mla_cache_append_workspace_bytes(d, 16), dtype=torch.uint8, device=DEV)
+    for sizes in ([1] * 20, [13, 7]):
+        note(f"append {wl} {kw} in calls of {sizes[:3]}...")
+        cache = torch.full((a["nb"], w.block_size, w.row), float("nan"), dtype=w.torch_dtype,
+                           device=DEV)
+        lo = 0
+        for k in sizes:
+            hi = lo + k
+            M.mla_cache_append(d, dev(a["x"][lo:hi]), dev(a["seq"][lo:hi]), dev(a["pos"][lo:hi]),
+                               dev(a["wts"]["w_dkv"]), dev(a["wts"]["gamma"]),
+                               dev(a["wts"]["w_kr"]), dev(a["table"]), a["nb"], cache,
+                               workspace=ws)
+            lo = hi
+        torch.cuda.synchronize()
+        assert torch.equal(cache.cpu().view(torch.int16), bulk.view(torch.int16))
+    ref = O.latent_rows(a["x"], a["wts"]["w_dkv"], a["wts"]["gamma"], a["wts"]["w_kr"], a["pos"],
+                        BASE, EPS)
+    k = 0
+    for b, L in enumerate(a["lens"]):
+        got = O.gather_rows(bulk, a["table"], b, int(L))
+        assert ulp_close(got, ref[k:k + L], w.dtype)
+        k += L
+
+
+@pytest.mark.parametrize("wl,s_q", [("long-128k", 1), ("gqla-g8", 4), ("mid-bf16", 1)])
+def test_append_absorb_in_one_launch(wl, s_q):
+    """mla_cache_append_absorb_q (the absorption in the projection's launch) writes the same
+    cache rows and absorbed queries, bit for bit, as mla_cache_append followed by mla_absorb_q
+    (a decode step's first two calls)."""
+    w = W.WORKLOADS[wl].replace(batch=4, s_q=s_q)
+    lens = np.array([70, 129, 64, 3 + s_q], np.int32)
+    table, nb = W.block_table(w, lens)
+    seq = np.repeat(np.arange(w.batch, dtype=np.int32), s_q)
+    qpos = W.query_positions(w, lens)
+    pos = qpos.reshape(-1).astype(np.int32)
+    x = W.tokens(w, len(seq), extra=3)
+    wts = W.weights(w, random_gamma=True)
+    q = W.queries(w)
+    d = M.dims_of(w)
+    outs = []
+    for fused in (False, True):
+        note(f"append+absorb {wl} s_q={s_q} fused={fused}")
+        cache = torch.full((nb, w.block_size, w.row), float("nan"), dtype=w.torch_dtype,
+                           device=DEV)
+        q_abs = torch.full((w.batch, s_q, w.n_heads, w.row), float("nan"), dtype=w.torch_dtype,
+                           device=DEV)
+        args = (dev(x), dev(seq), dev(pos), dev(wts["w_dkv"]), dev(wts["gamma"]),
+                dev(wts["w_kr"]), dev(table), nb, cache)
+        if fused:
+            M.mla_cache_append_absorb_q(d, *args, dev(q["q_nope"]), dev(q["q_pe"]), dev(qpos),
+                                        dev(wts["w_uk"]), q_abs)
+        else:
+            M.mla_cache_append(d, *args)
+            M.mla_absorb_q(d, dev(q["q_nope"]), dev(q["q_pe"]), dev(qpos), dev(wts["w_uk"]),
+                           q_abs)
+        torch.cuda.synchronize()
+        outs.append((cache.cpu(), q_abs.cpu()))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1].view(torch.int16), outs[1][1].view(torch.int16))
+    ref = O.absorb_query(q["q_nope"], q["q_pe"], qpos, wts["w_uk"], w.n_groups, BASE)
+    check(outs[1][1], ref, 4e-3, "q_abs")
+    rows = O.latent_rows(x, wts["w_dkv"], wts["gamma"], wts["w_kr"], pos, BASE, EPS)
+    flat = outs[1][0].view(-1, w.row)
+    slots = np.array([O.slot(table, int(b), int(p), w.block_size) for b, p in zip(seq, pos)])
+    assert ulp_close(flat[torch.from_numpy(slots)], rows, w.dtype)
+
+
 @pytest.mark.parametrize("wl", ["long-128k", "dsv3-paged"])
 def test_append_at_long_context_positions(wl):
     """Positions 131,000 .. 131,071 (the last 72 of a 131,072-position context) appended to a
