@@ -32,6 +32,11 @@ Readings where the pages are silent (each one is also listed in the design notes
 * Multi-token steps: the s_q new positions are in the cache; query i sees positions
   0 .. L - s_q + i.
 * bf16 storage rounds to nearest, ties to even.
+* FP8 latent rows (the pages name quantisation as a way to shrink a cache entry, [KV-cache]
+  "Les trois dimensions de compression", and one byte per value halves it, [Slides] trainer
+  notes on the INT8 check, but fix no format): OCP FP8 E4M3 bytes times one power-of-two
+  scale per position, the smallest s with max |row| <= 448 s; bytes rounded to nearest, ties
+  to the even code.
 
 Parity pins (what ties this oracle to something other than itself) live in
 tests/test_oracle_pins.py. Conventions no page fixes (the RoPE pair layout and frequency
@@ -51,6 +56,7 @@ __all__ = [
     "attend", "decode_reconstructed", "absorb_query", "decode_absorbed_latent",
     "project_values", "decode_absorbed", "gqa_expand_rows", "decode_gqa",
     "visible_lengths",
+    "e4m3_values", "e4m3_encode", "e4m3_row_scale", "quantize_rows_e4m3", "dequantize_rows_e4m3",
 ]
 
 
@@ -367,3 +373,73 @@ def output_project(o, w_o, b_o=None):
     if b_o is not None:
         y = y + f64(b_o)
     return y
+
+
+# ------------------------------------------------------------------ FP8 (E4M3) latent rows
+def e4m3_values() -> np.ndarray:
+    """f64 [256]: the value of every OCP FP8 E4M3 byte, NaN for its two NaN codes.
+
+    Byte s eeee mmm: sign s, exponent field E (bias 7), mantissa field m. E >= 1 is normal,
+    (-1)^s 2^(E - 7) (1 + m/8); E = 0 is subnormal, (-1)^s 2^-6 (m/8); E = 15 with m = 7 is
+    NaN (the format has no infinities, so E = 15 otherwise stays a normal binade, up to 448).
+    """
+    out = np.empty(256)
+    for b in range(256):
+        sign = -1.0 if b & 0x80 else 1.0
+        E, m = (b >> 3) & 0xF, b & 0x7
+        if E == 15 and m == 7:
+            out[b] = np.nan
+        elif E == 0:
+            out[b] = sign * 2.0 ** -6 * (m / 8.0)
+        else:
+            out[b] = sign * 2.0 ** (E - 7) * (1.0 + m / 8.0)
+    return out
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """uint8 codes of f64 values with |v| <= 448: the nearest E4M3 value, ties to the code with
+    an even mantissa (the even code); the sign bit is v's, also for values that round to 0.
+
+    Positive codes 0x00 .. 0x7E are the finite magnitudes in increasing order, so the two
+    candidates of |v| are found by a search in that list.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    if np.any(~np.isfinite(a)) or np.any(a > 448.0):
+        raise ValueError("e4m3_encode takes finite values of magnitude at most 448")
+    mags = e4m3_values()[:0x7F]
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 0x7E)  # first magnitude >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(a == mags[hi], hi, np.where(pick_hi, hi, lo)).astype(np.uint8)
+    return code | (np.signbit(v).astype(np.uint8) << 7)
+
+
+def e4m3_row_scale(amax: float) -> float:
+    """The smallest power of two s with amax <= 448 s (1.0 when amax is 0)."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 1.0
+    e = math.ceil(math.log2(amax / 448.0))
+    while amax > 448.0 * 2.0 ** e:        # log2 may land one off either way
+        e += 1
+    while amax <= 448.0 * 2.0 ** (e - 1):
+        e -= 1
+    return 2.0 ** e
+
+
+def quantize_rows_e4m3(rows):
+    """(codes uint8 [n, w], scales f64 [n]) of rows [n, w]: per row s = e4m3_row_scale(max
+    |row|) and codes = e4m3_encode(row / s) (row / s is exact: s is a power of two)."""
+    r = f64(rows)
+    r = r.reshape(-1, r.shape[-1])
+    scales = np.array([e4m3_row_scale(np.max(np.abs(row)) if row.size else 0.0) for row in r])
+    codes = e4m3_encode(r / scales[:, None])
+    return codes, scales
+
+
+def dequantize_rows_e4m3(codes, scales) -> np.ndarray:
+    """f64 [n, w]: value(code) * scale of each row."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return e4m3_values()[c] * np.asarray(scales, dtype=np.float64).reshape(-1, *([1] * (c.ndim - 1)))
