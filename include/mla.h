@@ -218,6 +218,79 @@ mla_status mla_decode_noalloc(const mla_dims* dims, int32_t batch, int32_t s_q,
                               void* out, float* lse, hipStream_t stream);
 
 /*
+ * FP8 latent cache. The pages count the bytes of one cache entry among the costs to cut and
+ * list quantisation among the ways to cut them, down to FP4 for the "CSA2" design's latent
+ * ([KV-cache] "Les trois dimensions de compression": the entry-size row of its table and
+ * CSA2's 512-channel FP4 latent; [Slides] trainer notes on the INT8 check: one byte per value
+ * halves the cache). They fix no format; this library stores a row as OCP FP8 E4M3 bytes (sign, 4
+ * exponent bits of bias 7, 3 mantissa bits; largest finite value 448, smallest subnormal
+ * 2^-9, no infinities) and one fp32 scale per position:
+ *     scale = the smallest power of two s with max_j |row_j| <= 448 s   (1 for a zero row)
+ *     byte_j = e4m3(row_j / s), rounded to nearest, ties to the even code
+ *     row_j ~ value(byte_j) * s   (exact in bf16)
+ *  A row costs d_c + d_r bytes plus 4 (580 instead of 1,152 for d_c 512, d_r 64). The rows
+ *  quantised are bf16 values: those the bf16 call (mla_cache_append) would have written.
+ *  Layout: cache_fp8 uint8 [num_blocks, bs, d_c + d_r] and cache_scale fp32 [num_blocks, bs],
+ *  both indexed by slot = block_table[b][p / bs] * bs + p % bs; owned by the caller.
+ *  Shapes: dims->dtype MLA_BF16 (every float tensor other than the cache), d_c + d_r a
+ *  multiple of 16 and at most 1024 (MLA_ERR_SHAPE otherwise).
+ *
+ * mla_cache_quantize_fp8 -- n_rows contiguous bf16 rows [n_rows, d_c + d_r] (a whole bf16
+ *  cache: n_rows = num_blocks * bs) to rows_fp8 uint8 [n_rows, d_c + d_r] and row_scale fp32
+ *  [n_rows]. n_rows == 0 enqueues nothing.
+ * mla_cache_append_fp8 -- mla_cache_append writing e4m3 rows and their scales (arguments,
+ *  workspace and errors otherwise mla_cache_append's).
+ * mla_cache_append_absorb_q_fp8 -- mla_cache_append_absorb_q writing e4m3 rows; s_q == 0
+ *  leaves out the absorption (q_nope, q_pe, q_pos, w_uk, q_abs are then not read).
+ */
+mla_status mla_cache_quantize_fp8(const mla_dims* dims, int64_t n_rows, const void* rows,
+                                  void* rows_fp8, float* row_scale, hipStream_t stream);
+mla_status mla_cache_append_fp8(const mla_dims* dims, int32_t n_tok, const void* x,
+                                const int32_t* seq_idx, const int32_t* pos, const void* w_dkv,
+                                const void* rms_gamma, const void* w_kr,
+                                const int32_t* block_table, int32_t batch, int32_t max_blocks,
+                                int32_t num_blocks, void* cache_fp8, float* cache_scale,
+                                void* workspace, size_t ws_bytes, hipStream_t stream);
+mla_status mla_cache_append_absorb_q_fp8(const mla_dims* dims, int32_t n_tok, const void* x,
+                                         const int32_t* seq_idx, const int32_t* pos,
+                                         const void* w_dkv, const void* rms_gamma,
+                                         const void* w_kr, const int32_t* block_table,
+                                         int32_t batch, int32_t max_blocks, int32_t num_blocks,
+                                         void* cache_fp8, float* cache_scale, void* workspace,
+                                         size_t ws_bytes, int32_t s_q, const void* q_nope,
+                                         const void* q_pe, const int32_t* q_pos,
+                                         const void* w_uk, void* q_abs, hipStream_t stream);
+
+/*
+ * mla_decode_fp8, mla_decode_fp8_splitk, mla_decode_fp8_merge -- mla_decode, mla_decode_splitk
+ *  and mla_decode_merge over an e4m3 cache (cache_fp8, cache_scale as above): every row is
+ *  read as value(byte) * scale, which is exact in bf16, so the result is that of the bf16
+ *  calls on the dequantised cache, bit for bit, from half the cache bytes. Shapes: H = 128,
+ *  d_c 512, d_r 64, D_v 128, block size a multiple of 32, dims->dtype MLA_BF16, no
+ *  MLA_FLAG_GENERIC_KERNELS (MLA_ERR_SHAPE otherwise). Workspace sizes, n_split, errors and
+ *  the exact recomputation of flagged splits are those of the bf16 calls.
+ */
+mla_status mla_decode_fp8(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_abs,
+                          const void* cache_fp8, const float* cache_scale, int32_t num_blocks,
+                          const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* seq_lens, const void* w_uv, int32_t n_split,
+                          void* workspace, size_t ws_bytes, void* out, float* lse,
+                          hipStream_t stream);
+mla_status mla_decode_fp8_splitk(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                 const void* q_abs, const void* cache_fp8,
+                                 const float* cache_scale, int32_t num_blocks,
+                                 const int32_t* block_table, int32_t max_blocks,
+                                 const int32_t* seq_lens, int32_t n_split, void* workspace,
+                                 size_t ws_bytes, hipStream_t stream);
+mla_status mla_decode_fp8_merge(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                const void* q_abs, const void* cache_fp8,
+                                const float* cache_scale, int32_t num_blocks,
+                                const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* seq_lens, const void* w_uv, int32_t n_split,
+                                void* workspace, size_t ws_bytes, void* out, float* lse,
+                                hipStream_t stream);
+
+/*
  * gqla_expand -- expand latent rows into the GQA cache once ([GQLA] "Chemin GQA"):
  *     gqa_row = [c · W_UK[:, 0] .. c · W_UK[:, G-1] || c · W_UV[:, 0] .. c · W_UV[:, G-1] || k_r]
  *  for positions start_pos[b] .. seq_lens[b]-1 of every sequence (start_pos NULL: from 0).

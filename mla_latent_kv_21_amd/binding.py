@@ -30,6 +30,8 @@ EXPORTS = ["mla_cache_append_workspace_bytes", "mla_cache_append", "mla_absorb_q
            "mla_output_project_workspace_bytes", "mla_output_project",
            "mla_decode_workspace_bytes", "mla_decode", "mla_decode_splitk", "mla_decode_merge",
            "mla_decode_noalloc",
+           "mla_cache_quantize_fp8", "mla_cache_append_fp8", "mla_cache_append_absorb_q_fp8",
+           "mla_decode_fp8", "mla_decode_fp8_splitk", "mla_decode_fp8_merge",
            "gqla_expand",
            "gqla_decode_workspace_bytes", "gqla_decode",
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_auto_split", "mla_select_path",
@@ -93,6 +95,13 @@ def lib() -> ctypes.CDLL:
             "mla_decode_splitk": (I, [D, I, I, P, P, I, P, I, P, I, P, S, P]),
             "mla_decode_merge": (I, [D, I, I, P, P, I, P, I, P, P, I, P, S, P, P, P]),
             "mla_decode_noalloc": (I, [D, I, I, P, P, I, P, I, P, P, I, P, P, P]),
+            "mla_cache_quantize_fp8": (I, [D, ctypes.c_int64, P, P, P, P]),
+            "mla_cache_append_fp8": (I, [D, I, P, P, P, P, P, P, P, I, I, I, P, P, P, S, P]),
+            "mla_cache_append_absorb_q_fp8": (I, [D, I, P, P, P, P, P, P, P, I, I, I, P, P, P, S,
+                                                  I, P, P, P, P, P, P]),
+            "mla_decode_fp8": (I, [D, I, I, P, P, P, I, P, I, P, P, I, P, S, P, P, P]),
+            "mla_decode_fp8_splitk": (I, [D, I, I, P, P, P, I, P, I, P, I, P, S, P]),
+            "mla_decode_fp8_merge": (I, [D, I, I, P, P, P, I, P, I, P, P, I, P, S, P, P, P]),
             "gqla_expand": (I, [D, I, P, I, P, I, P, P, P, P, P, P]),
             "gqla_decode_workspace_bytes": (S, [D, I, I, I, I]),
             "gqla_decode": (I, [D, I, I, P, P, P, P, I, P, I, P, I, P, S, P, P, P]),
@@ -264,6 +273,80 @@ def mla_decode_merge(dims, q_abs, latent_cache, block_table, seq_lens, w_uv, out
                                 _ptr(seq_lens), _ptr(w_uv), n_split, _ptr(workspace),
                                 workspace.numel(), _ptr(out), _ptr(lse), _stream())
     _check(st, "mla_decode_merge")
+
+
+# ---- e4m3 latent cache: uint8 rows [num_blocks, bs, d_c + d_r] and fp32 scales [num_blocks, bs]
+def mla_cache_quantize_fp8(dims, rows, rows_fp8, row_scale):
+    """bf16 rows [..., d_c + d_r] to e4m3 bytes of the same shape and one scale per row."""
+    n = row_scale.numel()
+    if rows.numel() != n * (dims.d_c + dims.d_r) or rows_fp8.numel() != rows.numel():
+        raise ValueError("rows, rows_fp8 and row_scale disagree")
+    st = lib().mla_cache_quantize_fp8(ctypes.byref(dims), n, _ptr(rows), _ptr(rows_fp8),
+                                      _ptr(row_scale), _stream())
+    _check(st, "mla_cache_quantize_fp8")
+
+
+def mla_cache_append_fp8(dims, x, seq_idx, pos, w_dkv, gamma, w_kr, block_table, num_blocks,
+                         cache_fp8, cache_scale, workspace=None):
+    n_tok = x.shape[0]
+    if workspace is None:
+        workspace = _workspace(mla_cache_append_workspace_bytes(dims, n_tok), x.device)
+    st = lib().mla_cache_append_fp8(
+        ctypes.byref(dims), n_tok, _ptr(x), _ptr(seq_idx), _ptr(pos), _ptr(w_dkv), _ptr(gamma),
+        _ptr(w_kr), _ptr(block_table), block_table.shape[0], block_table.shape[1], num_blocks,
+        _ptr(cache_fp8), _ptr(cache_scale), _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "mla_cache_append_fp8")
+
+
+def mla_cache_append_absorb_q_fp8(dims, x, seq_idx, pos, w_dkv, gamma, w_kr, block_table,
+                                  num_blocks, cache_fp8, cache_scale, q_nope, q_pe, q_pos, w_uk,
+                                  q_abs, workspace=None):
+    n_tok = x.shape[0]
+    B, s_q = q_nope.shape[0], q_nope.shape[1]
+    if block_table.shape[0] != B:
+        raise ValueError("the block table's rows and the query batch must agree")
+    if workspace is None:
+        workspace = _workspace(mla_cache_append_workspace_bytes(dims, n_tok), x.device)
+    st = lib().mla_cache_append_absorb_q_fp8(
+        ctypes.byref(dims), n_tok, _ptr(x), _ptr(seq_idx), _ptr(pos), _ptr(w_dkv), _ptr(gamma),
+        _ptr(w_kr), _ptr(block_table), B, block_table.shape[1], num_blocks, _ptr(cache_fp8),
+        _ptr(cache_scale), _ptr(workspace), workspace.numel(), s_q, _ptr(q_nope), _ptr(q_pe),
+        _ptr(q_pos), _ptr(w_uk), _ptr(q_abs), _stream())
+    _check(st, "mla_cache_append_absorb_q_fp8")
+
+
+def mla_decode_fp8(dims, q_abs, cache_fp8, cache_scale, block_table, seq_lens, w_uv, out,
+                   lse=None, n_split=0, workspace=None):
+    B, s_q = q_abs.shape[0], q_abs.shape[1]
+    mb = block_table.shape[1]
+    if workspace is None:
+        workspace = _workspace(mla_decode_workspace_bytes(dims, B, s_q, n_split, mb), q_abs.device)
+    st = lib().mla_decode_fp8(ctypes.byref(dims), B, s_q, _ptr(q_abs), _ptr(cache_fp8),
+                              _ptr(cache_scale), cache_fp8.shape[0], _ptr(block_table), mb,
+                              _ptr(seq_lens), _ptr(w_uv), n_split, _ptr(workspace),
+                              workspace.numel(), _ptr(out), _ptr(lse), _stream())
+    _check(st, "mla_decode_fp8")
+
+
+def mla_decode_fp8_splitk(dims, q_abs, cache_fp8, cache_scale, block_table, seq_lens, n_split,
+                          workspace):
+    B, s_q = q_abs.shape[0], q_abs.shape[1]
+    st = lib().mla_decode_fp8_splitk(ctypes.byref(dims), B, s_q, _ptr(q_abs), _ptr(cache_fp8),
+                                     _ptr(cache_scale), cache_fp8.shape[0], _ptr(block_table),
+                                     block_table.shape[1], _ptr(seq_lens), n_split,
+                                     _ptr(workspace), workspace.numel(), _stream())
+    _check(st, "mla_decode_fp8_splitk")
+
+
+def mla_decode_fp8_merge(dims, q_abs, cache_fp8, cache_scale, block_table, seq_lens, w_uv, out,
+                         lse, n_split, workspace):
+    B, s_q = q_abs.shape[0], q_abs.shape[1]
+    st = lib().mla_decode_fp8_merge(ctypes.byref(dims), B, s_q, _ptr(q_abs), _ptr(cache_fp8),
+                                    _ptr(cache_scale), cache_fp8.shape[0], _ptr(block_table),
+                                    block_table.shape[1], _ptr(seq_lens), _ptr(w_uv), n_split,
+                                    _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
+                                    _stream())
+    _check(st, "mla_decode_fp8_merge")
 
 
 def gqla_expand(dims, latent_cache, block_table, seq_lens, w_uk, w_uv, gqa_cache,

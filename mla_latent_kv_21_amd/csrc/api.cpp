@@ -117,6 +117,12 @@ namespace {
 
 // Host checks of mla_cache_append (dims already checked); MLA_OK with n_tok == 0 means
 // nothing to do.
+// e4m3 rows: quantised from bf16 values, 16-byte rows of at most 1024 values.
+bool fp8_rows_ok(const mla_dims& d) {
+  const int n = d.d_c + d.d_r;
+  return d.dtype == MLA_BF16 && n % 16 == 0 && n <= 1024;
+}
+
 mla_status check_append(const mla_dims* dims, int32_t n_tok, const void* x,
                         const int32_t* seq_idx, const int32_t* pos, const void* w_dkv,
                         const void* rms_gamma, const void* w_kr, const int32_t* block_table,
@@ -169,7 +175,7 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t n_tok, const void* x,
   if (st != MLA_OK || n_tok == 0) return st;
   return hip_status(mla::launch_append(*dims, n_tok, x, seq_idx, pos, w_dkv, rms_gamma, w_kr,
                                        block_table, batch, max_blocks, num_blocks, latent_cache,
-                                       workspace, stream));
+                                       nullptr, workspace, stream));
 }
 
 mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_nope,
@@ -203,8 +209,68 @@ mla_status mla_cache_append_absorb_q(const mla_dims* dims, int32_t n_tok, const 
                                          stream));
   return hip_status(mla::launch_append_absorb(*dims, n_tok, x, seq_idx, pos, w_dkv, rms_gamma,
                                               w_kr, block_table, batch, max_blocks, num_blocks,
-                                              latent_cache, workspace, batch, s_q, q_nope, q_pe,
-                                              q_pos, w_uk, q_abs, stream));
+                                              latent_cache, nullptr, workspace, batch, s_q, q_nope,
+                                              q_pe, q_pos, w_uk, q_abs, stream));
+}
+
+mla_status mla_cache_quantize_fp8(const mla_dims* dims, int64_t n_rows, const void* rows,
+                                  void* rows_fp8, float* row_scale, hipStream_t stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!fp8_rows_ok(*dims)) return MLA_ERR_SHAPE;
+  if (n_rows < 0) return MLA_ERR_RANGE;
+  if (n_rows == 0) return MLA_OK;
+  if (!rows || !rows_fp8 || !row_scale) return MLA_ERR_NULL;
+  if (!aligned16(rows) || !aligned16(rows_fp8) || !aligned16(row_scale)) return MLA_ERR_ALIGN;
+  return hip_status(mla::launch_quantize_e4m3(n_rows, dims->d_c + dims->d_r, rows, rows_fp8,
+                                              row_scale, stream));
+}
+
+mla_status mla_cache_append_fp8(const mla_dims* dims, int32_t n_tok, const void* x,
+                                const int32_t* seq_idx, const int32_t* pos, const void* w_dkv,
+                                const void* rms_gamma, const void* w_kr,
+                                const int32_t* block_table, int32_t batch, int32_t max_blocks,
+                                int32_t num_blocks, void* cache_fp8, float* cache_scale,
+                                void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return mla_cache_append_absorb_q_fp8(dims, n_tok, x, seq_idx, pos, w_dkv, rms_gamma, w_kr,
+                                       block_table, batch, max_blocks, num_blocks, cache_fp8,
+                                       cache_scale, workspace, ws_bytes, 0, nullptr, nullptr,
+                                       nullptr, nullptr, nullptr, stream);
+}
+
+mla_status mla_cache_append_absorb_q_fp8(const mla_dims* dims, int32_t n_tok, const void* x,
+                                         const int32_t* seq_idx, const int32_t* pos,
+                                         const void* w_dkv, const void* rms_gamma,
+                                         const void* w_kr, const int32_t* block_table,
+                                         int32_t batch, int32_t max_blocks, int32_t num_blocks,
+                                         void* cache_fp8, float* cache_scale, void* workspace,
+                                         size_t ws_bytes, int32_t s_q, const void* q_nope,
+                                         const void* q_pe, const int32_t* q_pos,
+                                         const void* w_uk, void* q_abs, hipStream_t stream) {
+  // s_q == 0: the append alone (mla_cache_append_fp8)
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (!fp8_rows_ok(*dims)) return MLA_ERR_SHAPE;
+  st = check_append(dims, n_tok, x, seq_idx, pos, w_dkv, rms_gamma, w_kr, block_table, batch,
+                    max_blocks, num_blocks, cache_fp8, workspace, ws_bytes);
+  if (st != MLA_OK) return st;
+  if (n_tok > 0) {
+    if (!cache_scale) return MLA_ERR_NULL;
+    if (!aligned16(cache_scale)) return MLA_ERR_ALIGN;
+  }
+  const int q_batch = s_q == 0 ? 0 : batch;
+  if (s_q != 0) {
+    st = check_absorb(dims, batch, s_q, q_nope, q_pe, q_pos, w_uk, q_abs);
+    if (st != MLA_OK) return st;
+  }
+  if (n_tok == 0 && q_batch == 0) return MLA_OK;
+  if (n_tok == 0)
+    return hip_status(mla::launch_absorb(*dims, q_batch, s_q, q_nope, q_pe, q_pos, w_uk, q_abs,
+                                         stream));
+  return hip_status(mla::launch_append_absorb(*dims, n_tok, x, seq_idx, pos, w_dkv, rms_gamma,
+                                              w_kr, block_table, batch, max_blocks, num_blocks,
+                                              cache_fp8, cache_scale, workspace, q_batch, s_q,
+                                              q_nope, q_pe, q_pos, w_uk, q_abs, stream));
 }
 
 size_t mla_query_project_workspace_bytes(const mla_dims* dims, int32_t n_tok, int32_t d_q) {
@@ -297,6 +363,42 @@ mla_status check_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const 
   return MLA_OK;
 }
 
+// The decode calls: the split-K core, the merge, or both, over bf16/fp32 rows (scales NULL) or
+// e4m3 rows with per-slot scales.
+enum DecodePart { kSplit = 1, kMerge = 2 };
+mla_status decode_call(int parts, const mla_dims* dims, int32_t batch, int32_t s_q,
+                       const void* q_abs, const void* latent_cache, const float* scales,
+                       bool fp8, int32_t num_blocks, const int32_t* block_table,
+                       int32_t max_blocks, const int32_t* seq_lens, const void* w_uv,
+                       int32_t n_split, void* workspace, size_t ws_bytes, void* out, float* lse,
+                       hipStream_t stream) {
+  int ns = 0;
+  mla_status st = check_decode(dims, batch, s_q, q_abs, latent_cache, num_blocks, block_table,
+                               max_blocks, seq_lens, n_split, workspace, ws_bytes, &ns);
+  if (st != MLA_OK || batch == 0) return st;
+  if (fp8) {
+    if (!mla::mfma_decode_fp8_fits(*dims) || (dims->flags & MLA_FLAG_GENERIC_KERNELS))
+      return MLA_ERR_SHAPE;
+    if (!scales) return MLA_ERR_NULL;
+    if (!aligned16(scales)) return MLA_ERR_ALIGN;
+  }
+  if (parts & kMerge) {
+    if (!w_uv || !out) return MLA_ERR_NULL;
+    if (!aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  }
+  if (parts & kSplit) {
+    st = hip_status(mla::launch_decode_splitk(*dims, batch, s_q, q_abs, latent_cache, scales,
+                                              num_blocks, block_table, max_blocks, seq_lens, ns,
+                                              workspace, stream));
+    if (st != MLA_OK) return st;
+  }
+  if (parts & kMerge)
+    st = hip_status(mla::launch_decode_merge(*dims, batch, s_q, q_abs, latent_cache, scales,
+                                             num_blocks, block_table, max_blocks, seq_lens, w_uv,
+                                             ns, workspace, out, lse, stream));
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -306,14 +408,9 @@ mla_status mla_decode_splitk(const mla_dims* dims, int32_t batch, int32_t s_q, c
                              const int32_t* block_table, int32_t max_blocks,
                              const int32_t* seq_lens, int32_t n_split, void* workspace,
                              size_t ws_bytes, hipStream_t stream) {
-  int ns = 0;
-  const mla_status st = check_decode(dims, batch, s_q, q_abs, latent_cache, num_blocks,
-                                     block_table, max_blocks, seq_lens, n_split, workspace,
-                                     ws_bytes, &ns);
-  if (st != MLA_OK || batch == 0) return st;
-  return hip_status(mla::launch_decode_splitk(*dims, batch, s_q, q_abs, latent_cache, num_blocks,
-                                              block_table, max_blocks, seq_lens, ns, workspace,
-                                              stream));
+  return decode_call(kSplit, dims, batch, s_q, q_abs, latent_cache, nullptr, false, num_blocks,
+                     block_table, max_blocks, seq_lens, nullptr, n_split, workspace, ws_bytes,
+                     nullptr, nullptr, stream);
 }
 
 mla_status mla_decode_merge(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_abs,
@@ -322,16 +419,9 @@ mla_status mla_decode_merge(const mla_dims* dims, int32_t batch, int32_t s_q, co
                             const int32_t* seq_lens, const void* w_uv, int32_t n_split,
                             void* workspace, size_t ws_bytes, void* out, float* lse,
                             hipStream_t stream) {
-  int ns = 0;
-  const mla_status st = check_decode(dims, batch, s_q, q_abs, latent_cache, num_blocks,
-                                     block_table, max_blocks, seq_lens, n_split, workspace,
-                                     ws_bytes, &ns);
-  if (st != MLA_OK || batch == 0) return st;
-  if (!w_uv || !out) return MLA_ERR_NULL;
-  if (!aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
-  return hip_status(mla::launch_decode_merge(*dims, batch, s_q, q_abs, latent_cache, num_blocks,
-                                             block_table, max_blocks, seq_lens, w_uv, ns,
-                                             workspace, out, lse, stream));
+  return decode_call(kMerge, dims, batch, s_q, q_abs, latent_cache, nullptr, false, num_blocks,
+                     block_table, max_blocks, seq_lens, w_uv, n_split, workspace, ws_bytes, out,
+                     lse, stream);
 }
 
 mla_status mla_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_abs,
@@ -339,19 +429,43 @@ mla_status mla_decode(const mla_dims* dims, int32_t batch, int32_t s_q, const vo
                       int32_t max_blocks, const int32_t* seq_lens, const void* w_uv,
                       int32_t n_split, void* workspace, size_t ws_bytes, void* out, float* lse,
                       hipStream_t stream) {
-  int ns = 0;
-  mla_status st = check_decode(dims, batch, s_q, q_abs, latent_cache, num_blocks, block_table,
-                               max_blocks, seq_lens, n_split, workspace, ws_bytes, &ns);
-  if (st != MLA_OK || batch == 0) return st;
-  if (!w_uv || !out) return MLA_ERR_NULL;
-  if (!aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
-  st = hip_status(mla::launch_decode_splitk(*dims, batch, s_q, q_abs, latent_cache, num_blocks,
-                                            block_table, max_blocks, seq_lens, ns, workspace,
-                                            stream));
-  if (st != MLA_OK) return st;
-  return hip_status(mla::launch_decode_merge(*dims, batch, s_q, q_abs, latent_cache, num_blocks,
-                                             block_table, max_blocks, seq_lens, w_uv, ns,
-                                             workspace, out, lse, stream));
+  return decode_call(kSplit | kMerge, dims, batch, s_q, q_abs, latent_cache, nullptr, false,
+                     num_blocks, block_table, max_blocks, seq_lens, w_uv, n_split, workspace,
+                     ws_bytes, out, lse, stream);
+}
+
+mla_status mla_decode_fp8(const mla_dims* dims, int32_t batch, int32_t s_q, const void* q_abs,
+                          const void* cache_fp8, const float* cache_scale, int32_t num_blocks,
+                          const int32_t* block_table, int32_t max_blocks,
+                          const int32_t* seq_lens, const void* w_uv, int32_t n_split,
+                          void* workspace, size_t ws_bytes, void* out, float* lse,
+                          hipStream_t stream) {
+  return decode_call(kSplit | kMerge, dims, batch, s_q, q_abs, cache_fp8, cache_scale, true,
+                     num_blocks, block_table, max_blocks, seq_lens, w_uv, n_split, workspace,
+                     ws_bytes, out, lse, stream);
+}
+
+mla_status mla_decode_fp8_splitk(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                 const void* q_abs, const void* cache_fp8,
+                                 const float* cache_scale, int32_t num_blocks,
+                                 const int32_t* block_table, int32_t max_blocks,
+                                 const int32_t* seq_lens, int32_t n_split, void* workspace,
+                                 size_t ws_bytes, hipStream_t stream) {
+  return decode_call(kSplit, dims, batch, s_q, q_abs, cache_fp8, cache_scale, true, num_blocks,
+                     block_table, max_blocks, seq_lens, nullptr, n_split, workspace, ws_bytes,
+                     nullptr, nullptr, stream);
+}
+
+mla_status mla_decode_fp8_merge(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                const void* q_abs, const void* cache_fp8,
+                                const float* cache_scale, int32_t num_blocks,
+                                const int32_t* block_table, int32_t max_blocks,
+                                const int32_t* seq_lens, const void* w_uv, int32_t n_split,
+                                void* workspace, size_t ws_bytes, void* out, float* lse,
+                                hipStream_t stream) {
+  return decode_call(kMerge, dims, batch, s_q, q_abs, cache_fp8, cache_scale, true, num_blocks,
+                     block_table, max_blocks, seq_lens, w_uv, n_split, workspace, ws_bytes, out,
+                     lse, stream);
 }
 
 mla_status gqla_expand(const mla_dims* dims, int32_t batch, const void* latent_cache,

@@ -216,12 +216,34 @@ __global__ __launch_bounds__(256) void append_project_mfma(const uint16_t* __res
                     blockIdx.z * 32);
 }
 
-template <typename T>
+// ---- e4m3 rows. A row is stored as OCP FP8 E4M3 bytes (1 sign, 4 exponent bits of bias 7,
+// 3 mantissa bits; largest finite 448, smallest subnormal 2^-9) times one fp32 scale per
+// position: the smallest power of two s with amax <= 448 s (s = 1 for an all-zero row), so
+// every value x / s is exact in fp32 and rounds (to nearest, ties to even) into the format's
+// finite range, and byte x s is exact in bf16.
+__device__ __forceinline__ int e4m3_scale_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int k;
+  const float m = frexpf(amax, &k);  // amax = m 2^k, m in [0.5, 1)
+  return m <= 0.875f ? k - 9 : k - 8;
+}
+
+// four values (already divided by the scale) as four e4m3 bytes, element 0 in the low byte
+__device__ __forceinline__ unsigned e4m3_pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<unsigned>(w);
+}
+
+// kFp8: the row goes out as e4m3 bytes (cache8) and its scale (scale8), quantised from the
+// values the bf16 row would hold.
+template <typename T, bool kFp8>
 __global__ __launch_bounds__(1024) void append_finalize(
     const float* __restrict__ y_part, int n_ksplit, int n_tok, const T* __restrict__ gamma,
     const int32_t* __restrict__ seq_idx, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ table, int batch, int max_blocks, int num_blocks, int bs,
-    int d_c, int d_r, float eps, float base, T* __restrict__ cache) {
+    int d_c, int d_r, float eps, float base, T* __restrict__ cache, uint8_t* __restrict__ cache8,
+    float* __restrict__ scale8) {
   extern __shared__ float ys[];  // [d_c + d_r]
   __shared__ float red[64];
   const int n = blockIdx.x;
@@ -261,6 +283,34 @@ __global__ __launch_bounds__(1024) void append_finalize(
   for (int j = 0; j < lat_blocks; ++j) ss += red[j];
   if (slot < 0) return;
   const float inv = 1.0f / sqrtf(ss / static_cast<float>(d_c) + eps);
+  if constexpr (kFp8) {
+    // the row rounded to bf16 in place (each thread rewrites only the columns it reads)
+    float amax = 0.f;
+    for (int c = threadIdx.x; c < d_c; c += blockDim.x) {
+      const float v = bf16_to_f32(f32_to_bf16(ys[c] * inv * ld(gamma, c)));
+      ys[c] = v;
+      amax = fmaxf(amax, fabsf(v));
+    }
+    for (int j = threadIdx.x; j < d_r / 2; j += blockDim.x) {
+      float cs, sn;
+      rope_cos_sin(p, j, d_r, base, &cs, &sn);
+      const float a = ys[d_c + 2 * j], q = ys[d_c + 2 * j + 1];
+      const float u = bf16_to_f32(f32_to_bf16(a * cs - q * sn));
+      const float v = bf16_to_f32(f32_to_bf16(a * sn + q * cs));
+      ys[d_c + 2 * j] = u;
+      ys[d_c + 2 * j + 1] = v;
+      amax = fmaxf(amax, fmaxf(fabsf(u), fabsf(v)));
+    }
+    amax = block_max(amax, red);  // its barriers also publish the rounded row
+    const int e = e4m3_scale_exp(amax);
+    const float rs = ldexpf(1.f, -e);
+    unsigned* out = reinterpret_cast<unsigned*>(cache8 + slot * ncols);
+    for (int i = threadIdx.x; i < ncols / 4; i += blockDim.x)
+      out[i] = e4m3_pack4(ys[4 * i] * rs, ys[4 * i + 1] * rs, ys[4 * i + 2] * rs,
+                          ys[4 * i + 3] * rs);
+    if (threadIdx.x == 0) scale8[slot] = ldexpf(1.f, e);
+    return;
+  }
   T* row = cache + slot * ncols;
   for (int c = threadIdx.x; c < d_c; c += blockDim.x) st(row, c, ys[c] * inv * ld(gamma, c));
   for (int j = threadIdx.x; j < d_r / 2; j += blockDim.x) {
@@ -272,6 +322,41 @@ __global__ __launch_bounds__(1024) void append_finalize(
   }
 }
 
+// Rows of bf16 values to e4m3 bytes and scales, one wave per row (the rule of append_finalize).
+__global__ __launch_bounds__(256) void quantize_rows_e4m3(const uint16_t* __restrict__ rows,
+                                                         int64_t n_rows, int ncols,
+                                                         uint8_t* __restrict__ out,
+                                                         float* __restrict__ scale) {
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= n_rows) return;
+  const int ng = ncols / 4;  // groups of four values
+  const uint2* src = reinterpret_cast<const uint2*>(rows + r * ncols);
+  constexpr int kMaxG = 4;   // ncols <= 1024
+  uint2 v[kMaxG];
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMaxG; ++k) {
+    const int g = lane + 64 * k;
+    v[k] = g < ng ? src[g] : make_uint2(0u, 0u);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(bf16_to_f32(v[k].x & 0xffffu)),
+                                   fabsf(bf16_to_f32(v[k].x >> 16))),
+                             fmaxf(fabsf(bf16_to_f32(v[k].y & 0xffffu)),
+                                   fabsf(bf16_to_f32(v[k].y >> 16)))));
+  }
+  amax = wave_max(amax);
+  const int e = e4m3_scale_exp(amax);
+  const float rs = ldexpf(1.f, -e);
+  unsigned* dst = reinterpret_cast<unsigned*>(out + r * ncols);
+#pragma unroll
+  for (int k = 0; k < kMaxG; ++k) {
+    const int g = lane + 64 * k;
+    if (g < ng)
+      dst[g] = e4m3_pack4(bf16_to_f32(v[k].x & 0xffffu) * rs, bf16_to_f32(v[k].x >> 16) * rs,
+                          bf16_to_f32(v[k].y & 0xffffu) * rs, bf16_to_f32(v[k].y >> 16) * rs);
+  }
+  if (lane == 0) scale[r] = ldexpf(1.f, e);
+}
 
 // ---- the append's projection and the query absorption of a decode step in one launch.
 //
@@ -340,6 +425,19 @@ AppendPlan append_plan(const mla_dims& d, int n_tok) {
   return p;
 }
 
+hipError_t launch_quantize_e4m3(int64_t n_rows, int ncols, const void* rows, void* out,
+                               float* scale, hipStream_t s) {
+  const int64_t nb = (n_rows + 3) / 4;
+  for (int64_t b0 = 0; b0 < nb; b0 += 0x7fffffff) {
+    const int64_t n = nb - b0 < 0x7fffffff ? nb - b0 : 0x7fffffff;
+    const int64_t r0 = b0 * 4;
+    hipLaunchKernelGGL(quantize_rows_e4m3, dim3(static_cast<unsigned>(n)), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(rows) + r0 * ncols, n_rows - r0, ncols,
+                       static_cast<uint8_t*>(out) + r0 * ncols, scale + r0);
+  }
+  return hipGetLastError();
+}
+
 size_t append_ws_bytes(const mla_dims& d, int n_tok) {
   const AppendPlan p = append_plan(d, n_tok);
   const size_t n = n_tok < kMaxTok ? n_tok : kMaxTok;
@@ -349,17 +447,18 @@ size_t append_ws_bytes(const mla_dims& d, int n_tok) {
 hipError_t launch_append(const mla_dims& d, int n_tok, const void* x, const int32_t* seq_idx,
                          const int32_t* pos, const void* w_dkv, const void* gamma,
                          const void* w_kr, const int32_t* table, int batch, int max_blocks,
-                         int num_blocks, void* cache, void* ws, hipStream_t s) {
+                         int num_blocks, void* cache, float* cache_scale, void* ws,
+                         hipStream_t s) {
   return launch_append_absorb(d, n_tok, x, seq_idx, pos, w_dkv, gamma, w_kr, table, batch,
-                              max_blocks, num_blocks, cache, ws, 0, 0, nullptr, nullptr, nullptr,
-                              nullptr, nullptr, s);
+                              max_blocks, num_blocks, cache, cache_scale, ws, 0, 0, nullptr,
+                              nullptr, nullptr, nullptr, nullptr, s);
 }
 
 hipError_t launch_append_absorb(const mla_dims& d, int n_tok, const void* x,
                                 const int32_t* seq_idx, const int32_t* pos, const void* w_dkv,
                                 const void* gamma, const void* w_kr, const int32_t* table,
-                                int batch, int max_blocks, int num_blocks, void* cache, void* ws,
-                                int q_batch, int s_q, const void* q_nope, const void* q_pe,
+                                int batch, int max_blocks, int num_blocks, void* cache,
+                                float* cache_scale, void* ws, int q_batch, int s_q, const void* q_nope, const void* q_pe,
                                 const int32_t* q_pos, const void* w_uk, void* q_abs,
                                 hipStream_t s) {
   float* y_part = static_cast<float*>(ws);
@@ -401,19 +500,26 @@ hipError_t launch_append_absorb(const mla_dims& d, int n_tok, const void* x,
                            static_cast<const bf16*>(w_dkv), static_cast<const bf16*>(w_kr), n,
                            d.d_model, d.d_c, d.d_r, p.k_chunk, y_part);
       }
-      hipLaunchKernelGGL(append_finalize<bf16>, dim3(n), fin_block, lds, s, y_part, p.n_ksplit,
-                         n, static_cast<const bf16*>(gamma), seq_idx + t0, pos + t0, table,
-                         batch, max_blocks, num_blocks, d.block_size, d.d_c, d.d_r, d.rms_eps,
-                         d.rope_base, static_cast<bf16*>(cache));
+      if (cache_scale != nullptr)
+        hipLaunchKernelGGL((append_finalize<bf16, true>), dim3(n), fin_block, lds, s, y_part,
+                           p.n_ksplit, n, static_cast<const bf16*>(gamma), seq_idx + t0, pos + t0,
+                           table, batch, max_blocks, num_blocks, d.block_size, d.d_c, d.d_r,
+                           d.rms_eps, d.rope_base, nullptr, static_cast<uint8_t*>(cache),
+                           cache_scale);
+      else
+        hipLaunchKernelGGL((append_finalize<bf16, false>), dim3(n), fin_block, lds, s, y_part,
+                           p.n_ksplit, n, static_cast<const bf16*>(gamma), seq_idx + t0, pos + t0,
+                           table, batch, max_blocks, num_blocks, d.block_size, d.d_c, d.d_r,
+                           d.rms_eps, d.rope_base, static_cast<bf16*>(cache), nullptr, nullptr);
     } else {
       hipLaunchKernelGGL(append_project<float>, g1, dim3(256), 0, s,
                          static_cast<const float*>(xc), static_cast<const float*>(w_dkv),
                          static_cast<const float*>(w_kr), n, d.d_model, d.d_c, d.d_r, p.k_chunk,
                          y_part);
-      hipLaunchKernelGGL(append_finalize<float>, dim3(n), fin_block, lds, s, y_part, p.n_ksplit,
-                         n, static_cast<const float*>(gamma), seq_idx + t0, pos + t0, table,
-                         batch, max_blocks, num_blocks, d.block_size, d.d_c, d.d_r, d.rms_eps,
-                         d.rope_base, static_cast<float*>(cache));
+      hipLaunchKernelGGL((append_finalize<float, false>), dim3(n), fin_block, lds, s, y_part,
+                         p.n_ksplit, n, static_cast<const float*>(gamma), seq_idx + t0, pos + t0,
+                         table, batch, max_blocks, num_blocks, d.block_size, d.d_c, d.d_r,
+                         d.rms_eps, d.rope_base, static_cast<float*>(cache), nullptr, nullptr);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

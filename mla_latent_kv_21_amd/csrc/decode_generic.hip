@@ -41,7 +41,20 @@ struct GenericArgs {
   // Length-balanced plan (in the workspace) or NULL: then split k of row m covers
   // [k chunk, min((k+1) chunk, lim)) and its partial rows sit at [(first[m] + k) H + h].
   const SplitPlan* plan;
+  // Latent path with e4m3 rows: one fp32 scale per cache slot (row = bytes x scale), else NULL
+  const float* row_scale;
 };
+
+// Element e of the cache row at `slot`: of type T, or an e4m3 byte times the row's scale.
+template <typename T>
+__device__ __forceinline__ float row_elt(const GenericArgs& a, int64_t slot, int e) {
+  if (a.row_scale != nullptr) {
+    const unsigned char byte =
+        static_cast<const unsigned char*>(a.cache)[slot * a.row_w + e];
+    return __builtin_amdgcn_cvt_pk_f32_fp8(byte, false)[0] * a.row_scale[slot];
+  }
+  return ld(static_cast<const T*>(a.cache), slot * a.row_w + e);
+}
 
 // One (sequence b, query i, split k, head h) partial: online softmax over the split's positions
 // blockDim.x at a time, one position per thread for the scores, one value column per thread
@@ -64,7 +77,6 @@ __device__ void split_head(const GenericArgs& a, int b, int i, int k, int h, flo
     split_range(lim, a.n_split, k, kSplitAlign, &t0, &t1);
     pidx = static_cast<int64_t>(k) * a.n_rows + qrow;
   }
-  const T* cache = static_cast<const T*>(a.cache);
   const int g = h / (a.H / a.G);
   // key segments inside a cache row, and the value segment
   int ko1, kl1, ko2, vo;
@@ -97,10 +109,9 @@ __device__ void split_head(const GenericArgs& a, int b, int i, int k, int h, flo
     int64_t slot = -1;
     if (t < t1) slot = cache_slot(a.table, a.max_blocks, a.bs, a.num_blocks, b, t);
     if (slot >= 0) {
-      const T* r = cache + slot * a.row_w;
       float acc = 0.f;
-      for (int e = 0; e < kl1; ++e) acc += qs[e] * ld(r, ko1 + e);
-      for (int e = 0; e < a.d_r; ++e) acc += qs[kl1 + e] * ld(r, ko2 + e);
+      for (int e = 0; e < kl1; ++e) acc += qs[e] * row_elt<T>(a, slot, ko1 + e);
+      for (int e = 0; e < a.d_r; ++e) acc += qs[kl1 + e] * row_elt<T>(a, slot, ko2 + e);
       s = acc * a.scale_log2;
     }
     sl[threadIdx.x] = slot;
@@ -117,7 +128,7 @@ __device__ void split_head(const GenericArgs& a, int b, int i, int k, int h, flo
     for (int e = threadIdx.x; e < a.part_w; e += blockDim.x) {
       float acc = os[e] * alpha;
       for (int u = 0; u < nt; ++u) {
-        if (sl[u] >= 0) acc += ps[u] * ld(cache, sl[u] * a.row_w + vo + e);
+        if (sl[u] >= 0) acc += ps[u] * row_elt<T>(a, sl[u], vo + e);
       }
       os[e] = acc;
     }
@@ -740,9 +751,10 @@ Partials partials_of(void* ws, int batch, int s_q, int heads, int n_split, int w
 }
 
 GenericArgs latent_args(const mla_dims& d, int batch, int s_q, const void* q_abs, const void* cache,
-                        int num_blocks, const int32_t* table, int max_blocks,
+                        const float* scales, int num_blocks, const int32_t* table, int max_blocks,
                         const int32_t* seq_lens, int n_split, const Partials& p) {
   GenericArgs a{};
+  a.row_scale = scales;
   a.q = q_abs; a.cache = cache; a.table = table; a.lens = seq_lens;
   a.num_blocks = num_blocks; a.max_blocks = max_blocks; a.bs = d.block_size;
   a.H = d.n_heads; a.G = d.n_groups; a.s_q = s_q; a.n_split = n_split;
@@ -779,43 +791,44 @@ size_t planned_workspace_bytes(const mla_dims& d) {
 // n_split == 0 here means the length-balanced plan (the caller checked plan_applies): the
 // plan sits at the start of the workspace, the partials of the kPlanSlots slots after it.
 hipError_t launch_decode_splitk(const mla_dims& d, int batch, int s_q, const void* q_abs,
-                                const void* cache, int num_blocks, const int32_t* table,
-                                int max_blocks, const int32_t* seq_lens, int n_split, void* ws,
-                                hipStream_t s) {
+                                const void* cache, const float* scales, int num_blocks,
+                                const int32_t* table, int max_blocks, const int32_t* seq_lens,
+                                int n_split, void* ws, hipStream_t s) {
   if (n_split == 0) {
     const Partials p = partials_of(static_cast<char*>(ws) + kPlanBytes, 1, 1, d.n_heads,
                                    kPlanSlots, d.d_c, 2);
-    return launch_decode_mfma(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
+    return launch_decode_mfma(d, batch, s_q, q_abs, cache, scales, num_blocks, table, max_blocks,
                               seq_lens, kPlanCap, p.o, p.lse, p.redo,
                               static_cast<SplitPlan*>(ws), s);
   }
   const Partials p = partials_of(ws, batch, s_q, d.n_heads, n_split, d.d_c, d.dtype == MLA_BF16 ? 2 : 4);
-  if (uses_mfma(d))
-    return launch_decode_mfma(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
+  if (uses_mfma(d) || scales != nullptr)
+    return launch_decode_mfma(d, batch, s_q, q_abs, cache, scales, num_blocks, table, max_blocks,
                               seq_lens, n_split, p.o, p.lse, p.redo, nullptr, s);
-  const GenericArgs a = latent_args(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
-                                    seq_lens, n_split, p);
+  const GenericArgs a = latent_args(d, batch, s_q, q_abs, cache, nullptr, num_blocks, table,
+                                    max_blocks, seq_lens, n_split, p);
   return d.dtype == MLA_BF16 ? run_generic<bf16, false>(a, batch, s)
                              : run_generic<float, false>(a, batch, s);
 }
 
 hipError_t launch_decode_merge(const mla_dims& d, int batch, int s_q, const void* q_abs,
-                               const void* cache, int num_blocks, const int32_t* table,
-                               int max_blocks, const int32_t* seq_lens, const void* w_uv,
-                               int n_split, void* ws, void* out, float* lse, hipStream_t s) {
+                               const void* cache, const float* scales, int num_blocks,
+                               const int32_t* table, int max_blocks, const int32_t* seq_lens,
+                               const void* w_uv, int n_split, void* ws, void* out, float* lse,
+                               hipStream_t s) {
   if (n_split == 0) {  // length-balanced plan, as in launch_decode_splitk
     const Partials p = partials_of(static_cast<char*>(ws) + kPlanBytes, 1, 1, d.n_heads,
                                    kPlanSlots, d.d_c, 2);
-    GenericArgs a = latent_args(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
-                                seq_lens, kPlanCap, p);
+    GenericArgs a = latent_args(d, batch, s_q, q_abs, cache, scales, num_blocks, table,
+                                max_blocks, seq_lens, kPlanCap, p);
     a.plan = static_cast<const SplitPlan*>(ws);
     return run_combine<bf16>(a, p.redo, batch, d.d_v, w_uv, out, lse, s);
   }
   const Partials p = partials_of(ws, batch, s_q, d.n_heads, n_split, d.d_c, d.dtype == MLA_BF16 ? 2 : 4);
-  const GenericArgs a = latent_args(d, batch, s_q, q_abs, cache, num_blocks, table, max_blocks,
-                                    seq_lens, n_split, p);
+  const GenericArgs a = latent_args(d, batch, s_q, q_abs, cache, scales, num_blocks, table,
+                                    max_blocks, seq_lens, n_split, p);
   // Only the MFMA kernel writes recompute flags; the portable kernel computes every split.
-  const int* redo = uses_mfma(d) ? p.redo : nullptr;
+  const int* redo = uses_mfma(d) || scales != nullptr ? p.redo : nullptr;
   return d.dtype == MLA_BF16 ? run_combine<bf16>(a, redo, batch, d.d_v, w_uv, out, lse, s)
                              : run_combine<float>(a, redo, batch, d.d_v, w_uv, out, lse, s);
 }

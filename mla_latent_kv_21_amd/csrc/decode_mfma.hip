@@ -50,6 +50,23 @@ constexpr float kHead = 64.0f;                    // P <= 2^kHead, else recomput
 constexpr int kPre = 10;                          // score fragments read ahead of their MFMA
 constexpr int kVPre = 2;                          // P · V steps whose V fragments are in flight
 constexpr int kSlots = 4;                         // ring slots: two tiles in flight
+// e4m3 rows (d_c + d_r bytes, one fp32 scale per position): 32-position tiles of 18,432 bytes
+// plus their 128 bytes of scales stream into a 3-slot staging ring after two bf16 tile slots
+constexpr int kF8RowBytes = kRowElems;                      // 576
+constexpr int kF8TileBytes = kTileTok * kF8RowBytes;        // 18,432
+constexpr int kF8SlotBytes = kF8TileBytes + 4 * kTileTok;   // + the tile's 32 scales
+constexpr int kF8Slots = 3;
+constexpr int kF8Base = 2 * kTileBytes;                     // staging after two bf16 slots
+constexpr int kDma8 = 5;                                    // copies per wave per fp8 tile
+static_assert(kF8Base + kF8Slots * kF8SlotBytes <= kSlots * kTileBytes, "fp8 staging fits");
+
+// A device address as a wave-uniform value (so that asm operands can take it in SGPRs).
+__device__ __forceinline__ const char* uniform_ptr(const char* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(v));
+  const unsigned hi = __builtin_amdgcn_readfirstlane(static_cast<unsigned>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<unsigned long long>(hi) << 32) | lo);
+}
 
 // Physical 16-byte chunk of logical chunk c in tile row t is c ^ swz(t). swz is a linear map
 // of the row's low four bits into three bits (a row's 72 chunks stay in their groups of 8).
@@ -86,9 +103,15 @@ struct SoftState {
   bf16x8 pf[2];
 };
 
-template <int NW>
+// kFp8: the cache rows are e4m3 bytes with one fp32 power-of-two scale per position
+// (`scales`, indexed like the cache slots). Tiles then stream into a staging ring and every
+// tile is dequantised exactly (byte x scale is a bf16 value) into a bf16 tile slot before the
+// same scores and P · V run on it: the result is the bf16 kernel's on the dequantised rows,
+// with half the bytes read from memory.
+template <int NW, bool kFp8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ cache,
+                        const float* __restrict__ scales,
                         const int32_t* __restrict__ table, const int32_t* __restrict__ lens,
                         int num_blocks, int max_blocks, int bs, int s_q, int n_split,
                         float scale_log2, uint16_t* __restrict__ part_o,
@@ -102,6 +125,13 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   __shared__ __attribute__((aligned(16))) char ring[kSlots][kTileBytes];
   __shared__ Shared<NW> sh;
   static_assert(sizeof(ring) + sizeof(Shared<NW>) <= 160 * 1024, "LDS");
+  // bf16 tile slots in use: four (two in flight, two computed on) or, with e4m3 rows, two
+  // (the staging ring holds the tiles in flight)
+  constexpr int kBMask = (kFp8 ? 2 : kSlots) - 1;
+  auto stage8 = [&](int i) -> char* {
+    return reinterpret_cast<char*>(ring) + kF8Base + (i % kF8Slots) * kF8SlotBytes;
+  };
+  static_assert(!kFp8 || NW == 4, "the e4m3 copy plan is laid out for four waves");
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -221,7 +251,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   int ids = load_ids();
   // Cache address of the tile at pos0 (a multiple of 32 inside one block) and its number of
   // valid positions (0 for a bad block id, whose rows are then never used).
-  const int64_t blk_bytes = static_cast<int64_t>(bs) * kRowBytes;
+  constexpr int kRB = kFp8 ? kF8RowBytes : kRowBytes;  // bytes per cache row in memory
+  const int64_t blk_bytes = static_cast<int64_t>(bs) * kRB;
+  int64_t tile_first_slot = 0;  // cache slot of the last tile looked up (e4m3: its scales)
   // jb = pos0 / bs and off = pos0 - jb * bs are passed in (the loop tracks them incrementally)
   auto tile_src_at = [&](int pos0, int jb, int off, int* nvalid) -> const char* {
     if (jb - jbase >= 64) {
@@ -232,7 +264,8 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     const bool ok = id >= 0 && id < num_blocks;
     const int n = t1 - pos0 < kTileTok ? t1 - pos0 : kTileTok;
     *nvalid = ok ? n : 0;
-    return reinterpret_cast<const char*>(cache) + (ok ? id : 0) * blk_bytes + off * kRowBytes;
+    if constexpr (kFp8) tile_first_slot = static_cast<int64_t>(ok ? id : 0) * bs + off;
+    return reinterpret_cast<const char*>(cache) + (ok ? id : 0) * blk_bytes + off * kRB;
   };
   auto tile_src = [&](int pos0, int* nvalid) -> const char* {
     const int jb = pos0 / bs;
@@ -248,10 +281,62 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   auto issue_part = [&](const char* src, unsigned lbase, int j) __attribute__((always_inline)) {
     if (src != nullptr) dma16(src, doff[j], lbase + j * NW * 64 * 16);
   };
+  // e4m3 tiles: copy j < 4 moves tile chunk (4 j + w) 64 + lane; copy 4 moves chunks
+  // 1024 .. 1151 (waves 0 and 1) or the tile's 32 scales (lanes 0..7 of waves 2 and 3, the
+  // same bytes twice), so that every wave issues the same number of copies per tile. The
+  // staging slot holds the tile's bytes in order, then the scales.
+  auto issue_part8 = [&](const char* src, const char* ssrc, unsigned lbase, int j)
+                         __attribute__((always_inline)) {
+    if (src == nullptr) return;
+    if (j < 4) {
+      dma16(src, static_cast<unsigned>(((4 * j + w) * 64 + lane) * 16),
+            lbase + (4 * j + w) * 64 * 16);
+    } else if (w < 2) {
+      dma16(src, static_cast<unsigned>((1024 + w * 64 + lane) * 16), lbase + (1024 + w * 64) * 16);
+    } else if (lane < 8) {
+      dma16(ssrc, static_cast<unsigned>(lane * 16), lbase + kF8TileBytes);
+    }
+  };
+  // the tile's scales in memory (e4m3 rows), from the slot tile_src_at just looked up
+  auto scales_src = [&]() -> const char* {
+    return uniform_ptr(reinterpret_cast<const char*>(scales + tile_first_slot));
+  };
+  // e4m3 rows: a staged tile dequantised into a bf16 tile slot, in the swizzled layout the
+  // scores and P · V read (thread 8 t + s converts 16-byte chunks s, s + 8, ... of row t:
+  // byte x scale, exact in bf16); rows past nvalid become zeros.
+  auto dequant = [&](const char* f8, char* bt, int nvalid) __attribute__((always_inline)) {
+    const int t = threadIdx.x >> 3, s8 = threadIdx.x & 7;
+    const float sc = *reinterpret_cast<const float*>(f8 + kF8TileBytes + 4 * t);
+    const bool ok = t < nvalid;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const int c = s8 + 8 * k;
+      if (c < kF8RowBytes / 16) {
+        uint4 lo = make_uint4(0u, 0u, 0u, 0u), up = lo;
+        if (ok) {
+          const uint4 v = *reinterpret_cast<const uint4*>(f8 + t * kF8RowBytes + 16 * c);
+          // bytes 0,1 (low word) then 2,3 (high word) of each dword: element order kept
+          auto lw = [&](unsigned x) {
+            return __builtin_bit_cast(unsigned,
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, sc, false));
+          };
+          auto hw = [&](unsigned x) {
+            return __builtin_bit_cast(unsigned,
+                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, sc, true));
+          };
+          lo = make_uint4(lw(v.x), hw(v.x), lw(v.y), hw(v.y));
+          up = make_uint4(lw(v.z), hw(v.z), lw(v.w), hw(v.w));
+        }
+        *reinterpret_cast<uint4*>(bt + t * kRowBytes + (((2 * c) ^ swz(t)) << 4)) = lo;
+        *reinterpret_cast<uint4*>(bt + t * kRowBytes + (((2 * c + 1) ^ swz(t)) << 4)) = up;
+      }
+    }
+  };
 
   // ---- scores S^T[position][head] of one tile over the 576-wide rows, each fragment read
   // kPre products ahead of its MFMA.
-  auto scores = [&](const char* cur, const char* dsrc, unsigned dlds)
+  constexpr int kCopies = kFp8 ? kDma8 : kDma;
+  auto scores = [&](const char* cur, const char* dsrc, unsigned dlds, const char* ssrc)
                     __attribute__((always_inline)) -> f32x16 {
     f32x16 sc;
 #pragma unroll
@@ -266,9 +351,13 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       const int nx = ks + kPre;
       if (nx < kKSteps) af[ks % kPre] = lds16(cur + qb[nx & 3] + 128 * (nx >> 2));
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur, qf[ks], sc, 0, 0, 0);
-      // copies spread evenly over the K-steps (kDma <= kKSteps)
-      if ((ks * kDma) / kKSteps != ((ks + 1) * kDma) / kKSteps)
-        issue_part(dsrc, dlds, (ks * kDma) / kKSteps);
+      // copies spread evenly over the K-steps (kCopies <= kKSteps)
+      if ((ks * kCopies) / kKSteps != ((ks + 1) * kCopies) / kKSteps) {
+        if constexpr (kFp8)
+          issue_part8(dsrc, ssrc, dlds, (ks * kCopies) / kKSteps);
+        else
+          issue_part(dsrc, dlds, (ks * kCopies) / kKSteps);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     return sc;
@@ -383,7 +472,13 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   int nv1 = 0, nv2 = 0;
   {
     int nv0;
-    issue_tile(tile_src(t0, &nv0), ring[0]);
+    if constexpr (kFp8) {
+      const char* src = tile_src(t0, &nv0);
+      const unsigned lb = lds_addr(stage8(0));
+      for (int j = 0; j < kDma8; ++j) issue_part8(src, scales_src(), lb, j);
+    } else {
+      issue_tile(tile_src(t0, &nv0), ring[0]);
+    }
     // vector memory completes in issue order: the query loads land before tiles 1 and 2, and
     // the compiler's waits for them (which do not count the copies) stay conservative
     {
@@ -392,36 +487,54 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
     }
-    if (ntiles > 1) issue_tile(tile_src(t0 + kTileTok, &nv1), ring[1]);
-    if (ntiles > 2) issue_tile(tile_src(t0 + 2 * kTileTok, &nv2), ring[2]);
+    if constexpr (kFp8) {
+      for (int i = 1; i < 3; ++i) {
+        if (ntiles > i) {
+          const char* src = tile_src(t0 + i * kTileTok, i == 1 ? &nv1 : &nv2);
+          const unsigned lb = lds_addr(stage8(i));
+          for (int j = 0; j < kDma8; ++j) issue_part8(src, scales_src(), lb, j);
+        }
+      }
+    } else {
+      if (ntiles > 1) issue_tile(tile_src(t0 + kTileTok, &nv1), ring[1]);
+      if (ntiles > 2) issue_tile(tile_src(t0 + 2 * kTileTok, &nv2), ring[2]);
+    }
     if (ntiles > 2)
-      wait_vm<2 * kDma>();
+      wait_vm<2 * kCopies>();
     else if (ntiles > 1)
-      wait_vm<kDma>();
+      wait_vm<kCopies>();
     else
       wait_vm<0>();
     __syncthreads();
-    softmax_all(scores(ring[0], nullptr, 0u), nv0, 0);
-    if (nv0 < kTileTok) zero_tail(ring[0], nv0);
+    if constexpr (kFp8) {
+      dequant(stage8(0), ring[0], nv0);
+      __syncthreads();
+    }
+    softmax_all(scores(ring[0], nullptr, 0u, nullptr), nv0, 0);
+    if constexpr (!kFp8) {
+      if (nv0 < kTileTok) zero_tail(ring[0], nv0);
+    }
   }
 
   // block and in-block offset of tile t+3, advanced by one tile per iteration
   int jb3 = (t0 + 3 * kTileTok) / bs;
   int off3 = t0 + 3 * kTileTok - jb3 * bs;
   for (int t = 0; t < ntiles; ++t) {
-    const int slot = t & (kSlots - 1);
-    const int nslot = (t + 1) & (kSlots - 1);
+    const int slot = t & kBMask;
+    const int nslot = (t + 1) & kBMask;
     const int pos0 = t0 + t * kTileTok;
     // tile t+1 has landed (tile t+2 may still be in flight); after the barrier P(t) and the
     // zeroed tail of tile t are visible to every wave and the slot of tile t-1 is free
     if (t + 2 < ntiles)
-      wait_vm<kDma>();
+      wait_vm<kCopies>();
     else
       wait_vm<0>();
     __syncthreads();
     int nv3 = 0;
     const char* src3 =
         t + 3 < ntiles ? tile_src_at(pos0 + 3 * kTileTok, jb3, off3, &nv3) : nullptr;
+    const char* ssrc3 = nullptr;
+    if constexpr (kFp8) ssrc3 = src3 != nullptr ? scales_src() : nullptr;
     off3 += kTileTok;
     if (off3 >= bs) {
       off3 -= bs;
@@ -433,12 +546,22 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     const int nv_next = t + 1 < ntiles ? nv1 : 0;
     nv1 = nv2;
     nv2 = nv3;
-    f32x16 sc = scores(ring[nslot], src3, lds_addr(ring[(t + 3) & (kSlots - 1)]) + w * 64 * 16);
+    if constexpr (kFp8) {
+      // tile t+1 is staged: dequantised into the bf16 slot tile t-1 used (every wave is past
+      // its P · V), then published by a second barrier
+      if (t + 1 < ntiles) dequant(stage8(t + 1), ring[nslot], nv_next);
+      __syncthreads();
+    }
+    const unsigned dlds = kFp8 ? lds_addr(stage8(t + 3))
+                               : lds_addr(ring[(t + 3) & (kSlots - 1)]) + w * 64 * 16;
+    f32x16 sc = scores(ring[nslot], src3, dlds, ssrc3);
     if (nv_next < kTileTok) mask_tail(sc, nv_next);
     pv(ring[slot], t & 1, sc, (t + 1) & 1);
     // zeroed before the next barrier; other waves may still be reading these rows for their
     // scores, which are masked anyway
-    if (t + 1 < ntiles && nv_next < kTileTok) zero_tail(ring[nslot], nv_next);
+    if constexpr (!kFp8) {
+      if (t + 1 < ntiles && nv_next < kTileTok) zero_tail(ring[nslot], nv_next);
+    }
   }
 
   // ---- partials: o / l and m_ref + log2(l) per head, plus the recompute flag.
@@ -498,27 +621,37 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
 
 }  // namespace
 
+bool mfma_decode_fp8_fits(const mla_dims& d) {
+  return d.dtype == MLA_BF16 && d.d_c == 512 && d.d_r == 64 && d.block_size % 32 == 0 &&
+         d.n_heads == 128;
+}
+
 bool mfma_decode_fits(const mla_dims& d) {
   return d.dtype == MLA_BF16 && d.d_c == 512 && d.d_r == 64 && d.block_size % 32 == 0 &&
          (d.n_heads == 32 || d.n_heads == 64 || d.n_heads == 128);
 }
 
 hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void* q_abs,
-                              const void* cache, int num_blocks, const int32_t* table,
-                              int max_blocks, const int32_t* seq_lens, int n_split,
-                              void* part_o, float* part_lse, int* redo, SplitPlan* plan,
-                              hipStream_t s) {
+                              const void* cache, const float* scales, int num_blocks,
+                              const int32_t* table, int max_blocks, const int32_t* seq_lens,
+                              int n_split, void* part_o, float* part_lse, int* redo,
+                              SplitPlan* plan, hipStream_t s) {
   const float scale_log2 = softmax_scale_of(d) * 1.4426950408889634f;
   const dim3 grid = plan != nullptr ? dim3(kPlanSlots) : dim3(n_split, s_q, batch);
-#define MLA_LAUNCH(NW_)                                                                      \
-  hipLaunchKernelGGL(decode_mfma_kernel<NW_>, grid, dim3(64 * NW_), 0, s,                     \
+#define MLA_LAUNCH(NW_, FP8_)                                                                \
+  hipLaunchKernelGGL((decode_mfma_kernel<NW_, FP8_>), grid, dim3(64 * NW_), 0, s,             \
                      static_cast<const uint16_t*>(q_abs), static_cast<const uint16_t*>(cache), \
-                     table, seq_lens, num_blocks, max_blocks, d.block_size, s_q, n_split,      \
-                     scale_log2, static_cast<uint16_t*>(part_o), part_lse, redo, batch, plan)
-  switch (d.n_heads) {
-    case 128: MLA_LAUNCH(4); break;
-    case 64: MLA_LAUNCH(2); break;
-    default: MLA_LAUNCH(1); break;
+                     scales, table, seq_lens, num_blocks, max_blocks, d.block_size, s_q,       \
+                     n_split, scale_log2, static_cast<uint16_t*>(part_o), part_lse, redo,      \
+                     batch, plan)
+  if (scales != nullptr) {
+    MLA_LAUNCH(4, true);  // e4m3 rows: H = 128 only (mfma_decode_fp8_fits)
+  } else {
+    switch (d.n_heads) {
+      case 128: MLA_LAUNCH(4, false); break;
+      case 64: MLA_LAUNCH(2, false); break;
+      default: MLA_LAUNCH(1, false); break;
+    }
   }
 #undef MLA_LAUNCH
   return hipGetLastError();

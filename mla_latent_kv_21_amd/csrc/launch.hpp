@@ -20,16 +20,22 @@ size_t append_ws_bytes(const mla_dims& d, int n_tok);
 hipError_t launch_append(const mla_dims& d, int n_tok, const void* x, const int32_t* seq_idx,
                          const int32_t* pos, const void* w_dkv, const void* gamma,
                          const void* w_kr, const int32_t* table, int batch, int max_blocks,
-                         int num_blocks, void* cache, void* ws, hipStream_t s);
+                         int num_blocks, void* cache, float* cache_scale, void* ws,
+                         hipStream_t s);
 // The append, then the absorption of q_batch x s_q queries (none when q_batch * s_q == 0). On
-// the matrix cores the absorption shares a launch with the append's projection.
+// the matrix cores the absorption shares a launch with the append's projection. cache_scale
+// non-null: bf16 dims, and the rows go out as e4m3 bytes with one scale per slot.
 hipError_t launch_append_absorb(const mla_dims& d, int n_tok, const void* x,
                                 const int32_t* seq_idx, const int32_t* pos, const void* w_dkv,
                                 const void* gamma, const void* w_kr, const int32_t* table,
-                                int batch, int max_blocks, int num_blocks, void* cache, void* ws,
-                                int q_batch, int s_q, const void* q_nope, const void* q_pe,
+                                int batch, int max_blocks, int num_blocks, void* cache,
+                                float* cache_scale, void* ws, int q_batch, int s_q, const void* q_nope, const void* q_pe,
                                 const int32_t* q_pos, const void* w_uk, void* q_abs,
                                 hipStream_t s);
+
+// bf16 rows of ncols (a multiple of 4, at most 1024) values to e4m3 bytes and one scale per row.
+hipError_t launch_quantize_e4m3(int64_t n_rows, int ncols, const void* rows, void* out,
+                               float* scale, hipStream_t s);
 
 // Split-K partial sums of y = x · [W_a | W_b] for n_tok tokens (K-wide rows of x):
 // y_part[k][n][c] over C range [256 k, 256 k + 256), k < projection_ksplit(K). The matrix-core
@@ -59,15 +65,18 @@ hipError_t launch_absorb(const mla_dims& d, int batch, int s_q, const void* q_no
 size_t partials_bytes(int batch, int s_q, int heads, int n_split, int width, int elt);
 
 // Split-K core: every (split, query, sequence) writes its partials (and recompute flag).
+// scales != NULL: the cache rows are e4m3 bytes, row r worth bytes x scales[r] (bf16 dims
+// otherwise, on the matrix-core kernel: mfma_decode_fp8_fits).
 hipError_t launch_decode_splitk(const mla_dims& d, int batch, int s_q, const void* q_abs,
-                                const void* cache, int num_blocks, const int32_t* table,
-                                int max_blocks, const int32_t* seq_lens, int n_split, void* ws,
-                                hipStream_t s);
+                                const void* cache, const float* scales, int num_blocks,
+                                const int32_t* table, int max_blocks, const int32_t* seq_lens,
+                                int n_split, void* ws, hipStream_t s);
 // Merge: flagged splits recomputed, log-sum-exp merge over splits, W_UV per group.
 hipError_t launch_decode_merge(const mla_dims& d, int batch, int s_q, const void* q_abs,
-                               const void* cache, int num_blocks, const int32_t* table,
-                               int max_blocks, const int32_t* seq_lens, const void* w_uv,
-                               int n_split, void* ws, void* out, float* lse, hipStream_t s);
+                               const void* cache, const float* scales, int num_blocks,
+                               const int32_t* table, int max_blocks, const int32_t* seq_lens,
+                               const void* w_uv, int n_split, void* ws, void* out, float* lse,
+                               hipStream_t s);
 
 hipError_t launch_expand(const mla_dims& d, int batch, const void* cache, int num_blocks,
                          const int32_t* table, int max_blocks, const int32_t* seq_lens,
@@ -80,16 +89,18 @@ hipError_t launch_gqa_decode(const mla_dims& d, int batch, int s_q, const void* 
                              const int32_t* seq_lens, int n_split, void* ws, void* out,
                              float* lse, hipStream_t s);
 
-// Whether the MFMA decode kernel handles these dims (bf16, d_c 512, d_r 64, H % 32 == 0).
+// Whether the MFMA decode kernel handles these dims (bf16, d_c 512, d_r 64, H % 32 == 0), and
+// with e4m3 rows (H = 128 as well).
 bool mfma_decode_fits(const mla_dims& d);
+bool mfma_decode_fp8_fits(const mla_dims& d);
 // With plan != NULL the splits follow the length-balanced plan (plan.hpp), which the kernel
 // computes and stores at *plan; else n_split uniform splits per (sequence, query).
 struct SplitPlan;
 hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void* q_abs,
-                              const void* cache, int num_blocks, const int32_t* table,
-                              int max_blocks, const int32_t* seq_lens, int n_split,
-                              void* part_o, float* part_lse, int* redo, SplitPlan* plan,
-                              hipStream_t s);
+                              const void* cache, const float* scales, int num_blocks,
+                              const int32_t* table, int max_blocks, const int32_t* seq_lens,
+                              int n_split, void* part_o, float* part_lse, int* redo,
+                              SplitPlan* plan, hipStream_t s);
 // Whether n_split = 0 takes the length-balanced plan for these dims and rows, and the
 // workspace of a planned decode (the plan, then partials for every slot).
 bool plan_applies(const mla_dims& d, int batch, int s_q);

@@ -219,3 +219,51 @@ def test_decode_noalloc_host_checks(L):
     # the largest workload shapes fit: long context (4 x 64 splits) and the balanced plan
     assert L.mla_decode_workspace_bytes(ctypes.byref(d), 4, 1, 64, 2048) <= M.MLA_NOALLOC_SCRATCH_BYTES
     assert L.mla_decode_workspace_bytes(ctypes.byref(d), 32, 4, 0, 512) <= M.MLA_NOALLOC_SCRATCH_BYTES
+
+
+def fp8_decode_call(L, d, scales=FAKE, ws=FAKE, ws_bytes=1 << 30, batch=2):
+    return L.mla_decode_fp8(ctypes.byref(d), batch, 1, P(FAKE), P(FAKE), P(scales), 8, P(FAKE),
+                            4, P(FAKE), P(FAKE), 0, P(ws), ws_bytes, P(FAKE), None, None)
+
+
+def test_fp8_host_checks(L):
+    """The e4m3 calls refuse, before launch, shapes their kernels do not cover (H != 128, the
+    portable-kernel flag, fp32 dims, rows not a multiple of 16 bytes) and missing or misaligned
+    scales; empty calls do nothing."""
+    d = dims()
+    assert fp8_decode_call(L, d, batch=0) == 0
+    assert fp8_decode_call(L, dims(n_heads=64, n_groups=64)) == -2
+    assert fp8_decode_call(L, dims(dtype="f32")) == -2
+    assert fp8_decode_call(L, M.make_dims(7168, 128, 128, 128, 512, 64, 128, 64, "bf16",
+                                          generic=True)) == -2
+    assert fp8_decode_call(L, d, scales=0) == -1
+    assert fp8_decode_call(L, d, scales=FAKE + 4) == -6
+    assert fp8_decode_call(L, d, ws=None, ws_bytes=0) == -5
+    assert L.mla_decode_fp8_splitk(ctypes.byref(d), 2, 1, P(FAKE), P(FAKE), None, 8, P(FAKE), 4,
+                                   P(FAKE), 0, P(FAKE), 1 << 30, None) == -1
+    assert L.mla_decode_fp8_merge(ctypes.byref(dims(block_size=48)), 2, 1, P(FAKE), P(FAKE),
+                                  P(FAKE), 8, P(FAKE), 4, P(FAKE), P(FAKE), 0, P(FAKE), 1 << 30,
+                                  P(FAKE), None, None) == -2
+    # quantisation: rows of d_c + d_r values, 16-byte multiples of at most 1024
+    qd = ctypes.byref(d)
+    assert L.mla_cache_quantize_fp8(qd, 0, None, None, None, None) == 0
+    assert L.mla_cache_quantize_fp8(qd, -1, P(FAKE), P(FAKE), P(FAKE), None) == -4
+    assert L.mla_cache_quantize_fp8(qd, 4, P(FAKE), None, P(FAKE), None) == -1
+    assert L.mla_cache_quantize_fp8(qd, 4, P(FAKE), P(FAKE), P(FAKE + 4), None) == -6
+    assert L.mla_cache_quantize_fp8(ctypes.byref(dims(d_c=504)), 4, P(FAKE), P(FAKE), P(FAKE),
+                                    None) == -2
+    assert L.mla_cache_quantize_fp8(ctypes.byref(dims(dtype="f32")), 4, P(FAKE), P(FAKE),
+                                    P(FAKE), None) == -2
+    # append: the scales are required once there is a token to write
+    need = L.mla_cache_append_workspace_bytes(qd, 4)
+    assert L.mla_cache_append_fp8(qd, 0, None, None, None, None, None, None, None, 1, 1, 1, None,
+                                  None, None, 0, None) == 0
+    assert L.mla_cache_append_fp8(qd, 4, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                                  P(FAKE), 1, 4, 8, P(FAKE), None, P(FAKE), need, None) == -1
+    assert L.mla_cache_append_fp8(qd, 4, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+                                  P(FAKE), 1, 4, 8, P(FAKE), P(FAKE), P(FAKE), need - 1,
+                                  None) == -5
+    assert L.mla_cache_append_absorb_q_fp8(
+        ctypes.byref(dims(d_r=40)), 4, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
+        P(FAKE), 1, 4, 8, P(FAKE), P(FAKE), P(FAKE), need, 1, P(FAKE), P(FAKE), P(FAKE),
+        P(FAKE), P(FAKE), None) == -2                       # 552 values: not 16-byte rows

@@ -1,0 +1,326 @@
+"""GPU parity of the FP8 (E4M3) latent cache: quantisation, append and decode.
+
+* mla_cache_quantize_fp8 against the oracle's encoder, bit for bit (bytes and scales);
+* mla_cache_append_fp8 (and the variant that also absorbs the queries) writes exactly the
+  bytes that quantising the bf16 append's rows gives, and rows within the format's half step
+  of the oracle's f64 rows;
+* mla_decode_fp8 equals mla_decode on the dequantised cache bit for bit (a byte times a
+  power-of-two scale is exact in bf16), and both match the oracle on the dequantised rows
+  within the bf16 tolerance of mla_decode.
+
+Caches for the decode tests are drawn directly as bytes and scales (workloads.cache_pool_e4m3);
+unowned slots hold the NaN code 0x7F and a NaN scale, so a stray read poisons the result.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_cases import (DEV, TOL, check_lse, check_per_seq, decode_ws_layout, dev, note, pick)
+from mla_latent_kv_21_amd import binding as M
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+BASE, EPS = 10000.0, 1e-6
+NAN_CODE = 0x7F
+
+
+def torch_dequant(codes: torch.Tensor, scales: torch.Tensor) -> torch.Tensor:
+    """bf16 [.., w] = value(code) x scale through torch's own float8_e4m3fn (exact in bf16)."""
+    v = codes.view(torch.float8_e4m3fn).float() * scales.float().unsqueeze(-1)
+    return v.to(torch.bfloat16)
+
+
+def fp8_case(w, lens, s_q=1, poison=True, extra=0, random_table=True):
+    lens = np.asarray(lens, np.int32)
+    wq = w.replace(batch=len(lens), s_q=s_q)
+    table, nb = W.block_table(wq, lens, random=random_table)
+    codes, scales = W.cache_pool_e4m3(wq, nb, extra=extra)
+    if poison:
+        mask = torch.from_numpy(~O.owned_slot_mask(table, lens, nb, w.block_size))
+        codes.view(-1, w.row)[mask] = NAN_CODE
+        scales.view(-1)[mask] = float("nan")
+    return dict(w=wq, lens=lens, table=table, nb=nb, codes=codes, scales=scales,
+                q_abs=W.absorbed_queries(wq), w_uv=W.weights(wq)["w_uv"])
+
+
+def run(c, fp8: bool, n_split=0, planned=False, codes=None, pool=None, ws_out=None):
+    """mla_decode_fp8 over the bytes, or mla_decode over torch's dequantised bf16 cache."""
+    w = c["w"]
+    d = M.dims_of(w)
+    mb = c["table"].shape[1]
+    ns = 0 if planned else n_split or M.mla_auto_split(d, w.batch, w.s_q, mb)
+    out = torch.empty(w.batch, w.s_q, w.n_heads, w.d_v, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(w.batch, w.s_q, w.n_heads, dtype=torch.float32, device=DEV)
+    ws = torch.zeros(M.mla_decode_workspace_bytes(d, w.batch, w.s_q, ns, mb), dtype=torch.uint8,
+                     device=DEV)
+    q, tab, lens, wuv = dev(c["q_abs"]), dev(c["table"]), dev(c["lens"]), dev(c["w_uv"])
+    if fp8:
+        M.mla_decode_fp8(d, q, dev(c["codes"]) if codes is None else codes,
+                         dev(c["scales"]), tab, lens, wuv, out, lse, n_split=ns, workspace=ws)
+    else:
+        p = dev(torch_dequant(c["codes"], c["scales"])) if pool is None else pool
+        M.mla_decode(d, q, p, tab, lens, wuv, out, lse, n_split=ns, workspace=ws)
+    torch.cuda.synchronize()
+    if ws_out is not None:
+        ws_out.append(ws.cpu())
+    return out.cpu(), lse.cpu()
+
+
+def oracle_fp8(c, seqs=None, heads=None):
+    """Expected (out, lse): the absorbed definition on the oracle's dequantised rows."""
+    w = c["w"]
+    seqs = range(w.batch) if seqs is None else seqs
+    scale = O.softmax_scale(w.d_nope, w.d_r)
+    outs, lses = [], []
+    for b in seqs:
+        L = int(c["lens"][b])
+        sl = O.seq_slots(c["table"], b, L, w.block_size)
+        codes = c["codes"].view(-1, w.row).numpy()[sl]
+        rows = O.dequantize_rows_e4m3(codes, c["scales"].view(-1).numpy()[sl])
+        o_lat, lse = O.decode_absorbed_latent(c["q_abs"][b], rows, w.d_c, scale, heads=heads)
+        outs.append(O.project_values(o_lat, c["w_uv"], w.n_groups, w.d_v, n_heads=w.n_heads,
+                                     heads=heads))
+        lses.append(lse)
+    return np.stack(outs), np.stack(lses)
+
+
+def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+# ----------------------------------------------------------------------------- quantisation
+def test_quantize_matches_oracle_bit_for_bit():
+    """Seeded bf16 rows (a ragged count: 4 rows per workgroup plus a tail of 3), with an
+    all-zero row, a negative-zero row, rows of tiny and huge magnitude, a lone outlier, and
+    values on the 448 s boundary."""
+    w = W.WORKLOADS["dsv3-paged"]
+    rows = W.cache_pool(w, 33, extra=1).view(-1, w.row)[:2047].clone()
+    rows[0] = 0.0
+    rows[1] = -0.0
+    rows[2] *= 2.0 ** -100
+    rows[3] *= 2.0 ** 100
+    rows[4, 17] = 3.0e4                                # one outlier sets the scale
+    rows[5] = 0.0
+    rows[5, 0] = 448.0                                 # amax exactly 448: scale 1
+    rows[6] = 0.0
+    rows[6, 1] = -0.875                                # 448 x 2^-9 exactly
+    rows[7, :] = torch.linspace(-3.5, 3.5, w.row).to(torch.bfloat16)
+    d = M.dims_of(w)
+    got_c = torch.empty(rows.shape, dtype=torch.uint8, device=DEV)
+    got_s = torch.empty(rows.shape[0], dtype=torch.float32, device=DEV)
+    note(f"quantize {rows.shape[0]} rows")
+    M.mla_cache_quantize_fp8(d, dev(rows), got_c, got_s)
+    torch.cuda.synchronize()
+    ref_c, ref_s = O.quantize_rows_e4m3(rows)
+    assert np.array_equal(got_c.cpu().numpy(), ref_c)
+    assert np.array_equal(got_s.cpu().double().numpy(), ref_s)
+    assert ref_s[5] == 1.0 and ref_s[6] == 2.0 ** -9 and ref_c[1, 0] == 0x80
+
+
+def test_quantize_of_nothing_is_a_no_op():
+    w = W.WORKLOADS["dsv3-paged"]
+    d = M.dims_of(w)
+    e = torch.empty(0, w.row, dtype=torch.bfloat16, device=DEV)
+    M.mla_cache_quantize_fp8(d, e, torch.empty(0, w.row, dtype=torch.uint8, device=DEV),
+                             torch.empty(0, dtype=torch.float32, device=DEV))
+
+
+# ----------------------------------------------------------------------------- append
+def append_inputs(w, lens, extra=0):
+    lens = np.asarray(lens, np.int32)
+    table, nb = W.block_table(w.replace(batch=len(lens)), lens)
+    seq = np.concatenate([np.full(L, b, np.int32) for b, L in enumerate(lens)])
+    pos = np.concatenate([np.arange(L, dtype=np.int32) for L in lens])
+    x = W.tokens(w, len(seq), extra=extra)
+    wts = W.weights(w, random_gamma=True)
+    return dict(lens=lens, table=table, nb=nb, seq=seq, pos=pos, x=x, wts=wts)
+
+
+@pytest.mark.parametrize("wl,lens", [("dsv3-paged", [3, 70, 129]), ("gqla-g8", [65])])
+def test_fp8_append_is_the_quantised_bf16_append(wl, lens):
+    w = W.WORKLOADS[wl]
+    a = append_inputs(w, lens, extra=2)
+    d = M.dims_of(w)
+    args = (dev(a["x"]), dev(a["seq"]), dev(a["pos"]), dev(a["wts"]["w_dkv"]),
+            dev(a["wts"]["gamma"]), dev(a["wts"]["w_kr"]), dev(a["table"]), a["nb"])
+    note(f"fp8 append {wl} lens={lens}")
+    bf = torch.full((a["nb"], w.block_size, w.row), float("nan"), dtype=torch.bfloat16,
+                    device=DEV)
+    M.mla_cache_append(d, *args, bf)
+    c8 = torch.full((a["nb"], w.block_size, w.row), NAN_CODE, dtype=torch.uint8, device=DEV)
+    s8 = torch.full((a["nb"], w.block_size), float("nan"), dtype=torch.float32, device=DEV)
+    M.mla_cache_append_fp8(d, *args, c8, s8)
+    qc = torch.empty_like(c8)
+    qs = torch.empty_like(s8)
+    M.mla_cache_quantize_fp8(d, bf, qc, qs)
+    torch.cuda.synchronize()
+    owned = torch.from_numpy(O.owned_slot_mask(a["table"], a["lens"], a["nb"], w.block_size))
+    c8, s8, qc, qs = c8.cpu(), s8.cpu(), qc.cpu(), qs.cpu()
+    # exactly the owned slots were written, with the bytes of the quantised bf16 rows
+    assert torch.equal(torch.isnan(s8.view(-1)), ~owned)
+    assert torch.equal(c8.view(-1, w.row)[owned], qc.view(-1, w.row)[owned])
+    assert torch.equal(s8.view(-1)[owned], qs.view(-1)[owned])
+    assert bool((c8.view(-1, w.row)[~owned] == NAN_CODE).all())
+    # and within the format's half step (plus a bf16 rounding) of the oracle's f64 rows
+    ref = O.latent_rows(a["x"], a["wts"]["w_dkv"], a["wts"]["gamma"], a["wts"]["w_kr"],
+                        a["pos"], BASE, EPS)
+    k = 0
+    for b, L in enumerate(a["lens"]):
+        sl = O.seq_slots(a["table"], b, int(L), w.block_size)
+        sc = s8.view(-1).double().numpy()[sl]
+        got = O.dequantize_rows_e4m3(c8.view(-1, w.row).numpy()[sl], sc)
+        r = ref[k:k + L]
+        bound = (2.0 ** -4 + 2.0 ** -8 + 1e-5) * np.abs(r) + 2.0 ** -10 * sc[:, None] + \
+            1e-5 * np.max(np.abs(r), axis=1, keepdims=True)
+        assert np.all(np.abs(got - r) <= bound)
+        # the scale is the oracle's (from its rows rounded to bf16) for every row whose
+        # largest magnitude is not within a bf16 step of a scale boundary 448 s or 224 s,
+        # where one ulp of fp32 accumulation may round the bf16 value across it
+        amax = np.max(np.abs(O.round_bf16(r)), axis=1)
+        want = np.array([O.e4m3_row_scale(m) for m in amax])
+        near = (np.abs(amax / (448.0 * want) - 1.0) < 2.0 ** -7) | \
+            (np.abs(amax / (224.0 * want) - 1.0) < 2.0 ** -7)
+        assert np.array_equal(sc[~near], want[~near])
+        assert np.all((sc[near] == want[near]) | (sc[near] == 2 * want[near]) |
+                      (sc[near] == want[near] / 2))
+        k += L
+
+
+def test_fp8_append_absorb_in_one_launch():
+    """mla_cache_append_absorb_q_fp8 writes the bytes of mla_cache_append_fp8 and the absorbed
+    queries of mla_absorb_q, bit for bit."""
+    w = W.WORKLOADS["gqla-g8"].replace(batch=4, s_q=2)
+    lens = np.array([70, 129, 64, 5], np.int32)
+    table, nb = W.block_table(w, lens)
+    seq = np.repeat(np.arange(w.batch, dtype=np.int32), w.s_q)
+    qpos = W.query_positions(w, lens)
+    pos = qpos.reshape(-1).astype(np.int32)
+    x = W.tokens(w, len(seq), extra=3)
+    wts = W.weights(w, random_gamma=True)
+    q = W.queries(w)
+    d = M.dims_of(w)
+    outs = []
+    for fused in (False, True):
+        note(f"fp8 append+absorb fused={fused}")
+        c8 = torch.full((nb, w.block_size, w.row), NAN_CODE, dtype=torch.uint8, device=DEV)
+        s8 = torch.full((nb, w.block_size), float("nan"), dtype=torch.float32, device=DEV)
+        q_abs = torch.full((w.batch, w.s_q, w.n_heads, w.row), float("nan"),
+                           dtype=torch.bfloat16, device=DEV)
+        args = (dev(x), dev(seq), dev(pos), dev(wts["w_dkv"]), dev(wts["gamma"]),
+                dev(wts["w_kr"]), dev(table), nb, c8, s8)
+        if fused:
+            M.mla_cache_append_absorb_q_fp8(d, *args, dev(q["q_nope"]), dev(q["q_pe"]),
+                                            dev(qpos), dev(wts["w_uk"]), q_abs)
+        else:
+            M.mla_cache_append_fp8(d, *args)
+            M.mla_absorb_q(d, dev(q["q_nope"]), dev(q["q_pe"]), dev(qpos), dev(wts["w_uk"]),
+                           q_abs)
+        torch.cuda.synchronize()
+        outs.append((c8.cpu(), s8.cpu(), q_abs.cpu()))
+    for i in range(3):
+        assert same_bits(outs[0][i], outs[1][i])
+
+
+# ----------------------------------------------------------------------------- decode
+CASES = [
+    # (name, workload, lens, s_q, n_split): n_split 0 takes the length-balanced plan
+    ("ragged-planned", "dsv3-paged", [64, 33, 2600, 1], 1, 0),
+    ("ragged-split3", "dsv3-paged", [1, 77, 300], 1, 3),
+    ("one-split", "dsv3-paged", [1500], 1, 1),
+    ("many-splits", "long-128k", [4096, 100], 1, 64),
+    ("gqla-sq2", "gqla-g8", [2, 300], 2, 0),
+    ("gqla-sq4-split5", "gqla-g8", [4, 257, 1030], 4, 5),
+]
+
+
+@pytest.mark.parametrize("name,wl,lens,s_q,n_split", CASES, ids=[c[0] for c in CASES])
+def test_fp8_decode_is_bf16_decode_of_the_dequantised_cache(name, wl, lens, s_q, n_split):
+    w = W.WORKLOADS[wl]
+    c = fp8_case(w, lens, s_q=s_q, extra=w.seed % 100)
+    note(f"fp8 decode {name} lens={lens} s_q={s_q} n_split={n_split}")
+    out8, lse8 = run(c, True, n_split=n_split, planned=n_split == 0)
+    out16, lse16 = run(c, False, n_split=n_split, planned=n_split == 0)
+    assert same_bits(out8, out16) and same_bits(lse8, lse16)
+    ref, ref_lse = oracle_fp8(c)
+    check_per_seq(out8, ref, TOL["bf16"])
+    check_lse(lse8.double().numpy(), ref_lse, TOL["bf16"])
+
+
+def test_fp8_decode_halves_run_in_two_calls():
+    """mla_decode_fp8_splitk then mla_decode_fp8_merge is mla_decode_fp8, bit for bit."""
+    w = W.WORKLOADS["dsv3-paged"]
+    c = fp8_case(w, [700, 2049, 5], extra=31)
+    d = M.dims_of(w)
+    mb = c["table"].shape[1]
+    out_a, lse_a = run(c, True, n_split=7)
+    ws = torch.zeros(M.mla_decode_workspace_bytes(d, 3, 1, 7, mb), dtype=torch.uint8,
+                     device=DEV)
+    out = torch.empty(3, 1, w.n_heads, w.d_v, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(3, 1, w.n_heads, dtype=torch.float32, device=DEV)
+    args = (dev(c["q_abs"]), dev(c["codes"]), dev(c["scales"]), dev(c["table"]), dev(c["lens"]))
+    note("fp8 decode in two calls")
+    M.mla_decode_fp8_splitk(d, *args, 7, ws)
+    M.mla_decode_fp8_merge(d, *args, dev(c["w_uv"]), out, lse, 7, ws)
+    torch.cuda.synchronize()
+    assert same_bits(out.cpu(), out_a) and same_bits(lse.cpu(), lse_a)
+
+
+def test_fp8_recompute_fallback():
+    """A late position whose score outgrows the split's reference by far more than 2^64 is
+    flagged and recomputed exactly from the bytes, as on the bf16 cache."""
+    w = W.WORKLOADS["dsv3-paged"]
+    c = fp8_case(w, [2048], extra=32, random_table=False, poison=False)
+    q = c["q_abs"][0, 0, 5].float()                    # head 5's absorbed query
+    s = 2.0 ** -2                                      # 4 q fits: |q| < 28 at this draw
+    assert float(q.abs().max()) * 4 <= 448 * s
+    row = (4.0 * q / s).to(torch.float8_e4m3fn).view(torch.uint8)
+    c["codes"][1500 // 64, 1500 % 64] = row
+    c["scales"][1500 // 64, 1500 % 64] = s
+    note("fp8 decode outgrown reference -> recompute")
+    ws = []
+    out8, lse8 = run(c, True, n_split=2, ws_out=ws)
+    off, n = decode_ws_layout(c, 2)
+    assert ws[0][off:off + 4 * n].view(torch.int32).any(), "expected a flagged split"
+    out16, lse16 = run(c, False, n_split=2)
+    assert same_bits(out8, out16) and same_bits(lse8, lse16)
+    ref, ref_lse = oracle_fp8(c)
+    check_per_seq(out8, ref, TOL["bf16"])
+    check_lse(lse8.double().numpy(), ref_lse, TOL["bf16"])
+
+
+def test_fp8_shape_is_checked():
+    """Head counts other than 128 and the portable-kernel flag are refused before launch."""
+    w = W.WORKLOADS["mid-bf16"]                         # H = 32
+    c = fp8_case(w, [100], extra=33)
+    with pytest.raises(M.MlaError) as e:
+        run(c, True, n_split=1)
+    assert e.value.status == -2
+    w = W.WORKLOADS["dsv3-paged"]
+    c = fp8_case(w, [100], extra=34)
+    d = M.dims_of(w, generic=True)
+    out = torch.empty(1, 1, w.n_heads, w.d_v, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(M.MlaError) as e:
+        M.mla_decode_fp8(d, dev(c["q_abs"]), dev(c["codes"]), dev(c["scales"]), dev(c["table"]),
+                         dev(c["lens"]), dev(c["w_uv"]), out, n_split=1)
+    assert e.value.status == -2
+
+
+def test_fp8_full_size_sampled():
+    """The paged benchmark workload (64 sequences of 1,024 .. 8,192 positions, H = 128) over
+    an e4m3 cache, with the balanced plan the benchmark times; every output equals the bf16
+    decode of the dequantised cache, and a sample of sequences and heads matches the oracle."""
+    w = W.WORKLOADS["dsv3-paged"]
+    lens = W.seq_lens(w)
+    c = fp8_case(w, lens, extra=35, poison=False)
+    note(f"fp8 decode full size B={w.batch} sum(L)={int(lens.sum())}")
+    out8, lse8 = run(c, True, planned=True)
+    out16, lse16 = run(c, False, planned=True)
+    assert same_bits(out8, out16) and same_bits(lse8, lse16)
+    seqs = sorted({0, w.batch - 1, int(np.argmax(lens))})
+    heads = [0, 37, w.n_heads - 1]
+    ref, ref_lse = oracle_fp8(c, seqs=seqs, heads=heads)
+    check_per_seq(pick(out8, seqs, heads), ref, TOL["bf16"])
+    check_lse(pick(lse8, seqs, heads), ref_lse, TOL["bf16"])

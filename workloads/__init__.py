@@ -31,6 +31,7 @@ import torch
 S_W_DKV, S_GAMMA, S_W_KR, S_W_UK, S_W_UV, S_X, S_Q_NOPE, S_Q_PE, S_LENS, S_TABLE = range(10)
 S_CACHE_C, S_CACHE_KR, S_Q_ABS, S_X_NEW, S_POS_SHIFT = 10, 11, 12, 13, 14
 S_W_DQ, S_GAMMA_Q, S_W_UQ, S_W_QR, S_W_O, S_B_O, S_O = 15, 16, 17, 18, 19, 20, 21
+S_CACHE_E4M3 = 22
 
 
 @dataclasses.dataclass(frozen=True)
@@ -247,3 +248,20 @@ def cache_pool_device(w: Workload, num_blocks: int, device, extra: int = 0) -> t
     a = torch.randn((num_blocks, w.block_size, w.row), generator=g, device=device,
                     dtype=torch.float32)
     return a.to(w.torch_dtype)
+
+
+def cache_pool_e4m3(w: Workload, num_blocks: int, extra: int = 0):
+    """An e4m3 paged cache drawn directly as bytes: (codes uint8 [num_blocks, bs, d_c + d_r],
+    scales float32 [num_blocks, bs]).
+
+    Sign bits uniform; magnitude codes (the low 7 bits, which order E4M3 magnitudes
+    log-linearly) ~ round(N(104, 10)) clipped to the finite codes 0 .. 126, i.e. magnitudes
+    near 2^6 spread over about three binades; one scale per slot 2^k, k uniform in -8 .. -6.
+    The values code x scale then have the spread of the N(0, 1) bf16 rows of cache_pool.
+    """
+    r = rng(w, S_CACHE_E4M3, extra)
+    shp = (num_blocks, w.block_size, w.row)
+    mag = np.clip(np.rint(r.normal(104.0, 10.0, size=shp)), 0, 126).astype(np.uint8)
+    sign = (r.integers(0, 2, size=shp, dtype=np.uint8) << 7).astype(np.uint8)
+    scales = np.exp2(r.integers(-8, -5, size=shp[:2], endpoint=False)).astype(np.float32)
+    return torch.from_numpy(mag | sign), torch.from_numpy(scales)
