@@ -173,10 +173,29 @@ def power_sample(fn, seconds: float, torch):
             "readings": len(busy), "source": "amd-smi metric -p -c, every ~50 ms"}
 
 
-def absorbed_row(dev, torch, w, planned=True, reps=20):
+def fp8_caches(w, nb, n, dev, torch):
+    """n e4m3 caches (codes, scales) of workload w, each the library's quantisation of a
+    seeded bf16 cache_pool_device draw."""
+    import workloads as W
+    from mla_latent_kv_21_amd import binding as M
+    d = M.dims_of(w)
+    out = []
+    for k in range(n):
+        bf = W.cache_pool_device(w, nb, dev, extra=k)
+        codes = torch.empty(bf.shape, dtype=torch.uint8, device=dev)
+        scales = torch.empty(bf.shape[:2], dtype=torch.float32, device=dev)
+        M.mla_cache_quantize_fp8(d, bf, codes, scales)
+        torch.cuda.synchronize()
+        del bf
+        out.append((codes, scales))
+    return out
+
+
+def absorbed_row(dev, torch, w, planned=True, reps=20, fp8=False):
     """mla_decode (split-K core + merge + W_UV) on workload w, timed with HIP events over
     reps calls that rotate over enough cache copies to keep the MALL from serving them, with
-    the call's algorithmic bytes and FLOPs priced against the binding roofline."""
+    the call's algorithmic bytes and FLOPs priced against the binding roofline. fp8: the same
+    over an e4m3 cache (mla_decode_fp8, 580 bytes per position)."""
     import workloads as W
     from mla_latent_kv_21_amd import accounting as A
     from mla_latent_kv_21_amd import binding as M
@@ -184,8 +203,12 @@ def absorbed_row(dev, torch, w, planned=True, reps=20):
     lens = W.seq_lens(w)
     table, nb = W.block_table(w, lens)
     d = M.dims_of(w)
-    n_copies = _copies(nb * w.block_size * w.row * w.elt)
-    caches = [W.cache_pool_device(w, nb, dev, extra=k) for k in range(n_copies)]
+    row_b = A.fp8_row_bytes(w.d_c, w.d_r) if fp8 else w.row * w.elt
+    n_copies = _copies(nb * w.block_size * row_b)
+    if fp8:
+        caches = fp8_caches(w, nb, n_copies, dev, torch)
+    else:
+        caches = [W.cache_pool_device(w, nb, dev, extra=k) for k in range(n_copies)]
     q_abs = g(W.absorbed_queries(w))
     wts = {k: g(v) for k, v in W.weights(w).items()}
     tab, lens_d = g(table), g(lens)
@@ -193,11 +216,18 @@ def absorbed_row(dev, torch, w, planned=True, reps=20):
     ns = 0 if planned else (w.n_split or M.mla_auto_split(d, w.batch, w.s_q, table.shape[1]))
     ws = torch.empty(M.mla_decode_workspace_bytes(d, w.batch, w.s_q, ns, table.shape[1]),
                      dtype=torch.uint8, device=dev)
-    ms = _time_calls(lambda i: M.mla_decode(d, q_abs, caches[i % n_copies], tab, lens_d,
-                                            wts["w_uv"], out, n_split=ns, workspace=ws),
-                     reps, torch)
-    tr = A.decode_traffic(lens, w.s_q, w.n_heads, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt)
-    row = {"workload": w.name, "call": "mla_decode", "batch": w.batch, "s_q": w.s_q,
+    if fp8:
+        call = lambda i: M.mla_decode_fp8(d, q_abs, *caches[i % n_copies], tab, lens_d,
+                                          wts["w_uv"], out, n_split=ns, workspace=ws)
+    else:
+        call = lambda i: M.mla_decode(d, q_abs, caches[i % n_copies], tab, lens_d, wts["w_uv"],
+                                      out, n_split=ns, workspace=ws)
+    ms = _time_calls(call, reps, torch)
+    tr = A.decode_traffic(lens, w.s_q, w.n_heads, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt,
+                          row_bytes=row_b)
+    row = {"workload": w.name, "call": "mla_decode_fp8" if fp8 else "mla_decode",
+           "cache": "e4m3 + fp32 scale per position" if fp8 else w.dtype,
+           "batch": w.batch, "s_q": w.s_q,
            "heads": w.n_heads, "context_max": int(lens.max()), "ms": ms,
            "tokens_per_s": w.batch * w.s_q / (ms * 1e-3),
            "GBps": tr["bytes"] / (ms * 1e-3) / 1e9,
@@ -229,6 +259,14 @@ def measure_rows(dev, torch):
                                                      ctx=L, n_split=0))
         sweep.append(r)
     rows["absorbed_h128_context_sweep"] = sweep
+    # the same over e4m3 caches (half the cache bytes, the same matrix-core work)
+    rows["fp8_dsv3_paged"], _ = absorbed_row(dev, torch, W.WORKLOADS["dsv3-paged"], fp8=True)
+    sweep = []
+    for B, L in ((64, 8192), (16, 32768), (4, 131072)):
+        r, _ = absorbed_row(dev, torch, base.replace(name=f"h128-ctx{L // 1024}k", batch=B,
+                                                     ctx=L, n_split=0), fp8=True)
+        sweep.append(r)
+    rows["fp8_h128_context_sweep"] = sweep
     w = W.WORKLOADS["gqla-g8"]
     rows["absorbed_gqla_g8"], ctx = absorbed_row(dev, torch, w)
     lens, table, nb, tab, lens_d, wts = ctx
@@ -314,6 +352,53 @@ def measure_prefill(dev, torch):
             "expand_ms": ms_x, "expand_TFLOPs": tf(f_exp, ms_x),
             "attention_ms": ms_a, "attention_TFLOPs": tf(f_attn, ms_a),
             "attention_frac_mfma": tf(f_attn, ms_a) / BF16_PEAK_TFLOPS}
+
+
+def measure_fp8_step(w, d, lens, cache, tab, lens_d, nb, ns, step_args, n_steps, dev, torch):
+    """The bench step over an e4m3 copy of its cache: mla_cache_append_absorb_q_fp8, then
+    mla_decode_fp8_splitk and mla_decode_fp8_merge, timed like the bf16 step, with the e4m3
+    split-K core in a loop of its own against the binding roofline (580 bytes per position)."""
+    from mla_latent_kv_21_amd import accounting as A
+    from mla_latent_kv_21_amd import binding as M
+    x_new, seq_idx, pos_new, wts, q, q_pos, q_abs, out, lse, ws, ws_app = step_args
+    codes = torch.empty(cache.shape, dtype=torch.uint8, device=dev)
+    scales = torch.empty(cache.shape[:2], dtype=torch.float32, device=dev)
+    M.mla_cache_quantize_fp8(d, cache, codes, scales)
+
+    def step8():
+        M.mla_cache_append_absorb_q_fp8(d, x_new, seq_idx, pos_new, wts["w_dkv"], wts["gamma"],
+                                        wts["w_kr"], tab, nb, codes, scales, q["q_nope"],
+                                        q["q_pe"], q_pos, wts["w_uk"], q_abs, workspace=ws_app)
+        M.mla_decode_fp8_splitk(d, q_abs, codes, scales, tab, lens_d, ns, ws)
+        M.mla_decode_fp8_merge(d, q_abs, codes, scales, tab, lens_d, wts["w_uv"], out, lse, ns,
+                               ws)
+    for _ in range(5):
+        step8()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(n_steps):
+        step8()
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n_steps
+    if not torch.isfinite(out.float()).all():
+        raise RuntimeError("non-finite fp8 decode output")
+    core = _time_calls(lambda i: M.mla_decode_fp8_splitk(d, q_abs, codes, scales, tab, lens_d,
+                                                         ns, ws),
+                       max(20, n_steps), torch, stats=True)
+    tr = A.decode_traffic(lens, w.s_q, w.n_heads, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt,
+                          row_bytes=A.fp8_row_bytes(w.d_c, w.d_r))
+    r = {"workload": w.name, "cache": "e4m3 + fp32 scale per position",
+         "calls": "mla_cache_append_absorb_q_fp8, mla_decode_fp8_splitk, mla_decode_fp8_merge",
+         "ms_per_step": ms, "tokens_per_s": w.batch * w.s_q / (ms * 1e-3),
+         "core_launch_stats": core, "core_bytes_per_launch": tr["core_bytes"],
+         "core_GBps": tr["core_bytes"] / (core["mean_ms"] * 1e-3) / 1e9,
+         "step_outside_core_ms": ms - core["mean_ms"]}
+    r["core_roofline"] = A.binding_roofline(tr["core_bytes"], tr["core_flops"], core["mean_ms"])
+    del codes, scales
+    return r
 
 
 def measure_layer(w, d, step, x_new, dev, torch):
@@ -530,7 +615,13 @@ def main():
             torch)
     rows = "none" if args.no_rows else args.rows
     if rows != "none":
-        rec["rows"] = measure_rows(dev, torch) if rows == "all" else {}
+        rec["rows"] = {}
+        if rows == "all":
+            rec["rows"]["fp8_step"] = measure_fp8_step(
+                w, d, lens, cache, tab, lens_d, nb, ns,
+                (x_new, seq_idx, pos_new, wts, q, q_pos, q_abs, out, lse, ws, ws_app), n_steps,
+                dev, torch)
+            rec["rows"].update(measure_rows(dev, torch))
         if rows == "prefill":
             rec["rows"]["prefill"] = measure_prefill(dev, torch)
         else:

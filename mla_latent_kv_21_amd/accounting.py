@@ -64,24 +64,30 @@ def roofline_tokens_per_s(ctx: int, bytes_per_pos: float, flops_per_pos: float,
     return 1.0 / t
 
 
+def fp8_row_bytes(d_c: int, d_r: int) -> int:
+    """An e4m3 latent row: one byte per value plus its fp32 scale."""
+    return d_c + d_r + 4
+
+
 def decode_traffic(lens, s_q: int, n_heads: int, d_c: int, d_r: int, d_v: int,
-                   n_groups: int, elt: int = 2) -> dict:
+                   n_groups: int, elt: int = 2, row_bytes: int = 0) -> dict:
     """Algorithmic bytes and FLOPs of one absorbed decode call over sequences of lengths lens.
 
-    Split-K core: every cache row once, the absorbed queries once.
-    Combine: W_UV once, the outputs once.
+    Split-K core: every cache row once (row_bytes each, default (d_c + d_r) * elt), the
+    absorbed queries once. Combine: W_UV once, the outputs once.
     """
     rows = sum(int(L) for L in lens)
     B = len(lens)
     vis = sum(sum(int(L) - s_q + i + 1 for i in range(s_q)) for L in lens)
-    core_bytes = rows * latent_row_bytes(d_c, d_r, elt) + B * s_q * n_heads * (d_c + d_r) * elt
+    rb = row_bytes or latent_row_bytes(d_c, d_r, elt)
+    core_bytes = rows * rb + B * s_q * n_heads * (d_c + d_r) * elt
     core_flops = vis * absorbed_flops_per_pos(n_heads, d_c, d_r)
     wuv_bytes = d_c * n_groups * d_v * elt + B * s_q * n_heads * d_v * elt
     wuv_flops = 2 * B * s_q * n_heads * d_c * d_v
     return {"core_bytes": core_bytes, "core_flops": core_flops,
             "combine_bytes": wuv_bytes, "combine_flops": wuv_flops,
             "bytes": core_bytes + wuv_bytes, "flops": core_flops + wuv_flops,
-            "cache_bytes": rows * latent_row_bytes(d_c, d_r, elt)}
+            "cache_bytes": rows * rb}
 
 
 def gqa_decode_traffic(lens, s_q: int, n_heads: int, n_groups: int, d_h: int, d_r: int,

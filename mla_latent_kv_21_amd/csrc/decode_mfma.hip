@@ -28,6 +28,13 @@
 //    several steps ahead, then P · V of tile t runs with the softmax of tile t+1 spread
 //    between its products, so the matrix cores are fed while the VALU and LDS work;
 //  * each split writes (O / l as bf16, m + log2 l) partials; the merge kernel combines them.
+//
+// e4m3 variant (H = 128): rows of d_c + d_r bytes with one fp32 power-of-two scale per slot.
+// Tiles (18,432 B + 128 B of scales) stream into a 3-slot staging ring, swizzled like the bf16
+// ring; at the top of each iteration the staged tile is dequantised once (byte x scale, exact
+// in bf16) into one of two bf16 slots and published by a second barrier, after which the
+// scores and P · V are the bf16 kernel's own, so the results equal the bf16 kernel's on the
+// dequantised rows bit for bit.
 #include "common.hpp"
 #include "launch.hpp"
 #include "mfma_util.hpp"
@@ -51,14 +58,22 @@ constexpr int kPre = 10;                          // score fragments read ahead 
 constexpr int kVPre = 2;                          // P · V steps whose V fragments are in flight
 constexpr int kSlots = 4;                         // ring slots: two tiles in flight
 // e4m3 rows (d_c + d_r bytes, one fp32 scale per position): 32-position tiles of 18,432 bytes
-// plus their 128 bytes of scales stream into a 3-slot staging ring after two bf16 tile slots
+// plus their 128 bytes of scales stream into a 3-slot staging ring placed after two bf16
+// value slots (which hold only the dequantised latent columns the P · V product reads)
 constexpr int kF8RowBytes = kRowElems;                      // 576
+constexpr int kF8Chunks = kF8RowBytes / 16;                 // 36
 constexpr int kF8TileBytes = kTileTok * kF8RowBytes;        // 18,432
 constexpr int kF8SlotBytes = kF8TileBytes + 4 * kTileTok;   // + the tile's 32 scales
 constexpr int kF8Slots = 3;
 constexpr int kF8Base = 2 * kTileBytes;                     // staging after two bf16 slots
 constexpr int kDma8 = 5;                                    // copies per wave per fp8 tile
+constexpr int kPreF8 = 6;                                   // score fragments ahead (e4m3)
 static_assert(kF8Base + kF8Slots * kF8SlotBytes <= kSlots * kTileBytes, "fp8 staging fits");
+
+// Physical 16-byte chunk of logical chunk c in row t of an e4m3 staging tile: XOR-swizzled
+// inside groups of four by bits 2..3 of the row, so that the score reads (8 bytes per lane,
+// one chunk of all 32 rows) spread evenly over the banks.
+__host__ __device__ constexpr int swz8(int t, int c) { return (c & ~3) | ((c & 3) ^ ((t >> 2) & 3)); }
 
 // A device address as a wave-uniform value (so that asm operands can take it in SGPRs).
 __device__ __forceinline__ const char* uniform_ptr(const char* p) {
@@ -104,10 +119,7 @@ struct SoftState {
 };
 
 // kFp8: the cache rows are e4m3 bytes with one fp32 power-of-two scale per position
-// (`scales`, indexed like the cache slots). Tiles then stream into a staging ring and every
-// tile is dequantised exactly (byte x scale is a bf16 value) into a bf16 tile slot before the
-// same scores and P · V run on it: the result is the bf16 kernel's on the dequantised rows,
-// with half the bytes read from memory.
+// (`scales`, indexed like the cache slots); see the e4m3 variant above.
 template <int NW, bool kFp8>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ cache,
@@ -281,29 +293,45 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   auto issue_part = [&](const char* src, unsigned lbase, int j) __attribute__((always_inline)) {
     if (src != nullptr) dma16(src, doff[j], lbase + j * NW * 64 * 16);
   };
-  // e4m3 tiles: copy j < 4 moves tile chunk (4 j + w) 64 + lane; copy 4 moves chunks
-  // 1024 .. 1151 (waves 0 and 1) or the tile's 32 scales (lanes 0..7 of waves 2 and 3, the
-  // same bytes twice), so that every wave issues the same number of copies per tile. The
-  // staging slot holds the tile's bytes in order, then the scales.
+  // e4m3 tiles: LDS chunk p of a staging slot (row p / 36, physical chunk p % 36) is filled
+  // from the row's logical chunk swz8(row, p % 36) (the swizzle is its own inverse). Copy
+  // j < 4 fills chunks (4 j + w) 64 + lane; copy 4 fills chunks 1024 .. 1151 (waves 0 and 1)
+  // or the tile's 32 scales (lanes 0..7 of waves 2 and 3, the same bytes twice), so that every
+  // wave issues the same number of copies per tile.
+  unsigned doff8[kFp8 ? kDma8 : 1];
+  if constexpr (kFp8) {
+#pragma unroll
+    for (int j = 0; j < kDma8; ++j) {
+      const int p = j < 4 ? (4 * j + w) * 64 + lane : 1024 + w * 64 + lane;
+      const int t = p / kF8Chunks, pc = p - t * kF8Chunks;
+      doff8[j] = j < 4 || w < 2 ? static_cast<unsigned>(t * kF8RowBytes + 16 * swz8(t, pc))
+                                : static_cast<unsigned>(lane * 16);
+    }
+  }
   auto issue_part8 = [&](const char* src, const char* ssrc, unsigned lbase, int j)
                          __attribute__((always_inline)) {
     if (src == nullptr) return;
     if (j < 4) {
-      dma16(src, static_cast<unsigned>(((4 * j + w) * 64 + lane) * 16),
-            lbase + (4 * j + w) * 64 * 16);
+      dma16(src, doff8[j], lbase + (4 * j + w) * 64 * 16);
     } else if (w < 2) {
-      dma16(src, static_cast<unsigned>((1024 + w * 64 + lane) * 16), lbase + (1024 + w * 64) * 16);
+      dma16(src, doff8[j], lbase + (1024 + w * 64) * 16);
     } else if (lane < 8) {
-      dma16(ssrc, static_cast<unsigned>(lane * 16), lbase + kF8TileBytes);
+      dma16(ssrc, doff8[j], lbase + kF8TileBytes);
     }
   };
   // the tile's scales in memory (e4m3 rows), from the slot tile_src_at just looked up
   auto scales_src = [&]() -> const char* {
     return uniform_ptr(reinterpret_cast<const char*>(scales + tile_first_slot));
   };
-  // e4m3 rows: a staged tile dequantised into a bf16 tile slot, in the swizzled layout the
-  // scores and P · V read (thread 8 t + s converts 16-byte chunks s, s + 8, ... of row t:
-  // byte x scale, exact in bf16); rows past nvalid become zeros.
+  // e4m3 -> bf16 of four bytes times a power-of-two scale (exact), element 0 in the low half
+  auto cvt4 = [&](unsigned x, float sc, unsigned* lo, unsigned* hi) __attribute__((always_inline)) {
+    *lo = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, sc, false));
+    *hi = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, sc, true));
+  };
+  // A staged e4m3 tile dequantised into a bf16 tile slot, in the swizzled layout the scores
+  // and P · V read: thread 8 t + s converts logical chunks s, s + 8, ... of row t (16 values
+  // each, byte x scale, exact in bf16) into bf16 chunks 2 c and 2 c + 1; rows past nvalid
+  // become zeros.
   auto dequant = [&](const char* f8, char* bt, int nvalid) __attribute__((always_inline)) {
     const int t = threadIdx.x >> 3, s8 = threadIdx.x & 7;
     const float sc = *reinterpret_cast<const float*>(f8 + kF8TileBytes + 4 * t);
@@ -311,21 +339,14 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
       const int c = s8 + 8 * k;
-      if (c < kF8RowBytes / 16) {
+      if (k < 4 || c < kF8Chunks) {
         uint4 lo = make_uint4(0u, 0u, 0u, 0u), up = lo;
         if (ok) {
-          const uint4 v = *reinterpret_cast<const uint4*>(f8 + t * kF8RowBytes + 16 * c);
-          // bytes 0,1 (low word) then 2,3 (high word) of each dword: element order kept
-          auto lw = [&](unsigned x) {
-            return __builtin_bit_cast(unsigned,
-                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, sc, false));
-          };
-          auto hw = [&](unsigned x) {
-            return __builtin_bit_cast(unsigned,
-                                      __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, sc, true));
-          };
-          lo = make_uint4(lw(v.x), hw(v.x), lw(v.y), hw(v.y));
-          up = make_uint4(lw(v.z), hw(v.z), lw(v.w), hw(v.w));
+          const uint4 v = *reinterpret_cast<const uint4*>(f8 + t * kF8RowBytes + 16 * swz8(t, c));
+          cvt4(v.x, sc, &lo.x, &lo.y);
+          cvt4(v.y, sc, &lo.z, &lo.w);
+          cvt4(v.z, sc, &up.x, &up.y);
+          cvt4(v.w, sc, &up.z, &up.w);
         }
         *reinterpret_cast<uint4*>(bt + t * kRowBytes + (((2 * c) ^ swz(t)) << 4)) = lo;
         *reinterpret_cast<uint4*>(bt + t * kRowBytes + (((2 * c + 1) ^ swz(t)) << 4)) = up;
@@ -341,15 +362,17 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     f32x16 sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-    bf16x8 af[kPre];
+    // e4m3 rows: fewer fragments ahead, for the registers their copy offsets take
+    constexpr int kP = kFp8 ? kPreF8 : kPre;
+    bf16x8 af[kP];
 #pragma unroll
-    for (int i = 0; i < kPre; ++i) af[i] = lds16(cur + qb[i & 3] + 128 * (i >> 2));
+    for (int i = 0; i < kP; ++i) af[i] = lds16(cur + qb[i & 3] + 128 * (i >> 2));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
-      const bf16x8 acur = af[ks % kPre];
-      const int nx = ks + kPre;
-      if (nx < kKSteps) af[ks % kPre] = lds16(cur + qb[nx & 3] + 128 * (nx >> 2));
+      const bf16x8 acur = af[ks % kP];
+      const int nx = ks + kP;
+      if (nx < kKSteps) af[ks % kP] = lds16(cur + qb[nx & 3] + 128 * (nx >> 2));
       sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur, qf[ks], sc, 0, 0, 0);
       // copies spread evenly over the K-steps (kCopies <= kKSteps)
       if ((ks * kCopies) / kKSteps != ((ks + 1) * kCopies) / kKSteps) {
@@ -362,7 +385,6 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     }
     return sc;
   };
-
   // ---- softmax numerators of one tile against the head's fixed reference m_ref (log2
   // units): the first finite tile max. A tile exceeding it by more than kHead marks the split
   // for exact recomputation instead of rescaling O, so O is only ever touched by MFMAs. The
@@ -547,8 +569,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     nv1 = nv2;
     nv2 = nv3;
     if constexpr (kFp8) {
-      // tile t+1 is staged: dequantised into the bf16 slot tile t-1 used (every wave is past
-      // its P · V), then published by a second barrier
+      // staged tile t+1 dequantised into the bf16 slot tile t-1 used (every wave is past its
+      // P · V), published by a second barrier; the copies of tile t+3 then go to the staging
+      // slot of tile t, dequantised in the previous iteration
       if (t + 1 < ntiles) dequant(stage8(t + 1), ring[nslot], nv_next);
       __syncthreads();
     }
