@@ -108,6 +108,23 @@ def _time_calls(fn, reps: int, torch, stats: bool = False):
             "launches": reps}
 
 
+def _interleaved(fa, fb, n: int, rounds: int, torch):
+    """Mean per-call ms of fa and of fb, each run n times back to back (one event pair around
+    the n calls) in `rounds` alternating rounds, so that clock and power drift cancel."""
+    stream = torch.cuda.current_stream()
+    ta, tb = [], []
+    for _ in range(rounds):
+        for fn, acc in ((fa, ta), (fb, tb)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            acc.append(e0.elapsed_time(e1) / n)
+    return float(np.mean(ta)), float(np.mean(tb))
+
+
 ROTATE_BYTES = 1 << 30   # caches smaller than the 256 MB MALL are rotated over >= 1 GiB
 
 
@@ -385,9 +402,9 @@ def measure_fp8_step(w, d, lens, cache, tab, lens_d, nb, ns, step_args, n_steps,
     ms = a.elapsed_time(b) / n_steps
     if not torch.isfinite(out.float()).all():
         raise RuntimeError("non-finite fp8 decode output")
-    core = _time_calls(lambda i: M.mla_decode_fp8_splitk(d, q_abs, codes, scales, tab, lens_d,
-                                                         ns, ws),
-                       max(20, n_steps), torch, stats=True)
+    core8 = lambda: M.mla_decode_fp8_splitk(d, q_abs, codes, scales, tab, lens_d, ns, ws)
+    core = _time_calls(lambda i: core8(), max(20, n_steps), torch, stats=True)
+    bb_step, bb_core = _interleaved(step8, core8, 10, 5, torch)
     tr = A.decode_traffic(lens, w.s_q, w.n_heads, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt,
                           row_bytes=A.fp8_row_bytes(w.d_c, w.d_r))
     r = {"workload": w.name, "cache": "e4m3 + fp32 scale per position",
@@ -395,7 +412,8 @@ def measure_fp8_step(w, d, lens, cache, tab, lens_d, nb, ns, step_args, n_steps,
          "ms_per_step": ms, "tokens_per_s": w.batch * w.s_q / (ms * 1e-3),
          "core_launch_stats": core, "core_bytes_per_launch": tr["core_bytes"],
          "core_GBps": tr["core_bytes"] / (core["mean_ms"] * 1e-3) / 1e9,
-         "step_outside_core_ms": ms - core["mean_ms"]}
+         "step_outside_core_ms": bb_step - bb_core,
+         "back_to_back_ms": {"step": bb_step, "core": bb_core}}
     r["core_roofline"] = A.binding_roofline(tr["core_bytes"], tr["core_flops"], core["mean_ms"])
     del codes, scales
     return r
@@ -581,6 +599,10 @@ def main():
     core = _time_calls(lambda i: M.mla_decode_splitk(d, q_abs, cache, tab, lens_d, ns, ws),
                        max(20, n_steps), torch, stats=True)
     core_ms = core["mean_ms"]
+    # the step and the core alone, both back to back, in alternating rounds: what the step
+    # spends outside the core
+    bb_step, bb_core = _interleaved(
+        step, lambda: M.mla_decode_splitk(d, q_abs, cache, tab, lens_d, ns, ws), 10, 5, torch)
 
     tr = A.decode_traffic(lens, s_q, H, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt)
     core_bytes = tr["core_bytes"]
@@ -604,7 +626,8 @@ def main():
                      "algorithmic_bytes_per_launch": core_bytes,
                      "algorithmic_flops_per_launch": tr["core_flops"],
                      "frac_mfma": tr["core_flops"] / (core_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS},
-        "step_outside_core_ms": ms_step - core_ms,
+        "step_outside_core_ms": bb_step - bb_core,
+        "back_to_back_ms": {"step": bb_step, "core": bb_core, "rounds": 5, "calls_per_round": 10},
         "latent_cache_GBps": tr["cache_bytes"] / (core_ms * 1e-3) / 1e9,
         "step_latent_cache_GBps": tr["cache_bytes"] / (ms_step * 1e-3) / 1e9,
         "wall_s": wall,
