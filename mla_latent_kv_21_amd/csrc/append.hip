@@ -248,35 +248,35 @@ __global__ __launch_bounds__(1024) void append_finalize(
   __shared__ float red[64];
   const int n = blockIdx.x;
   const int ncols = d_c + d_r;
+  const int lat_blocks = cdiv(d_c, kColTile);  // 64-column blocks of the latent part
   // the row's slot first: its dependent loads (sequence, position, block table) overlap the
   // partial sums below
   const int b = seq_idx[n], p = pos[n];
   const int64_t slot = (b < 0 || b >= batch) ? -1 : cache_slot(table, max_blocks, bs, num_blocks, b, p);
-  for (int c = threadIdx.x; c < ncols; c += blockDim.x) {
-    // partial sums added in the fixed order k = 0, 1, ...; up to 32 loads in flight
+  // blockDim.x is a multiple of 64: pass c0 gives wave w the 64-column block c0 / 64 + w
+  for (int c0 = 0; c0 < ncols; c0 += blockDim.x) {
+    const int c = c0 + static_cast<int>(threadIdx.x);
     float y = 0.f;
-    for (int k = 0; k < n_ksplit; k += 32) {
-      float v[32];
+    if (c < ncols) {
+      // partial sums added in the fixed order k = 0, 1, ...; up to 32 loads in flight
+      for (int k = 0; k < n_ksplit; k += 32) {
+        float v[32];
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        v[u] = k + u < n_ksplit ? y_part[(static_cast<int64_t>(k + u) * n_tok + n) * ncols + c] : 0.f;
+        for (int u = 0; u < 32; ++u)
+          v[u] = k + u < n_ksplit ? y_part[(static_cast<int64_t>(k + u) * n_tok + n) * ncols + c] : 0.f;
 #pragma unroll
-      for (int u = 0; u < 32; ++u)
-        if (k + u < n_ksplit) y += v[u];
+        for (int u = 0; u < 32; ++u)
+          if (k + u < n_ksplit) y += v[u];
+      }
+      ys[c] = y;
     }
-    ys[c] = y;
-  }
-  __syncthreads();
-  // sum of squares of the latent part: each 64-column block in column order, then the blocks
-  // in order (a fixed order, independent of the block size)
-  const int lat_blocks = cdiv(d_c, kColTile);
-  if (static_cast<int>(threadIdx.x) < lat_blocks) {
-    float s2 = 0.f;
-    for (int cc = 0; cc < kColTile; ++cc) {
-      const int c = threadIdx.x * kColTile + cc;
-      s2 += c < d_c ? ys[c] * ys[c] : 0.f;
+    // sum of squares of the latent part: each 64-column block by a butterfly over its wave
+    // (a fixed order, independent of the block size), then the blocks in order below
+    const int blk = c0 / 64 + static_cast<int>(threadIdx.x >> 6);
+    if (blk < lat_blocks) {
+      const float s2 = wave_sum(c < d_c ? y * y : 0.f);
+      if ((threadIdx.x & 63) == 0) red[blk] = s2;
     }
-    red[threadIdx.x] = s2;
   }
   __syncthreads();
   float ss = 0.f;

@@ -17,7 +17,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from gpu_cases import (DEV, TOL, check_lse, check_per_seq, decode_ws_layout, dev, note, pick)
+from gpu_cases import (DEV, TOL, check, check_lse, check_per_seq, decode_ws_layout, dev, note,
+                       oracle_decode, pick)
 from mla_latent_kv_21_amd import binding as M
 
 pytestmark = [pytest.mark.gpu,
@@ -324,3 +325,33 @@ def test_fp8_full_size_sampled():
     ref, ref_lse = oracle_fp8(c, seqs=seqs, heads=heads)
     check_per_seq(pick(out8, seqs, heads), ref, TOL["bf16"])
     check_lse(pick(lse8, seqs, heads), ref_lse, TOL["bf16"])
+
+
+def test_fp8_decode_against_the_unquantised_cache():
+    """The cost of the format: a bf16 cache quantised by the library and decoded from its
+    bytes, against the oracle on the bf16 rows themselves. Each row element moves by at most
+    2^-4 of itself (half a step of three mantissa bits) or 2^-10 of its row's scale; with the
+    rounding error spread evenly over that half step, its relative spread is 2^-4 / sqrt(3)
+    = 3.6 %, once in the values averaged into the output and once more through the scores
+    that weight them: about 5 % normwise expected (measured 1.7-7 % on N(0, 1) rows, more for
+    short histories). Held here to twice that, 10 % normwise and 15 % on any head's row."""
+    w = W.WORKLOADS["dsv3-paged"]
+    lens = [300, 2049, 5000]
+    wq = w.replace(batch=len(lens))
+    lens_np = np.asarray(lens, np.int32)
+    table, nb = W.block_table(wq, lens_np)
+    pool = W.cache_pool(wq, nb, extra=36)
+    d = M.dims_of(wq)
+    codes = torch.empty(pool.shape, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(pool.shape[:2], dtype=torch.float32, device=DEV)
+    note("fp8 decode of a quantised bf16 cache")
+    M.mla_cache_quantize_fp8(d, dev(pool), codes, scales)
+    c = dict(w=wq, lens=lens_np, table=table, nb=nb, codes=codes.cpu(), scales=scales.cpu(),
+             q_abs=W.absorbed_queries(wq), w_uv=W.weights(wq)["w_uv"])
+    out8, lse8 = run(c, True, planned=True)
+    ref, ref_lse = oracle_decode(dict(c, pool=pool))
+    for b in range(len(lens)):
+        check(out8[b], ref[b], 0.10, f"out[seq {b}] vs unquantised")
+        rows = np.max(np.abs(O.f64(out8[b]) - ref[b]), axis=-1) / np.max(np.abs(ref[b]), axis=-1)
+        assert float(np.max(rows)) <= 0.15, float(np.max(rows))
+    check_lse(lse8.double().numpy(), ref_lse, 0.05, "lse vs unquantised")
