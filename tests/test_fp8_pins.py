@@ -123,3 +123,43 @@ def test_quantised_rows_match_torch_per_row():
     codes, scales = O.quantize_rows_e4m3(rows)
     for r in range(rows.shape[0]):
         assert np.array_equal(codes[r], torch_encode(rows[r] / scales[r]))
+
+
+def _pins_hold(values, encode, row_scale) -> bool:
+    """The pins above, as one predicate over a (value table, encoder, row scale) triple."""
+    v = values()
+    if not (v[0x7E] == 448.0 and v[0x01] == 2.0 ** -9 and v[0x38] == 1.0):
+        return False
+    mags = v[:0x7F]
+    mids = (mags[:-1] + mags[1:]) / 2
+    if not np.all(encode(mids).astype(int) % 2 == 0):
+        return False
+    if not (row_scale(1.0) == 2.0 ** -8 and row_scale(448.0) == 1.0 and row_scale(224.0) == 0.5):
+        return False
+    return True
+
+
+def test_planted_mistakes_fail_the_pins():
+    """Mistakes planted in copies of the oracle's FP8 functions: a wrong exponent bias, ties
+    rounded away from zero, a scale twice too large. Each must break a pin; the real
+    functions must pass."""
+    assert _pins_hold(O.e4m3_values, O.e4m3_encode, O.e4m3_row_scale)
+
+    def biased_values():
+        return O.e4m3_values() / 2.0              # bias 8 instead of 7
+
+    def ties_away(x):
+        x = np.asarray(x, dtype=np.float64)
+        mags = O.e4m3_values()[:0x7F]
+        a = np.abs(x)
+        hi = np.clip(np.searchsorted(mags, a, side="left"), 0, 0x7E)
+        lo = np.maximum(hi - 1, 0)
+        pick_hi = (mags[hi] - a) <= (a - mags[lo])  # a tie goes up, whatever the code
+        return np.where(pick_hi, hi, lo).astype(np.uint8) | (np.signbit(x).astype(np.uint8) << 7)
+
+    def double_scale(amax):
+        return 2.0 * O.e4m3_row_scale(amax)
+
+    assert not _pins_hold(biased_values, O.e4m3_encode, O.e4m3_row_scale)
+    assert not _pins_hold(O.e4m3_values, ties_away, O.e4m3_row_scale)
+    assert not _pins_hold(O.e4m3_values, O.e4m3_encode, double_scale)
