@@ -569,15 +569,17 @@ def main():
                      dtype=torch.uint8, device=dev)
     ws_app = torch.empty(max(M.mla_cache_append_workspace_bytes(d, B * s_q), 256),
                          dtype=torch.uint8, device=dev)
+    ws_step = torch.empty(M.mla_decode_step_workspace_bytes(d, B, s_q, ns, table.shape[1]),
+                          dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     n_steps = args.steps
 
     def step():
-        M.mla_cache_append_absorb_q(d, x_new, seq_idx, pos_new, wts["w_dkv"], wts["gamma"],
-                                    wts["w_kr"], tab, nb, cache, q["q_nope"], q["q_pe"], q_pos,
-                                    wts["w_uk"], q_abs, workspace=ws_app)
-        M.mla_decode_splitk(d, q_abs, cache, tab, lens_d, ns, ws)
-        M.mla_decode_merge(d, q_abs, cache, tab, lens_d, wts["w_uv"], out, lse, ns, ws)
+        # append the B * s_q new tokens (each sequence's last s_q positions), absorb their
+        # queries, split-K core (which forms the new rows), merge + W_UV
+        M.mla_decode_step(d, x_new, wts["w_dkv"], wts["gamma"], wts["w_kr"], q["q_nope"],
+                          q["q_pe"], wts["w_uk"], wts["w_uv"], cache, tab, lens_d, out, lse,
+                          n_split=ns, workspace=ws_step)
 
     for _ in range(args.warmup):
         step()
@@ -593,6 +595,10 @@ def main():
     ms_step = t_start.elapsed_time(t_end) / n_steps
     if not torch.isfinite(out.float()).all():
         raise RuntimeError("non-finite decode output")
+    # the absorbed queries the step forms inside its workspace, for the core on its own
+    M.mla_cache_append_absorb_q(d, x_new, seq_idx, pos_new, wts["w_dkv"], wts["gamma"],
+                                wts["w_kr"], tab, nb, cache, q["q_nope"], q["q_pe"], q_pos,
+                                wts["w_uk"], q_abs, workspace=ws_app)
     # The split-K core (the dominant kernel) in a loop of its own, every launch bracketed by
     # HIP events on the stream it runs on (an event pair inside the step would add its own
     # barrier packets to the step time).

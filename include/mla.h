@@ -196,6 +196,35 @@ mla_status mla_decode_merge(const mla_dims* dims, int32_t batch, int32_t s_q, co
                             hipStream_t stream);
 
 /*
+ * mla_decode_step -- one decode step of one layer over the latent cache ([Smallem] "Le code":
+ * the cache is extended by the new tokens, then attended over its whole length; "Ce que
+ * DeepSeek fait de plus" for the absorbed form): the s_q new tokens of every sequence b are
+ * its positions L_b - s_q .. L_b - 1 (L_b = seq_lens[b], already counting them), token
+ * n = b * s_q + i of x and of the queries. Results are those of
+ *     mla_cache_append_absorb_q(dims, B * s_q, x, seq_idx, pos, w_dkv, rms_gamma, w_kr, ...,
+ *                               s_q, q_nope, q_pe, q_pos = pos, w_uk, q_abs)
+ *     mla_decode(dims, B, s_q, q_abs, latent_cache, ..., w_uv, n_split, ..., out, lse)
+ *  with seq_idx[n] = n / s_q and pos[n] = L_b - s_q + n % s_q, bit for bit; the new rows are
+ *  left in the cache. On the matrix-core path (bf16, d_c 512, d_r 64, H = 128, block size a
+ *  multiple of 32, B * s_q <= 2048) the step takes three launches instead of four: the split-K
+ *  core forms the new rows itself, each split workgroup those inside its range, from the
+ *  projection's partial sums.
+ *  x [B * s_q, C]; q_nope [B, s_q, H, D]; q_pe [B, s_q, H, d_r]; other arguments as in the
+ *  calls above. workspace: mla_decode_step_workspace_bytes(dims, B, s_q, n_split, max_blocks)
+ *  bytes (the append's partial sums, the absorbed queries, the new tokens' indices, then the
+ *  decode's workspace). Errors: those of the calls above; nothing is enqueued when a check fails.
+ */
+size_t mla_decode_step_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                       int32_t n_split, int32_t max_blocks);
+mla_status mla_decode_step(const mla_dims* dims, int32_t batch, int32_t s_q, const void* x,
+                           const void* w_dkv, const void* rms_gamma, const void* w_kr,
+                           const void* q_nope, const void* q_pe, const void* w_uk,
+                           const void* w_uv, void* latent_cache, int32_t num_blocks,
+                           const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* seq_lens, int32_t n_split, void* workspace,
+                           size_t ws_bytes, void* out, float* lse, hipStream_t stream);
+
+/*
  * mla_decode_noalloc -- mla_decode for callers that cannot allocate device memory: code under
  *  HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Arguments, results
  *  and errors are mla_decode's, without workspace and ws_bytes: the split-K partials live in a

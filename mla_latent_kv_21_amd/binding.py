@@ -29,7 +29,7 @@ EXPORTS = ["mla_cache_append_workspace_bytes", "mla_cache_append", "mla_absorb_q
            "mla_query_project_workspace_bytes", "mla_query_project",
            "mla_output_project_workspace_bytes", "mla_output_project",
            "mla_decode_workspace_bytes", "mla_decode", "mla_decode_splitk", "mla_decode_merge",
-           "mla_decode_noalloc",
+           "mla_decode_noalloc", "mla_decode_step_workspace_bytes", "mla_decode_step",
            "mla_cache_quantize_fp8", "mla_cache_append_fp8", "mla_cache_append_absorb_q_fp8",
            "mla_decode_fp8", "mla_decode_fp8_splitk", "mla_decode_fp8_merge",
            "gqla_expand",
@@ -95,6 +95,9 @@ def lib() -> ctypes.CDLL:
             "mla_decode_splitk": (I, [D, I, I, P, P, I, P, I, P, I, P, S, P]),
             "mla_decode_merge": (I, [D, I, I, P, P, I, P, I, P, P, I, P, S, P, P, P]),
             "mla_decode_noalloc": (I, [D, I, I, P, P, I, P, I, P, P, I, P, P, P]),
+            "mla_decode_step_workspace_bytes": (S, [D, I, I, I, I]),
+            "mla_decode_step": (I, [D, I, I, P, P, P, P, P, P, P, P, P, I, P, I, P, I, P, S, P,
+                                    P, P]),
             "mla_cache_quantize_fp8": (I, [D, ctypes.c_int64, P, P, P, P]),
             "mla_cache_append_fp8": (I, [D, I, P, P, P, P, P, P, P, I, I, I, P, P, P, S, P]),
             "mla_cache_append_absorb_q_fp8": (I, [D, I, P, P, P, P, P, P, P, I, I, I, P, P, P, S,
@@ -254,6 +257,30 @@ def mla_decode_noalloc(dims, q_abs, latent_cache, block_table, seq_lens, w_uv, o
                                   _ptr(seq_lens), _ptr(w_uv), n_split, _ptr(out), _ptr(lse),
                                   _stream())
     _check(st, "mla_decode_noalloc")
+
+
+def mla_decode_step_workspace_bytes(dims, batch, s_q, n_split, max_blocks) -> int:
+    return lib().mla_decode_step_workspace_bytes(ctypes.byref(dims), batch, s_q, n_split,
+                                                 max_blocks)
+
+
+def mla_decode_step(dims, x, w_dkv, gamma, w_kr, q_nope, q_pe, w_uk, w_uv, latent_cache,
+                    block_table, seq_lens, out, lse=None, n_split=0, workspace=None):
+    """One decode step: append the s_q new tokens of every sequence (its last s_q positions),
+    absorb their queries, decode; out [B, s_q, H, D_v]."""
+    B, s_q = q_nope.shape[0], q_nope.shape[1]
+    mb = block_table.shape[1]
+    if x.shape[0] != B * s_q or block_table.shape[0] != B:
+        raise ValueError("x must hold B * s_q tokens and the block table B rows")
+    if workspace is None:
+        workspace = _workspace(mla_decode_step_workspace_bytes(dims, B, s_q, n_split, mb),
+                               x.device)
+    st = lib().mla_decode_step(ctypes.byref(dims), B, s_q, _ptr(x), _ptr(w_dkv), _ptr(gamma),
+                               _ptr(w_kr), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
+                               _ptr(latent_cache), latent_cache.shape[0], _ptr(block_table), mb,
+                               _ptr(seq_lens), n_split, _ptr(workspace), workspace.numel(),
+                               _ptr(out), _ptr(lse), _stream())
+    _check(st, "mla_decode_step")
 
 
 def mla_decode_splitk(dims, q_abs, latent_cache, block_table, seq_lens, n_split, workspace):

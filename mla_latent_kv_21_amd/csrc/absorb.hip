@@ -82,6 +82,8 @@ AbsorbArgs absorb_args(const mla_dims& d, int M, const void* q_nope, const void*
   q.q_nope = static_cast<const uint16_t*>(q_nope);
   q.q_pe = static_cast<const uint16_t*>(q_pe);
   q.q_pos = q_pos;
+  q.lens = nullptr;
+  q.s_q = 1;
   q.w_uk = static_cast<const uint16_t*>(w_uk);
   q.M = M; q.H = d.n_heads; q.G = d.n_groups; q.D = d.d_nope; q.d_c = d.d_c; q.d_r = d.d_r;
   q.base = d.rope_base;

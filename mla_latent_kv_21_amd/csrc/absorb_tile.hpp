@@ -12,7 +12,9 @@ namespace mla {
 struct AbsorbArgs {
   const uint16_t* q_nope;
   const uint16_t* q_pe;
-  const int32_t* q_pos;
+  const int32_t* q_pos;     // [M] query positions, or NULL: row m = b s_q + i is at
+  const int32_t* lens;      // position lens[b] - s_q + i (a decode step's new tokens)
+  int s_q;
   const uint16_t* w_uk;
   int M, H, G, D, d_c, d_r;
   float base;
@@ -87,7 +89,8 @@ __device__ inline void absorb_tile_mfma(const AbsorbArgs& q, int h, int m0, int 
     const int mm = m0 + r;
     if (mm >= M) continue;
     float cs, sn;
-    rope_cos_sin(q_pos[mm], jj, d_r, base, &cs, &sn);
+    const int qp = q_pos != nullptr ? q_pos[mm] : q.lens[mm / q.s_q] - q.s_q + mm % q.s_q;
+    rope_cos_sin(qp, jj, d_r, base, &cs, &sn);
     const int64_t src = (static_cast<int64_t>(mm) * H + h) * d_r + 2 * jj;
     const float x0 = bf16_to_f32(q_pe[src]), x1 = bf16_to_f32(q_pe[src + 1]);
     const int64_t dst = (static_cast<int64_t>(mm) * H + h) * row + d_c + 2 * jj;

@@ -468,6 +468,105 @@ mla_status mla_decode_fp8_merge(const mla_dims* dims, int32_t batch, int32_t s_q
                      lse, stream);
 }
 
+}  // extern "C"
+
+// ---- a whole decode step: the workspace holds, each part 256-byte aligned, the append's
+// partial sums, the absorbed queries, the new tokens' sequence and position indices, then the
+// decode's own workspace.
+namespace {
+struct StepLayout {
+  size_t y_part, q_abs, idx, dec, total;
+};
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+StepLayout step_layout(const mla_dims& d, int32_t batch, int32_t s_q, size_t dec_bytes) {
+  StepLayout l;
+  const size_t n_tok = static_cast<size_t>(batch) * s_q;
+  l.y_part = 0;
+  l.q_abs = al256(mla::append_ws_bytes(d, static_cast<int>(n_tok)));
+  l.idx = l.q_abs + al256(n_tok * d.n_heads * (d.d_c + d.d_r) * elt_of(d));
+  l.dec = l.idx + al256(2 * n_tok * sizeof(int32_t));
+  l.total = l.dec + dec_bytes;
+  return l;
+}
+}  // namespace
+
+extern "C" {
+
+size_t mla_decode_step_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t s_q,
+                                       int32_t n_split, int32_t max_blocks) {
+  const size_t dec = mla_decode_workspace_bytes(dims, batch, s_q, n_split, max_blocks);
+  if (dec == 0 || static_cast<int64_t>(batch) * s_q > 65535 * 16) return 0;
+  return step_layout(*dims, batch, s_q, dec).total;
+}
+
+mla_status mla_decode_step(const mla_dims* dims, int32_t batch, int32_t s_q, const void* x,
+                           const void* w_dkv, const void* rms_gamma, const void* w_kr,
+                           const void* q_nope, const void* q_pe, const void* w_uk,
+                           const void* w_uv, void* latent_cache, int32_t num_blocks,
+                           const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* seq_lens, int32_t n_split, void* workspace,
+                           size_t ws_bytes, void* out, float* lse, hipStream_t stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 0 || s_q < 1 || max_blocks < 1 || num_blocks < 1 || n_split < 0 ||
+      n_split > MLA_MAX_SPLIT)
+    return MLA_ERR_RANGE;
+  if (batch == 0) return MLA_OK;
+  if (static_cast<int64_t>(batch) * s_q > 65535 * 16) return MLA_ERR_RANGE;
+  if (!workspace || !seq_lens || !w_uv || !out) return MLA_ERR_NULL;
+  const size_t need = mla_decode_step_workspace_bytes(dims, batch, s_q, n_split, max_blocks);
+  if (need == 0) return MLA_ERR_RANGE;
+  if (ws_bytes < need) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  const mla_dims& d = *dims;
+  const StepLayout l = step_layout(d, batch, s_q, 0);
+  char* ws = static_cast<char*>(workspace);
+  float* y_part = reinterpret_cast<float*>(ws + l.y_part);
+  void* q_abs = ws + l.q_abs;
+  int32_t* seq_idx = reinterpret_cast<int32_t*>(ws + l.idx);
+  const int n_tok = batch * s_q;
+  int32_t* pos = seq_idx + n_tok;
+  void* dws = ws + l.dec;
+  const size_t dws_bytes = ws_bytes - l.dec;
+  // the checks of the calls the step stands for
+  st = check_append(dims, n_tok, x, seq_idx, pos, w_dkv, rms_gamma, w_kr, block_table, batch,
+                    max_blocks, num_blocks, latent_cache, y_part, l.q_abs - l.y_part);
+  if (st != MLA_OK) return st;
+  st = check_absorb(dims, batch, s_q, q_nope, q_pe, pos, w_uk, q_abs);
+  if (st != MLA_OK) return st;
+  int ns = 0;
+  st = check_decode(dims, batch, s_q, q_abs, latent_cache, num_blocks, block_table, max_blocks,
+                    seq_lens, n_split, dws, dws_bytes, &ns);
+  if (st != MLA_OK) return st;
+  if (mla::mfma_step_fits(d) && mla::step_project_fits(d, n_tok)) {
+    // three launches: projection with the absorption, the core forming the new rows, merge
+    st = hip_status(mla::launch_step_project(d, batch, s_q, x, w_dkv, w_kr, y_part, q_nope, q_pe,
+                                             seq_lens, w_uk, q_abs, stream));
+    if (st != MLA_OK) return st;
+    const mla::StepRows rows{y_part, rms_gamma, latent_cache,
+                             mla::projection_ksplit(d.d_model), d.rms_eps, d.rope_base};
+    st = hip_status(mla::launch_decode_step_splitk(d, batch, s_q, q_abs, latent_cache,
+                                                   num_blocks, block_table, max_blocks,
+                                                   seq_lens, ns, dws, rows, stream));
+  } else {
+    // the separate calls, the new tokens' indices written by the device from the lengths
+    st = hip_status(mla::launch_step_positions(batch, s_q, seq_lens, seq_idx, pos, stream));
+    if (st != MLA_OK) return st;
+    st = hip_status(mla::launch_append_absorb(d, n_tok, x, seq_idx, pos, w_dkv, rms_gamma,
+                                              w_kr, block_table, batch, max_blocks, num_blocks,
+                                              latent_cache, nullptr, y_part, batch, s_q, q_nope,
+                                              q_pe, pos, w_uk, q_abs, stream));
+    if (st != MLA_OK) return st;
+    st = hip_status(mla::launch_decode_splitk(d, batch, s_q, q_abs, latent_cache, nullptr,
+                                              num_blocks, block_table, max_blocks, seq_lens, ns,
+                                              dws, stream));
+  }
+  if (st != MLA_OK) return st;
+  return hip_status(mla::launch_decode_merge(d, batch, s_q, q_abs, latent_cache, nullptr,
+                                             num_blocks, block_table, max_blocks, seq_lens, w_uv,
+                                             ns, dws, out, lse, stream));
+}
+
 mla_status gqla_expand(const mla_dims* dims, int32_t batch, const void* latent_cache,
                        int32_t num_blocks, const int32_t* block_table, int32_t max_blocks,
                        const int32_t* seq_lens, const int32_t* start_pos, const void* w_uk,

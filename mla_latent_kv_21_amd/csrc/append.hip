@@ -274,7 +274,7 @@ __global__ __launch_bounds__(1024) void append_finalize(
     // (a fixed order, independent of the block size), then the blocks in order below
     const int blk = c0 / 64 + static_cast<int>(threadIdx.x >> 6);
     if (blk < lat_blocks) {
-      const float s2 = wave_sum(c < d_c ? y * y : 0.f);
+      const float s2 = wave_sum(c < d_c ? square_rn(y) : 0.f);
       if ((threadIdx.x & 63) == 0) red[blk] = s2;
     }
   }
@@ -295,8 +295,10 @@ __global__ __launch_bounds__(1024) void append_finalize(
       float cs, sn;
       rope_cos_sin(p, j, d_r, base, &cs, &sn);
       const float a = ys[d_c + 2 * j], q = ys[d_c + 2 * j + 1];
-      const float u = bf16_to_f32(f32_to_bf16(a * cs - q * sn));
-      const float v = bf16_to_f32(f32_to_bf16(a * sn + q * cs));
+      float u, v;
+      rope_rotate(a, q, cs, sn, &u, &v);
+      u = bf16_to_f32(f32_to_bf16(u));
+      v = bf16_to_f32(f32_to_bf16(v));
       ys[d_c + 2 * j] = u;
       ys[d_c + 2 * j + 1] = v;
       amax = fmaxf(amax, fmaxf(fabsf(u), fabsf(v)));
@@ -317,8 +319,10 @@ __global__ __launch_bounds__(1024) void append_finalize(
     float cs, sn;
     rope_cos_sin(p, j, d_r, base, &cs, &sn);
     const float a = ys[d_c + 2 * j], q = ys[d_c + 2 * j + 1];
-    st(row, d_c + 2 * j, a * cs - q * sn);
-    st(row, d_c + 2 * j + 1, a * sn + q * cs);
+    float u, v;
+    rope_rotate(a, q, cs, sn, &u, &v);
+    st(row, d_c + 2 * j, u);
+    st(row, d_c + 2 * j + 1, v);
   }
 }
 
@@ -385,9 +389,54 @@ __global__ __launch_bounds__(256) void project_absorb(const uint16_t* __restrict
   project_tile_mfma(x, w_a, w_b, n_tok, C, n_a, n_b, y_part, cb, ks, 32 * nt);
 }
 
+// Token n of a decode step: sequence n / s_q, position seq_lens[n / s_q] - s_q + n % s_q.
+__global__ __launch_bounds__(256) void step_positions(int n_tok, int s_q,
+                                                      const int32_t* __restrict__ seq_lens,
+                                                      int32_t* __restrict__ seq_idx,
+                                                      int32_t* __restrict__ pos) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= n_tok) return;
+  const int b = n / s_q;
+  seq_idx[n] = b;
+  pos[n] = seq_lens[b] - s_q + (n - b * s_q);
+}
+
 }  // namespace
 
 int projection_ksplit(int K) { return cdiv(K, kKChunk); }
+
+bool step_project_fits(const mla_dims& d, int n_tok) {
+  return d.dtype == MLA_BF16 && !(d.flags & MLA_FLAG_GENERIC_KERNELS) && d.d_model % 8 == 0 &&
+         d.d_c % 8 == 0 && d.d_r % 8 == 0 && absorb_mfma_fits(d) && n_tok >= 1 &&
+         n_tok <= kMaxTok;
+}
+
+hipError_t launch_step_project(const mla_dims& d, int batch, int s_q, const void* x,
+                               const void* w_dkv, const void* w_kr, float* y_part,
+                               const void* q_nope, const void* q_pe, const int32_t* seq_lens,
+                               const void* w_uk, void* q_abs, hipStream_t s) {
+  const int n = batch * s_q;
+  const AppendPlan p = append_plan(d, n);
+  AbsorbArgs q = absorb_args(d, n, q_nope, q_pe, nullptr, w_uk, q_abs);
+  q.lens = seq_lens;
+  q.s_q = s_q;
+  int rb = 1, zb = 1;
+  const int tiles = absorb_tiles(q, &rb, &zb);
+  const int proj = p.col_blocks * p.n_ksplit * cdiv(n, 32);
+  hipLaunchKernelGGL(project_absorb, dim3(proj + tiles), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_dkv),
+                     static_cast<const uint16_t*>(w_kr), n, d.d_model, d.d_c, d.d_r, y_part,
+                     p.col_blocks, p.n_ksplit, q, rb, zb);
+  return hipGetLastError();
+}
+
+hipError_t launch_step_positions(int batch, int s_q, const int32_t* seq_lens, int32_t* seq_idx,
+                                 int32_t* pos, hipStream_t s) {
+  const int n = batch * s_q;
+  hipLaunchKernelGGL(step_positions, dim3(cdiv(n, 256)), dim3(256), 0, s, n, s_q, seq_lens,
+                     seq_idx, pos);
+  return hipGetLastError();
+}
 
 hipError_t launch_projection_partials(int dt, bool mfma, int n_tok, int K, const void* x,
                                       const void* w_a, int n_a, const void* w_b, int n_b,

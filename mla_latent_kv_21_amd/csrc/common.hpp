@@ -95,6 +95,17 @@ __device__ __forceinline__ void rope_cos_sin(int pos, int j, int d, float base, 
   sincosf(static_cast<float>(red), s, c);
 }
 
+// Rotation of one rotary pair (a, q) by (cs, sn): (a cs - q sn, a sn + q cs), written with
+// explicit fused multiply-adds so that every kernel that forms a cache row rounds it alike.
+__device__ __forceinline__ void rope_rotate(float a, float q, float cs, float sn, float* u,
+                                            float* v) {
+  *u = fmaf(a, cs, -(q * sn));
+  *v = fmaf(a, sn, q * cs);
+}
+
+// y * y rounded on its own (never fused into the add that follows it).
+__device__ __forceinline__ float square_rn(float y) { return fmaf(y, y, 0.0f); }
+
 // Slot of position p of sequence b, or -1 when the table does not hold it in bounds.
 __device__ __forceinline__ int64_t cache_slot(const int32_t* table, int max_blocks, int bs,
                                               int num_blocks, int b, int p) {

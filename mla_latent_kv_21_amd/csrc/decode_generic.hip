@@ -799,16 +799,33 @@ hipError_t launch_decode_splitk(const mla_dims& d, int batch, int s_q, const voi
                                    kPlanSlots, d.d_c, 2);
     return launch_decode_mfma(d, batch, s_q, q_abs, cache, scales, num_blocks, table, max_blocks,
                               seq_lens, kPlanCap, p.o, p.lse, p.redo,
-                              static_cast<SplitPlan*>(ws), s);
+                              static_cast<SplitPlan*>(ws), nullptr, s);
   }
   const Partials p = partials_of(ws, batch, s_q, d.n_heads, n_split, d.d_c, d.dtype == MLA_BF16 ? 2 : 4);
   if (uses_mfma(d) || scales != nullptr)
     return launch_decode_mfma(d, batch, s_q, q_abs, cache, scales, num_blocks, table, max_blocks,
-                              seq_lens, n_split, p.o, p.lse, p.redo, nullptr, s);
+                              seq_lens, n_split, p.o, p.lse, p.redo, nullptr, nullptr, s);
   const GenericArgs a = latent_args(d, batch, s_q, q_abs, cache, nullptr, num_blocks, table,
                                     max_blocks, seq_lens, n_split, p);
   return d.dtype == MLA_BF16 ? run_generic<bf16, false>(a, batch, s)
                              : run_generic<float, false>(a, batch, s);
+}
+
+hipError_t launch_decode_step_splitk(const mla_dims& d, int batch, int s_q, const void* q_abs,
+                                     void* cache, int num_blocks, const int32_t* table,
+                                     int max_blocks, const int32_t* seq_lens, int n_split,
+                                     void* ws, const StepRows& rows, hipStream_t s) {
+  // as launch_decode_splitk on the matrix-core kernel, with the new rows formed in the core
+  if (n_split == 0) {
+    const Partials p = partials_of(static_cast<char*>(ws) + kPlanBytes, 1, 1, d.n_heads,
+                                   kPlanSlots, d.d_c, 2);
+    return launch_decode_mfma(d, batch, s_q, q_abs, cache, nullptr, num_blocks, table,
+                              max_blocks, seq_lens, kPlanCap, p.o, p.lse, p.redo,
+                              static_cast<SplitPlan*>(ws), &rows, s);
+  }
+  const Partials p = partials_of(ws, batch, s_q, d.n_heads, n_split, d.d_c, 2);
+  return launch_decode_mfma(d, batch, s_q, q_abs, cache, nullptr, num_blocks, table, max_blocks,
+                            seq_lens, n_split, p.o, p.lse, p.redo, nullptr, &rows, s);
 }
 
 hipError_t launch_decode_merge(const mla_dims& d, int batch, int s_q, const void* q_abs,

@@ -120,10 +120,15 @@ struct SoftState {
 
 // kFp8: the cache rows are e4m3 bytes with one fp32 power-of-two scale per position
 // (`scales`, indexed like the cache slots); see the e4m3 variant above.
-template <int NW, bool kFp8>
+// kApp: a decode step whose s_q new tokens (positions L - s_q .. L - 1 of each sequence, token
+// n = b s_q + i) were projected but not yet written: every workgroup first forms the new rows
+// inside its own range from the projection's partial sums (`app`), exactly as the append's
+// finalize does, stores them at their slots and waits for the stores before its copies read
+// them. Workgroups of several query rows may form the same row; they store the same bytes.
+template <int NW, bool kFp8, bool kApp>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ cache,
-                        const float* __restrict__ scales,
+                        const float* __restrict__ scales, StepRows app,
                         const int32_t* __restrict__ table, const int32_t* __restrict__ lens,
                         int num_blocks, int max_blocks, int bs, int s_q, int n_split,
                         float scale_log2, uint16_t* __restrict__ part_o,
@@ -195,6 +200,78 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       *reinterpret_cast<uint4*>(part_o + prow0 * kLat + 8 * e) = make_uint4(0u, 0u, 0u, 0u);
     if (threadIdx.x == 0) redo[split_id] = 0;
     return;
+  }
+
+  if constexpr (kApp) {
+    static_assert(NW == 4 && !kFp8, "new rows are formed by four waves over bf16 rows");
+    const int L = __builtin_amdgcn_readfirstlane(lens[b]);
+    const int n_tok = batch * s_q;
+    float* ys = reinterpret_cast<float*>(ring[3]);  // the ring is not in use yet
+    float* red = ys + kRowElems;
+    const float* __restrict__ yp = app.y_part;
+    const uint16_t* __restrict__ gam = static_cast<const uint16_t*>(app.gamma);
+    uint16_t* __restrict__ cw = static_cast<uint16_t*>(app.cache);
+    const int first_new = max(t0, L - s_q);
+    for (int p = first_new; p < t1; ++p) {
+      const int n = b * s_q + (p - (L - s_q));
+      const int64_t slot = cache_slot(table, max_blocks, bs, num_blocks, b, p);
+      // column c = threadIdx.x + 256 j: the partial sums in the fixed order k = 0, 1, ...
+      float y[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const int c = threadIdx.x + 256 * j;
+        y[j] = 0.f;
+        if (c < kRowElems) {
+          for (int kk = 0; kk < app.n_ksplit; kk += 16) {
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+              v[u] = kk + u < app.n_ksplit
+                         ? yp[(static_cast<int64_t>(kk + u) * n_tok + n) * kRowElems + c]
+                         : 0.f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+              if (kk + u < app.n_ksplit) y[j] += v[u];
+          }
+        }
+      }
+      // the latent's sum of squares: 64-column block w + 4 j by a butterfly over wave w, then
+      // the eight blocks in order
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float s2 = wave_sum(square_rn(y[j]));
+        if (lane == 0) red[w + 4 * j] = s2;
+      }
+      __syncthreads();
+      float ss = 0.f;
+#pragma unroll
+      for (int blk = 0; blk < kLat / 64; ++blk) ss += red[blk];
+      const float inv = 1.0f / sqrtf(ss / static_cast<float>(kLat) + app.eps);
+      // the rotary pair of column 512 + threadIdx.x (wave 0) is held by lanes 2 jj, 2 jj + 1
+      const float partner = __shfl_xor(y[2], 1, 64);
+      if (slot >= 0) {
+        uint16_t* row = cw + slot * kRowElems;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int c = threadIdx.x + 256 * j;
+          row[c] = f32_to_bf16(y[j] * inv * bf16_to_f32(gam[c]));
+        }
+        if (threadIdx.x < kRowElems - kLat) {
+          const int jj = threadIdx.x >> 1;
+          float cs, sn, u, v;
+          rope_cos_sin(p, jj, kRowElems - kLat, app.base, &cs, &sn);
+          const bool even = (threadIdx.x & 1) == 0;
+          rope_rotate(even ? y[2] : partner, even ? partner : y[2], cs, sn, &u, &v);
+          row[kLat + threadIdx.x] = f32_to_bf16(even ? u : v);
+        }
+      }
+      __syncthreads();  // red is free for the next row
+    }
+    if (first_new < t1) {
+      // every wave's stores are done before any wave's copies read the rows
+      wait_vm<0>();
+      __syncthreads();
+    }
   }
 
   const int l32 = lane & 31, hi = lane >> 5;
@@ -644,6 +721,11 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
 
 }  // namespace
 
+bool mfma_step_fits(const mla_dims& d) {
+  return d.dtype == MLA_BF16 && d.d_c == 512 && d.d_r == 64 && d.block_size % 32 == 0 &&
+         d.n_heads == 128 && !(d.flags & MLA_FLAG_GENERIC_KERNELS);
+}
+
 bool mfma_decode_fp8_fits(const mla_dims& d) {
   return d.dtype == MLA_BF16 && d.d_c == 512 && d.d_r == 64 && d.block_size % 32 == 0 &&
          d.n_heads == 128;
@@ -658,22 +740,25 @@ hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void*
                               const void* cache, const float* scales, int num_blocks,
                               const int32_t* table, int max_blocks, const int32_t* seq_lens,
                               int n_split, void* part_o, float* part_lse, int* redo,
-                              SplitPlan* plan, hipStream_t s) {
+                              SplitPlan* plan, const StepRows* app, hipStream_t s) {
+  const StepRows none{};
   const float scale_log2 = softmax_scale_of(d) * 1.4426950408889634f;
   const dim3 grid = plan != nullptr ? dim3(kPlanSlots) : dim3(n_split, s_q, batch);
-#define MLA_LAUNCH(NW_, FP8_)                                                                \
-  hipLaunchKernelGGL((decode_mfma_kernel<NW_, FP8_>), grid, dim3(64 * NW_), 0, s,             \
+#define MLA_LAUNCH(NW_, FP8_, APP_)                                                          \
+  hipLaunchKernelGGL((decode_mfma_kernel<NW_, FP8_, APP_>), grid, dim3(64 * NW_), 0, s,       \
                      static_cast<const uint16_t*>(q_abs), static_cast<const uint16_t*>(cache), \
-                     scales, table, seq_lens, num_blocks, max_blocks, d.block_size, s_q,       \
-                     n_split, scale_log2, static_cast<uint16_t*>(part_o), part_lse, redo,      \
-                     batch, plan)
-  if (scales != nullptr) {
-    MLA_LAUNCH(4, true);  // e4m3 rows: H = 128 only (mfma_decode_fp8_fits)
+                     scales, app != nullptr ? *app : none, table, seq_lens, num_blocks,        \
+                     max_blocks, d.block_size, s_q, n_split, scale_log2,                       \
+                     static_cast<uint16_t*>(part_o), part_lse, redo, batch, plan)
+  if (app != nullptr) {
+    MLA_LAUNCH(4, false, true);  // new rows formed in the core: H = 128 (mfma_step_fits)
+  } else if (scales != nullptr) {
+    MLA_LAUNCH(4, true, false);  // e4m3 rows: H = 128 only (mfma_decode_fp8_fits)
   } else {
     switch (d.n_heads) {
-      case 128: MLA_LAUNCH(4, false); break;
-      case 64: MLA_LAUNCH(2, false); break;
-      default: MLA_LAUNCH(1, false); break;
+      case 128: MLA_LAUNCH(4, false, false); break;
+      case 64: MLA_LAUNCH(2, false, false); break;
+      default: MLA_LAUNCH(1, false, false); break;
     }
   }
 #undef MLA_LAUNCH

@@ -71,6 +71,36 @@ hipError_t launch_decode_splitk(const mla_dims& d, int batch, int s_q, const voi
                                 const void* cache, const float* scales, int num_blocks,
                                 const int32_t* table, int max_blocks, const int32_t* seq_lens,
                                 int n_split, void* ws, hipStream_t s);
+
+// A decode step's new rows, formed inside the split-K core: the s_q new tokens of every
+// sequence are its positions L - s_q .. L - 1 (token n = b s_q + i), projected but not yet
+// written (y_part: the append's split-K partial sums, [n_ksplit][B s_q][d_c + d_r]).
+struct StepRows {
+  const float* y_part;
+  const void* gamma;  // RMSNorm gain [d_c]
+  void* cache;        // the latent cache, written at the new rows' slots
+  int n_ksplit;
+  float eps, base;
+};
+// Whether the core can form the new rows itself (bf16, d_c 512, d_r 64, H = 128), and the
+// split-K core of such a step (the merge is launch_decode_merge's).
+bool mfma_step_fits(const mla_dims& d);
+hipError_t launch_decode_step_splitk(const mla_dims& d, int batch, int s_q, const void* q_abs,
+                                     void* cache, int num_blocks, const int32_t* table,
+                                     int max_blocks, const int32_t* seq_lens, int n_split,
+                                     void* ws, const StepRows& rows, hipStream_t s);
+// The step's projection of the B s_q new tokens into y_part together with the absorption of
+// their queries (positions implied by the lengths) in one launch; needs
+// step_project_fits(d, B s_q). The rows themselves are formed by the core.
+bool step_project_fits(const mla_dims& d, int n_tok);
+hipError_t launch_step_project(const mla_dims& d, int batch, int s_q, const void* x,
+                               const void* w_dkv, const void* w_kr, float* y_part,
+                               const void* q_nope, const void* q_pe, const int32_t* seq_lens,
+                               const void* w_uk, void* q_abs, hipStream_t s);
+// Positions of a step's new tokens for the separate calls: seq_idx[n] = n / s_q,
+// pos[n] = seq_lens[n / s_q] - s_q + n % s_q (pos doubles as the queries' positions).
+hipError_t launch_step_positions(int batch, int s_q, const int32_t* seq_lens, int32_t* seq_idx,
+                                 int32_t* pos, hipStream_t s);
 // Merge: flagged splits recomputed, log-sum-exp merge over splits, W_UV per group.
 hipError_t launch_decode_merge(const mla_dims& d, int batch, int s_q, const void* q_abs,
                                const void* cache, const float* scales, int num_blocks,
@@ -93,6 +123,7 @@ hipError_t launch_gqa_decode(const mla_dims& d, int batch, int s_q, const void* 
 // with e4m3 rows (H = 128 as well).
 bool mfma_decode_fits(const mla_dims& d);
 bool mfma_decode_fp8_fits(const mla_dims& d);
+struct StepRows;
 // With plan != NULL the splits follow the length-balanced plan (plan.hpp), which the kernel
 // computes and stores at *plan; else n_split uniform splits per (sequence, query).
 struct SplitPlan;
@@ -100,7 +131,7 @@ hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void*
                               const void* cache, const float* scales, int num_blocks,
                               const int32_t* table, int max_blocks, const int32_t* seq_lens,
                               int n_split, void* part_o, float* part_lse, int* redo,
-                              SplitPlan* plan, hipStream_t s);
+                              SplitPlan* plan, const StepRows* app, hipStream_t s);
 // Whether n_split = 0 takes the length-balanced plan for these dims and rows, and the
 // workspace of a planned decode (the plan, then partials for every slot).
 bool plan_applies(const mla_dims& d, int batch, int s_q);

@@ -1,0 +1,123 @@
+"""GPU parity of mla_decode_step, a whole decode step in one call.
+
+The step appends the s_q new tokens of every sequence (its last s_q positions), absorbs their
+queries and decodes. On the matrix-core path it forms the new rows inside the split-K core;
+elsewhere it runs the separate calls. Either way it must equal, bit for bit, the separate
+calls made by hand (mla_cache_append_absorb_q with the new tokens' sequence and position
+indices, then mla_decode): the output, the lse and every byte of the cache. One case also
+goes end to end against the oracle's reconstructed attention.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from gpu_cases import DEV, TOL, check, check_lse, dev, note
+from mla_latent_kv_21_amd import binding as M
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+BASE, EPS = 10000.0, 1e-6
+
+
+def step_case(wl, lens, s_q, extra):
+    w = W.WORKLOADS[wl].replace(batch=len(lens), s_q=s_q)
+    lens = np.asarray(lens, np.int32)
+    table, nb = W.block_table(w, lens)
+    pool = W.cache_pool(w, nb, extra=extra)          # the history (new slots overwritten)
+    x = W.tokens(w, w.batch * s_q, extra=extra)
+    wts = W.weights(w, random_gamma=True)
+    q = W.queries(w)
+    qpos = W.query_positions(w, lens)
+    return dict(w=w, lens=lens, table=table, nb=nb, pool=pool, x=x, wts=wts, q=q, qpos=qpos)
+
+
+def run_step(c, n_split):
+    w = c["w"]
+    d = M.dims_of(w)
+    cache = dev(c["pool"].clone())
+    out = torch.empty(w.batch, w.s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=DEV)
+    lse = torch.empty(w.batch, w.s_q, w.n_heads, dtype=torch.float32, device=DEV)
+    M.mla_decode_step(d, dev(c["x"]), dev(c["wts"]["w_dkv"]), dev(c["wts"]["gamma"]),
+                      dev(c["wts"]["w_kr"]), dev(c["q"]["q_nope"]), dev(c["q"]["q_pe"]),
+                      dev(c["wts"]["w_uk"]), dev(c["wts"]["w_uv"]), cache, dev(c["table"]),
+                      dev(c["lens"]), out, lse, n_split=n_split)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu(), cache.cpu()
+
+
+def run_separate(c, n_split):
+    w = c["w"]
+    d = M.dims_of(w)
+    cache = dev(c["pool"].clone())
+    seq = np.repeat(np.arange(w.batch, dtype=np.int32), w.s_q)
+    pos = c["qpos"].reshape(-1).astype(np.int32)
+    q_abs = torch.empty(w.batch, w.s_q, w.n_heads, w.row, dtype=w.torch_dtype, device=DEV)
+    M.mla_cache_append_absorb_q(d, dev(c["x"]), dev(seq), dev(pos), dev(c["wts"]["w_dkv"]),
+                                dev(c["wts"]["gamma"]), dev(c["wts"]["w_kr"]), dev(c["table"]),
+                                c["nb"], cache, dev(c["q"]["q_nope"]), dev(c["q"]["q_pe"]),
+                                dev(c["qpos"]), dev(c["wts"]["w_uk"]), q_abs)
+    out = torch.empty(w.batch, w.s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=DEV)
+    lse = torch.empty(w.batch, w.s_q, w.n_heads, dtype=torch.float32, device=DEV)
+    M.mla_decode(d, q_abs, cache, dev(c["table"]), dev(c["lens"]), dev(c["wts"]["w_uv"]), out,
+                 lse, n_split=n_split)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu(), cache.cpu()
+
+
+def same_bits(a, b):
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+CASES = [
+    # (name, workload, lens, s_q, n_split): the fused path is H = 128 bf16
+    ("paged-planned", "dsv3-paged", [300, 2049, 65, 1], 1, 0),
+    ("paged-split7", "dsv3-paged", [300, 2049, 65], 1, 7),
+    ("long-split64", "long-128k", [4096, 100], 1, 64),
+    # new rows 126..129 straddle the 64-position chunk boundary at 128
+    ("gqla-sq4-straddle", "gqla-g8", [130, 700], 4, 0),
+    ("gqla-sq2-split5", "gqla-g8", [2, 301], 2, 5),
+    # the separate calls inside the step: H = 32 and fp32 caches
+    ("mid-h32", "mid-bf16", [300, 45], 1, 0),
+    ("smallem-f32", "smallem-fp32", [512, 3], 2, 3),
+]
+
+
+@pytest.mark.parametrize("name,wl,lens,s_q,n_split", CASES, ids=[c[0] for c in CASES])
+def test_step_equals_the_separate_calls(name, wl, lens, s_q, n_split):
+    c = step_case(wl, lens, s_q, extra=W.WORKLOADS[wl].seed % 97)
+    note(f"decode step {name} lens={lens} s_q={s_q} n_split={n_split}")
+    out_a, lse_a, cache_a = run_step(c, n_split)
+    out_b, lse_b, cache_b = run_separate(c, n_split)
+    assert same_bits(cache_a, cache_b), "the cache rows differ"
+    assert same_bits(out_a, out_b) and same_bits(lse_a, lse_b)
+    assert np.all(np.isfinite(O.f64(out_a)))
+
+
+def test_step_end_to_end_against_the_oracle():
+    """A step over a history drawn as cache rows: the new rows formed from x, then the
+    attention of the queries over the whole cache, against keys and values rebuilt from the
+    latents by the oracle."""
+    c = step_case("gqla-g8", [200, 131], 2, extra=7)
+    w = c["w"]
+    note("decode step end to end")
+    out, lse, cache = run_step(c, 0)
+    pos = c["qpos"].reshape(-1)
+    rows_new = O.round_storage(O.latent_rows(c["x"], c["wts"]["w_dkv"], c["wts"]["gamma"],
+                                             c["wts"]["w_kr"], pos, BASE, EPS), w.dtype)
+    pool = O.f64(c["pool"]).reshape(-1, w.row).copy()
+    k = 0
+    for b, L in enumerate(c["lens"]):
+        for i in range(w.s_q):
+            pool[O.slot(c["table"], b, int(L) - w.s_q + i, w.block_size)] = rows_new[k]
+            k += 1
+    pool = pool.reshape(c["nb"], w.block_size, w.row)
+    for b, L in enumerate(c["lens"]):
+        hist = O.gather_rows(pool, c["table"], b, int(L))
+        ref, ref_lse = O.decode_reconstructed(c["q"]["q_nope"][b], c["q"]["q_pe"][b],
+                                              c["qpos"][b], hist, c["wts"]["w_uk"],
+                                              c["wts"]["w_uv"], w.n_groups, w.d_c, w.d_v, BASE)
+        check(out[b], ref, TOL[w.dtype])
+        check_lse(lse[b].double().numpy(), ref_lse, TOL[w.dtype])
