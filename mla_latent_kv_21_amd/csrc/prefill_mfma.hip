@@ -1,5 +1,6 @@
 // Prefill attention over the expanded cache on gfx950 matrix cores: bf16, D = D_v = 128,
-// d_r = 64, one split, many query rows per group (heads of one group x new tokens).
+// d_r = 64, many query rows per group (heads of one group x new tokens), in one or several
+// splits of the history (the latter for multi-token decode steps).
 //
 // What is computed is the no-cache pass of the Smallem article ("Le code": every head's keys
 // and values are key_up and value_up of the latent; "Deux produits ou une concaténation ?":
@@ -22,7 +23,9 @@
 //    transposing LDS reads); a wave skips the tiles past its rows' causal end;
 //  * two workgroups per CU (registers capped at 256 per lane), so that one wave's softmax
 //    overlaps the other's products on each SIMD;
-//  * the output O / l (bf16) and the natural-log lse are written directly.
+//  * with one split (direct) the output O / l (bf16) and the natural-log lse are written
+//    directly; with several, split k writes its normalised bf16 partial and its log2-domain
+//    lse at row k * n_rows + row, the layout gqa_mfma_kernel writes, for the GQA merge.
 #include <climits>
 #include <type_traits>
 
