@@ -267,3 +267,29 @@ def test_fp8_host_checks(L):
         ctypes.byref(dims(d_r=40)), 4, P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE),
         P(FAKE), 1, 4, 8, P(FAKE), P(FAKE), P(FAKE), need, 1, P(FAKE), P(FAKE), P(FAKE),
         P(FAKE), P(FAKE), None) == -2                       # 552 values: not 16-byte rows
+
+
+def test_decode_step_host_checks(L):
+    """mla_decode_step refuses what its component calls refuse, and a short workspace, before
+    anything is launched; an empty batch does nothing."""
+    d = dims()
+    dp = ctypes.byref(d)
+    need = L.mla_decode_step_workspace_bytes(dp, 4, 1, 64, 2048)
+    dec = L.mla_decode_workspace_bytes(dp, 4, 1, 64, 2048)
+    assert need > dec > 0
+
+    def call(dd=d, batch=4, s_q=1, x=FAKE, gamma=FAKE, w_uv=FAKE, ws=FAKE, ws_bytes=need,
+             out=FAKE, n_split=64):
+        return L.mla_decode_step(ctypes.byref(dd), batch, s_q, P(x), P(FAKE), P(gamma), P(FAKE),
+                                 P(FAKE), P(FAKE), P(FAKE), P(w_uv), P(FAKE), 8192, P(FAKE),
+                                 2048, P(FAKE), n_split, P(ws), ws_bytes, P(out), None, None)
+    assert call(batch=0) == 0
+    assert call(s_q=0) == -4
+    assert call(n_split=M.MLA_MAX_SPLIT + 1) == -4
+    assert call(ws_bytes=need - 1) == -5
+    assert call(ws=None) == -1
+    assert call(x=None) == -1                       # the append's input
+    assert call(gamma=None) == -1
+    assert call(w_uv=None) == -1
+    assert call(out=FAKE + 4) == -6
+    assert call(dd=dims(n_groups=3)) == -2

@@ -121,3 +121,39 @@ def test_step_end_to_end_against_the_oracle():
                                               c["wts"]["w_uv"], w.n_groups, w.d_c, w.d_v, BASE)
         check(out[b], ref, TOL[w.dtype])
         check_lse(lse[b].double().numpy(), ref_lse, TOL[w.dtype])
+
+
+def test_step_at_the_benchmark_size():
+    """The long-context workload the benchmark times (4 sequences x 131,072 positions, 64
+    uniform splits): the step equals the separate calls bit for bit, new rows included."""
+    w = W.WORKLOADS["long-128k"]
+    lens = W.seq_lens(w)
+    table, nb = W.block_table(w, lens)
+    d = M.dims_of(w)
+    cache = W.cache_pool_device(w, nb, DEV)
+    x = dev(W.tokens(w, w.batch, extra=1))
+    wts = {k: dev(v) for k, v in W.weights(w, random_gamma=True).items()}
+    q = {k: dev(v) for k, v in W.queries(w).items()}
+    qpos = W.query_positions(w, lens)
+    tab, lens_d = dev(table), dev(lens)
+    note(f"decode step full size B={w.batch} L={int(lens[0])} n_split={w.n_split}")
+    cache_a = cache.clone()
+    out_a = torch.empty(w.batch, 1, w.n_heads, w.d_v, dtype=torch.bfloat16, device=DEV)
+    lse_a = torch.empty(w.batch, 1, w.n_heads, dtype=torch.float32, device=DEV)
+    M.mla_decode_step(d, x, wts["w_dkv"], wts["gamma"], wts["w_kr"], q["q_nope"], q["q_pe"],
+                      wts["w_uk"], wts["w_uv"], cache_a, tab, lens_d, out_a, lse_a,
+                      n_split=w.n_split)
+    cache_b = cache.clone()
+    q_abs = torch.empty(w.batch, 1, w.n_heads, w.row, dtype=torch.bfloat16, device=DEV)
+    seq = dev(np.arange(w.batch, dtype=np.int32))
+    pos = dev(qpos.reshape(-1).astype(np.int32))
+    M.mla_cache_append_absorb_q(d, x, seq, pos, wts["w_dkv"], wts["gamma"], wts["w_kr"], tab,
+                                nb, cache_b, q["q_nope"], q["q_pe"], dev(qpos), wts["w_uk"],
+                                q_abs)
+    out_b = torch.empty_like(out_a)
+    lse_b = torch.empty_like(lse_a)
+    M.mla_decode(d, q_abs, cache_b, tab, lens_d, wts["w_uv"], out_b, lse_b, n_split=w.n_split)
+    torch.cuda.synchronize()
+    assert torch.equal(cache_a.view(torch.int16), cache_b.view(torch.int16))
+    assert same_bits(out_a, out_b) and same_bits(lse_a, lse_b)
+    assert bool(torch.isfinite(out_a.float()).all())
