@@ -25,12 +25,17 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
-SPLITK_SRC = os.path.join(ROOT, "mla_latent_kv_21_amd", "csrc", "decode_mfma.hip")
+# the split-K core's source and the headers it includes
+SPLITK_SRC = [os.path.join(ROOT, "mla_latent_kv_21_amd", "csrc", f)
+              for f in ("decode_mfma.hip", "mfma_util.hpp", "common.hpp", "plan.hpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_mfma_traffic.json")
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(SPLITK_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in SPLITK_SRC:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
