@@ -68,6 +68,7 @@ constexpr int kF8Slots = 3;
 constexpr int kF8Base = 2 * kTileBytes;                     // staging after two bf16 slots
 constexpr int kDma8 = 5;                                    // copies per wave per fp8 tile
 constexpr int kPreF8 = 6;                                   // score fragments ahead (e4m3)
+constexpr int kPreW1 = 4;                                   // score fragments ahead (H = 32)
 static_assert(kF8Base + kF8Slots * kF8SlotBytes <= kSlots * kTileBytes, "fp8 staging fits");
 
 // Physical 16-byte chunk of logical chunk c in row t of an e4m3 staging tile: XOR-swizzled
@@ -439,8 +440,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     f32x16 sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-    // e4m3 rows: fewer fragments ahead, for the registers their copy offsets take
-    constexpr int kP = kFp8 ? kPreF8 : kPre;
+    // fewer fragments ahead where the copy offsets take more registers: e4m3 rows, and one
+    // wave per workgroup (36 copies per tile, one offset register each)
+    constexpr int kP = kFp8 ? kPreF8 : NW == 1 ? kPreW1 : kPre;
     bf16x8 af[kP];
 #pragma unroll
     for (int i = 0; i < kP; ++i) af[i] = lds16(cur + qb[i & 3] + 128 * (i >> 2));
