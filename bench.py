@@ -377,23 +377,21 @@ def measure_prefill(dev, torch):
 
 
 def measure_fp8_step(w, d, lens, cache, tab, lens_d, nb, ns, step_args, n_steps, dev, torch):
-    """The bench step over an e4m3 copy of its cache: mla_cache_append_absorb_q_fp8, then
-    mla_decode_fp8_splitk and mla_decode_fp8_merge, timed like the bf16 step, with the e4m3
-    split-K core in a loop of its own against the binding roofline (580 bytes per position)."""
+    """The bench step over an e4m3 copy of its cache (mla_decode_step_fp8: the projection with
+    the absorption, the e4m3 split-K core quantising the new rows, the merge), timed like the
+    bf16 step, with the e4m3 split-K core in a loop of its own against the binding roofline
+    (580 bytes per position)."""
     from mla_latent_kv_21_amd import accounting as A
     from mla_latent_kv_21_amd import binding as M
-    x_new, seq_idx, pos_new, wts, q, q_pos, q_abs, out, lse, ws, ws_app = step_args
+    x_new, seq_idx, pos_new, wts, q, q_pos, q_abs, out, lse, ws, ws_app, ws_step = step_args
     codes = torch.empty(cache.shape, dtype=torch.uint8, device=dev)
     scales = torch.empty(cache.shape[:2], dtype=torch.float32, device=dev)
     M.mla_cache_quantize_fp8(d, cache, codes, scales)
 
     def step8():
-        M.mla_cache_append_absorb_q_fp8(d, x_new, seq_idx, pos_new, wts["w_dkv"], wts["gamma"],
-                                        wts["w_kr"], tab, nb, codes, scales, q["q_nope"],
-                                        q["q_pe"], q_pos, wts["w_uk"], q_abs, workspace=ws_app)
-        M.mla_decode_fp8_splitk(d, q_abs, codes, scales, tab, lens_d, ns, ws)
-        M.mla_decode_fp8_merge(d, q_abs, codes, scales, tab, lens_d, wts["w_uv"], out, lse, ns,
-                               ws)
+        M.mla_decode_step_fp8(d, x_new, wts["w_dkv"], wts["gamma"], wts["w_kr"], q["q_nope"],
+                              q["q_pe"], wts["w_uk"], wts["w_uv"], codes, scales, tab, lens_d,
+                              out, lse, n_split=ns, workspace=ws_step)
     for _ in range(5):
         step8()
     stream = torch.cuda.current_stream()
@@ -407,13 +405,18 @@ def measure_fp8_step(w, d, lens, cache, tab, lens_d, nb, ns, step_args, n_steps,
     ms = a.elapsed_time(b) / n_steps
     if not torch.isfinite(out.float()).all():
         raise RuntimeError("non-finite fp8 decode output")
+    # the absorbed queries, for the core on its own
+    M.mla_cache_append_absorb_q_fp8(d, x_new, seq_idx, pos_new, wts["w_dkv"], wts["gamma"],
+                                    wts["w_kr"], tab, nb, codes, scales, q["q_nope"], q["q_pe"],
+                                    q_pos, wts["w_uk"], q_abs, workspace=ws_app)
     core8 = lambda: M.mla_decode_fp8_splitk(d, q_abs, codes, scales, tab, lens_d, ns, ws)
     core = _time_calls(lambda i: core8(), max(20, n_steps), torch, stats=True)
     bb_step, bb_core = _interleaved(step8, core8, 10, 5, torch)
     tr = A.decode_traffic(lens, w.s_q, w.n_heads, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt,
                           row_bytes=A.fp8_row_bytes(w.d_c, w.d_r))
     r = {"workload": w.name, "cache": "e4m3 + fp32 scale per position",
-         "calls": "mla_cache_append_absorb_q_fp8, mla_decode_fp8_splitk, mla_decode_fp8_merge",
+         "calls": "mla_decode_step_fp8 (project_absorb, decode_mfma_kernel<4, true, true>, "
+                  "merge_project_kernel)",
          "ms_per_step": ms, "tokens_per_s": w.batch * w.s_q / (ms * 1e-3),
          "core_launch_stats": core, "core_bytes_per_launch": tr["core_bytes"],
          "core_GBps": tr["core_bytes"] / (core["mean_ms"] * 1e-3) / 1e9,
@@ -653,7 +656,8 @@ def main():
         if rows == "all":
             rec["rows"]["fp8_step"] = measure_fp8_step(
                 w, d, lens, cache, tab, lens_d, nb, ns,
-                (x_new, seq_idx, pos_new, wts, q, q_pos, q_abs, out, lse, ws, ws_app), n_steps,
+                (x_new, seq_idx, pos_new, wts, q, q_pos, q_abs, out, lse, ws, ws_app, ws_step),
+                n_steps,
                 dev, torch)
             rec["rows"].update(measure_rows(dev, torch))
         if rows == "prefill":

@@ -320,6 +320,26 @@ mla_status mla_decode_fp8_merge(const mla_dims* dims, int32_t batch, int32_t s_q
                                 hipStream_t stream);
 
 /*
+ * mla_decode_step_fp8 -- mla_decode_step over an e4m3 cache (cache_fp8, cache_scale as in
+ *  mla_cache_append_fp8): results are those of
+ *     mla_cache_append_absorb_q_fp8(dims, B * s_q, x, seq_idx, pos, ..., cache_fp8,
+ *                                   cache_scale, ..., s_q, q_nope, q_pe, q_pos = pos, w_uk, q_abs)
+ *     mla_decode_fp8(dims, B, s_q, q_abs, cache_fp8, cache_scale, ..., w_uv, n_split, ...)
+ *  bit for bit (the new rows' bytes and scales left in the cache). The split-K core quantises
+ *  the new rows itself, by the append's rule, when B * s_q <= 2048 and C % 8 == 0; otherwise
+ *  the step runs the separate calls. Shapes, workspace (mla_decode_step_workspace_bytes) and
+ *  errors as for mla_decode_step and mla_decode_fp8.
+ */
+mla_status mla_decode_step_fp8(const mla_dims* dims, int32_t batch, int32_t s_q, const void* x,
+                               const void* w_dkv, const void* rms_gamma, const void* w_kr,
+                               const void* q_nope, const void* q_pe, const void* w_uk,
+                               const void* w_uv, void* cache_fp8, float* cache_scale,
+                               int32_t num_blocks, const int32_t* block_table,
+                               int32_t max_blocks, const int32_t* seq_lens, int32_t n_split,
+                               void* workspace, size_t ws_bytes, void* out, float* lse,
+                               hipStream_t stream);
+
+/*
  * gqla_expand -- expand latent rows into the GQA cache once ([GQLA] "Chemin GQA"):
  *     gqa_row = [c · W_UK[:, 0] .. c · W_UK[:, G-1] || c · W_UV[:, 0] .. c · W_UV[:, G-1] || k_r]
  *  for positions start_pos[b] .. seq_lens[b]-1 of every sequence (start_pos NULL: from 0).

@@ -32,7 +32,7 @@ EXPORTS = ["mla_cache_append_workspace_bytes", "mla_cache_append", "mla_absorb_q
            "mla_decode_noalloc", "mla_decode_step_workspace_bytes", "mla_decode_step",
            "mla_cache_quantize_fp8", "mla_cache_append_fp8", "mla_cache_append_absorb_q_fp8",
            "mla_decode_fp8", "mla_decode_fp8_splitk", "mla_decode_fp8_merge",
-           "gqla_expand",
+           "mla_decode_step_fp8", "gqla_expand",
            "gqla_decode_workspace_bytes", "gqla_decode",
            "mla_prefill_workspace_bytes", "mla_prefill", "mla_auto_split", "mla_select_path",
            "mla_status_string",
@@ -98,6 +98,8 @@ def lib() -> ctypes.CDLL:
             "mla_decode_step_workspace_bytes": (S, [D, I, I, I, I]),
             "mla_decode_step": (I, [D, I, I, P, P, P, P, P, P, P, P, P, I, P, I, P, I, P, S, P,
                                     P, P]),
+            "mla_decode_step_fp8": (I, [D, I, I, P, P, P, P, P, P, P, P, P, P, I, P, I, P, I, P,
+                                        S, P, P, P]),
             "mla_cache_quantize_fp8": (I, [D, ctypes.c_int64, P, P, P, P]),
             "mla_cache_append_fp8": (I, [D, I, P, P, P, P, P, P, P, I, I, I, P, P, P, S, P]),
             "mla_cache_append_absorb_q_fp8": (I, [D, I, P, P, P, P, P, P, P, I, I, I, P, P, P, S,
@@ -281,6 +283,27 @@ def mla_decode_step(dims, x, w_dkv, gamma, w_kr, q_nope, q_pe, w_uk, w_uv, laten
                                _ptr(seq_lens), n_split, _ptr(workspace), workspace.numel(),
                                _ptr(out), _ptr(lse), _stream())
     _check(st, "mla_decode_step")
+
+
+def mla_decode_step_fp8(dims, x, w_dkv, gamma, w_kr, q_nope, q_pe, w_uk, w_uv, cache_fp8,
+                        cache_scale, block_table, seq_lens, out, lse=None, n_split=0,
+                        workspace=None):
+    """mla_decode_step over an e4m3 cache (bytes [num_blocks, bs, d_c + d_r], scales
+    [num_blocks, bs])."""
+    B, s_q = q_nope.shape[0], q_nope.shape[1]
+    mb = block_table.shape[1]
+    if x.shape[0] != B * s_q or block_table.shape[0] != B:
+        raise ValueError("x must hold B * s_q tokens and the block table B rows")
+    if workspace is None:
+        workspace = _workspace(mla_decode_step_workspace_bytes(dims, B, s_q, n_split, mb),
+                               x.device)
+    st = lib().mla_decode_step_fp8(ctypes.byref(dims), B, s_q, _ptr(x), _ptr(w_dkv), _ptr(gamma),
+                                   _ptr(w_kr), _ptr(q_nope), _ptr(q_pe), _ptr(w_uk), _ptr(w_uv),
+                                   _ptr(cache_fp8), _ptr(cache_scale), cache_fp8.shape[0],
+                                   _ptr(block_table), mb, _ptr(seq_lens), n_split,
+                                   _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse),
+                                   _stream())
+    _check(st, "mla_decode_step_fp8")
 
 
 def mla_decode_splitk(dims, q_abs, latent_cache, block_table, seq_lens, n_split, workspace):

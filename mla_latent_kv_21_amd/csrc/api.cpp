@@ -499,25 +499,35 @@ size_t mla_decode_step_workspace_bytes(const mla_dims* dims, int32_t batch, int3
   return step_layout(*dims, batch, s_q, dec).total;
 }
 
-mla_status mla_decode_step(const mla_dims* dims, int32_t batch, int32_t s_q, const void* x,
-                           const void* w_dkv, const void* rms_gamma, const void* w_kr,
-                           const void* q_nope, const void* q_pe, const void* w_uk,
-                           const void* w_uv, void* latent_cache, int32_t num_blocks,
-                           const int32_t* block_table, int32_t max_blocks,
-                           const int32_t* seq_lens, int32_t n_split, void* workspace,
-                           size_t ws_bytes, void* out, float* lse, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The decode step over bf16 rows (scales NULL) or e4m3 rows with per-slot scales.
+mla_status decode_step(const mla_dims* dims, int32_t batch, int32_t s_q, const void* x,
+                       const void* w_dkv, const void* rms_gamma, const void* w_kr,
+                       const void* q_nope, const void* q_pe, const void* w_uk, const void* w_uv,
+                       void* latent_cache, float* scales, bool fp8, int32_t num_blocks,
+                       const int32_t* block_table, int32_t max_blocks, const int32_t* seq_lens,
+                       int32_t n_split, void* workspace, size_t ws_bytes, void* out, float* lse,
+                       hipStream_t stream) {
   mla_status st = check_dims(dims);
   if (st != MLA_OK) return st;
+  if (fp8 && (!fp8_rows_ok(*dims) || !mla::mfma_decode_fp8_fits(*dims) ||
+              (dims->flags & MLA_FLAG_GENERIC_KERNELS)))
+    return MLA_ERR_SHAPE;
   if (batch < 0 || s_q < 1 || max_blocks < 1 || num_blocks < 1 || n_split < 0 ||
       n_split > MLA_MAX_SPLIT)
     return MLA_ERR_RANGE;
   if (batch == 0) return MLA_OK;
   if (static_cast<int64_t>(batch) * s_q > 65535 * 16) return MLA_ERR_RANGE;
-  if (!workspace || !seq_lens || !w_uv || !out) return MLA_ERR_NULL;
+  if (!workspace || !seq_lens || !w_uv || !out || (fp8 && !scales)) return MLA_ERR_NULL;
   const size_t need = mla_decode_step_workspace_bytes(dims, batch, s_q, n_split, max_blocks);
   if (need == 0) return MLA_ERR_RANGE;
   if (ws_bytes < need) return MLA_ERR_WORKSPACE;
-  if (!aligned16(workspace) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  if (!aligned16(workspace) || !aligned16(w_uv) || !aligned16(out) ||
+      (fp8 && !aligned16(scales)))
+    return MLA_ERR_ALIGN;
   const mla_dims& d = *dims;
   const StepLayout l = step_layout(d, batch, s_q, 0);
   char* ws = static_cast<char*>(workspace);
@@ -538,12 +548,13 @@ mla_status mla_decode_step(const mla_dims* dims, int32_t batch, int32_t s_q, con
   st = check_decode(dims, batch, s_q, q_abs, latent_cache, num_blocks, block_table, max_blocks,
                     seq_lens, n_split, dws, dws_bytes, &ns);
   if (st != MLA_OK) return st;
-  if (mla::mfma_step_fits(d) && mla::step_project_fits(d, n_tok)) {
+  const bool core_rows = fp8 ? mla::mfma_decode_fp8_fits(d) : mla::mfma_step_fits(d);
+  if (core_rows && mla::step_project_fits(d, n_tok)) {
     // three launches: projection with the absorption, the core forming the new rows, merge
     st = hip_status(mla::launch_step_project(d, batch, s_q, x, w_dkv, w_kr, y_part, q_nope, q_pe,
                                              seq_lens, w_uk, q_abs, stream));
     if (st != MLA_OK) return st;
-    const mla::StepRows rows{y_part, rms_gamma, latent_cache,
+    const mla::StepRows rows{y_part, rms_gamma, latent_cache, fp8 ? scales : nullptr,
                              mla::projection_ksplit(d.d_model), d.rms_eps, d.rope_base};
     st = hip_status(mla::launch_decode_step_splitk(d, batch, s_q, q_abs, latent_cache,
                                                    num_blocks, block_table, max_blocks,
@@ -554,17 +565,48 @@ mla_status mla_decode_step(const mla_dims* dims, int32_t batch, int32_t s_q, con
     if (st != MLA_OK) return st;
     st = hip_status(mla::launch_append_absorb(d, n_tok, x, seq_idx, pos, w_dkv, rms_gamma,
                                               w_kr, block_table, batch, max_blocks, num_blocks,
-                                              latent_cache, nullptr, y_part, batch, s_q, q_nope,
-                                              q_pe, pos, w_uk, q_abs, stream));
+                                              latent_cache, fp8 ? scales : nullptr, y_part,
+                                              batch, s_q, q_nope, q_pe, pos, w_uk, q_abs,
+                                              stream));
     if (st != MLA_OK) return st;
-    st = hip_status(mla::launch_decode_splitk(d, batch, s_q, q_abs, latent_cache, nullptr,
-                                              num_blocks, block_table, max_blocks, seq_lens, ns,
-                                              dws, stream));
+    st = hip_status(mla::launch_decode_splitk(d, batch, s_q, q_abs, latent_cache,
+                                              fp8 ? scales : nullptr, num_blocks, block_table,
+                                              max_blocks, seq_lens, ns, dws, stream));
   }
   if (st != MLA_OK) return st;
-  return hip_status(mla::launch_decode_merge(d, batch, s_q, q_abs, latent_cache, nullptr,
-                                             num_blocks, block_table, max_blocks, seq_lens, w_uv,
-                                             ns, dws, out, lse, stream));
+  return hip_status(mla::launch_decode_merge(d, batch, s_q, q_abs, latent_cache,
+                                             fp8 ? scales : nullptr, num_blocks, block_table,
+                                             max_blocks, seq_lens, w_uv, ns, dws, out, lse,
+                                             stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode_step(const mla_dims* dims, int32_t batch, int32_t s_q, const void* x,
+                           const void* w_dkv, const void* rms_gamma, const void* w_kr,
+                           const void* q_nope, const void* q_pe, const void* w_uk,
+                           const void* w_uv, void* latent_cache, int32_t num_blocks,
+                           const int32_t* block_table, int32_t max_blocks,
+                           const int32_t* seq_lens, int32_t n_split, void* workspace,
+                           size_t ws_bytes, void* out, float* lse, hipStream_t stream) {
+  return decode_step(dims, batch, s_q, x, w_dkv, rms_gamma, w_kr, q_nope, q_pe, w_uk, w_uv,
+                     latent_cache, nullptr, false, num_blocks, block_table, max_blocks, seq_lens,
+                     n_split, workspace, ws_bytes, out, lse, stream);
+}
+
+mla_status mla_decode_step_fp8(const mla_dims* dims, int32_t batch, int32_t s_q, const void* x,
+                               const void* w_dkv, const void* rms_gamma, const void* w_kr,
+                               const void* q_nope, const void* q_pe, const void* w_uk,
+                               const void* w_uv, void* cache_fp8, float* cache_scale,
+                               int32_t num_blocks, const int32_t* block_table,
+                               int32_t max_blocks, const int32_t* seq_lens, int32_t n_split,
+                               void* workspace, size_t ws_bytes, void* out, float* lse,
+                               hipStream_t stream) {
+  return decode_step(dims, batch, s_q, x, w_dkv, rms_gamma, w_kr, q_nope, q_pe, w_uk, w_uv,
+                     cache_fp8, cache_scale, true, num_blocks, block_table, max_blocks, seq_lens,
+                     n_split, workspace, ws_bytes, out, lse, stream);
 }
 
 mla_status gqla_expand(const mla_dims* dims, int32_t batch, const void* latent_cache,

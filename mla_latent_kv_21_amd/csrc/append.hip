@@ -216,25 +216,6 @@ __global__ __launch_bounds__(256) void append_project_mfma(const uint16_t* __res
                     blockIdx.z * 32);
 }
 
-// ---- e4m3 rows. A row is stored as OCP FP8 E4M3 bytes (1 sign, 4 exponent bits of bias 7,
-// 3 mantissa bits; largest finite 448, smallest subnormal 2^-9) times one fp32 scale per
-// position: the smallest power of two s with amax <= 448 s (s = 1 for an all-zero row), so
-// every value x / s is exact in fp32 and rounds (to nearest, ties to even) into the format's
-// finite range, and byte x s is exact in bf16.
-__device__ __forceinline__ int e4m3_scale_exp(float amax) {
-  if (!(amax > 0.f)) return 0;
-  int k;
-  const float m = frexpf(amax, &k);  // amax = m 2^k, m in [0.5, 1)
-  return m <= 0.875f ? k - 9 : k - 8;
-}
-
-// four values (already divided by the scale) as four e4m3 bytes, element 0 in the low byte
-__device__ __forceinline__ unsigned e4m3_pack4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return static_cast<unsigned>(w);
-}
-
 // kFp8: the row goes out as e4m3 bytes (cache8) and its scale (scale8), quantised from the
 // values the bf16 row would hold.
 template <typename T, bool kFp8>

@@ -106,6 +106,25 @@ __device__ __forceinline__ void rope_rotate(float a, float q, float cs, float sn
 // y * y rounded on its own (never fused into the add that follows it).
 __device__ __forceinline__ float square_rn(float y) { return fmaf(y, y, 0.0f); }
 
+// e4m3 rows. A row is stored as OCP FP8 E4M3 bytes (1 sign, 4 exponent bits of bias 7,
+// 3 mantissa bits; largest finite 448, smallest subnormal 2^-9) times one fp32 scale per
+// position: the smallest power of two s with amax <= 448 s (s = 1 for an all-zero row), so
+// every value x / s is exact in fp32 and rounds (to nearest, ties to even) into the format's
+// finite range, and byte x s is exact in bf16.
+__device__ __forceinline__ int e4m3_scale_exp(float amax) {
+  if (!(amax > 0.f)) return 0;
+  int k;
+  const float m = frexpf(amax, &k);  // amax = m 2^k, m in [0.5, 1)
+  return m <= 0.875f ? k - 9 : k - 8;
+}
+
+// four values (already divided by the scale) as four e4m3 bytes, element 0 in the low byte
+__device__ __forceinline__ unsigned e4m3_pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<unsigned>(w);
+}
+
 // Slot of position p of sequence b, or -1 when the table does not hold it in bounds.
 __device__ __forceinline__ int64_t cache_slot(const int32_t* table, int max_blocks, int bs,
                                               int num_blocks, int b, int p) {

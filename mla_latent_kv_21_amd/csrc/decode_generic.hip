@@ -816,16 +816,17 @@ hipError_t launch_decode_step_splitk(const mla_dims& d, int batch, int s_q, cons
                                      int max_blocks, const int32_t* seq_lens, int n_split,
                                      void* ws, const StepRows& rows, hipStream_t s) {
   // as launch_decode_splitk on the matrix-core kernel, with the new rows formed in the core
+  // (e4m3 rows when rows.scale is set: the core reads the scales it writes)
   if (n_split == 0) {
     const Partials p = partials_of(static_cast<char*>(ws) + kPlanBytes, 1, 1, d.n_heads,
                                    kPlanSlots, d.d_c, 2);
-    return launch_decode_mfma(d, batch, s_q, q_abs, cache, nullptr, num_blocks, table,
+    return launch_decode_mfma(d, batch, s_q, q_abs, cache, rows.scale, num_blocks, table,
                               max_blocks, seq_lens, kPlanCap, p.o, p.lse, p.redo,
                               static_cast<SplitPlan*>(ws), &rows, s);
   }
   const Partials p = partials_of(ws, batch, s_q, d.n_heads, n_split, d.d_c, 2);
-  return launch_decode_mfma(d, batch, s_q, q_abs, cache, nullptr, num_blocks, table, max_blocks,
-                            seq_lens, n_split, p.o, p.lse, p.redo, nullptr, &rows, s);
+  return launch_decode_mfma(d, batch, s_q, q_abs, cache, rows.scale, num_blocks, table,
+                            max_blocks, seq_lens, n_split, p.o, p.lse, p.redo, nullptr, &rows, s);
 }
 
 hipError_t launch_decode_merge(const mla_dims& d, int batch, int s_q, const void* q_abs,

@@ -124,8 +124,9 @@ struct SoftState {
 // kApp: a decode step whose s_q new tokens (positions L - s_q .. L - 1 of each sequence, token
 // n = b s_q + i) were projected but not yet written: every workgroup first forms the new rows
 // inside its own range from the projection's partial sums (`app`), exactly as the append's
-// finalize does, stores them at their slots and waits for the stores before its copies read
-// them. Workgroups of several query rows may form the same row; they store the same bytes.
+// finalize does (with kFp8, quantised to e4m3 bytes and a scale by the finalize's rule),
+// stores them at their slots and waits for the stores before its copies read them.
+// Workgroups of several query rows may form the same row; they store the same bytes.
 template <int NW, bool kFp8, bool kApp>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ cache,
@@ -204,7 +205,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   }
 
   if constexpr (kApp) {
-    static_assert(NW == 4 && !kFp8, "new rows are formed by four waves over bf16 rows");
+    static_assert(NW == 4, "new rows are formed by four waves");
     const int L = __builtin_amdgcn_readfirstlane(lens[b]);
     const int n_tok = batch * s_q;
     float* ys = reinterpret_cast<float*>(ring[3]);  // the ring is not in use yet
@@ -250,7 +251,41 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       const float inv = 1.0f / sqrtf(ss / static_cast<float>(kLat) + app.eps);
       // the rotary pair of column 512 + threadIdx.x (wave 0) is held by lanes 2 jj, 2 jj + 1
       const float partner = __shfl_xor(y[2], 1, 64);
-      if (slot >= 0) {
+      if constexpr (kFp8) {
+        // the values the bf16 row would hold, then their e4m3 bytes and the row's scale
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int c = threadIdx.x + 256 * j;
+          const float v = bf16_to_f32(f32_to_bf16(y[j] * inv * bf16_to_f32(gam[c])));
+          ys[c] = v;
+          amax = fmaxf(amax, fabsf(v));
+        }
+        if (threadIdx.x < kRowElems - kLat) {
+          const int jj = threadIdx.x >> 1;
+          float cs, sn, u, v;
+          rope_cos_sin(p, jj, kRowElems - kLat, app.base, &cs, &sn);
+          const bool even = (threadIdx.x & 1) == 0;
+          rope_rotate(even ? y[2] : partner, even ? partner : y[2], cs, sn, &u, &v);
+          const float r = bf16_to_f32(f32_to_bf16(even ? u : v));
+          ys[kLat + threadIdx.x] = r;
+          amax = fmaxf(amax, fabsf(r));
+        }
+        amax = wave_max(amax);
+        if (lane == 0) red[8 + w] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red[8], red[9]), fmaxf(red[10], red[11]));
+        const int e = e4m3_scale_exp(amax);
+        const float rs = ldexpf(1.f, -e);
+        if (slot >= 0) {
+          if (threadIdx.x < kRowElems / 4) {
+            const float* v4 = ys + 4 * threadIdx.x;
+            reinterpret_cast<unsigned*>(static_cast<uint8_t*>(app.cache) + slot * kRowElems)
+                [threadIdx.x] = e4m3_pack4(v4[0] * rs, v4[1] * rs, v4[2] * rs, v4[3] * rs);
+          }
+          if (threadIdx.x == 0) app.scale[slot] = ldexpf(1.f, e);
+        }
+      } else if (slot >= 0) {
         uint16_t* row = cw + slot * kRowElems;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -752,7 +787,9 @@ hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void*
                      scales, app != nullptr ? *app : none, table, seq_lens, num_blocks,        \
                      max_blocks, d.block_size, s_q, n_split, scale_log2,                       \
                      static_cast<uint16_t*>(part_o), part_lse, redo, batch, plan)
-  if (app != nullptr) {
+  if (app != nullptr && scales != nullptr) {
+    MLA_LAUNCH(4, true, true);   // e4m3 rows formed in the core: H = 128
+  } else if (app != nullptr) {
     MLA_LAUNCH(4, false, true);  // new rows formed in the core: H = 128 (mfma_step_fits)
   } else if (scales != nullptr) {
     MLA_LAUNCH(4, true, false);  // e4m3 rows: H = 128 only (mfma_decode_fp8_fits)

@@ -79,6 +79,7 @@ struct StepRows {
   const float* y_part;
   const void* gamma;  // RMSNorm gain [d_c]
   void* cache;        // the latent cache, written at the new rows' slots
+  float* scale;       // e4m3 rows: the per-slot scales, written with them (NULL for bf16 rows)
   int n_ksplit;
   float eps, base;
 };

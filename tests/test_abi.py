@@ -293,3 +293,25 @@ def test_decode_step_host_checks(L):
     assert call(w_uv=None) == -1
     assert call(out=FAKE + 4) == -6
     assert call(dd=dims(n_groups=3)) == -2
+
+
+def test_decode_step_fp8_host_checks(L):
+    """mla_decode_step_fp8 refuses what mla_decode_step and the e4m3 decode refuse (shapes
+    without an e4m3 core, a missing or misaligned scale array), before anything is launched."""
+    d = dims()
+    dp = ctypes.byref(d)
+    need = L.mla_decode_step_workspace_bytes(dp, 4, 1, 64, 2048)
+
+    def call(dd=d, batch=4, x=FAKE, scale=FAKE, ws=FAKE, ws_bytes=need, n_split=64):
+        return L.mla_decode_step_fp8(ctypes.byref(dd), batch, 1, P(x), P(FAKE), P(FAKE), P(FAKE),
+                                     P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(FAKE), P(scale), 8192,
+                                     P(FAKE), 2048, P(FAKE), n_split, P(ws), ws_bytes, P(FAKE),
+                                     None, None)
+    assert call(batch=0) == 0
+    assert call(scale=None) == -1
+    assert call(scale=FAKE + 4) == -6
+    assert call(ws_bytes=need - 1) == -5
+    assert call(x=None) == -1
+    assert call(n_split=M.MLA_MAX_SPLIT + 1) == -4
+    assert call(dd=dims(n_heads=32, n_groups=32)) == -2            # no e4m3 core for H = 32
+    assert call(dd=dims(generic=True)) == -2

@@ -157,3 +157,102 @@ def test_step_at_the_benchmark_size():
     assert torch.equal(cache_a.view(torch.int16), cache_b.view(torch.int16))
     assert same_bits(out_a, out_b) and same_bits(lse_a, lse_b)
     assert bool(torch.isfinite(out_a.float()).all())
+
+
+# ---- the same step over an e4m3 cache (mla_decode_step_fp8): the core quantises the new rows
+#      by the append's rule; bytes, scales, output and lse equal the separate e4m3 calls'
+
+def run_step_fp8(c, codes, scales, n_split):
+    w = c["w"]
+    d = M.dims_of(w)
+    cd, sd = dev(codes.clone()), dev(scales.clone())
+    out = torch.empty(w.batch, w.s_q, w.n_heads, w.d_v, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(w.batch, w.s_q, w.n_heads, dtype=torch.float32, device=DEV)
+    M.mla_decode_step_fp8(d, dev(c["x"]), dev(c["wts"]["w_dkv"]), dev(c["wts"]["gamma"]),
+                          dev(c["wts"]["w_kr"]), dev(c["q"]["q_nope"]), dev(c["q"]["q_pe"]),
+                          dev(c["wts"]["w_uk"]), dev(c["wts"]["w_uv"]), cd, sd, dev(c["table"]),
+                          dev(c["lens"]), out, lse, n_split=n_split)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu(), cd.cpu(), sd.cpu()
+
+
+def run_separate_fp8(c, codes, scales, n_split):
+    w = c["w"]
+    d = M.dims_of(w)
+    cd, sd = dev(codes.clone()), dev(scales.clone())
+    seq = np.repeat(np.arange(w.batch, dtype=np.int32), w.s_q)
+    pos = c["qpos"].reshape(-1).astype(np.int32)
+    q_abs = torch.empty(w.batch, w.s_q, w.n_heads, w.row, dtype=torch.bfloat16, device=DEV)
+    M.mla_cache_append_absorb_q_fp8(d, dev(c["x"]), dev(seq), dev(pos), dev(c["wts"]["w_dkv"]),
+                                    dev(c["wts"]["gamma"]), dev(c["wts"]["w_kr"]),
+                                    dev(c["table"]), c["nb"], cd, sd, dev(c["q"]["q_nope"]),
+                                    dev(c["q"]["q_pe"]), dev(c["qpos"]), dev(c["wts"]["w_uk"]),
+                                    q_abs)
+    out = torch.empty(w.batch, w.s_q, w.n_heads, w.d_v, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(w.batch, w.s_q, w.n_heads, dtype=torch.float32, device=DEV)
+    M.mla_decode_fp8(d, q_abs, cd, sd, dev(c["table"]), dev(c["lens"]), dev(c["wts"]["w_uv"]),
+                     out, lse, n_split=n_split)
+    torch.cuda.synchronize()
+    return out.cpu(), lse.cpu(), cd.cpu(), sd.cpu()
+
+
+FP8_CASES = [
+    ("paged-planned", "dsv3-paged", [300, 2049, 65, 1], 1, 0),
+    ("paged-split7", "dsv3-paged", [300, 2049, 65], 1, 7),
+    ("long-split64", "long-128k", [4096, 100], 1, 64),
+    ("gqla-sq4-straddle", "gqla-g8", [130, 700], 4, 0),
+    ("gqla-sq2-split5", "gqla-g8", [2, 301], 2, 5),
+]
+
+
+@pytest.mark.parametrize("name,wl,lens,s_q,n_split", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_fp8_step_equals_the_separate_calls(name, wl, lens, s_q, n_split):
+    c = step_case(wl, lens, s_q, extra=W.WORKLOADS[wl].seed % 89)
+    codes, scales = W.cache_pool_e4m3(c["w"], c["nb"], extra=3)
+    note(f"fp8 decode step {name} lens={lens} s_q={s_q} n_split={n_split}")
+    out_a, lse_a, codes_a, sc_a = run_step_fp8(c, codes, scales, n_split)
+    out_b, lse_b, codes_b, sc_b = run_separate_fp8(c, codes, scales, n_split)
+    assert torch.equal(codes_a, codes_b), "the cache bytes differ"
+    assert same_bits(sc_a, sc_b), "the scales differ"
+    assert same_bits(out_a, out_b) and same_bits(lse_a, lse_b)
+    assert np.all(np.isfinite(O.f64(out_a)))
+    # the new rows are the oracle's e4m3 encoding of the bf16 rows the append would store
+    w = c["w"]
+    rows = O.round_storage(O.latent_rows(c["x"], c["wts"]["w_dkv"], c["wts"]["gamma"],
+                                         c["wts"]["w_kr"], c["qpos"].reshape(-1), BASE, EPS),
+                           w.dtype)
+    k = 0
+    for b, L in enumerate(c["lens"]):
+        for i in range(w.s_q):
+            slot = O.slot(c["table"], b, int(L) - w.s_q + i, w.block_size)
+            got = O.dequantize_rows_e4m3(codes_a.view(-1, w.row)[slot].numpy()[None],
+                                         sc_a.view(-1)[slot].numpy()[None])[0]
+            assert np.max(np.abs(got - rows[k])) <= np.max(np.abs(rows[k])) * 2.0 ** -4
+            k += 1
+
+
+def test_fp8_step_shape_is_checked():
+    """H = 32 has no e4m3 decode: the call refuses before enqueueing anything."""
+    c = step_case("mid-bf16", [300, 45], 1, extra=1)
+    w = c["w"]
+    codes, scales = W.cache_pool_e4m3(w, c["nb"], extra=1)
+    with pytest.raises(RuntimeError, match="MLA_ERR_SHAPE"):
+        run_step_fp8(c, codes, scales, 0)
+
+
+def test_fp8_step_at_the_benchmark_size():
+    """long-128k (4 x 131,072 positions, 64 uniform splits) over an e4m3 cache: the step equals
+    the separate calls bit for bit, new rows and scales included."""
+    w = W.WORKLOADS["long-128k"]
+    lens = W.seq_lens(w)
+    table, nb = W.block_table(w, lens)
+    note(f"fp8 decode step full size B={w.batch} L={int(lens[0])} n_split={w.n_split}")
+    codes, scales = W.cache_pool_e4m3(w, nb, extra=2)
+    c = dict(w=w, lens=lens, table=table, nb=nb, x=W.tokens(w, w.batch, extra=1),
+             wts=W.weights(w, random_gamma=True), q=W.queries(w),
+             qpos=W.query_positions(w, lens))
+    out_a, lse_a, codes_a, sc_a = run_step_fp8(c, codes, scales, w.n_split)
+    out_b, lse_b, codes_b, sc_b = run_separate_fp8(c, codes, scales, w.n_split)
+    assert torch.equal(codes_a, codes_b) and same_bits(sc_a, sc_b)
+    assert same_bits(out_a, out_b) and same_bits(lse_a, lse_b)
+    assert bool(torch.isfinite(out_a.float()).all())
