@@ -256,3 +256,23 @@ def test_fp8_step_at_the_benchmark_size():
     assert torch.equal(codes_a, codes_b) and same_bits(sc_a, sc_b)
     assert same_bits(out_a, out_b) and same_bits(lse_a, lse_b)
     assert bool(torch.isfinite(out_a.float()).all())
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "e4m3"])
+def test_step_past_2048_tokens_runs_the_separate_calls(fp8):
+    """3 sequences x 700 new tokens (2,100 > 2,048): the step takes its separate-calls path
+    (positions from the lengths on the device, append with absorption, split-K, merge) and
+    still equals the calls made by hand, bit for bit."""
+    c = step_case("dsv3-paged", [900, 705, 1400], 700, extra=5)
+    note(f"decode step past 2048 tokens fp8={fp8}")
+    if fp8:
+        codes, scales = W.cache_pool_e4m3(c["w"], c["nb"], extra=4)
+        a = run_step_fp8(c, codes, scales, 3)
+        b = run_separate_fp8(c, codes, scales, 3)
+        assert torch.equal(a[2], b[2]) and same_bits(a[3], b[3])
+    else:
+        a = run_step(c, 3)
+        b = run_separate(c, 3)
+        assert same_bits(a[2], b[2])
+    assert same_bits(a[0], b[0]) and same_bits(a[1], b[1])
+    assert np.all(np.isfinite(O.f64(a[0])))
