@@ -8,9 +8,11 @@
 // (GQLA summary, section 1), so the kernel is organised around reading each cache row from
 // HBM exactly once and sharing it across all H heads:
 //
-//  * one workgroup per (split, query, sequence); NW = H/32 waves; wave w owns heads
-//    [32w, 32w+32) for the scores and latent columns [512w/NW, 512(w+1)/NW) of all heads for
-//    the output;
+//  * one workgroup per (split, query, sequence) of NW waves, H/32 blocks of 32 heads: with
+//    H = 64 or 128, NW = H/32 and wave w owns heads [32w, 32w+32) for the scores; with H = 32
+//    four waves each compute the one block's scores (an eighth of the tile's products each,
+//    against a quarter of the chip's matrix cores idle with a single wave). Wave w owns
+//    latent columns [512w/NW, 512(w+1)/NW) of all heads for the output;
 //  * 32-position tiles (36,864 B, always inside one cache block) stream HBM -> LDS with
 //    global_load_lds_dwordx4 into a 4-slot ring, two tiles in flight; 16-byte
 //    chunks are XOR-swizzled by position so every LDS read pattern below is free of bank
@@ -22,8 +24,8 @@
 //    which the merge kernel then recomputes exactly;
 //  * P (bf16) leaves each wave in the register layout the P · V product consumes as its A
 //    operand (the position order inside a K-step is permuted identically on both operands)
-//    and is exchanged through LDS; O[H x 512/NW] += P · V with V read by transposing LDS
-//    reads from the same tile;
+//    and is exchanged through LDS (with H = 32 every wave holds the whole P itself);
+//    O[H x 512/NW] += P · V with V read by transposing LDS reads from the same tile;
 //  * the loop body is scheduled by hand: the scores of tile t+1 run with their LDS reads
 //    several steps ahead, then P · V of tile t runs with the softmax of tile t+1 spread
 //    between its products, so the matrix cores are fed while the VALU and LDS work;
@@ -68,7 +70,6 @@ constexpr int kF8Slots = 3;
 constexpr int kF8Base = 2 * kTileBytes;                     // staging after two bf16 slots
 constexpr int kDma8 = 5;                                    // copies per wave per fp8 tile
 constexpr int kPreF8 = 6;                                   // score fragments ahead (e4m3)
-constexpr int kPreW1 = 4;                                   // score fragments ahead (H = 32)
 static_assert(kF8Base + kF8Slots * kF8SlotBytes <= kSlots * kTileBytes, "fp8 staging fits");
 
 // Physical 16-byte chunk of logical chunk c in row t of an e4m3 staging tile: XOR-swizzled
@@ -103,15 +104,18 @@ __device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& a, const bf16x8&
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
 }
 
-template <int NW>
+// Waves of a workgroup with HB blocks of 32 heads: one per block, or four for one block.
+__host__ __device__ constexpr int waves_of(int hb) { return hb == 1 ? 4 : hb; }
+
+template <int HB>
 struct Shared {
-  bf16x8 p[2][NW][2][64];         // P fragments: [parity][head block][K-step][lane]
+  bf16x8 p[2][HB][2][64];         // P fragments: [parity][head block][K-step][lane]
 };
 // After the loop the ring is free and holds the per-head 1/l and the waves' flags.
-template <int NW>
+template <int HB>
 struct Tail {
-  float inv_l[NW * 32];
-  int over[NW];                   // a head of the wave outgrew its reference
+  float inv_l[HB * 32];
+  int over[waves_of(HB)];         // a head of the wave outgrew its reference
 };
 
 struct SoftState {
@@ -127,8 +131,8 @@ struct SoftState {
 // finalize does (with kFp8, quantised to e4m3 bytes and a scale by the finalize's rule),
 // stores them at their slots and waits for the stores before its copies read them.
 // Workgroups of several query rows may form the same row; they store the same bytes.
-template <int NW, bool kFp8, bool kApp>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int HB, bool kFp8, bool kApp>
+__global__ __launch_bounds__(waves_of(HB) * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ cache,
                         const float* __restrict__ scales, StepRows app,
                         const int32_t* __restrict__ table, const int32_t* __restrict__ lens,
@@ -136,21 +140,23 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
                         float scale_log2, uint16_t* __restrict__ part_o,
                         float* __restrict__ part_lse, int* __restrict__ redo, int batch,
                         SplitPlan* __restrict__ plan_out) {
-  constexpr int H = NW * 32;
+  constexpr int NW = waves_of(HB);                  // waves
+  constexpr bool kDup = NW > HB;                    // every wave computes the one block's scores
+  constexpr int H = HB * 32;
   constexpr int kDB = 16 / NW;                      // 32-column latent blocks per wave
-  constexpr int kPV = 2 * kDB * NW;                 // P · V products per tile (32)
+  constexpr int kPV = 2 * kDB * HB;                 // P · V products per tile per wave
   constexpr int kDma = kTileChunks / (NW * 64);     // copies per wave per tile
   static_assert(kDma <= kKSteps, "copies are spread over the score K-steps");
   __shared__ __attribute__((aligned(16))) char ring[kSlots][kTileBytes];
-  __shared__ Shared<NW> sh;
-  static_assert(sizeof(ring) + sizeof(Shared<NW>) <= 160 * 1024, "LDS");
+  __shared__ Shared<HB> sh;
+  static_assert(sizeof(ring) + sizeof(Shared<HB>) <= 160 * 1024, "LDS");
   // bf16 tile slots in use: four (two in flight, two computed on) or, with e4m3 rows, two
   // (the staging ring holds the tiles in flight)
   constexpr int kBMask = (kFp8 ? 2 : kSlots) - 1;
   auto stage8 = [&](int i) -> char* {
     return reinterpret_cast<char*>(ring) + kF8Base + (i % kF8Slots) * kF8SlotBytes;
   };
-  static_assert(!kFp8 || NW == 4, "the e4m3 copy plan is laid out for four waves");
+  static_assert(!kFp8 || HB == 4, "the e4m3 copy plan is laid out for four waves, H = 128");
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -205,7 +211,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   }
 
   if constexpr (kApp) {
-    static_assert(NW == 4, "new rows are formed by four waves");
+    static_assert(HB == 4, "new rows are formed by four waves, H = 128");
     const int L = __builtin_amdgcn_readfirstlane(lens[b]);
     const int n_tok = batch * s_q;
     float* ys = reinterpret_cast<float*>(ring[3]);  // the ring is not in use yet
@@ -311,6 +317,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   }
 
   const int l32 = lane & 31, hi = lane >> 5;
+  const int hbw = kDup ? 0 : w;  // the wave's head block for the scores
 
   // Absorbed queries of this wave's 32 heads as MFMA B operands, in registers for the whole
   // split: lane -> head 32w + l32, K-step ks covers row elements [16 ks + 8 hi, +8). Loaded
@@ -350,9 +357,10 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       }
   }
 
-  f32x16 o[NW * kDB];
+  constexpr int kNO = HB * kDB;  // O accumulators per wave (16, or 4 with H = 32)
+  f32x16 o[kNO];
 #pragma unroll
-  for (int j = 0; j < NW * kDB; ++j)
+  for (int j = 0; j < kNO; ++j)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
   float m_ref = -INFINITY;  // reference max (log2 units) of head 32w + l32
@@ -475,9 +483,8 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     f32x16 sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-    // fewer fragments ahead where the copy offsets take more registers: e4m3 rows, and one
-    // wave per workgroup (36 copies per tile, one offset register each)
-    constexpr int kP = kFp8 ? kPreF8 : NW == 1 ? kPreW1 : kPre;
+    // fewer fragments ahead where the copy offsets take more registers (e4m3 rows)
+    constexpr int kP = kFp8 ? kPreF8 : kPre;
     bf16x8 af[kP];
 #pragma unroll
     for (int i = 0; i < kP; ++i) af[i] = lds16(cur + qb[i & 3] + 128 * (i >> 2));
@@ -506,6 +513,9 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   // Split in pieces (compile-time numbers) so the unmasked case can be spread between the
   // P · V products.
   constexpr int kSoftPieces = 26;
+  // with H = 32 the wave keeps P in registers: P of the tile P · V is working on (p_cur) and
+  // of the next tile, formed by the softmax pieces meanwhile (p_next)
+  bf16x8 p_cur[2], p_next[2];
   auto soft_piece = [&](int piece, f32x16& sc, SoftState& s, int par)
                         __attribute__((always_inline)) {
     if (piece == 0) {
@@ -539,8 +549,13 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       for (int e = 0; e < 4; ++e) s.pf[r >> 3][(r & 7) + e] = static_cast<__bf16>(sc[r + e]);
     } else {
       l_part += s.psum;
-      sh.p[par][w][0][lane] = s.pf[0];
-      sh.p[par][w][1][lane] = s.pf[1];
+      if constexpr (kDup) {
+        p_next[0] = s.pf[0];
+        p_next[1] = s.pf[1];
+      } else {
+        sh.p[par][w][0][lane] = s.pf[0];
+        sh.p[par][w][1][lane] = s.pf[1];
+      }
     }
   };
   auto mask_tail = [&](f32x16& sc, int nvalid) __attribute__((always_inline)) {
@@ -567,7 +582,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   // with the softmax pieces of the next tile's scores `sc` between the products.
   auto pv = [&](const char* cur, int par, f32x16& sc, int npar) __attribute__((always_inline)) {
     SoftState s;
-    bf16x8 pa[2][NW];
+    bf16x8 pa[2][HB];
     i16x4 va[kVPre + 1][2];  // V fragments of kVPre + 1 (k2, db) steps: [buffer][rb]
     auto read_v = [&](int step, i16x4 (&dst)[2]) __attribute__((always_inline)) {
       const int n2 = step / kDB, ndb = step % kDB;
@@ -575,20 +590,25 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       dst[0] = lds_read_tr(vp + vt[ndb & 1][0]);
       dst[1] = lds_read_tr(vp + vt[ndb & 1][1]);
     };
+    if constexpr (kDup) {
+      pa[0][0] = p_cur[0];
+      pa[1][0] = p_cur[1];
+    } else {
 #pragma unroll
-    for (int hb = 0; hb < NW; ++hb) pa[0][hb] = sh.p[par][hb][0][lane];
+      for (int hb = 0; hb < HB; ++hb) pa[0][hb] = sh.p[par][hb][0][lane];
+    }
 #pragma unroll
     for (int st = 0; st < kVPre; ++st) read_v(st, va[st]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < kPV; ++i) {
-      const int k2 = i / (kDB * NW), db = (i / NW) % kDB, hb = i % NW;
-      const int step = i / NW;
+      const int k2 = i / (kDB * HB), db = (i / HB) % kDB, hb = i % HB;
+      const int step = i / HB;
       const int buf = step % (kVPre + 1);
       if (hb == 0 && step + kVPre < 2 * kDB) read_v(step + kVPre, va[(step + kVPre) % (kVPre + 1)]);
-      if (i == kPV / 4) {
+      if (!kDup && i == kPV / 4) {
 #pragma unroll
-        for (int h2 = 0; h2 < NW; ++h2) pa[1][h2] = sh.p[par][h2][1][lane];
+        for (int h2 = 0; h2 < HB; ++h2) pa[1][h2] = sh.p[par][h2][1][lane];
       }
       const bf16x8 vf = __builtin_bit_cast(
           bf16x8, __builtin_shufflevector(va[buf][0], va[buf][1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -619,7 +639,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     // the compiler's waits for them (which do not count the copies) stay conservative
     {
       const char* qp = reinterpret_cast<const char*>(q_abs) +
-                       (row0 + 32 * w + l32) * kRowBytes + hi * 16;
+                       (row0 + 32 * hbw + l32) * kRowBytes + hi * 16;
 #pragma unroll
       for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
     }
@@ -647,6 +667,10 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       __syncthreads();
     }
     softmax_all(scores(ring[0], nullptr, 0u, nullptr), nv0, 0);
+    if constexpr (kDup) {
+      p_cur[0] = p_next[0];
+      p_cur[1] = p_next[1];
+    }
     if constexpr (!kFp8) {
       if (nv0 < kTileTok) zero_tail(ring[0], nv0);
     }
@@ -694,6 +718,10 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     f32x16 sc = scores(ring[nslot], src3, dlds, ssrc3);
     if (nv_next < kTileTok) mask_tail(sc, nv_next);
     pv(ring[slot], t & 1, sc, (t + 1) & 1);
+    if constexpr (kDup) {
+      p_cur[0] = p_next[0];
+      p_cur[1] = p_next[1];
+    }
     // zeroed before the next barrier; other waves may still be reading these rows for their
     // scores, which are masked anyway
     if constexpr (!kFp8) {
@@ -704,17 +732,21 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   // ---- partials: o / l and m_ref + log2(l) per head, plus the recompute flag.
   // The last O products must have landed before VALU reads of O: 32 wait states, more than
   // any matrix-core result latency.
-  asm volatile("s_nop 15\n\ts_nop 15"
-               : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
-                 "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
-                 "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
+  if constexpr (kNO == 16)
+    asm volatile("s_nop 15\n\ts_nop 15"
+                 : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                   "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
+                   "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
+  else
+    asm volatile("s_nop 15\n\ts_nop 15" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
+  static_assert(kNO == 16 || kNO == 4, "the wait above names every accumulator");
   const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
   const bool wover = __builtin_amdgcn_ballot_w64(over) != 0;
-  Tail<NW>& tl = *reinterpret_cast<Tail<NW>*>(ring[0]);
+  Tail<HB>& tl = *reinterpret_cast<Tail<HB>*>(ring[0]);
   __syncthreads();  // every wave is done with the ring
   if (lane == 0) tl.over[w] = wover ? 1 : 0;
-  if (lane < 32) {
-    const int h = 32 * w + lane;
+  if (lane < 32 && (!kDup || w == 0)) {  // (with H = 32 every wave holds the same l)
+    const int h = 32 * hbw + lane;
     tl.inv_l[h] = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     part_lse[prow0 + h] = l_tot > 0.f ? m_ref + log2f(l_tot) : -INFINITY;
   }
@@ -730,10 +762,10 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   constexpr int kStageRow = kLat * 4 + 32;
   char* stage = ring[0] + 1024;  // after the Tail
   static_assert(1024 + 32 * kStageRow <= kSlots * kTileBytes, "stage fits in the ring");
-  static_assert(sizeof(Tail<NW>) <= 1024, "tail fits before the stage");
+  static_assert(sizeof(Tail<HB>) <= 1024, "tail fits before the stage");
   uint16_t* dst = part_o + prow0 * kLat;
 #pragma unroll
-  for (int hb = 0; hb < NW; ++hb) {
+  for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int hl = 8 * (r >> 2) + 4 * hi + (r & 3);
@@ -781,8 +813,8 @@ hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void*
   const StepRows none{};
   const float scale_log2 = softmax_scale_of(d) * 1.4426950408889634f;
   const dim3 grid = plan != nullptr ? dim3(kPlanSlots) : dim3(n_split, s_q, batch);
-#define MLA_LAUNCH(NW_, FP8_, APP_)                                                          \
-  hipLaunchKernelGGL((decode_mfma_kernel<NW_, FP8_, APP_>), grid, dim3(64 * NW_), 0, s,       \
+#define MLA_LAUNCH(HB_, FP8_, APP_)                                                          \
+  hipLaunchKernelGGL((decode_mfma_kernel<HB_, FP8_, APP_>), grid, dim3(64 * waves_of(HB_)), 0, s,\
                      static_cast<const uint16_t*>(q_abs), static_cast<const uint16_t*>(cache), \
                      scales, app != nullptr ? *app : none, table, seq_lens, num_blocks,        \
                      max_blocks, d.block_size, s_q, n_split, scale_log2,                       \
