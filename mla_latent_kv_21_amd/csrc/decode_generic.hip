@@ -365,8 +365,8 @@ __global__ __launch_bounds__(kMergeThreads, 4) void merge_kernel(GenericArgs a,
 }
 
 // ---------------------------------------------------------------------------------------
-// Merge (+ W_UV) for bf16 partials, one workgroup per (head h, block of kRpb = 32 or 16 query
-// rows; the launch takes 16 when that gives the chip more workgroups):
+// Merge (+ W_UV) for bf16 partials, one workgroup per (head h, block of kRpb query rows: 32,
+// or 16, 8, 4 while halving gives the chip more workgroups):
 //  * latent path (PW = d_c = 512, D_v = 128): the head's W_UV slice (512 x 128, 128 KiB) is
 //    read once for the block's rows instead of once per row, and the projection runs on
 //    matrix cores: out^T [128 x 32 rows] = W_UV^T · o_lat^T with v_mfma_f32_32x32x16_bf16,
@@ -391,7 +391,8 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
                                                                 const uint16_t* __restrict__ w_uv,
                                                                 uint16_t* __restrict__ out,
                                                                 float* lse_out) {
-  static_assert(kRpb == kPjRows || kRpb == kPjRows / 2, "rows per workgroup");
+  static_assert(kRpb == 32 || kRpb == 16 || kRpb == 8 || kRpb == 4, "rows per workgroup");
+  static_assert(kPjRows == 32, "rows of the staged o_lat and of the projection's products");
   typedef mfma::bf16x8 bf16x8;
   typedef mfma::f32x16 f32x16;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -690,31 +691,38 @@ hipError_t run_combine(const GenericArgs& a, const int* redo, int batch, int dv,
                        void* out, float* lse, hipStream_t s) {
   const int M = batch * a.s_q;
   if constexpr (sizeof(T) == 2) {
-    // rows per workgroup of the latent merge: kPjRows, or 16 when that leaves CUs idle (the
-    // rows then spread over twice the workgroups, each reading the head's W_UV slice; fewer
-    // rows per workgroup measured slower, the merge of a handful of rows being latency-bound).
+    // rows per workgroup of the latent merge: the largest of 32, 16, 8, 4 whose grid fills
+    // the chip, else the largest giving the most workgroups (each workgroup reads the head's
+    // W_UV slice; splitting a handful of rows that already make one block per head measured
+    // slower, but 32 workgroups for 16 rows of 32 heads leave most of the chip idle).
     // A compile-time count: as a run-time one it made the GQA merge twice as slow.
     const bool proj = w_uv != nullptr;
-    const bool half = proj && static_cast<int64_t>(a.H) * cdiv(M, kPjRows) < kPjTargetWgs &&
-                      cdiv(M, kPjRows / 2) > cdiv(M, kPjRows);
-    const dim3 grid(a.H, cdiv(M, half ? kPjRows / 2 : kPjRows));
+    int rpb = kPjRows;
+    if (proj && static_cast<int64_t>(a.H) * cdiv(M, kPjRows) < kPjTargetWgs) {
+      rpb = 4;
+      for (int r = kPjRows; r > 4; r /= 2)
+        if (static_cast<int64_t>(a.H) * cdiv(M, r) >= kPjTargetWgs || cdiv(M, r) == cdiv(M, 4)) {
+          rpb = r;
+          break;
+        }
+    }
+    const dim3 grid(a.H, cdiv(M, rpb));
     const bool fits32 = a.plan != nullptr ||
                         static_cast<uint64_t>(a.n_split) * a.n_rows * a.part_w * 2 < (1ull << 32);
     if (fits32 && proj && a.part_w == 512 && dv == kPjDv) {
       const uint16_t* wp = static_cast<const uint16_t*>(w_uv);
       uint16_t* op = static_cast<uint16_t*>(out);
-      if (a.plan != nullptr && half)
-        hipLaunchKernelGGL((merge_project_kernel<512, true, true, kPjRows / 2>), grid,
-                           dim3(kPjThreads), 0, s, a, redo, wp, op, lse);
-      else if (a.plan != nullptr)
-        hipLaunchKernelGGL((merge_project_kernel<512, true, true, kPjRows>), grid,
-                           dim3(kPjThreads), 0, s, a, redo, wp, op, lse);
-      else if (half)
-        hipLaunchKernelGGL((merge_project_kernel<512, true, false, kPjRows / 2>), grid,
-                           dim3(kPjThreads), 0, s, a, redo, wp, op, lse);
-      else
-        hipLaunchKernelGGL((merge_project_kernel<512, true, false, kPjRows>), grid,
-                           dim3(kPjThreads), 0, s, a, redo, wp, op, lse);
+#define MLA_MERGE(PLAN_, RPB_)                                                                 \
+  hipLaunchKernelGGL((merge_project_kernel<512, true, PLAN_, RPB_>), grid, dim3(kPjThreads), 0, \
+                     s, a, redo, wp, op, lse)
+      const bool plan = a.plan != nullptr;
+      switch (rpb) {
+        case 4: if (plan) MLA_MERGE(true, 4); else MLA_MERGE(false, 4); break;
+        case 8: if (plan) MLA_MERGE(true, 8); else MLA_MERGE(false, 8); break;
+        case 16: if (plan) MLA_MERGE(true, 16); else MLA_MERGE(false, 16); break;
+        default: if (plan) MLA_MERGE(true, kPjRows); else MLA_MERGE(false, kPjRows); break;
+      }
+#undef MLA_MERGE
       return hipGetLastError();
     }
     if (fits32 && a.plan == nullptr && !proj && redo == nullptr && a.part_w == kPjDv &&
