@@ -8,11 +8,11 @@
 // (GQLA summary, section 1), so the kernel is organised around reading each cache row from
 // HBM exactly once and sharing it across all H heads:
 //
-//  * one workgroup per (split, query, sequence) of NW waves, H/32 blocks of 32 heads: with
-//    H = 64 or 128, NW = H/32 and wave w owns heads [32w, 32w+32) for the scores; with H = 32
-//    four waves each compute the one block's scores (an eighth of the tile's products each,
-//    against a quarter of the chip's matrix cores idle with a single wave). Wave w owns
-//    latent columns [512w/NW, 512(w+1)/NW) of all heads for the output;
+//  * one workgroup per (split, query, sequence) of NW = 4 waves and H/32 blocks of 32 heads;
+//    wave w forms the scores of block w % (H/32), so at H = 32 and 64 each block's scores are
+//    formed by 128/H waves alike (fewer waves than SIMDs would leave matrix cores idle while
+//    one wave works through a tile). Wave w owns latent columns [128w, 128w+128) of all heads
+//    for the output;
 //  * 32-position tiles (36,864 B, always inside one cache block) stream HBM -> LDS with
 //    global_load_lds_dwordx4 into a 4-slot ring, two tiles in flight; 16-byte
 //    chunks are XOR-swizzled by position so every LDS read pattern below is free of bank
@@ -24,7 +24,7 @@
 //    which the merge kernel then recomputes exactly;
 //  * P (bf16) leaves each wave in the register layout the P · V product consumes as its A
 //    operand (the position order inside a K-step is permuted identically on both operands)
-//    and is exchanged through LDS (with H = 32 every wave holds the whole P itself);
+//    and is exchanged through LDS (at H = 32 every wave holds the whole P itself);
 //    O[H x 512/NW] += P · V with V read by transposing LDS reads from the same tile;
 //  * the loop body is scheduled by hand: the scores of tile t+1 run with their LDS reads
 //    several steps ahead, then P · V of tile t runs with the softmax of tile t+1 spread
@@ -104,8 +104,9 @@ __device__ __forceinline__ void mfma_o(f32x16& o, const bf16x8& a, const bf16x8&
   asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
 }
 
-// Waves of a workgroup with HB blocks of 32 heads: one per block, or four for one block.
-__host__ __device__ constexpr int waves_of(int hb) { return hb == 1 ? 4 : hb; }
+// Waves of a workgroup with HB blocks of 32 heads: always four (with fewer than four blocks,
+// wave w takes block w % HB for the scores, each block's scores formed by 4 / HB waves).
+__host__ __device__ constexpr int waves_of(int) { return 4; }
 
 template <int HB>
 struct Shared {
@@ -141,7 +142,8 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
                         float* __restrict__ part_lse, int* __restrict__ redo, int batch,
                         SplitPlan* __restrict__ plan_out) {
   constexpr int NW = waves_of(HB);                  // waves
-  constexpr bool kDup = NW > HB;                    // every wave computes the one block's scores
+  constexpr bool kDup = NW > HB;                    // several waves form each block's scores
+  constexpr bool kRegP = HB == 1;                   // P stays in registers (one head block)
   constexpr int H = HB * 32;
   constexpr int kDB = 16 / NW;                      // 32-column latent blocks per wave
   constexpr int kPV = 2 * kDB * HB;                 // P · V products per tile per wave
@@ -317,7 +319,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   }
 
   const int l32 = lane & 31, hi = lane >> 5;
-  const int hbw = kDup ? 0 : w;  // the wave's head block for the scores
+  const int hbw = w % HB;  // the wave's head block for the scores
 
   // Absorbed queries of this wave's 32 heads as MFMA B operands, in registers for the whole
   // split: lane -> head 32w + l32, K-step ks covers row elements [16 ks + 8 hi, +8). Loaded
@@ -357,7 +359,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       }
   }
 
-  constexpr int kNO = HB * kDB;  // O accumulators per wave (16, or 4 with H = 32)
+  constexpr int kNO = HB * kDB;  // O accumulators per wave (16; 8 at H = 64, 4 at H = 32)
   f32x16 o[kNO];
 #pragma unroll
   for (int j = 0; j < kNO; ++j)
@@ -549,12 +551,12 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       for (int e = 0; e < 4; ++e) s.pf[r >> 3][(r & 7) + e] = static_cast<__bf16>(sc[r + e]);
     } else {
       l_part += s.psum;
-      if constexpr (kDup) {
+      if constexpr (kRegP) {
         p_next[0] = s.pf[0];
         p_next[1] = s.pf[1];
-      } else {
-        sh.p[par][w][0][lane] = s.pf[0];
-        sh.p[par][w][1][lane] = s.pf[1];
+      } else if (!kDup || w < HB) {  // one of the waves that formed the block's P
+        sh.p[par][hbw][0][lane] = s.pf[0];
+        sh.p[par][hbw][1][lane] = s.pf[1];
       }
     }
   };
@@ -590,7 +592,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       dst[0] = lds_read_tr(vp + vt[ndb & 1][0]);
       dst[1] = lds_read_tr(vp + vt[ndb & 1][1]);
     };
-    if constexpr (kDup) {
+    if constexpr (kRegP) {
       pa[0][0] = p_cur[0];
       pa[1][0] = p_cur[1];
     } else {
@@ -606,7 +608,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       const int step = i / HB;
       const int buf = step % (kVPre + 1);
       if (hb == 0 && step + kVPre < 2 * kDB) read_v(step + kVPre, va[(step + kVPre) % (kVPre + 1)]);
-      if (!kDup && i == kPV / 4) {
+      if (!kRegP && i == kPV / 4) {
 #pragma unroll
         for (int h2 = 0; h2 < HB; ++h2) pa[1][h2] = sh.p[par][h2][1][lane];
       }
@@ -667,7 +669,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       __syncthreads();
     }
     softmax_all(scores(ring[0], nullptr, 0u, nullptr), nv0, 0);
-    if constexpr (kDup) {
+    if constexpr (kRegP) {
       p_cur[0] = p_next[0];
       p_cur[1] = p_next[1];
     }
@@ -718,7 +720,7 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     f32x16 sc = scores(ring[nslot], src3, dlds, ssrc3);
     if (nv_next < kTileTok) mask_tail(sc, nv_next);
     pv(ring[slot], t & 1, sc, (t + 1) & 1);
-    if constexpr (kDup) {
+    if constexpr (kRegP) {
       p_cur[0] = p_next[0];
       p_cur[1] = p_next[1];
     }
@@ -737,15 +739,19 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
                  : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
                    "+a"(o[6]), "+a"(o[7]), "+a"(o[8]), "+a"(o[9]), "+a"(o[10]), "+a"(o[11]),
                    "+a"(o[12]), "+a"(o[13]), "+a"(o[14]), "+a"(o[15]));
+  else if constexpr (kNO == 8)
+    asm volatile("s_nop 15\n\ts_nop 15"
+                 : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]), "+a"(o[4]), "+a"(o[5]),
+                   "+a"(o[6]), "+a"(o[7]));
   else
     asm volatile("s_nop 15\n\ts_nop 15" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
-  static_assert(kNO == 16 || kNO == 4, "the wait above names every accumulator");
+  static_assert(kNO == 16 || kNO == 8 || kNO == 4, "the wait above names every accumulator");
   const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
   const bool wover = __builtin_amdgcn_ballot_w64(over) != 0;
   Tail<HB>& tl = *reinterpret_cast<Tail<HB>*>(ring[0]);
   __syncthreads();  // every wave is done with the ring
   if (lane == 0) tl.over[w] = wover ? 1 : 0;
-  if (lane < 32 && (!kDup || w == 0)) {  // (with H = 32 every wave holds the same l)
+  if (lane < 32 && w < HB) {  // (waves w and w + HB hold the same l)
     const int h = 32 * hbw + lane;
     tl.inv_l[h] = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     part_lse[prow0 + h] = l_tot > 0.f ? m_ref + log2f(l_tot) : -INFINITY;

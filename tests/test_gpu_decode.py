@@ -242,3 +242,19 @@ def test_planned_matches_uniform_and_falls_back_past_128_rows():
     out, _, _ = run_decode(c2, planned=True)
     ref, _ = oracle_decode(c2, seqs=[0, 64, 129], heads=[0, 127])
     check_per_seq(pick(out, [0, 64, 129], [0, 127]), ref, TOL["bf16"])
+
+
+@pytest.mark.parametrize("generic", [False, True], ids=["mfma", "portable"])
+@pytest.mark.parametrize("lens,s_q,n_split", [([1, 65, 1000], 1, 0), ([700, 2049, 33], 2, 7)],
+                         ids=["planned", "sq2-split7"])
+def test_decode_h64_matches_oracle(lens, s_q, n_split, generic):
+    """H = 64 (two blocks of 32 heads, each block's scores formed by two of the four waves)."""
+    w = W.WORKLOADS["mid-bf16"].replace(n_heads=64, n_groups=64)
+    c = decode_case(w, lens, s_q=s_q, extra=stream_tag(w) + 3)
+    note(f"decode h64 generic={generic} lens={lens} s_q={s_q} n_split={n_split}")
+    out, lse, flags = run_decode(c, n_split=n_split, generic=generic)
+    ref, ref_lse = oracle_decode(c)
+    check_per_seq(out, ref, TOL[w.dtype])
+    check_lse(lse.double().numpy(), ref_lse, TOL[w.dtype])
+    if not generic:
+        assert not flags.any(), "MFMA kernel fell back to the portable kernel"
