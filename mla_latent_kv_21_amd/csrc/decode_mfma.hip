@@ -112,6 +112,11 @@ template <int HB>
 struct Shared {
   bf16x8 p[2][HB][2][64];         // P fragments: [parity][head block][K-step][lane]
 };
+// H = 32: the four waves' partial scores of one tile, [wave][register quad][lane]
+template <>
+struct Shared<1> {
+  float4 s[4][4][64];
+};
 // After the loop the ring is free and holds the per-head 1/l and the waves' flags.
 template <int HB>
 struct Tail {
@@ -144,6 +149,10 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   constexpr int NW = waves_of(HB);                  // waves
   constexpr bool kDup = NW > HB;                    // several waves form each block's scores
   constexpr bool kRegP = HB == 1;                   // P stays in registers (one head block)
+  // H = 32: the score contraction is split over the four waves (a quarter of the 576-wide
+  // rows each, 9 K-steps), the partial scores added through LDS in wave order
+  constexpr bool kKS = HB == 1;
+  constexpr int kQS = kKS ? kKSteps / NW : kKSteps;  // K-steps of the wave's score products
   constexpr int H = HB * 32;
   constexpr int kDB = 16 / NW;                      // 32-column latent blocks per wave
   constexpr int kPV = 2 * kDB * HB;                 // P · V products per tile per wave
@@ -324,7 +333,8 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   // Absorbed queries of this wave's 32 heads as MFMA B operands, in registers for the whole
   // split: lane -> head 32w + l32, K-step ks covers row elements [16 ks + 8 hi, +8). Loaded
   // after the first tile's copies are issued.
-  bf16x8 qf[kKSteps];
+  bf16x8 qf[kQS];
+  const int ks0 = kKS ? kQS * w : 0;  // the wave's first score K-step
 
   // Per-lane byte offsets; the rest of every swizzled address is a compile-time constant.
   //  copies: LDS chunk p = (j NW + w) 64 + lane of a slot holds row p / 72, physical chunk
@@ -480,33 +490,70 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
   // ---- scores S^T[position][head] of one tile over the 576-wide rows, each fragment read
   // kPre products ahead of its MFMA.
   constexpr int kCopies = kFp8 ? kDma8 : kDma;
+  // H = 32: byte offsets of the wave's K-steps in a tile (logical chunk 2 ks + hi of row l32)
+  int koff[kKS ? kQS : 1];
+  if constexpr (kKS) {
+#pragma unroll
+    for (int j = 0; j < kQS; ++j)
+      koff[j] = l32 * kRowBytes + (((2 * (ks0 + j) + hi) ^ swz(l32)) << 4);
+  }
   auto scores = [&](const char* cur, const char* dsrc, unsigned dlds, const char* ssrc)
                     __attribute__((always_inline)) -> f32x16 {
     f32x16 sc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
-    // fewer fragments ahead where the copy offsets take more registers (e4m3 rows)
-    constexpr int kP = kFp8 ? kPreF8 : kPre;
-    bf16x8 af[kP];
+    if constexpr (kKS) {
+      static_assert(kKSteps % NW == 0 && kDma == kQS, "one copy per K-step of the wave");
+      bf16x8 af[kQS];
 #pragma unroll
-    for (int i = 0; i < kP; ++i) af[i] = lds16(cur + qb[i & 3] + 128 * (i >> 2));
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      const bf16x8 acur = af[ks % kP];
-      const int nx = ks + kP;
-      if (nx < kKSteps) af[ks % kP] = lds16(cur + qb[nx & 3] + 128 * (nx >> 2));
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur, qf[ks], sc, 0, 0, 0);
-      // copies spread evenly over the K-steps (kCopies <= kKSteps)
-      if ((ks * kCopies) / kKSteps != ((ks + 1) * kCopies) / kKSteps) {
-        if constexpr (kFp8)
-          issue_part8(dsrc, ssrc, dlds, (ks * kCopies) / kKSteps);
-        else
-          issue_part(dsrc, dlds, (ks * kCopies) / kKSteps);
-      }
+      for (int j = 0; j < kQS; ++j) af[j] = lds16(cur + koff[j]);
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < kQS; ++j) {
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[j], qf[j], sc, 0, 0, 0);
+        issue_part(dsrc, dlds, j);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the partial sums through LDS; every wave adds the four in wave order (the same bits
+      // in every wave). The previous tile's partials were read before the loop's barrier.
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        sh.s[w][k][lane] = make_float4(sc[4 * k], sc[4 * k + 1], sc[4 * k + 2], sc[4 * k + 3]);
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float4 a = sh.s[0][k][lane], b = sh.s[1][k][lane], c = sh.s[2][k][lane],
+                     d = sh.s[3][k][lane];
+        sc[4 * k] = ((a.x + b.x) + c.x) + d.x;
+        sc[4 * k + 1] = ((a.y + b.y) + c.y) + d.y;
+        sc[4 * k + 2] = ((a.z + b.z) + c.z) + d.z;
+        sc[4 * k + 3] = ((a.w + b.w) + c.w) + d.w;
+      }
+      return sc;
+    } else {
+      // fewer fragments ahead where the copy offsets take more registers (e4m3 rows)
+      constexpr int kP = kFp8 ? kPreF8 : kPre;
+      bf16x8 af[kP];
+#pragma unroll
+      for (int i = 0; i < kP; ++i) af[i] = lds16(cur + qb[i & 3] + 128 * (i >> 2));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+        const bf16x8 acur = af[ks % kP];
+        const int nx = ks + kP;
+        if (nx < kKSteps) af[ks % kP] = lds16(cur + qb[nx & 3] + 128 * (nx >> 2));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur, qf[ks], sc, 0, 0, 0);
+        // copies spread evenly over the K-steps (kCopies <= kKSteps)
+        if ((ks * kCopies) / kKSteps != ((ks + 1) * kCopies) / kKSteps) {
+          if constexpr (kFp8)
+            issue_part8(dsrc, ssrc, dlds, (ks * kCopies) / kKSteps);
+          else
+            issue_part(dsrc, dlds, (ks * kCopies) / kKSteps);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      return sc;
     }
-    return sc;
   };
   // ---- softmax numerators of one tile against the head's fixed reference m_ref (log2
   // units): the first finite tile max. A tile exceeding it by more than kHead marks the split
@@ -608,9 +655,11 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       const int step = i / HB;
       const int buf = step % (kVPre + 1);
       if (hb == 0 && step + kVPre < 2 * kDB) read_v(step + kVPre, va[(step + kVPre) % (kVPre + 1)]);
-      if (!kRegP && i == kPV / 4) {
+      if constexpr (!kRegP) {
+        if (i == kPV / 4) {
 #pragma unroll
-        for (int h2 = 0; h2 < HB; ++h2) pa[1][h2] = sh.p[par][h2][1][lane];
+          for (int h2 = 0; h2 < HB; ++h2) pa[1][h2] = sh.p[par][h2][1][lane];
+        }
       }
       const bf16x8 vf = __builtin_bit_cast(
           bf16x8, __builtin_shufflevector(va[buf][0], va[buf][1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -643,7 +692,8 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       const char* qp = reinterpret_cast<const char*>(q_abs) +
                        (row0 + 32 * hbw + l32) * kRowBytes + hi * 16;
 #pragma unroll
-      for (int ks = 0; ks < kKSteps; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+      for (int ks = 0; ks < kQS; ++ks)
+        qf[ks] = *reinterpret_cast<const bf16x8*>(qp + (ks0 + ks) * 32);
     }
     if constexpr (kFp8) {
       for (int i = 1; i < 3; ++i) {
