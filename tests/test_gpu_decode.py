@@ -258,3 +258,21 @@ def test_decode_h64_matches_oracle(lens, s_q, n_split, generic):
     check_lse(lse.double().numpy(), ref_lse, TOL[w.dtype])
     if not generic:
         assert not flags.any(), "MFMA kernel fell back to the portable kernel"
+
+
+@pytest.mark.parametrize("heads", [32, 64])
+def test_small_head_counts_on_ragged_lengths(heads):
+    """H = 32 (the score contraction split over four waves) and H = 64 (two waves per head
+    block) over lengths around the 32-position tile and 64-position block edges, planned and
+    uniform splits, s_q = 1 and 3."""
+    w = W.WORKLOADS["mid-bf16"].replace(n_heads=heads, n_groups=heads)
+    lens = [1, 2, 31, 32, 33, 64, 65, 97, 160, 1000]
+    for s_q, n_split in ((1, 0), (1, 7), (3, 0)):
+        ls = [max(L, s_q) for L in lens]
+        c = decode_case(w, ls, s_q=s_q, extra=stream_tag(w) + 5 + s_q)
+        note(f"decode H={heads} ragged s_q={s_q} n_split={n_split}")
+        out, lse, flags = run_decode(c, n_split=n_split)
+        ref, ref_lse = oracle_decode(c)
+        check_per_seq(out, ref, TOL[w.dtype])
+        check_lse(lse.double().numpy(), ref_lse, TOL[w.dtype])
+        assert not flags.any(), "MFMA kernel fell back to the portable kernel"
