@@ -397,7 +397,10 @@ __global__ __launch_bounds__(kPjThreads) void merge_project_kernel(GenericArgs a
   typedef mfma::f32x16 f32x16;
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   static_assert(!kProj || PW == 512, "the projection takes 512-wide latent rows");
-  constexpr int kPjL = kProj ? 16 : 32;  // partial chunks in flight per thread
+  // partial chunks in flight per thread (with W_UV: 8, as 16 and 32 measured slower)
+  constexpr int kPjL = kProj ? 8 : 32;
+  // a wide batch takes kPjL / S pairs of S <= 8 splits each: at least one, or it never ends
+  static_assert(kPjL >= 8, "a wide batch covers at least one pair");
   __shared__ __attribute__((aligned(16))) char wbuf[kProj ? kPjWHalf : 16384];  // W half; scratch
   __shared__ __attribute__((aligned(16))) char obuf[kProj ? kPjRows * kPjORow : 16];
   __shared__ float wts[kPjRows][MLA_MAX_SPLIT];
