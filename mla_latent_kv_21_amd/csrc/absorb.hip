@@ -65,8 +65,9 @@ __global__ __launch_bounds__(256) void absorb_kernel(const T* __restrict__ q_nop
 }
 
 // One workgroup per absorb tile (absorb_tile.hpp).
+template <int kKS>
 __global__ __launch_bounds__(256) void absorb_mfma(AbsorbArgs q) {
-  absorb_tile_mfma(q, blockIdx.x, blockIdx.y * 32, blockIdx.z, gridDim.z);
+  absorb_tile_mfma<kKS>(q, blockIdx.x, blockIdx.y * 32, blockIdx.z, gridDim.z);
 }
 
 }  // namespace
@@ -97,8 +98,11 @@ hipError_t launch_absorb(const mla_dims& d, int batch, int s_q, const void* q_no
   const int M = batch * s_q;
   if (absorb_mfma_fits(d)) {
     const AbsorbArgs q = absorb_args(d, M, q_nope, q_pe, q_pos, w_uk, q_abs);
-    hipLaunchKernelGGL(absorb_mfma, dim3(d.n_heads, cdiv(M, 32), cdiv(d.d_c / 32, 4)), dim3(256), 0,
-                       s, q);
+    const dim3 grid(d.n_heads, cdiv(M, 32), cdiv(d.d_c / 32, 4));
+    if (d.d_nope <= 128)
+      hipLaunchKernelGGL(absorb_mfma<8>, grid, dim3(256), 0, s, q);
+    else
+      hipLaunchKernelGGL(absorb_mfma<16>, grid, dim3(256), 0, s, q);
     return hipGetLastError();
   }
   const dim3 grid(d.n_heads, cdiv(M, kRows));

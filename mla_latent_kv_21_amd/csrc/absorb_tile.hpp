@@ -44,7 +44,10 @@ typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 // (rows of q_nope and rows of W_UK), so MFMA fragments load straight from memory. Tile
 // (h, 32 rows from m0, column blocks 4 z .. 4 z + 3); wave w computes one 32-column block.
 // The rotary (row, pair) items of the head's 32 rows are shared out over its z tiles.
-// Needs blockDim.x == 256, d_c % 32 == 0, D % 16 == 0, D <= 256.
+// kKS: the most K-steps (D / 16) the tile is built for, 8 (D <= 128) or 16 (D <= 256): the
+// fragments of both operands take 8 kKS registers, so the smaller build keeps more waves
+// resident. Needs blockDim.x == 256, d_c % 32 == 0, D % 16 == 0, D <= 16 kKS.
+template <int kKS>
 __device__ inline void absorb_tile_mfma(const AbsorbArgs& q, int h, int m0, int z, int nz) {
   using namespace absorb_detail;
   const uint16_t* __restrict__ q_nope = q.q_nope;
@@ -58,12 +61,12 @@ __device__ inline void absorb_tile_mfma(const AbsorbArgs& q, int h, int m0, int 
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int row = d_c + d_r;
-  const int ksteps = D / 16;  // at most 16 (D <= 256)
+  const int ksteps = D / 16;  // at most kKS
   const int m = m0 + l32;
-  bf16x8 af[16];
+  bf16x8 af[kKS];
   const bf16x8 zero = {};
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
+  for (int ks = 0; ks < kKS; ++ks) {
     af[ks] = zero;
     if (ks < ksteps && m < M)
       af[ks] = *reinterpret_cast<const bf16x8*>(q_nope + (static_cast<int64_t>(m) * H + h) * D +
@@ -71,11 +74,11 @@ __device__ inline void absorb_tile_mfma(const AbsorbArgs& q, int h, int m0, int 
   }
   const int64_t ldw = static_cast<int64_t>(G) * D;
   // B fragments of one 32-column block: all requested before the first MFMA
-  bf16x8 bv[16];
+  bf16x8 bv[kKS];
   auto load_b = [&](int nb) __attribute__((always_inline)) {
     const uint16_t* wr = w_uk + (nb * 32 + l32) * ldw + static_cast<int64_t>(g) * D + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks)
+    for (int ks = 0; ks < kKS; ++ks)
       bv[ks] = ks < ksteps ? *reinterpret_cast<const bf16x8*>(wr + 16 * ks) : zero;
   };
   int nb = 4 * z + w;
@@ -102,7 +105,7 @@ __device__ inline void absorb_tile_mfma(const AbsorbArgs& q, int h, int m0, int 
     const int j = nb * 32 + l32;
     f32x16 acc = {};
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks)
+    for (int ks = 0; ks < kKS; ++ks)
       if (ks < ksteps) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], bv[ks], acc, 0, 0, 0);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {

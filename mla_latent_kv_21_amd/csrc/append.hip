@@ -349,6 +349,7 @@ __global__ __launch_bounds__(256) void quantize_rows_e4m3(const uint16_t* __rest
 // W_UK for the queries), each too small to fill the chip for long: run as one grid, the
 // absorb tiles fill the CUs the projection leaves idle and the step saves a launch. The
 // append's finalize (sum of the partials in k order, RMSNorm, RoPE, store) follows as before.
+template <int kKS>
 __global__ __launch_bounds__(256) void project_absorb(const uint16_t* __restrict__ x,
                                                       const uint16_t* __restrict__ w_a,
                                                       const uint16_t* __restrict__ w_b,
@@ -362,7 +363,7 @@ __global__ __launch_bounds__(256) void project_absorb(const uint16_t* __restrict
     int t = blockIdx.x - n_proj;
     const int z = t % absorb_zb;
     t /= absorb_zb;
-    absorb_tile_mfma(q, t / absorb_rb, (t % absorb_rb) * 32, z, absorb_zb);
+    absorb_tile_mfma<kKS>(q, t / absorb_rb, (t % absorb_rb) * 32, z, absorb_zb);
     return;
   }
   const int t = blockIdx.x;
@@ -380,6 +381,21 @@ __global__ __launch_bounds__(256) void step_positions(int n_tok, int s_q,
   const int b = n / s_q;
   seq_idx[n] = b;
   pos[n] = seq_lens[b] - s_q + (n - b * s_q);
+}
+
+// project_absorb built for the absorbed queries' K-steps: 8 (D <= 128) or 16.
+void launch_project_absorb(const mla_dims& d, dim3 grid, hipStream_t s, const void* x,
+                           const void* w_dkv, const void* w_kr, int n, float* y_part,
+                           const AppendPlan& p, const AbsorbArgs& q, int rb, int zb) {
+  const auto* xp = static_cast<const uint16_t*>(x);
+  const auto* wa = static_cast<const uint16_t*>(w_dkv);
+  const auto* wb = static_cast<const uint16_t*>(w_kr);
+  if (d.d_nope <= 128)
+    hipLaunchKernelGGL(project_absorb<8>, grid, dim3(256), 0, s, xp, wa, wb, n, d.d_model, d.d_c,
+                       d.d_r, y_part, p.col_blocks, p.n_ksplit, q, rb, zb);
+  else
+    hipLaunchKernelGGL(project_absorb<16>, grid, dim3(256), 0, s, xp, wa, wb, n, d.d_model,
+                       d.d_c, d.d_r, y_part, p.col_blocks, p.n_ksplit, q, rb, zb);
 }
 
 }  // namespace
@@ -404,10 +420,7 @@ hipError_t launch_step_project(const mla_dims& d, int batch, int s_q, const void
   int rb = 1, zb = 1;
   const int tiles = absorb_tiles(q, &rb, &zb);
   const int proj = p.col_blocks * p.n_ksplit * cdiv(n, 32);
-  hipLaunchKernelGGL(project_absorb, dim3(proj + tiles), dim3(256), 0, s,
-                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_dkv),
-                     static_cast<const uint16_t*>(w_kr), n, d.d_model, d.d_c, d.d_r, y_part,
-                     p.col_blocks, p.n_ksplit, q, rb, zb);
+  launch_project_absorb(d, dim3(proj + tiles), s, x, w_dkv, w_kr, n, y_part, p, q, rb, zb);
   return hipGetLastError();
 }
 
@@ -515,10 +528,7 @@ hipError_t launch_append_absorb(const mla_dims& d, int n_tok, const void* x,
         int rb = 1, zb = 1;
         const int tiles = absorb_tiles(q, &rb, &zb);
         const int proj = p.col_blocks * p.n_ksplit * cdiv(n, 32);
-        hipLaunchKernelGGL(project_absorb, dim3(proj + tiles), dim3(256), 0, s,
-                           static_cast<const uint16_t*>(xc), static_cast<const uint16_t*>(w_dkv),
-                           static_cast<const uint16_t*>(w_kr), n, d.d_model, d.d_c, d.d_r, y_part,
-                           p.col_blocks, p.n_ksplit, q, rb, zb);
+        launch_project_absorb(d, dim3(proj + tiles), s, xc, w_dkv, w_kr, n, y_part, p, q, rb, zb);
         absorb_pending = false;
       } else if (mfma_ok) {
         hipLaunchKernelGGL(append_project_mfma, dim3(p.col_blocks, p.n_ksplit, cdiv(n, 32)),
