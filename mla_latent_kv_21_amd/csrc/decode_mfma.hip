@@ -8,11 +8,11 @@
 // (GQLA summary, section 1), so the kernel is organised around reading each cache row from
 // HBM exactly once and sharing it across all H heads:
 //
-//  * one workgroup per (split, query, sequence) of NW = 4 waves and H/32 blocks of 32 heads;
-//    wave w forms the scores of block w % (H/32), so at H = 32 and 64 each block's scores are
-//    formed by 128/H waves alike (fewer waves than SIMDs would leave matrix cores idle while
-//    one wave works through a tile). Wave w owns latent columns [128w, 128w+128) of all heads
-//    for the output;
+//  * one workgroup per (split, query, sequence) of NW = 4 waves and H/32 blocks of 32 heads
+//    (fewer waves than SIMDs would leave matrix cores idle while one wave works through a
+//    tile): wave w forms the scores of block w % (H/32), at H = 64 two waves alike; at H = 32
+//    the four waves split the block's score contraction and add their partial sums through
+//    LDS. Wave w owns latent columns [128w, 128w+128) of all heads for the output;
 //  * 32-position tiles (36,864 B, always inside one cache block) stream HBM -> LDS with
 //    global_load_lds_dwordx4 into a 4-slot ring, two tiles in flight; 16-byte
 //    chunks are XOR-swizzled by position so every LDS read pattern below is free of bank
