@@ -276,3 +276,20 @@ def test_small_head_counts_on_ragged_lengths(heads):
         check_per_seq(out, ref, TOL[w.dtype])
         check_lse(lse.double().numpy(), ref_lse, TOL[w.dtype])
         assert not flags.any(), "MFMA kernel fell back to the portable kernel"
+
+
+@pytest.mark.parametrize("bs", [32, 128])
+@pytest.mark.parametrize("wl", ["dsv3-paged", "mid-bf16"])
+def test_block_sizes_and_long_splits(wl, bs):
+    """Cache blocks of 32 and 128 positions, with single-split sequences long enough (5,000
+    positions: 157 blocks of 32) that a workgroup walks past its first 64 block ids and reloads
+    them, and planned splits; H = 128 and H = 32."""
+    w = W.WORKLOADS[wl].replace(block_size=bs)
+    c = decode_case(w, [5000, 2100, 33], extra=stream_tag(w) + bs)
+    ref, ref_lse = oracle_decode(c)
+    for n_split in (1, 0):
+        note(f"decode {wl} block_size={bs} n_split={n_split}")
+        out, lse, flags = run_decode(c, n_split=n_split)
+        check_per_seq(out, ref, TOL[w.dtype])
+        check_lse(lse.double().numpy(), ref_lse, TOL[w.dtype])
+        assert not flags.any(), "MFMA kernel fell back to the portable kernel"

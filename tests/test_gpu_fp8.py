@@ -234,12 +234,16 @@ CASES = [
     ("many-splits", "long-128k", [4096, 100], 1, 64),
     ("gqla-sq2", "gqla-g8", [2, 300], 2, 0),
     ("gqla-sq4-split5", "gqla-g8", [4, 257, 1030], 4, 5),
+    # 32-position blocks, one split per sequence: a workgroup walks past 64 block ids
+    ("bs32-one-split", "dsv3-paged@32", [5000, 33], 1, 1),
+    ("bs128-planned", "dsv3-paged@128", [5000, 2100, 33], 1, 0),
 ]
 
 
 @pytest.mark.parametrize("name,wl,lens,s_q,n_split", CASES, ids=[c[0] for c in CASES])
 def test_fp8_decode_is_bf16_decode_of_the_dequantised_cache(name, wl, lens, s_q, n_split):
-    w = W.WORKLOADS[wl]
+    base, _, bs = wl.partition("@")  # "workload@block_size" overrides the block size
+    w = W.WORKLOADS[base] if not bs else W.WORKLOADS[base].replace(block_size=int(bs))
     c = fp8_case(w, lens, s_q=s_q, extra=w.seed % 100)
     note(f"fp8 decode {name} lens={lens} s_q={s_q} n_split={n_split}")
     out8, lse8 = run(c, True, n_split=n_split, planned=n_split == 0)
