@@ -293,3 +293,17 @@ def test_block_sizes_and_long_splits(wl, bs):
         check_per_seq(out, ref, TOL[w.dtype])
         check_lse(lse.double().numpy(), ref_lse, TOL[w.dtype])
         assert not flags.any(), "MFMA kernel fell back to the portable kernel"
+
+
+@pytest.mark.parametrize("wl", ["dsv3-paged", "mid-bf16"])
+def test_the_largest_split_count(wl):
+    """n_split = 256 (the most the library takes): 20,000 positions in 64-position splits
+    beside a 70-position sequence whose splits are nearly all empty (weight zero)."""
+    w = W.WORKLOADS[wl]
+    c = decode_case(w, [20000, 70], extra=stream_tag(w) + 256)
+    note(f"decode {wl} n_split=256")
+    out, lse, flags = run_decode(c, n_split=256)
+    ref, ref_lse = oracle_decode(c)
+    check_per_seq(out, ref, TOL[w.dtype])
+    check_lse(lse.double().numpy(), ref_lse, TOL[w.dtype])
+    assert not flags.any(), "MFMA kernel fell back to the portable kernel"
