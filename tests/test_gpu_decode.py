@@ -307,3 +307,20 @@ def test_the_largest_split_count(wl):
     check_per_seq(out, ref, TOL[w.dtype])
     check_lse(lse.double().numpy(), ref_lse, TOL[w.dtype])
     assert not flags.any(), "MFMA kernel fell back to the portable kernel"
+
+
+@pytest.mark.parametrize("generic", [False, True], ids=["mfma", "portable"])
+@pytest.mark.parametrize("n_split", [0, 3])
+def test_queries_with_nothing_visible(n_split, generic):
+    """A sequence of length 0 (its query sees no position) gets out = 0 and lse = -inf, as the
+    header states, beside an ordinary sequence, on either split layout."""
+    w = W.WORKLOADS["dsv3-paged"]
+    c = decode_case(w, [0, 300, 0], extra=stream_tag(w) + 40)
+    note(f"decode nothing visible n_split={n_split} generic={generic}")
+    out, lse, _ = run_decode(c, n_split=n_split, generic=generic)
+    for b in (0, 2):
+        assert torch.equal(out[b].float(), torch.zeros_like(out[b].float())), f"sequence {b}"
+        assert bool(torch.isinf(lse[b]).all()) and bool((lse[b] < 0).all())
+    ref, ref_lse = oracle_decode(c, seqs=[1])
+    check_per_seq(out[1:2], ref, TOL[w.dtype])
+    check_lse(lse[1:2].double().numpy(), ref_lse, TOL[w.dtype])
