@@ -236,6 +236,7 @@ void expand_mfma(const uint16_t* __restrict__ latent, int num_blocks,
   // last chunks reload themselves)
   auto chunk = [&](int kk, u32x4_t (&ra_)[2], u32x4_t (&rw_)[4]) __attribute__((always_inline)) {
     char* cur = lds + ((kk / kXK) & 1) * kXBuf;
+    __builtin_amdgcn_sched_barrier(0);
     store_chunk(cur, ra_, rw_);
     __syncthreads();
     load_chunk(kk + 2 * kXK < d_c ? kk + 2 * kXK : kk, ra_, rw_);
@@ -251,12 +252,19 @@ void expand_mfma(const uint16_t* __restrict__ latent, int num_blocks,
           acc[2 * cm + pn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ks][cm], cf[ks][pn],
                                                                       acc[2 * cm + pn], 0, 0, 0);
   };
+  // The loop body has no branch: the compiler then knows at every store which loads are still
+  // in flight and waits only for the older register set (with a conditional second chunk in
+  // the body its waits at the loop head drained both sets, every other chunk). The barrier at
+  // the head of each chunk keeps one chunk's stores, and their waits, from being hoisted into
+  // the chunk before.
   load_chunk(0, ra[0], rw[0]);
   load_chunk(kXK < d_c ? kXK : 0, ra[1], rw[1]);
-  for (int kk = 0; kk < d_c; kk += 2 * kXK) {
+  int kk = 0;
+  for (; kk + 2 * kXK <= d_c; kk += 2 * kXK) {
     chunk(kk, ra[0], rw[0]);
-    if (kk + kXK < d_c) chunk(kk + kXK, ra[1], rw[1]);
+    chunk(kk + kXK, ra[1], rw[1]);
   }
+  if (kk < d_c) chunk(kk, ra[0], rw[0]);
 
   // outputs through LDS, 32 positions of each wave at a time, as whole 256-byte row pieces
   __syncthreads();  // every wave is done with the chunk buffers

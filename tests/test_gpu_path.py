@@ -292,18 +292,20 @@ def test_gqla_expand_matches_oracle():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_gqla_expand_ragged_shapes(dtype):
+@pytest.mark.parametrize("d_c", [128, 160])
+def test_gqla_expand_ragged_shapes(dtype, d_c):
     """Expansion where the expanded width (3 groups x (24 + 16) = 120 columns) fills part of
-    a column tile, d_c = 128 spans two latent chunks, and the lengths leave ragged position
-    tiles (1, 255, 257 and 600 positions, block size 16); bf16 runs on the matrix cores, fp32 on
-    the portable kernel."""
-    w = W.WORKLOADS["gqla-g8"].replace(n_groups=3, n_heads=6, d_nope=24, d_v=16, d_c=128, d_r=16,
+    a column tile, d_c = 128 spans four 32-row latent chunks and d_c = 160 an odd number (five,
+    the last after the two-chunk loop), and the lengths leave ragged position tiles (1, 255,
+    257 and 600 positions, block size 16); bf16 runs on the matrix cores, fp32 on the portable
+    kernel."""
+    w = W.WORKLOADS["gqla-g8"].replace(n_groups=3, n_heads=6, d_nope=24, d_v=16, d_c=d_c, d_r=16,
                              block_size=16, dtype=dtype)
     c = decode_case(w, [1, 255, 257, 600], extra=23)
     wts = W.weights(c["w"])
     d = M.dims_of(c["w"])
     g = gqa_cache_empty(w, c["nb"])
-    note(f"gqla_expand ragged shapes {dtype}")
+    note(f"gqla_expand ragged shapes {dtype} d_c {d_c}")
     M.gqla_expand(d, dev(c["pool"]), dev(c["table"]), dev(c["lens"]), dev(wts["w_uk"]),
                   dev(wts["w_uv"]), g)
     torch.cuda.synchronize()
