@@ -254,9 +254,9 @@ void expand_mfma(const uint16_t* __restrict__ latent, int num_blocks,
   };
   // The loop body has no branch: the compiler then knows at every store which loads are still
   // in flight and waits only for the older register set (with a conditional second chunk in
-  // the body its waits at the loop head drained both sets, every other chunk). The barrier at
-  // the head of each chunk keeps one chunk's stores, and their waits, from being hoisted into
-  // the chunk before.
+  // the body its waits at the loop head drained both sets, every other chunk). The scheduling
+  // barrier at the head of each chunk keeps one chunk's stores, and their waits, from being
+  // hoisted into the chunk before.
   load_chunk(0, ra[0], rw[0]);
   load_chunk(kXK < d_c ? kXK : 0, ra[1], rw[1]);
   int kk = 0;
