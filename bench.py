@@ -293,19 +293,7 @@ def measure_rows(dev, torch):
     rows["absorbed_gqla_g8"], ctx = absorbed_row(dev, torch, w)
     lens, table, nb, tab, lens_d, wts = ctx
     d = M.dims_of(w)
-    cache = W.cache_pool_device(w, nb, dev)
-    gqa = torch.empty(nb, w.block_size, w.n_groups * (w.d_nope + w.d_v) + w.d_r,
-                      dtype=w.torch_dtype, device=dev)
-    ms = _time_calls(lambda i: M.gqla_expand(d, cache, tab, lens_d, wts["w_uk"], wts["w_uv"], gqa),
-                     5, torch)
-    L = int(np.sum(lens))
-    eb = L * (A.latent_row_bytes(w.d_c, w.d_r, w.elt) + A.gqa_row_bytes(w.n_groups, w.d_nope,
-                                                                        w.d_r, w.elt))
-    ef = L * 2 * w.d_c * w.n_groups * (w.d_nope + w.d_v)
-    rows["gqla_expand"] = {"workload": w.name, "call": "gqla_expand", "ms": ms,
-                           "positions_per_s": L / (ms * 1e-3), "GBps": eb / (ms * 1e-3) / 1e9,
-                           "TFLOPs": ef / (ms * 1e-3) / 1e12}
-    rows["gqla_expand"].update(A.binding_roofline(eb, ef, ms))
+    rows["gqla_expand"], cache, gqa = expand_row(dev, torch, w, ctx)
     g = lambda a: (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
     q = {k: g(v) for k, v in W.queries(w).items()}
     qpos = g(W.query_positions(w, lens))
@@ -324,6 +312,39 @@ def measure_rows(dev, torch):
     del cache, gqa
     rows["prefill"] = measure_prefill(dev, torch)
     return rows
+
+
+def expand_row(dev, torch, w, ctx=None, reps=5):
+    """gqla_expand of every cached position of workload w into the expanded GQA cache, timed
+    with HIP events over reps calls, priced in bytes (latent rows read, expanded rows written)
+    and FLOPs (2 d_c G (D + D_v) per position) against the binding roofline. ctx: the
+    workload's (lens, table, nb, tab, lens_d, wts) when the caller already has them on the
+    device. Returns the row, the latent cache and the expanded cache."""
+    import workloads as W
+    from mla_latent_kv_21_amd import accounting as A
+    from mla_latent_kv_21_amd import binding as M
+    if ctx is None:
+        g = lambda a: (a if isinstance(a, torch.Tensor)
+                       else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
+        lens = W.seq_lens(w)
+        table, nb = W.block_table(w, lens)
+        ctx = (lens, table, nb, g(table), g(lens), {k: g(v) for k, v in W.weights(w).items()})
+    lens, table, nb, tab, lens_d, wts = ctx
+    d = M.dims_of(w)
+    cache = W.cache_pool_device(w, nb, dev)
+    gqa = torch.empty(nb, w.block_size, w.n_groups * (w.d_nope + w.d_v) + w.d_r,
+                      dtype=w.torch_dtype, device=dev)
+    ms = _time_calls(lambda i: M.gqla_expand(d, cache, tab, lens_d, wts["w_uk"], wts["w_uv"], gqa),
+                     reps, torch)
+    L = int(np.sum(lens))
+    eb = L * (A.latent_row_bytes(w.d_c, w.d_r, w.elt) + A.gqa_row_bytes(w.n_groups, w.d_nope,
+                                                                        w.d_r, w.elt))
+    ef = L * 2 * w.d_c * w.n_groups * (w.d_nope + w.d_v)
+    row = {"workload": w.name, "call": "gqla_expand", "ms": ms,
+           "positions_per_s": L / (ms * 1e-3), "GBps": eb / (ms * 1e-3) / 1e9,
+           "TFLOPs": ef / (ms * 1e-3) / 1e12}
+    row.update(A.binding_roofline(eb, ef, ms))
+    return row, cache, gqa
 
 
 def measure_prefill(dev, torch):
@@ -524,9 +545,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip timing the path's other rows on their own workloads")
-    ap.add_argument("--rows", choices=("all", "layer", "prefill", "none"), default="all",
+    ap.add_argument("--rows", choices=("all", "layer", "prefill", "expand", "none"),
+                    default="all",
                     help="rows timed after the step: all of them, only the decode layer, only "
-                         "the prefill, or none")
+                         "the prefill, only the GQA expansion (gqla-g8), or none")
     ap.add_argument("--power-seconds", type=float, default=2.0,
                     help="run the split-K core back to back for this long while sampling board "
                          "power and shader clock with amd-smi (0: skip)")
@@ -662,6 +684,8 @@ def main():
             rec["rows"].update(measure_rows(dev, torch))
         if rows == "prefill":
             rec["rows"]["prefill"] = measure_prefill(dev, torch)
+        elif rows == "expand":
+            rec["rows"]["gqla_expand"], _, _ = expand_row(dev, torch, W.WORKLOADS["gqla-g8"])
         else:
             rec["rows"]["decode_layer"] = measure_layer(w, d, step, x_new, dev, torch)
     if args.copy_calibration_mib > 0:

@@ -266,7 +266,9 @@ void expand_mfma(const uint16_t* __restrict__ latent, int num_blocks,
   }
   if (kk < d_c) chunk(kk, ra[0], rw[0]);
 
-  // outputs through LDS, 32 positions of each wave at a time, as whole 256-byte row pieces
+  // outputs through LDS, 32 positions of each wave at a time, as whole 256-byte row pieces;
+  // streaming (non-temporal) stores, so that the 4.4 GB of expanded rows do not push out of
+  // L2 the latent rows and W that the position tile's other column tiles still read
   __syncthreads();  // every wave is done with the chunk buffers
   {
     char* stage = lds + w * 32 * kXORow;
@@ -289,7 +291,7 @@ void expand_mfma(const uint16_t* __restrict__ latent, int num_blocks,
           const int row = 4 * i + (lane >> 4);
           const int64_t sl = slot_of[64 * wp + 32 * pn + row];
           const u32x4_t v = *reinterpret_cast<const u32x4_t*>(stage + row * kXORow + 16 * seg);
-          if (sl >= 0) *reinterpret_cast<u32x4_t*>(gqa + sl * gw + col) = v;
+          if (sl >= 0) __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(gqa + sl * gw + col));
         }
       }
     }
