@@ -452,13 +452,14 @@ mla_status mla_output_project(const mla_dims* dims, int32_t n_tok, const void* o
  *  rates that are not both positive (or both 0). Host only: launches nothing.
  */
 typedef enum { MLA_PATH_ABSORBED = 0, MLA_PATH_GQA = 1 } mla_path;
-/* MI355X rates used by default, as measured: a stream read by 256 workgroups reaches
- * 6.0e12 B/s; the absorbed split-K decode sustains 1.0e15 bf16 FLOP/s (146 GFLOP in about
- * 0.15 ms on 4 x 131,072 positions at H = 128). The chip's dense bf16 peak is 2.5e15, but
- * under a sustained matrix-core load it holds about 1.75e15 (the clock falls to ~1.7 GHz),
- * and the decode's matrix cores are busy about half of its launch. */
-#define MLA_MI355X_HBM_BYTES_PER_S 6.0e12
-#define MLA_MI355X_BF16_FLOPS 1.0e15
+/* MI355X rates used by default, as measured: the GQA decode streams its expanded cache at
+ * 6.8e12 B/s (4.43 GB in 0.65 ms at G = 8, 32 x 32,768 positions); the absorbed split-K
+ * decode sustains 0.87e15 bf16 FLOP/s at s_q = 2 on the same workload (584 GFLOP in
+ * 0.67 ms; 0.86-0.96e15 over s_q = 1..8). The chip's dense bf16 peak is 2.5e15, but under a
+ * sustained matrix-core load it holds about 1.3-1.4e15 (the clock falls below 2 GHz), and
+ * the decode's matrix cores are busy about half of its launch. */
+#define MLA_MI355X_HBM_BYTES_PER_S 6.8e12
+#define MLA_MI355X_BF16_FLOPS 0.87e15
 int32_t mla_select_path(const mla_dims* dims, int32_t s_q, int64_t context,
                         double hbm_bytes_per_s, double flops_per_s, double* t_absorbed,
                         double* t_gqa);

@@ -416,15 +416,18 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     const int jb = pos0 / bs;
     return tile_src_at(pos0, jb, pos0 - jb * bs, nvalid);
   };
+  // Every cache tile is copied once, by one workgroup. At H = 128 the copies carry the
+  // non-temporal hint (measured faster there: the long-128k step by ≈ 3 %); with fewer head
+  // blocks they keep the default policy, which measured as fast or faster.
   auto issue_tile = [&](const char* src, char* slot) __attribute__((always_inline)) {
     const unsigned lbase = lds_addr(slot) + w * 64 * 16;
 #pragma unroll
-    for (int j = 0; j < kDma; ++j) dma16(src, doff[j], lbase + j * NW * 64 * 16);
+    for (int j = 0; j < kDma; ++j) dma16<HB == 4>(src, doff[j], lbase + j * NW * 64 * 16);
   };
   // Copy j of a tile issued from inside the score loop: the copies of the four waves then
   // spread over the score phase instead of queueing at the vector-memory unit together.
   auto issue_part = [&](const char* src, unsigned lbase, int j) __attribute__((always_inline)) {
-    if (src != nullptr) dma16(src, doff[j], lbase + j * NW * 64 * 16);
+    if (src != nullptr) dma16<HB == 4>(src, doff[j], lbase + j * NW * 64 * 16);
   };
   // e4m3 tiles: LDS chunk p of a staging slot (row p / 36, physical chunk p % 36) is filled
   // from the row's logical chunk swz8(row, p % 36) (the swizzle is its own inverse). Copy
@@ -445,11 +448,11 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
                          __attribute__((always_inline)) {
     if (src == nullptr) return;
     if (j < 4) {
-      dma16(src, doff8[j], lbase + (4 * j + w) * 64 * 16);
+      dma16<HB == 4>(src, doff8[j], lbase + (4 * j + w) * 64 * 16);
     } else if (w < 2) {
-      dma16(src, doff8[j], lbase + (1024 + w * 64) * 16);
+      dma16<HB == 4>(src, doff8[j], lbase + (1024 + w * 64) * 16);
     } else if (lane < 8) {
-      dma16(ssrc, doff8[j], lbase + kF8TileBytes);
+      dma16<HB == 4>(ssrc, doff8[j], lbase + kF8TileBytes);
     }
   };
   // the tile's scales in memory (e4m3 rows), from the slot tile_src_at just looked up

@@ -150,8 +150,10 @@ __global__ __launch_bounds__(64) void gqa_mfma_kernel(
       const int p = 4 * i + pk;
       const unsigned row = static_cast<unsigned>(p < plim ? p : plim) * rb_bytes;
       const unsigned ch = 16u * (ck ^ swz256(p));
-      dma16(gbase, row + koff + ch, lbase + 1024 * i);
-      dma16(gbase, row + voff + ch, lbase + kKBytes + 1024 * i);
+      // K_g and V_g rows are read once (one workgroup per split and group): streamed; the k_r
+      // rows below, which the groups of a unit share through L2, keep the default policy
+      dma16<true>(gbase, row + koff + ch, lbase + 1024 * i);
+      dma16<true>(gbase, row + voff + ch, lbase + kKBytes + 1024 * i);
     }
 #pragma unroll
     for (int i = 0; i < kDmaR; ++i) {

@@ -20,15 +20,27 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 // not order LDS reads of other buffers behind it; the caller waits for these copies itself
 // (vmcnt) before reading what they wrote. M0 is declared clobbered rather than saved and
 // restored (two scalar instructions fewer per copy): the compiler sets it again wherever it
-// needs it.
+// needs it. kStream: the copy carries the non-temporal hint, for data that one workgroup reads
+// once (a streamed cache tile), so that it does not displace what other workgroups share.
+template <bool kStream = false>
 __device__ __forceinline__ void dma16(const char* gbase, unsigned off, unsigned lds) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
-      :
-      : "s"(lds), "v"(off), "s"(gbase)
-      : "memory", "m0");
+  if constexpr (kStream) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt"
+        :
+        : "s"(lds), "v"(off), "s"(gbase)
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(lds), "v"(off), "s"(gbase)
+        : "memory", "m0");
+  }
 }
 
 __device__ __forceinline__ unsigned lds_addr(const char* p) {

@@ -49,12 +49,12 @@ def test_choices_follow_the_summary():
 
 def test_default_rates_pick_the_measured_faster_path():
     """MI355X defaults (the rates the kernels sustain) at H = 128, G = 8 and 32,768 cached
-    positions: the absorbed path for s_q = 1 and 2, the GQA path for s_q = 4 and 8, which is
-    what timing both paths on the chip shows."""
+    positions: the absorbed path for s_q = 1, the GQA path for s_q = 2, 4 and 8, which is what
+    timing both paths on the chip shows (at s_q = 2 the streamed GQA decode, 0.65 ms, is a few
+    percent ahead of the absorbed one, 0.67 ms)."""
     L = 32768
-    for s_q in (1, 2):
-        assert M.mla_select_path(dims(8), s_q, L)[0] == M.MLA_PATH_ABSORBED
-    for s_q in (4, 8):
+    assert M.mla_select_path(dims(8), 1, L)[0] == M.MLA_PATH_ABSORBED
+    for s_q in (2, 4, 8):
         assert M.mla_select_path(dims(8), s_q, L)[0] == M.MLA_PATH_GQA
 
 
