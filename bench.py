@@ -485,6 +485,40 @@ def measure_layer(w, d, step, x_new, dev, torch):
             "output_project_ms": ms_o, "output_project_weight_GBps": bo / (ms_o * 1e-3) / 1e9}
 
 
+def mtp_rows(dev, torch, reps=5):
+    """The absorbed decode (mla_decode, planned splits) on gqla-g8 at s_q = 1, 2 and 4: the
+    s_q query tokens of a sequence attend over one cache, so the HBM bytes of the cache stay
+    those of one read while the FLOPs grow with s_q. Each row carries its binding roofline;
+    under a counter pass (FETCH_SIZE) the launches run in this order, reps + 2 per s_q."""
+    import workloads as W
+    from mla_latent_kv_21_amd import accounting as A
+    from mla_latent_kv_21_amd import binding as M
+    g = lambda a: (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(dev)
+    w = W.WORKLOADS["gqla-g8"]
+    lens = W.seq_lens(w)
+    table, nb = W.block_table(w, lens)
+    cache = W.cache_pool_device(w, nb, dev)
+    tab, lens_d = g(table), g(lens)
+    w_uv = g(W.weights(w)["w_uv"])
+    res = []
+    for s_q in (1, 2, 4):
+        ws_ = w.replace(s_q=s_q)
+        d = M.dims_of(ws_)
+        q_abs = g(W.absorbed_queries(ws_))
+        out = torch.empty(w.batch, s_q, w.n_heads, w.d_v, dtype=w.torch_dtype, device=dev)
+        wsa = torch.empty(M.mla_decode_workspace_bytes(d, w.batch, s_q, 0, table.shape[1]),
+                          dtype=torch.uint8, device=dev)
+        ms = _time_calls(lambda i: M.mla_decode(d, q_abs, cache, tab, lens_d, w_uv, out,
+                                              n_split=0, workspace=wsa), reps, torch)
+        tr = A.decode_traffic(lens, s_q, w.n_heads, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt)
+        row = {"s_q": s_q, "ms": ms, "tokens_per_s": w.batch * s_q / (ms * 1e-3),
+               "cache_bytes": tr["cache_bytes"], "core_bytes": tr["core_bytes"],
+               "flops": tr["flops"], "launches": reps + 2}
+        row.update(A.binding_roofline(tr["bytes"], tr["flops"], ms))
+        res.append(row)
+    return {"workload": w.name, "call": "mla_decode (planned splits)", "cases": res}
+
+
 def select_paths(dev, torch, w, lens, table, cache, gqa, tab, lens_d, wts):
     """Both decode paths of the GQLA workload timed at s_q = 1, 2, 4, 8 (the absorbed one with
     planned splits, the GQA one with the automatic split count), beside mla_select_path's
@@ -545,10 +579,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true",
                     help="skip timing the path's other rows on their own workloads")
-    ap.add_argument("--rows", choices=("all", "layer", "prefill", "expand", "none"),
+    ap.add_argument("--rows", choices=("all", "layer", "prefill", "expand", "mtp", "none"),
                     default="all",
                     help="rows timed after the step: all of them, only the decode layer, only "
-                         "the prefill, only the GQA expansion (gqla-g8), or none")
+                         "the prefill, only the GQA expansion (gqla-g8), only the absorbed "
+                         "decode of gqla-g8 at s_q = 1, 2, 4, or none")
     ap.add_argument("--power-seconds", type=float, default=2.0,
                     help="run the split-K core back to back for this long while sampling board "
                          "power and shader clock with amd-smi (0: skip)")
@@ -686,6 +721,8 @@ def main():
             rec["rows"]["prefill"] = measure_prefill(dev, torch)
         elif rows == "expand":
             rec["rows"]["gqla_expand"], _, _ = expand_row(dev, torch, W.WORKLOADS["gqla-g8"])
+        elif rows == "mtp":
+            rec["rows"]["absorbed_mtp"] = mtp_rows(dev, torch)
         else:
             rec["rows"]["decode_layer"] = measure_layer(w, d, step, x_new, dev, torch)
     if args.copy_calibration_mib > 0:

@@ -131,13 +131,15 @@ struct SoftState {
 
 // kFp8: the cache rows are e4m3 bytes with one fp32 power-of-two scale per position
 // (`scales`, indexed like the cache slots); see the e4m3 variant above.
+// kNT: the cache-tile copies carry the non-temporal hint (H = 128 with one query row per
+// sequence, where each tile has one reader).
 // kApp: a decode step whose s_q new tokens (positions L - s_q .. L - 1 of each sequence, token
 // n = b s_q + i) were projected but not yet written: every workgroup first forms the new rows
 // inside its own range from the projection's partial sums (`app`), exactly as the append's
 // finalize does (with kFp8, quantised to e4m3 bytes and a scale by the finalize's rule),
 // stores them at their slots and waits for the stores before its copies read them.
 // Workgroups of several query rows may form the same row; they store the same bytes.
-template <int HB, bool kFp8, bool kApp>
+template <int HB, bool kFp8, bool kApp, bool kNT>
 __global__ __launch_bounds__(waves_of(HB) * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ cache,
                         const float* __restrict__ scales, StepRows app,
@@ -416,18 +418,21 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
     const int jb = pos0 / bs;
     return tile_src_at(pos0, jb, pos0 - jb * bs, nvalid);
   };
-  // Every cache tile is copied once, by one workgroup. At H = 128 the copies carry the
-  // non-temporal hint (measured faster there: the long-128k step by ≈ 3 %); with fewer head
-  // blocks they keep the default policy, which measured as fast or faster.
+  // At H = 128 with one query row per sequence every cache tile is copied once, by one
+  // workgroup, and the copies carry the non-temporal hint (measured faster there: the
+  // long-128k step by ≈ 3 %). With several query rows per sequence (s_q > 1) the rows'
+  // workgroups of one split read the same tiles on one XCD and the copies keep the default
+  // policy, so that a tile stays in L2 for the other rows; with fewer head blocks the
+  // default policy measured as fast or faster.
   auto issue_tile = [&](const char* src, char* slot) __attribute__((always_inline)) {
     const unsigned lbase = lds_addr(slot) + w * 64 * 16;
 #pragma unroll
-    for (int j = 0; j < kDma; ++j) dma16<HB == 4>(src, doff[j], lbase + j * NW * 64 * 16);
+    for (int j = 0; j < kDma; ++j) dma16<kNT>(src, doff[j], lbase + j * NW * 64 * 16);
   };
   // Copy j of a tile issued from inside the score loop: the copies of the four waves then
   // spread over the score phase instead of queueing at the vector-memory unit together.
   auto issue_part = [&](const char* src, unsigned lbase, int j) __attribute__((always_inline)) {
-    if (src != nullptr) dma16<HB == 4>(src, doff[j], lbase + j * NW * 64 * 16);
+    if (src != nullptr) dma16<kNT>(src, doff[j], lbase + j * NW * 64 * 16);
   };
   // e4m3 tiles: LDS chunk p of a staging slot (row p / 36, physical chunk p % 36) is filled
   // from the row's logical chunk swz8(row, p % 36) (the swizzle is its own inverse). Copy
@@ -448,11 +453,11 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
                          __attribute__((always_inline)) {
     if (src == nullptr) return;
     if (j < 4) {
-      dma16<HB == 4>(src, doff8[j], lbase + (4 * j + w) * 64 * 16);
+      dma16<kNT>(src, doff8[j], lbase + (4 * j + w) * 64 * 16);
     } else if (w < 2) {
-      dma16<HB == 4>(src, doff8[j], lbase + (1024 + w * 64) * 16);
+      dma16<kNT>(src, doff8[j], lbase + (1024 + w * 64) * 16);
     } else if (lane < 8) {
-      dma16<HB == 4>(ssrc, doff8[j], lbase + kF8TileBytes);
+      dma16<kNT>(ssrc, doff8[j], lbase + kF8TileBytes);
     }
   };
   // the tile's scales in memory (e4m3 rows), from the slot tile_src_at just looked up
@@ -872,12 +877,26 @@ hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void*
   const StepRows none{};
   const float scale_log2 = softmax_scale_of(d) * 1.4426950408889634f;
   const dim3 grid = plan != nullptr ? dim3(kPlanSlots) : dim3(n_split, s_q, batch);
-#define MLA_LAUNCH(HB_, FP8_, APP_)                                                          \
-  hipLaunchKernelGGL((decode_mfma_kernel<HB_, FP8_, APP_>), grid, dim3(64 * waves_of(HB_)), 0, s,\
+#define MLA_LAUNCH1(HB_, FP8_, APP_, NT_)                                                    \
+  hipLaunchKernelGGL((decode_mfma_kernel<HB_, FP8_, APP_, NT_>), grid, dim3(64 * waves_of(HB_)), \
+                     0, s,                                                                       \
                      static_cast<const uint16_t*>(q_abs), static_cast<const uint16_t*>(cache), \
                      scales, app != nullptr ? *app : none, table, seq_lens, num_blocks,        \
                      max_blocks, d.block_size, s_q, n_split, scale_log2,                       \
                      static_cast<uint16_t*>(part_o), part_lse, redo, batch, plan)
+  // H = 128: streaming copies when each tile has one reader (s_q = 1)
+#ifdef MLA_NT_ALWAYS
+  const bool nt = true;
+#else
+  const bool nt = s_q == 1;
+#endif
+#define MLA_LAUNCH(HB_, FP8_, APP_)    \
+  do {                                 \
+    if (nt)                            \
+      MLA_LAUNCH1(HB_, FP8_, APP_, true);  \
+    else                               \
+      MLA_LAUNCH1(HB_, FP8_, APP_, false); \
+  } while (0)
   if (app != nullptr && scales != nullptr) {
     MLA_LAUNCH(4, true, true);   // e4m3 rows formed in the core: H = 128
   } else if (app != nullptr) {
@@ -887,11 +906,12 @@ hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void*
   } else {
     switch (d.n_heads) {
       case 128: MLA_LAUNCH(4, false, false); break;
-      case 64: MLA_LAUNCH(2, false, false); break;
-      default: MLA_LAUNCH(1, false, false); break;
+      case 64: MLA_LAUNCH1(2, false, false, false); break;
+      default: MLA_LAUNCH1(1, false, false, false); break;
     }
   }
 #undef MLA_LAUNCH
+#undef MLA_LAUNCH1
   return hipGetLastError();
 }
 

@@ -60,8 +60,8 @@ def test_no_private_segment(asm, src):
 
 
 def test_the_core_variants_are_all_there(asm):
-    """The split-K core's six instantiations (one, two and four waves; the e4m3 cache; the
-    decode step's row forming over bf16 and over e4m3 rows) are all compiled and so all checked
-    above."""
+    """The split-K core's ten instantiations (one and two head blocks; four head blocks over
+    bf16 and e4m3 rows, plain and forming a decode step's new rows, each with streaming and with
+    default-policy tile copies) are all compiled and so all checked above."""
     names = [n for n, _ in kernels(asm["decode_mfma.hip"])]
-    assert len([n for n in names if "decode_mfma_kernel" in n]) == 6
+    assert len([n for n in names if "decode_mfma_kernel" in n]) == 10
