@@ -237,24 +237,29 @@ void decode_mfma_kernel(const uint16_t* __restrict__ q_abs, const uint16_t* __re
       const int n = b * s_q + (p - (L - s_q));
       const int64_t slot = cache_slot(table, max_blocks, bs, num_blocks, b, p);
       // column c = threadIdx.x + 256 j: the partial sums in the fixed order k = 0, 1, ...
+      // The three columns' partials are requested together, kYB per column at a time (one
+      // round trip for d_model <= 8,192): only this workgroup forms the row, and its copies
+      // wait for it.
+      constexpr int kYB = 32;
       float y[3];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        const int c = threadIdx.x + 256 * j;
-        y[j] = 0.f;
-        if (c < kRowElems) {
-          for (int kk = 0; kk < app.n_ksplit; kk += 16) {
-            float v[16];
+      for (int j = 0; j < 3; ++j) y[j] = 0.f;
+      for (int kk = 0; kk < app.n_ksplit; kk += kYB) {
+        float v[3][kYB];
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-              v[u] = kk + u < app.n_ksplit
-                         ? yp[(static_cast<int64_t>(kk + u) * n_tok + n) * kRowElems + c]
-                         : 0.f;
+        for (int j = 0; j < 3; ++j) {
+          const int c = threadIdx.x + 256 * j;
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-              if (kk + u < app.n_ksplit) y[j] += v[u];
-          }
+          for (int u = 0; u < kYB; ++u)
+            v[j][u] = c < kRowElems && kk + u < app.n_ksplit
+                          ? yp[(static_cast<int64_t>(kk + u) * n_tok + n) * kRowElems + c]
+                          : 0.f;
         }
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+#pragma unroll
+          for (int u = 0; u < kYB; ++u)
+            if (kk + u < app.n_ksplit) y[j] += v[j][u];
       }
       // the latent's sum of squares: 64-column block w + 4 j by a butterfly over wave w, then
       // the eight blocks in order
