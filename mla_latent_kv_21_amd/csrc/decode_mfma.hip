@@ -890,11 +890,7 @@ hipError_t launch_decode_mfma(const mla_dims& d, int batch, int s_q, const void*
                      max_blocks, d.block_size, s_q, n_split, scale_log2,                       \
                      static_cast<uint16_t*>(part_o), part_lse, redo, batch, plan)
   // H = 128: streaming copies when each tile has one reader (s_q = 1)
-#ifdef MLA_NT_ALWAYS
-  const bool nt = true;
-#else
   const bool nt = s_q == 1;
-#endif
 #define MLA_LAUNCH(HB_, FP8_, APP_)    \
   do {                                 \
     if (nt)                            \
