@@ -436,7 +436,7 @@ def measure_fp8_step(w, d, lens, cache, tab, lens_d, nb, ns, step_args, n_steps,
     tr = A.decode_traffic(lens, w.s_q, w.n_heads, w.d_c, w.d_r, w.d_v, w.n_groups, w.elt,
                           row_bytes=A.fp8_row_bytes(w.d_c, w.d_r))
     r = {"workload": w.name, "cache": "e4m3 + fp32 scale per position",
-         "calls": "mla_decode_step_fp8 (project_absorb, decode_mfma_kernel<4, true, true>, "
+         "calls": "mla_decode_step_fp8 (project_absorb, decode_mfma_kernel<4, true, true, NT>, "
                   "merge_project_kernel)",
          "ms_per_step": ms, "tokens_per_s": w.batch * w.s_q / (ms * 1e-3),
          "core_launch_stats": core, "core_bytes_per_launch": tr["core_bytes"],
